@@ -1,0 +1,245 @@
+"""CPU oracle for the weight-only quantized linear layer (ctypes wrapper).
+
+TEST INFRASTRUCTURE ONLY: tests/, __graft_entry__.smoke() and bench.py's
+cpu_baseline leg are the only permitted users. The product package
+(spec_verify_amd) never imports this module, and this module never imports the
+product package. The arithmetic lives in ``oracle.c`` (plain C, built with gcc,
+OpenMP over output columns); every function there writes out the plain
+definition of the quantized matmul with k ascending.
+
+Functions with no pin (see tests/test_oracle_pins.py): none -- every exported
+computation is checked against closed forms, brute force, library routines or
+the pages' stated format rules. The conventions themselves (zero point 8, nibble
+order, scale layout) are readings of the pages and are not pinned against a real
+checkpoint, of which there is none here.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+_lib = None
+
+_i64 = ctypes.c_int64
+_int = ctypes.c_int
+_p = ctypes.c_void_p
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        from . import build as _build
+        _build.build()
+    lib = ctypes.CDLL(LIB_PATH)
+    lib.oracle_bf16_to_f64.restype = ctypes.c_double
+    lib.oracle_bf16_to_f64.argtypes = [ctypes.c_uint16]
+    lib.oracle_fp16_to_f64.restype = ctypes.c_double
+    lib.oracle_fp16_to_f64.argtypes = [ctypes.c_uint16]
+    lib.oracle_e4m3_to_f64.restype = ctypes.c_double
+    lib.oracle_e4m3_to_f64.argtypes = [ctypes.c_uint8]
+    lib.oracle_e8m0_to_f64.restype = ctypes.c_double
+    lib.oracle_e8m0_to_f64.argtypes = [ctypes.c_uint8]
+    lib.oracle_bf16_rne.restype = ctypes.c_uint16
+    lib.oracle_bf16_rne.argtypes = [ctypes.c_float]
+    lib.oracle_bf16_rne_array.restype = None
+    lib.oracle_bf16_rne_array.argtypes = [_p, _p, _i64]
+    lib.oracle_num_threads.restype = _int
+    lib.oracle_set_num_threads.argtypes = [_int]
+    lib.oracle_q4_unpack.argtypes = [_p, _p, _i64, _i64]
+    lib.oracle_w4a16.restype = _int
+    lib.oracle_w4a16.argtypes = [_p, _p, _p, _i64, _i64, _i64, _int, _p, _p]
+    lib.oracle_w4a16_points.restype = _int
+    lib.oracle_w4a16_points.argtypes = [_p, _p, _p, _i64, _i64, _i64, _int, _p, _p, _i64, _p, _p]
+    lib.oracle_mxfp8.restype = _int
+    lib.oracle_mxfp8.argtypes = [_p, _p, _p, _i64, _i64, _i64, _p, _p]
+    lib.oracle_mxfp8_points.restype = _int
+    lib.oracle_mxfp8_points.argtypes = [_p, _p, _p, _i64, _i64, _i64, _p, _p, _i64, _p, _p]
+    lib.oracle_q4_repack.restype = _int
+    lib.oracle_q4_repack.argtypes = [_p, _p, _i64, _i64]
+    lib.oracle_q4_unrepack.restype = _int
+    lib.oracle_q4_unrepack.argtypes = [_p, _p, _i64, _i64]
+    _lib = lib
+    return lib
+
+
+def _c(a, dtype):
+    a = np.ascontiguousarray(a)
+    if a.dtype != np.dtype(dtype):
+        raise TypeError(f"expected {np.dtype(dtype)}, got {a.dtype}")
+    return a
+
+
+def _ptr(a):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def num_threads() -> int:
+    return _load().oracle_num_threads()
+
+
+def set_num_threads(n: int) -> None:
+    _load().oracle_set_num_threads(int(n))
+
+
+# ---- scalar decoders ---------------------------------------------------------
+
+def bf16_to_f64(b: int) -> float:
+    return _load().oracle_bf16_to_f64(int(b))
+
+
+def fp16_to_f64(h: int) -> float:
+    return _load().oracle_fp16_to_f64(int(h))
+
+
+def e4m3_to_f64(b: int) -> float:
+    return _load().oracle_e4m3_to_f64(int(b))
+
+
+def e8m0_to_f64(b: int) -> float:
+    return _load().oracle_e8m0_to_f64(int(b))
+
+
+def e4m3_table() -> np.ndarray:
+    return np.array([e4m3_to_f64(b) for b in range(256)], dtype=np.float64)
+
+
+def bf16_rne(f) -> np.ndarray:
+    """fp32 values -> bf16 bit patterns (round to nearest even)."""
+    f = np.ascontiguousarray(f, dtype=np.float32)
+    out = np.empty(f.shape, dtype=np.uint16)
+    _load().oracle_bf16_rne_array(_ptr(f), _ptr(out), f.size)
+    return out
+
+
+def bf16_bits_to_f64(b) -> np.ndarray:
+    b = np.ascontiguousarray(b, dtype=np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+# ---- W4A16 -------------------------------------------------------------------
+
+def q4_unpack(qweight: np.ndarray) -> np.ndarray:
+    qweight = _c(qweight, np.int32)
+    K8, N = qweight.shape
+    q = np.empty((K8 * 8, N), dtype=np.uint8)
+    _load().oracle_q4_unpack(_ptr(qweight), _ptr(q), N, K8 * 8)
+    return q
+
+
+def w4a16(x: np.ndarray, qweight: np.ndarray, scales: np.ndarray, group_size: int = 128):
+    """(y64, y32) for bf16 x [M,K] (uint16 bits), GPTQ words [K/8,N], fp16 scales [K/G,N]."""
+    x = _c(x, np.uint16)
+    qweight = _c(qweight, np.int32)
+    scales = _c(scales, np.uint16)
+    M, K = x.shape
+    N = qweight.shape[1]
+    if qweight.shape[0] * 8 != K or scales.shape != (K // group_size, N):
+        raise ValueError("shape mismatch")
+    y64 = np.empty((M, N), dtype=np.float64)
+    y32 = np.empty((M, N), dtype=np.float32)
+    rc = _load().oracle_w4a16(_ptr(x), _ptr(qweight), _ptr(scales), M, N, K, group_size,
+                              _ptr(y64), _ptr(y32))
+    if rc:
+        raise ValueError("oracle_w4a16 rejected its arguments")
+    return y64, y32
+
+
+def w4a16_points(x, qweight, scales, group_size, rows, cols):
+    x = _c(x, np.uint16)
+    qweight = _c(qweight, np.int32)
+    scales = _c(scales, np.uint16)
+    rows = _c(np.asarray(rows, dtype=np.int64), np.int64)
+    cols = _c(np.asarray(cols, dtype=np.int64), np.int64)
+    M, K = x.shape
+    N = qweight.shape[1]
+    if qweight.shape[0] * 8 != K or scales.shape != (K // group_size, N) or rows.shape != cols.shape:
+        raise ValueError("shape mismatch")
+    y64 = np.empty(rows.shape, dtype=np.float64)
+    y32 = np.empty(rows.shape, dtype=np.float32)
+    rc = _load().oracle_w4a16_points(_ptr(x), _ptr(qweight), _ptr(scales), M, N, K, group_size,
+                                     _ptr(rows), _ptr(cols), rows.size, _ptr(y64), _ptr(y32))
+    if rc:
+        raise ValueError("oracle_w4a16_points rejected its arguments")
+    return y64, y32
+
+
+# ---- MXFP8 -------------------------------------------------------------------
+
+def mxfp8(x: np.ndarray, w: np.ndarray, scales: np.ndarray):
+    """(y64, y32) for bf16 x [M,K], E4M3FN codes [N,K], E8M0 codes [N,K/32]."""
+    x = _c(x, np.uint16)
+    w = _c(w, np.uint8)
+    scales = _c(scales, np.uint8)
+    M, K = x.shape
+    N = w.shape[0]
+    if w.shape != (N, K) or scales.shape != (N, K // 32):
+        raise ValueError("shape mismatch")
+    y64 = np.empty((M, N), dtype=np.float64)
+    y32 = np.empty((M, N), dtype=np.float32)
+    rc = _load().oracle_mxfp8(_ptr(x), _ptr(w), _ptr(scales), M, N, K, _ptr(y64), _ptr(y32))
+    if rc:
+        raise ValueError("oracle_mxfp8 rejected its arguments")
+    return y64, y32
+
+
+def mxfp8_points(x, w, scales, rows, cols):
+    x = _c(x, np.uint16)
+    w = _c(w, np.uint8)
+    scales = _c(scales, np.uint8)
+    rows = _c(np.asarray(rows, dtype=np.int64), np.int64)
+    cols = _c(np.asarray(cols, dtype=np.int64), np.int64)
+    M, K = x.shape
+    N = w.shape[0]
+    if w.shape != (N, K) or scales.shape != (N, K // 32) or rows.shape != cols.shape:
+        raise ValueError("shape mismatch")
+    y64 = np.empty(rows.shape, dtype=np.float64)
+    y32 = np.empty(rows.shape, dtype=np.float32)
+    rc = _load().oracle_mxfp8_points(_ptr(x), _ptr(w), _ptr(scales), M, N, K,
+                                     _ptr(rows), _ptr(cols), rows.size, _ptr(y64), _ptr(y32))
+    if rc:
+        raise ValueError("oracle_mxfp8_points rejected its arguments")
+    return y64, y32
+
+
+# ---- device layout of packed INT4 weights ------------------------------------
+
+def q4_repack(qweight: np.ndarray) -> np.ndarray:
+    """GPTQ words [K/8, N] -> tiled words (flat int32, K*N/8 entries)."""
+    qweight = _c(qweight, np.int32)
+    K8, N = qweight.shape
+    out = np.empty(K8 * N, dtype=np.int32)
+    if _load().oracle_q4_repack(_ptr(qweight), _ptr(out), N, K8 * 8):
+        raise ValueError("repack needs N % 16 == 0 and K % 128 == 0")
+    return out
+
+
+def q4_unrepack(tiled: np.ndarray, N: int, K: int) -> np.ndarray:
+    tiled = _c(tiled, np.int32).reshape(-1)
+    if tiled.size != K * N // 8:
+        raise ValueError("size mismatch")
+    out = np.empty((K // 8, N), dtype=np.int32)
+    if _load().oracle_q4_unrepack(_ptr(tiled), _ptr(out), N, K):
+        raise ValueError("unrepack needs N % 16 == 0 and K % 128 == 0")
+    return out
+
+
+# ---- the parity gate ---------------------------------------------------------
+
+def gate(out_bits: np.ndarray, y_ref: np.ndarray, rel_tol: float = 2e-2):
+    """max |fp32(out) - y_ref| <= rel_tol * RMS(y_ref) over all outputs.
+
+    Returns (ok, max_err, rms). The tolerance is the one the layer's accuracy
+    target states for bf16 outputs against an fp32-accumulated reference.
+    """
+    out = bf16_bits_to_f64(out_bits)
+    y_ref = np.asarray(y_ref, dtype=np.float64)
+    rms = float(np.sqrt(np.mean(y_ref * y_ref))) if y_ref.size else 0.0
+    err = float(np.max(np.abs(out - y_ref))) if y_ref.size else 0.0
+    return err <= rel_tol * rms, err, rms

@@ -1,0 +1,345 @@
+"""Pins for the CPU oracle: each check ties the oracle to something other than
+itself -- hand-worked values, closed forms, exact rational brute force, integer
+matmul, BLAS, torch's E4M3 decoder, a summation error bound -- so that a dropped
+term, a wrong sign, a wrong index or a transposed operand fails at least one.
+"""
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rows(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                yield line.split()
+
+
+# ---- P6 / P7: element and scale decoders ------------------------------------
+
+def test_e4m3_e8m0_handworked_points():
+    n = 0
+    for kind, code, value in _rows("e4m3_e8m0_points.txt"):
+        c = int(code, 0)
+        got = oracle.e4m3_to_f64(c) if kind == "e4m3" else oracle.e8m0_to_f64(c)
+        if value == "nan":
+            assert math.isnan(got), (kind, code)
+        else:
+            assert got == float(value), (kind, code, got)
+            if value == "-0":
+                assert math.copysign(1.0, got) < 0
+        n += 1
+    assert n >= 20
+
+
+def test_e4m3_all_codes_closed_form_and_torch():
+    torch = pytest.importorskip("torch")
+    table = oracle.e4m3_table()
+    # closed form from the OCP definition, computed a different way: enumerate
+    # (sign, exponent, mantissa) fields explicitly
+    for b in range(256):
+        s, e, m = b >> 7, (b >> 3) & 15, b & 7
+        if e == 15 and m == 7:
+            assert math.isnan(table[b])
+            continue
+        mag = (m / 8.0) * 2.0 ** -6 if e == 0 else (1 + m / 8.0) * 2.0 ** (e - 7)
+        assert table[b] == (-mag if s else mag), b
+    codes = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn)
+    ref = codes.to(torch.float32).double().numpy()
+    finite = ~np.isnan(ref)
+    assert finite.sum() == 254
+    np.testing.assert_array_equal(table[finite], ref[finite])
+    assert np.isnan(table[~finite]).all()
+
+
+def test_e8m0_all_codes():
+    for b in range(255):
+        assert oracle.e8m0_to_f64(b) == math.ldexp(1.0, b - 127)
+    assert math.isnan(oracle.e8m0_to_f64(255))
+
+
+def test_fp16_and_bf16_decoders_against_numpy():
+    h = np.arange(65536, dtype=np.uint16)
+    ref = h.view(np.float16).astype(np.float64)
+    got = np.array([oracle.fp16_to_f64(int(v)) for v in h[::97]])
+    r = ref[::97]
+    same = (got == r) | (np.isnan(got) & np.isnan(r))
+    assert same.all()
+    for b in (0x0000, 0x3F80, 0xBF80, 0x4300, 0x0001, 0x7F7F):
+        ref = np.array([b], dtype=np.uint32) << 16
+        assert oracle.bf16_to_f64(b) == float(ref.view(np.float32)[0])
+
+
+def test_bf16_rne_ties_and_carries():
+    # 257 is halfway between bf16 neighbours 256 and 258 -> ties to even = 256
+    # 259 is halfway between 258 and 260 -> ties to even = 260
+    vals = np.array([257.0, 259.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -257.0, 0.0], np.float32)
+    out = oracle.bf16_rne(vals)
+    back = oracle.bf16_bits_to_f64(out)
+    np.testing.assert_array_equal(back, [256.0, 260.0, 1.0, 1.0 + 2 ** -6, -256.0, 0.0])
+    # against an independent rounding: nearest representable by exhaustive search
+    rng = np.random.default_rng(7)
+    f = rng.standard_normal(2000).astype(np.float32) * 100
+    got = oracle.bf16_bits_to_f64(oracle.bf16_rne(f))
+    u = f.view(np.uint32)
+    lo = ((u >> 16) << 16).view(np.float32).astype(np.float64)
+    hi = (((u >> 16) + 1) << 16).view(np.float32).astype(np.float64)
+    fd = f.astype(np.float64)
+    dlo, dhi = np.abs(fd - lo), np.abs(hi - fd)
+    exp = np.where(dlo < dhi, lo, np.where(dhi < dlo, hi, np.where(((u >> 16) & 1) == 0, lo, hi)))
+    np.testing.assert_array_equal(got, exp)
+
+
+# ---- P1: GPTQ packing and nibble order --------------------------------------
+
+def test_unpack_roundtrip_and_one_hot_nibbles():
+    rng = np.random.default_rng(1)
+    q = rng.integers(0, 16, size=(64, 24), dtype=np.uint8)
+    np.testing.assert_array_equal(oracle.q4_unpack(synth.pack_gptq(q)), q)
+    for i in range(8):
+        word = np.zeros((1, 1), dtype=np.uint32)
+        word[0, 0] = 0xB << (4 * i)
+        got = oracle.q4_unpack(word.view(np.int32))[:, 0]
+        exp = np.zeros(8, dtype=np.uint8)
+        exp[i] = 0xB
+        np.testing.assert_array_equal(got, exp)
+
+
+def test_w4a16_handworked_cases():
+    for case, word, scale, xpat, expected in _rows("w4a16_handworked.txt"):
+        qw = np.array([[int(word, 0)]], dtype=np.uint32).view(np.int32)
+        sc = np.array([[int(scale, 0)]], dtype=np.uint16)
+        xs = {"ones": [1.0] * 8, "kplus1": [k + 1.0 for k in range(8)],
+              "alternating": [1.0, -1.0] * 4}[xpat]
+        x = synth.bf16_bits(np.array([xs], dtype=np.float32))
+        y64, y32 = oracle.w4a16(x, qw, sc, group_size=8)
+        assert y64[0, 0] == float(expected), case
+        assert y32[0, 0] == float(expected), case
+
+
+# ---- P2: identity-scale integer case, exact ---------------------------------
+
+@pytest.mark.parametrize("M,K,N,G", [(3, 256, 48, 128), (5, 384, 32, 64), (2, 128, 16, 32)])
+def test_integer_exact_matches_int64_matmul(M, K, N, G):
+    inp = synth.gen_w4a16(11 + M, M, K, N, G, kind="intexact", keep_q=True)
+    xi = oracle.bf16_bits_to_f64(inp.x).astype(np.int64)
+    exact = xi @ (inp.q.astype(np.int64) - 8)           # library integer matmul
+    y64, y32 = oracle.w4a16(inp.x, inp.qweight, inp.scales, G)
+    np.testing.assert_array_equal(y64, exact.astype(np.float64))
+    np.testing.assert_array_equal(y32.astype(np.float64), exact.astype(np.float64))
+
+
+def test_integer_exact_largest_shape_stays_below_2p24():
+    # |y| <= 8 * 4 * 17408 = 557056 < 2^24: fp32 accumulation is exact in any order
+    assert 8 * 4 * 17408 < 2 ** 24
+
+
+# ---- P3: exact rational brute force on tiny shapes --------------------------
+
+@pytest.mark.parametrize("M,K,N,G", [(1, 128, 16, 128), (2, 256, 8, 128), (2, 64, 4, 32)])
+def test_bruteforce_fraction(M, K, N, G):
+    inp = synth.gen_w4a16(5 * K + N, M, K, N, G, keep_q=True)
+    y64, _ = oracle.w4a16(inp.x, inp.qweight, inp.scales, G)
+    xf = oracle.bf16_bits_to_f64(inp.x)
+    sf = inp.scales.view(np.float16).astype(np.float64)
+    for m in range(M):
+        for n in range(N):
+            acc = Fraction(0)
+            for k in range(K):
+                acc += Fraction(float(xf[m, k])) * (int(inp.q[k, n]) - 8) * Fraction(float(sf[k // G, n]))
+            # y64 is the exact sum rounded once per addition in fp64: within K ulps
+            assert abs(Fraction(y64[m, n]) - acc) <= Fraction(K) * Fraction(2) ** -52 * (
+                sum(abs(Fraction(float(xf[m, k])) * (int(inp.q[k, n]) - 8) * Fraction(float(sf[k // G, n])))
+                    for k in range(K)) + 1)
+
+
+# ---- P4: closed forms that isolate group and nibble indexing ----------------
+
+def test_constant_code_closed_form():
+    M, K, N, G = 2, 256, 16, 128
+    rng = np.random.default_rng(3)
+    x = synth.bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
+    xf = oracle.bf16_bits_to_f64(x)
+    s = synth.fp16_bits(rng.uniform(0.002, 0.02, (K // G, N)).astype(np.float32))
+    sf = s.view(np.float16).astype(np.float64)
+    for c in (0, 3, 8, 15):
+        q = np.full((K, N), c, dtype=np.uint8)
+        y64, _ = oracle.w4a16(x, synth.pack_gptq(q), s, G)
+        xs = xf.reshape(M, K // G, G).sum(axis=2)          # per-group sums of x
+        exp = (c - 8) * (xs @ sf)
+        np.testing.assert_allclose(y64, exp, rtol=1e-12, atol=1e-12)
+
+
+def test_one_hot_group_scale_and_single_nibble():
+    M, K, N, G = 2, 512, 16, 128
+    rng = np.random.default_rng(4)
+    x = synth.bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
+    xf = oracle.bf16_bits_to_f64(x)
+    q = rng.integers(0, 16, size=(K, N), dtype=np.uint8)
+    for g in range(K // G):
+        s = np.zeros((K // G, N), dtype=np.float32)
+        s[g, :] = 1.0
+        y64, _ = oracle.w4a16(x, synth.pack_gptq(q), synth.fp16_bits(s), G)
+        sl = slice(g * G, (g + 1) * G)
+        exp = xf[:, sl] @ (q[sl].astype(np.float64) - 8)
+        np.testing.assert_allclose(y64, exp, rtol=1e-12, atol=1e-9)
+    # one non-8 nibble at (k*, n*): y[:, n*] = x[:, k*] * (q* - 8) * s, all else 0
+    q = np.full((K, N), 8, dtype=np.uint8)
+    ks, ns, qs = 301, 9, 13
+    q[ks, ns] = qs
+    s = synth.fp16_bits(np.full((K // G, N), 0.25, dtype=np.float32))
+    y64, _ = oracle.w4a16(x, synth.pack_gptq(q), s, G)
+    exp = np.zeros((M, N))
+    exp[:, ns] = xf[:, ks] * (qs - 8) * 0.25
+    np.testing.assert_array_equal(y64, exp)
+
+
+# ---- P5: dense reduction against BLAS ---------------------------------------
+
+def test_reduction_against_blas():
+    M, K, N, G = 4, 1024, 64, 128
+    inp = synth.gen_w4a16(9, M, K, N, G, keep_q=True)
+    y64, _ = oracle.w4a16(inp.x, inp.qweight, inp.scales, G)
+    xf = oracle.bf16_bits_to_f64(inp.x)
+    sf = inp.scales.view(np.float16).astype(np.float64)
+    W = (inp.q.astype(np.float64) - 8) * np.repeat(sf, G, axis=0)
+    ref = xf @ W
+    rms = np.sqrt(np.mean(ref ** 2))
+    assert np.max(np.abs(y64 - ref)) <= 1e-12 * rms
+
+
+def test_fp32_sequential_sum_within_recursive_summation_bound():
+    M, K, N, G = 3, 2048, 32, 128
+    inp = synth.gen_w4a16(21, M, K, N, G, keep_q=True)
+    y64, y32 = oracle.w4a16(inp.x, inp.qweight, inp.scales, G)
+    xf = oracle.bf16_bits_to_f64(inp.x)
+    sf = inp.scales.view(np.float16).astype(np.float64)
+    W = (inp.q.astype(np.float64) - 8) * np.repeat(sf, G, axis=0)
+    absum = np.abs(xf) @ np.abs(W)
+    u = 2.0 ** -24
+    bound = (K - 1) * u / (1 - (K - 1) * u) * absum
+    assert np.all(np.abs(y32.astype(np.float64) - y64) <= bound + 1e-300)
+    assert np.any(y32.astype(np.float64) != y64)   # the fp32 mode really rounds
+
+
+# ---- P8: MXFP8 ---------------------------------------------------------------
+
+def test_mxfp8_integer_exact():
+    M, K, N = 3, 256, 16
+    inp = synth.gen_mxfp8(31, M, K, N, kind="intexact")
+    table = oracle.e4m3_table()
+    wi = table[inp.w].astype(np.int64)                  # codes of -8..8 decode exactly
+    assert np.all(np.abs(wi) <= 8)
+    xi = oracle.bf16_bits_to_f64(inp.x).astype(np.int64)
+    exact = xi @ wi.T
+    y64, y32 = oracle.mxfp8(inp.x, inp.w, inp.scales)
+    np.testing.assert_array_equal(y64, exact.astype(np.float64))
+    np.testing.assert_array_equal(y32.astype(np.float64), exact.astype(np.float64))
+
+
+def test_mxfp8_block_scale_indexing_closed_form():
+    # one block scale raised by 2^3 multiplies exactly that block's contribution by 8
+    M, K, N = 2, 128, 8
+    inp = synth.gen_mxfp8(32, M, K, N)
+    base, _ = oracle.mxfp8(inp.x, inp.w, inp.scales)
+    sc = inp.scales.copy()
+    n0, b0 = 5, 2
+    sc[n0, b0] += 3
+    bumped, _ = oracle.mxfp8(inp.x, inp.w, sc)
+    table = oracle.e4m3_table()
+    xf = oracle.bf16_bits_to_f64(inp.x)
+    blk = slice(32 * b0, 32 * b0 + 32)
+    contrib = xf[:, blk] @ (table[inp.w[n0, blk]] * 2.0 ** (int(inp.scales[n0, b0]) - 127))
+    np.testing.assert_allclose(bumped[:, n0] - base[:, n0], 7 * contrib, rtol=1e-9, atol=1e-12)
+    other = [n for n in range(N) if n != n0]
+    np.testing.assert_array_equal(bumped[:, other], base[:, other])
+
+
+def test_mxfp8_against_blas():
+    M, K, N = 4, 512, 160
+    inp = synth.gen_mxfp8(33, M, K, N)
+    y64, _ = oracle.mxfp8(inp.x, inp.w, inp.scales)
+    table = oracle.e4m3_table()
+    W = table[inp.w] * np.exp2(np.repeat(inp.scales.astype(np.float64) - 127, 32, axis=1))
+    ref = oracle.bf16_bits_to_f64(inp.x) @ W.T
+    assert np.max(np.abs(y64 - ref)) <= 1e-12 * np.sqrt(np.mean(ref ** 2))
+
+
+# ---- P9: invariances ---------------------------------------------------------
+
+def test_power_of_two_scaling_of_x_is_exact():
+    inp = synth.gen_w4a16(41, 2, 256, 32, 128)
+    y64, y32 = oracle.w4a16(inp.x, inp.qweight, inp.scales)
+    x4 = synth.bf16_bits(oracle.bf16_bits_to_f64(inp.x).astype(np.float32) * 4)
+    y64b, y32b = oracle.w4a16(x4, inp.qweight, inp.scales)
+    np.testing.assert_array_equal(y64b, 4 * y64)
+    np.testing.assert_array_equal(y32b, 4 * y32)
+
+
+def test_group_aligned_k_permutation():
+    M, K, N, G = 2, 512, 16, 128
+    inp = synth.gen_w4a16(42, M, K, N, G, keep_q=True)
+    y64, _ = oracle.w4a16(inp.x, inp.qweight, inp.scales, G)
+    rng = np.random.default_rng(0)
+    gperm = rng.permutation(K // G)
+    inner = [rng.permutation(G) for _ in range(K // G)]
+    perm = np.concatenate([g * G + inner[i] for i, g in enumerate(gperm)])
+    xp = inp.x[:, perm]
+    qp = inp.q[perm]
+    sp = inp.scales[gperm]
+    y64p, _ = oracle.w4a16(xp, synth.pack_gptq(qp), sp, G)
+    np.testing.assert_allclose(y64p, y64, rtol=0, atol=1e-12 * np.sqrt(np.mean(y64 ** 2)))
+
+
+# ---- P10: the repack layout -------------------------------------------------
+
+def test_repack_handworked_words():
+    N, K = 16, 128
+    k = np.arange(K)[:, None]
+    n = np.arange(N)[None, :]
+    q = ((k + n) % 16).astype(np.uint8)
+    tiled = oracle.q4_repack(synth.pack_gptq(q)).view(np.uint32)
+    cnt = 0
+    for lane, j, word in _rows("q4_tile_words.txt"):
+        assert tiled[int(lane) * 4 + int(j)] == int(word, 0), (lane, j)
+        cnt += 1
+    assert cnt == 3
+
+
+@pytest.mark.parametrize("N,K", [(16, 128), (48, 384), (160, 1280)])
+def test_repack_bijection_and_tile_contents(N, K):
+    rng = np.random.default_rng(N + K)
+    q = rng.integers(0, 16, size=(K, N), dtype=np.uint8)
+    qw = synth.pack_gptq(q)
+    tiled = oracle.q4_repack(qw)
+    np.testing.assert_array_equal(oracle.q4_unrepack(tiled, N, K), qw)
+    assert tiled.size == K * N // 8
+    # independent reading of one random element straight from the layout rule
+    slot_of_e = [0, 4, 1, 5, 2, 6, 3, 7]
+    t = tiled.view(np.uint32)
+    for _ in range(200):
+        kk, nn = int(rng.integers(K)), int(rng.integers(N))
+        nb, kt, r = nn // 16, kk // 128, kk % 128
+        lane = 16 * (r // 32) + nn % 16
+        j, e = (r % 32) // 8, r % 8
+        word = t[((nb * (K // 128) + kt) * 64 + lane) * 4 + j]
+        assert (word >> (4 * slot_of_e[e])) & 15 == q[kk, nn]
+
+
+def test_gate_accepts_rounding_and_rejects_a_wrong_weight():
+    inp = synth.gen_w4a16(51, 1, 5120, 64, 128, keep_q=True)
+    y64, _ = oracle.w4a16(inp.x, inp.qweight, inp.scales)
+    good = oracle.bf16_rne(y64.astype(np.float32))
+    ok, err, rms = oracle.gate(good, y64)
+    assert ok and err <= 2 ** -8 * np.max(np.abs(y64))
+    bad = oracle.bf16_rne((y64 + 0.05 * rms).astype(np.float32))
+    assert not oracle.gate(bad, y64)[0]

@@ -1,0 +1,300 @@
+"""Benchmark of the weight-only quantized linear layer on one MI355X.
+
+A step is one decode step's worth of the hot path: the three W4A16 (INT4, g128)
+GEMVs of a single-stream decode at M=1, K=5120, N in {5120, 6144, 1024}, on
+inputs resident in HBM. Weights rotate through a pool of distinct copies larger
+than 1 GiB so every launch streams them from HBM, not from the 256 MB Infinity
+Cache. `value` is the step's algorithmic bytes (packed weights + scales + x + y,
+each once) per second.
+
+Also reported (stderr table and the JSON line's "workloads" list): per-kernel
+time, GB/s, TFLOP/s and roofline fraction for every named workload (decode,
+M=3/5 verify chunks, M=128 batched verify, MXFP8 at M=1/5/128), and the CPU
+oracle's throughput on a bounded sample (``cpu_baseline``).
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--quick] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, vendor figure
+POOL_BYTES = 1.2 * (1 << 30)
+METRIC = "W4A16 GEMM µs, weight-stream GB/s and % HBM peak at M=1/5/128; TFLOP/s"
+DECODE = ["decode_n5120", "decode_n6144", "decode_n1024"]
+DOMINANT = "decode_n6144"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algo_bytes(w):
+    M, K, N = w["M"], w["K"], w["N"]
+    if w["op"] == "w4a16":
+        return K * N // 2 + (K // 128) * N * 2 + 2 * M * K + 2 * M * N
+    return K * N + (K // 32) * N + 2 * M * K + 2 * M * N
+
+
+def weight_bytes(w):
+    K, N = w["K"], w["N"]
+    if w["op"] == "w4a16":
+        return K * N // 2 + (K // 128) * N * 2
+    return K * N + (K // 32) * N
+
+
+class Problem:
+    """Device-resident inputs of one workload with a rotation pool of weight copies."""
+
+    def __init__(self, torch, svq, name, pool_bytes):
+        self.name = name
+        self.w = synth.WORKLOADS[name]
+        self.torch, self.svq = torch, svq
+        inp = synth.gen_workload(name)
+        self.inp = inp
+        dev = torch.device("cuda:0")
+
+        def d(a):
+            a = np.ascontiguousarray(a)
+            if a.dtype == np.uint16:
+                a = a.view(np.int16)
+            return torch.from_numpy(a).to(dev)
+
+        self.x = d(inp.x)
+        M, K, N = self.w["M"], self.w["K"], self.w["N"]
+        self.out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        ncopy = max(2, int(pool_bytes // max(weight_bytes(self.w), 1)))
+        if self.w["op"] == "w4a16":
+            base_w = svq.q4_repack(d(inp.qweight))
+            base_s = d(inp.scales)
+            self.kernel = svq.w4a16_kernel_name(M, N, K)
+            nb = svq.w4a16_workspace_bytes(M, N, K)
+        else:
+            base_w = d(inp.w)
+            base_s = d(inp.scales)
+            self.kernel = svq.mxfp8_kernel_name(M, N, K)
+            nb = svq.mxfp8_workspace_bytes(M, N, K)
+        self.ws = torch.zeros(max(nb, 256), dtype=torch.uint8, device=dev) if nb else None
+        self.ws_w = [base_w] + [base_w.clone() for _ in range(ncopy - 1)]
+        self.ws_s = [base_s] + [base_s.clone() for _ in range(ncopy - 1)]
+        self.i = 0
+
+    def launch(self, i=None):
+        i = self.i if i is None else i
+        self.i = (self.i + 1) % len(self.ws_w)
+        w = self.w
+        if w["op"] == "w4a16":
+            self.svq.w4a16_gemm(self.x, self.ws_w[i], self.ws_s[i], w["N"], 128, out=self.out,
+                                workspace=self.ws)
+        else:
+            self.svq.mxfp8_gemm(self.x, self.ws_w[i], self.ws_s[i], out=self.out, workspace=self.ws)
+
+    def check(self, oracle):
+        """Parity of the first and last pool copies against the oracle (sampled)."""
+        torch = self.torch
+        inp, w = self.inp, self.w
+        rng = np.random.default_rng(1)
+        rows = rng.integers(0, w["M"], 256)
+        cols = rng.integers(0, w["N"], 256)
+        for i in (0, len(self.ws_w) - 1):
+            self.launch(i)
+            torch.cuda.synchronize()
+            bits = self.out.view(torch.int16).cpu().numpy().view(np.uint16)[rows, cols]
+            if w["op"] == "w4a16":
+                y64, _ = oracle.w4a16_points(inp.x, inp.qweight, inp.scales, 128, rows, cols)
+            else:
+                y64, _ = oracle.mxfp8_points(inp.x, inp.w, inp.scales, rows, cols)
+            ok, err, rms = oracle.gate(bits, y64)
+            if not ok:
+                raise SystemExit(f"parity failure in {self.name} copy {i}: err {err} rms {rms}")
+
+    def release(self):
+        self.ws_w = self.ws_s = None
+
+
+def time_kernel(torch, prob, launches, warmup):
+    """Mean per-launch kernel time (µs) from event pairs around each launch, and
+    the mean time per launch of a back-to-back sequence."""
+    for _ in range(warmup):
+        prob.launch()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(launches)]
+    for a, b in ev:
+        a.record()
+        prob.launch()
+        b.record()
+    torch.cuda.synchronize()
+    per = np.array([a.elapsed_time(b) * 1e3 for a, b in ev])
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(launches):
+        prob.launch()
+    e.record()
+    torch.cuda.synchronize()
+    return float(np.mean(per)), float(np.median(per)), s.elapsed_time(e) * 1e3 / launches
+
+
+def cpu_baseline(budget_s=12.0):
+    """The oracle as it stands, timed on this host on a bounded sample of the decode step."""
+    import oracle
+    probs = [synth.gen_workload(n) for n in DECODE]
+    bytes_step = sum(algo_bytes(synth.WORKLOADS[n]) for n in DECODE)
+    for p in probs:                              # warm-up
+        oracle.w4a16(p.x, p.qweight, p.scales)
+    t0 = time.perf_counter()
+    steps = 0
+    while time.perf_counter() - t0 < budget_s:
+        for p in probs:
+            oracle.w4a16(p.x, p.qweight, p.scales)
+        steps += 1
+    dt = time.perf_counter() - t0
+    return {"value": round(bytes_step * steps / dt / 1e9, 4), "unit": "GB/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{steps} full decode steps (3 GEMVs, M=1, K=5120, N=5120/6144/1024) in {dt:.1f} s; "
+                      "fp64 sums plus the fp32-sequential sum, OpenMP over output columns",
+            "ms_per_step": round(dt / steps * 1e3, 3)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=300)
+    ap.add_argument("--warmup", type=int, default=30)
+    ap.add_argument("--quick", action="store_true", help="decode step only, no per-workload table")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import spec_verify_amd as svq
+    import oracle
+
+    if not os.path.exists(svq.library_path):
+        from spec_verify_amd import build
+        build.build()
+    svq.lib()
+    props = torch.cuda.get_device_properties(0)
+    log(f"device: {props.name} ({getattr(props, 'gcnArchName', '?')}), CUs {props.multi_processor_count}, "
+        f"torch {torch.__version__}, hip {torch.version.hip}")
+
+    # ---- the decode step ----------------------------------------------------
+    probs = [Problem(torch, svq, n, POOL_BYTES / len(DECODE)) for n in DECODE]
+    for p in probs:
+        p.check(oracle)
+    bytes_step = sum(algo_bytes(p.w) for p in probs)
+    dom = probs[DECODE.index(DOMINANT)]
+    for _ in range(args.warmup):
+        for p in probs:
+            p.launch()
+    torch.cuda.synchronize()
+    dom_ev = []
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(args.steps):
+        for p in probs:
+            if p is dom:
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                p.launch()
+                b.record()
+                dom_ev.append((a, b))
+            else:
+                p.launch()
+    end.record()
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(end) / args.steps
+    dom_us = float(np.mean([a.elapsed_time(b) * 1e3 for a, b in dom_ev]))
+    value = bytes_step / (ms_step * 1e-3) / 1e9
+    dom_gbs = algo_bytes(dom.w) / (dom_us * 1e-6) / 1e9
+    log(f"decode step: {ms_step * 1e3:.2f} µs/step, {value:.1f} GB/s; {DOMINANT} ({dom.kernel}) "
+        f"{dom_us:.2f} µs/launch = {dom_gbs:.1f} GB/s ({100 * dom_gbs / HBM_PEAK_GBS:.1f}% of HBM peak)")
+    for p in probs:
+        p.release()
+    torch.cuda.empty_cache()
+
+    # ---- per-workload table ------------------------------------------------------
+    detail = []
+    if not args.quick:
+        names = ["decode_n5120", "decode_n6144", "decode_n1024", "verify3_up", "verify3_down",
+                 "verify5_up", "verify5_down", "batch128_up", "batch128_down", "mxfp8_m1", "mxfp8_m5",
+                 "mxfp8_m128"]
+        log(f"{'workload':15s} {'kernel':22s} {'µs(ev)':>8s} {'µs(b2b)':>8s} {'GB/s':>8s} {'%HBM':>6s} "
+            f"{'TFLOP/s':>8s} {'%MFMA':>6s}")
+        for n in names:
+            p = Problem(torch, svq, n, POOL_BYTES)
+            p.check(oracle)
+            us, med, b2b = time_kernel(torch, p, 200, 20)
+            w = p.w
+            gbs = algo_bytes(w) / (us * 1e-6) / 1e9
+            tfl = 2.0 * w["M"] * w["N"] * w["K"] / (us * 1e-6) / 1e12
+            row = {"workload": n, "op": w["op"], "M": w["M"], "K": w["K"], "N": w["N"], "kernel": p.kernel,
+                   "us": round(us, 3), "us_median": round(med, 3), "us_back_to_back": round(b2b, 3),
+                   "GBps": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+                   "weight_GBps": round(weight_bytes(w) / (us * 1e-6) / 1e9, 1),
+                   "TFLOPs": round(tfl, 2), "mfma_frac": round(tfl / MFMA_BF16_PEAK_TFLOPS, 4)}
+            detail.append(row)
+            log(f"{n:15s} {p.kernel:22s} {us:8.2f} {b2b:8.2f} {gbs:8.1f} {100 * gbs / HBM_PEAK_GBS:6.1f} "
+                f"{tfl:8.2f} {100 * tfl / MFMA_BF16_PEAK_TFLOPS:6.2f}")
+            p.release()
+            del p
+            torch.cuda.empty_cache()
+
+    cpu = None if args.no_cpu else cpu_baseline()
+    if cpu:
+        log(f"cpu oracle: {cpu['value']} GB/s on {cpu['cores']} threads ({cpu['sample']})")
+
+    traffic = None
+    tf_path = os.path.join(ROOT, "profiles", "traffic.json")
+    if os.path.exists(tf_path):
+        with open(tf_path) as f:
+            t = json.load(f).get(DOMINANT)
+        if t and t.get("kernel_source_sha") == _kernel_source_sha():
+            traffic = t.get("bytes_per_launch")
+
+    line = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 6), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "single-stream decode step: three W4A16 g128 GEMVs, M=1, K=5120, "
+                               "N=5120/6144/1024, weights rotated over >1 GiB of copies",
+                   "M": 1, "K": 5120, "N": [5120, 6144, 1024], "group_size": 128,
+                   "bytes_per_step": bytes_step},
+        "roofline": {"bound": "hbm", "achieved": round(dom_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "kernel": dom.kernel, "workload": DOMINANT, "us_per_launch": round(dom_us, 3),
+                     "bytes_per_launch": algo_bytes(dom.w)},
+        "cpu_baseline": cpu,
+        "workloads": detail,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def _kernel_source_sha():
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "spec_verify_amd", "csrc")
+    for n in sorted(os.listdir(csrc)):
+        if n.endswith((".hip", ".h", ".cpp")):
+            with open(os.path.join(csrc, n), "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+if __name__ == "__main__":
+    main()

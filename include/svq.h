@@ -1,0 +1,165 @@
+/*
+ * svq.h -- C ABI of the weight-only quantized linear layer for decode and
+ * speculative-verify shapes on AMD Instinct MI355X (gfx950).
+ *
+ *   y[M][N] = x[M][K] . deq(W)^T     (bf16 x, fp32 accumulation, bf16 y)
+ *
+ * Two weight formats:
+ *  - W4A16: symmetric INT4 with zero point 8, one fp16 scale per group of G
+ *    K-rows (G = 32, 64 or 128), GPTQ words packed 8 per int32 along K, no
+ *    group reordering. GPTQ INT4 card "Qwen3.8-27B-GPTQ-Int4-sym-G128-MTP-BF16",
+ *    section "Quantization contract"; Eole recipe "Qwen3.8-27B and native MTP
+ *    speculative decoding", section "Compressed-tensors INT4 layout".
+ *  - MXFP8: OCP E4M3FN elements with one E8M0 scale per 32 K-elements. MXFP8
+ *    card "Qwen3.8-27B-MXFP8-CT-AutoRound-mtp", opening summary, sections
+ *    "2. Precision plan" (N >= 128, K % 32 == 0) and "8. License and
+ *    attribution" (OCP MX, E8M0 scale per 32-element block).
+ *
+ * M is the number of tokens verified per call: streams x (1 + draft tokens)
+ * (Eole recipe, opening paragraph: the main model verifies a chunk of drafted
+ * tokens). Packed INT4 weights are repacked once at setup, as the Eole recipe's
+ * section "Pack inference projections" does before its own GEMM kernel runs.
+ *
+ * Conventions for every entry point:
+ *  - All buffer pointers are DEVICE pointers to memory the caller owns. The
+ *    library keeps no pointer after returning and allocates, frees and
+ *    synchronizes nothing.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream). Work
+ *    is enqueued asynchronously on it; buffers must stay alive until it runs.
+ *  - Every argument is checked on the host BEFORE anything is enqueued. On any
+ *    error nothing is launched and outputs are left untouched. Unsupported
+ *    formats (asymmetric weights, zero points, group reordering, activation
+ *    quantization) cannot be expressed: there are no such parameters.
+ *  - Row-major everywhere; bf16 and fp16 values are passed as their 16-bit
+ *    patterns.
+ *  - Results are deterministic: repeated calls with equal inputs give equal
+ *    bits (all reductions run in a fixed order).
+ */
+#ifndef SVQ_H
+#define SVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SVQ_ABI_VERSION 1
+
+typedef enum svq_status {
+    SVQ_OK = 0,
+    SVQ_ERR_NULL = 1,          /* a required pointer is NULL */
+    SVQ_ERR_DIM = 2,           /* M, N or K out of range (<= 0 or too large) */
+    SVQ_ERR_GROUP = 3,         /* group size not supported for this format */
+    SVQ_ERR_DIVISIBILITY = 4,  /* N % 16 != 0, K % 128 != 0 or K % G != 0 */
+    SVQ_ERR_MXFP8_SHAPE = 5,   /* MXFP8 needs N >= 128 and K % 32 == 0 */
+    SVQ_ERR_ALIGN = 6,         /* a pointer is not suitably aligned */
+    SVQ_ERR_OVERLAP = 7,       /* output overlaps an input */
+    SVQ_ERR_WORKSPACE = 8,     /* workspace missing, too small or misaligned */
+    SVQ_ERR_HIP = 9,           /* the HIP runtime refused the launch */
+    SVQ_ERR_UNSUPPORTED = 10   /* the requested kernel cannot run this shape */
+} svq_status;
+
+/* Kernel selectors for the *_with entry points (diagnostics and benchmarks).
+ * SVQ_KERNEL_AUTO is what svq_w4a16_gemm / svq_mxfp8_gemm use. */
+typedef enum svq_kernel {
+    SVQ_KERNEL_AUTO = 0,
+    SVQ_KERNEL_DOT2 = 1,        /* VALU bf16 dot2 with row broadcast of x, M <= 8 */
+    SVQ_KERNEL_MFMA_SKINNY = 2, /* one 16-row MFMA tile, waves split K, M <= 16 */
+    SVQ_KERNEL_MFMA_WIDE = 3    /* LDS-staged x, 64/128-row MFMA tiles, split-K, any M */
+} svq_kernel;
+
+int svq_abi_version(void);
+
+/* Static text for a status code; never NULL. */
+const char *svq_status_string(int status);
+
+/* ---- W4A16 ------------------------------------------------------------------ */
+
+/* Bytes of the repacked weight buffer: K*N/2 (the same as the GPTQ input). */
+size_t svq_q4_repacked_bytes(int64_t N, int64_t K);
+
+/*
+ * One-time repack of GPTQ INT4 words into the device tile layout read by the
+ * W4A16 kernels (a pure bit permutation; reads and writes K*N/2 bytes once).
+ *   qweight_gptq  int32 [K/8][N]; nibble i (bits 4i..4i+3) of word [j][n] is
+ *                 the code of row 8j+i, column n. 16-byte aligned.
+ *   qweight_tiled int32, svq_q4_repacked_bytes(N, K) bytes, 16-byte aligned,
+ *                 must not overlap qweight_gptq. Layout: tiles of 16 columns x
+ *                 128 rows (1 KiB), column-block-major with the K-tiles of a
+ *                 column block consecutive; lane l of a tile owns 16 bytes:
+ *                 column 16*nb + l%16, word j = rows 128*kt + 32*(l/16) + 8*j
+ *                 + e (e = 0..7) with row e in nibble slot p, e = (0,2,4,6,
+ *                 1,3,5,7)[p].
+ * Requires N % 16 == 0, K % 128 == 0.
+ */
+int svq_q4_repack(const int32_t *qweight_gptq, int32_t *qweight_tiled, int64_t N,
+                  int64_t K, void *stream);
+
+/* Workspace bytes needed by svq_w4a16_gemm (kernel = SVQ_KERNEL_AUTO) or by
+ * svq_w4a16_gemm_with for the given kernel; 0 if none. (size_t)-1 if the
+ * arguments are invalid or the kernel cannot run the shape. */
+size_t svq_w4a16_workspace_bytes(int kernel, int64_t M, int64_t N, int64_t K,
+                                 int32_t group_size);
+
+/*
+ * y = x . ((q - 8) * s)^T
+ *   x             bf16 [M][K], 16-byte aligned
+ *   qweight_tiled output of svq_q4_repack, 16-byte aligned
+ *   scales        fp16 [K/G][N], 2-byte aligned
+ *   out           bf16 [M][N], 4-byte aligned, fully overwritten, must not
+ *                 overlap any input or the workspace
+ *   group_size    G in {32, 64, 128}; K % 128 == 0, N % 16 == 0
+ *   workspace     device buffer of at least svq_w4a16_workspace_bytes(...)
+ *                 bytes, 256-byte aligned, ZERO-FILLED before its first use;
+ *                 the kernels leave it zero-filled again where it matters
+ *                 (split-K arrival counters). NULL/0 when 0 bytes are needed.
+ *                 Calls that share a workspace must be stream-ordered.
+ */
+int svq_w4a16_gemm(const void *x, const int32_t *qweight_tiled, const void *scales,
+                   void *out, int64_t M, int64_t N, int64_t K, int32_t group_size,
+                   void *workspace, size_t workspace_bytes, void *stream);
+
+/* Same, with an explicit kernel choice; SVQ_ERR_UNSUPPORTED if that kernel
+ * cannot run M (SVQ_KERNEL_DOT2: M <= 8; SVQ_KERNEL_MFMA_SKINNY: M <= 16). */
+int svq_w4a16_gemm_with(int kernel, const void *x, const int32_t *qweight_tiled,
+                        const void *scales, void *out, int64_t M, int64_t N, int64_t K,
+                        int32_t group_size, void *workspace, size_t workspace_bytes,
+                        void *stream);
+
+/* Name of the kernel the call would launch (static text), or NULL if invalid. */
+const char *svq_w4a16_kernel_name(int kernel, int64_t M, int64_t N, int64_t K,
+                                  int32_t group_size);
+
+/* ---- MXFP8 ------------------------------------------------------------------ */
+
+size_t svq_mxfp8_workspace_bytes(int kernel, int64_t M, int64_t N, int64_t K);
+
+/*
+ * y = x . (e4m3(w) * 2^(e8m0(s) - 127))^T
+ *   x       bf16 [M][K], 16-byte aligned
+ *   w       E4M3FN codes [N][K] (row n holds the K elements of output column n),
+ *           16-byte aligned
+ *   scales  E8M0 codes [N][K/32], one per 32 consecutive K-elements of a row
+ *   out     bf16 [M][N], 4-byte aligned, fully overwritten, no overlap
+ *   group_size must be 32. Requires N >= 128, N % 16 == 0, K % 128 == 0.
+ *   workspace as for svq_w4a16_gemm.
+ * Element code 0x7F/0xFF (NaN) and scale code 255 (NaN) are not supported
+ * inputs: the result for them is unspecified.
+ */
+int svq_mxfp8_gemm(const void *x, const uint8_t *w, const uint8_t *scales, void *out,
+                   int64_t M, int64_t N, int64_t K, int32_t group_size, void *workspace,
+                   size_t workspace_bytes, void *stream);
+
+int svq_mxfp8_gemm_with(int kernel, const void *x, const uint8_t *w, const uint8_t *scales,
+                        void *out, int64_t M, int64_t N, int64_t K, int32_t group_size,
+                        void *workspace, size_t workspace_bytes, void *stream);
+
+const char *svq_mxfp8_kernel_name(int kernel, int64_t M, int64_t N, int64_t K);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SVQ_H */

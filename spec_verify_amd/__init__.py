@@ -1,0 +1,238 @@
+"""Python binding of libsvq (include/svq.h): weight-only quantized linear layers
+(W4A16 GPTQ-style INT4, MXFP8) for decode and speculative-verify shapes on
+MI355X (gfx950).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of libsvq.so, which must be built in-tree (``python -m
+spec_verify_amd.build``). There is no CPU or PyTorch fallback: if the library
+is missing or a call fails, an exception is raised.
+
+PyTorch supplies device memory and the current stream; tensors are passed as
+raw device pointers. bf16/fp16 values travel as torch.bfloat16/float16 tensors
+or as their 16-bit patterns in int16/uint16 tensors.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+__all__ = [
+    "SvqError", "KERNEL_AUTO", "KERNEL_DOT2", "KERNEL_MFMA_SKINNY", "KERNEL_MFMA_WIDE",
+    "lib", "library_path", "q4_repack", "w4a16_gemm", "mxfp8_gemm", "w4a16_kernel_name",
+    "mxfp8_kernel_name", "w4a16_workspace_bytes", "mxfp8_workspace_bytes", "Workspace",
+    "EXPORTED_SYMBOLS",
+]
+
+KERNEL_AUTO, KERNEL_DOT2, KERNEL_MFMA_SKINNY, KERNEL_MFMA_WIDE = 0, 1, 2, 3
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "libsvq.so")
+
+EXPORTED_SYMBOLS = (
+    "svq_abi_version", "svq_status_string", "svq_q4_repacked_bytes", "svq_q4_repack",
+    "svq_w4a16_workspace_bytes", "svq_w4a16_gemm", "svq_w4a16_gemm_with",
+    "svq_w4a16_kernel_name", "svq_mxfp8_workspace_bytes", "svq_mxfp8_gemm",
+    "svq_mxfp8_gemm_with", "svq_mxfp8_kernel_name",
+)
+
+_i64, _i32, _p, _sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t
+_lib = None
+_lock = threading.Lock()
+
+
+class SvqError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: svq status {status}: {_status_text(status)}")
+
+
+def lib():
+    """The loaded libsvq.so (ctypes.CDLL). Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(library_path):
+            raise RuntimeError(
+                f"libsvq.so not found at {library_path}; build it with "
+                "`python -m spec_verify_amd.build` (hipcc, gfx950)")
+        L = ctypes.CDLL(library_path)
+        L.svq_abi_version.restype = ctypes.c_int
+        L.svq_status_string.restype = ctypes.c_char_p
+        L.svq_status_string.argtypes = [ctypes.c_int]
+        L.svq_q4_repacked_bytes.restype = _sz
+        L.svq_q4_repacked_bytes.argtypes = [_i64, _i64]
+        L.svq_q4_repack.restype = ctypes.c_int
+        L.svq_q4_repack.argtypes = [_p, _p, _i64, _i64, _p]
+        L.svq_w4a16_workspace_bytes.restype = _sz
+        L.svq_w4a16_workspace_bytes.argtypes = [ctypes.c_int, _i64, _i64, _i64, _i32]
+        L.svq_w4a16_gemm.restype = ctypes.c_int
+        L.svq_w4a16_gemm.argtypes = [_p, _p, _p, _p, _i64, _i64, _i64, _i32, _p, _sz, _p]
+        L.svq_w4a16_gemm_with.restype = ctypes.c_int
+        L.svq_w4a16_gemm_with.argtypes = [ctypes.c_int, _p, _p, _p, _p, _i64, _i64, _i64, _i32, _p, _sz, _p]
+        L.svq_w4a16_kernel_name.restype = ctypes.c_char_p
+        L.svq_w4a16_kernel_name.argtypes = [ctypes.c_int, _i64, _i64, _i64, _i32]
+        L.svq_mxfp8_workspace_bytes.restype = _sz
+        L.svq_mxfp8_workspace_bytes.argtypes = [ctypes.c_int, _i64, _i64, _i64]
+        L.svq_mxfp8_gemm.restype = ctypes.c_int
+        L.svq_mxfp8_gemm.argtypes = [_p, _p, _p, _p, _i64, _i64, _i64, _i32, _p, _sz, _p]
+        L.svq_mxfp8_gemm_with.restype = ctypes.c_int
+        L.svq_mxfp8_gemm_with.argtypes = [ctypes.c_int, _p, _p, _p, _p, _i64, _i64, _i64, _i32, _p, _sz, _p]
+        L.svq_mxfp8_kernel_name.restype = ctypes.c_char_p
+        L.svq_mxfp8_kernel_name.argtypes = [ctypes.c_int, _i64, _i64, _i64]
+        _lib = L
+        return L
+
+
+def _status_text(status: int) -> str:
+    try:
+        return lib().svq_status_string(int(status)).decode()
+    except Exception:  # pragma: no cover - library missing
+        return "unknown"
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise SvqError(status, where)
+
+
+# ---- torch plumbing ------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_ptr(t):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _dev_ptr(t, name):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _check_elem(t, name, bytes_per_elem):
+    if t.element_size() != bytes_per_elem:
+        raise TypeError(f"{name} must have {bytes_per_elem}-byte elements, got {t.dtype}")
+
+
+class Workspace:
+    """Zero-filled device scratch for the split-K arrival counters and partials.
+
+    One per (device, stream); grows on demand (a new buffer is zero-filled). The
+    kernels leave the counters at zero after every call, so the buffer can be
+    reused by later calls on the same stream without clearing it again.
+    """
+
+    _cache: dict = {}
+
+    @classmethod
+    def get(cls, nbytes: int, device, stream_handle: int):
+        torch = _torch()
+        if nbytes == 0:
+            return None
+        key = (device.index, stream_handle)
+        buf = cls._cache.get(key)
+        if buf is None or buf.numel() < nbytes:
+            buf = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+            cls._cache[key] = buf
+        return buf
+
+
+def w4a16_workspace_bytes(M, N, K, group_size=128, kernel=KERNEL_AUTO) -> int:
+    v = lib().svq_w4a16_workspace_bytes(kernel, M, N, K, group_size)
+    if v == ctypes.c_size_t(-1).value:
+        raise SvqError(10, "svq_w4a16_workspace_bytes")
+    return v
+
+
+def mxfp8_workspace_bytes(M, N, K, kernel=KERNEL_AUTO) -> int:
+    v = lib().svq_mxfp8_workspace_bytes(kernel, M, N, K)
+    if v == ctypes.c_size_t(-1).value:
+        raise SvqError(10, "svq_mxfp8_workspace_bytes")
+    return v
+
+
+def w4a16_kernel_name(M, N, K, group_size=128, kernel=KERNEL_AUTO):
+    r = lib().svq_w4a16_kernel_name(kernel, M, N, K, group_size)
+    return r.decode() if r else None
+
+
+def mxfp8_kernel_name(M, N, K, kernel=KERNEL_AUTO):
+    r = lib().svq_mxfp8_kernel_name(kernel, M, N, K)
+    return r.decode() if r else None
+
+
+def q4_repack(qweight, out=None):
+    """GPTQ int32 [K/8, N] (device) -> tiled int32 buffer of K*N/8 words."""
+    torch = _torch()
+    K8, N = qweight.shape
+    _check_elem(qweight, "qweight", 4)
+    if out is None:
+        out = torch.empty(K8 * N, dtype=torch.int32, device=qweight.device)
+    _check_elem(out, "out", 4)
+    if out.numel() * 4 < K8 * N * 4:
+        raise ValueError("out too small")
+    _check(lib().svq_q4_repack(_dev_ptr(qweight, "qweight"), _dev_ptr(out, "out"), N, K8 * 8,
+                               _stream_ptr(qweight)), "svq_q4_repack")
+    return out
+
+
+def w4a16_gemm(x, qweight_tiled, scales, N, group_size=128, out=None, kernel=KERNEL_AUTO,
+               workspace=None):
+    """bf16 x [M, K] . deq(W)^T -> bf16 [M, N]; W given as the svq_q4_repack output."""
+    torch = _torch()
+    M, K = x.shape
+    _check_elem(x, "x", 2)
+    _check_elem(scales, "scales", 2)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    _check_elem(out, "out", 2)
+    if tuple(out.shape) != (M, N):
+        raise ValueError(f"out must have shape {(M, N)}")
+    stream = _stream_ptr(x)
+    if workspace is None:
+        nbytes = w4a16_workspace_bytes(M, N, K, group_size, kernel)
+        workspace = Workspace.get(nbytes, x.device, stream.value or 0)
+    ws_ptr = _dev_ptr(workspace, "workspace") if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().svq_w4a16_gemm_with(kernel, _dev_ptr(x, "x"), _dev_ptr(qweight_tiled, "qweight_tiled"),
+                                     _dev_ptr(scales, "scales"), _dev_ptr(out, "out"), M, N, K,
+                                     group_size, ws_ptr, ws_bytes, stream), "svq_w4a16_gemm")
+    return out
+
+
+def mxfp8_gemm(x, w, scales, out=None, kernel=KERNEL_AUTO, workspace=None):
+    """bf16 x [M, K] . (E4M3 w [N, K] * 2^(E8M0 scales [N, K/32] - 127))^T -> bf16 [M, N]."""
+    torch = _torch()
+    M, K = x.shape
+    N = w.shape[0]
+    _check_elem(x, "x", 2)
+    _check_elem(w, "w", 1)
+    _check_elem(scales, "scales", 1)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    _check_elem(out, "out", 2)
+    if tuple(out.shape) != (M, N):
+        raise ValueError(f"out must have shape {(M, N)}")
+    stream = _stream_ptr(x)
+    if workspace is None:
+        nbytes = mxfp8_workspace_bytes(M, N, K, kernel)
+        workspace = Workspace.get(nbytes, x.device, stream.value or 0)
+    ws_ptr = _dev_ptr(workspace, "workspace") if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().svq_mxfp8_gemm_with(kernel, _dev_ptr(x, "x"), _dev_ptr(w, "w"), _dev_ptr(scales, "scales"),
+                                     _dev_ptr(out, "out"), M, N, K, 32, ws_ptr, ws_bytes, stream),
+           "svq_mxfp8_gemm")
+    return out

@@ -1,0 +1,302 @@
+// C ABI of the quantized linear layer (include/svq.h): argument validation,
+// kernel selection and launch. Validation is pure host code that runs before
+// any HIP call, so every error path is reachable without a GPU.
+#include "../../include/svq.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
+#include <cstdint>
+
+#include "svq_launch.h"
+
+namespace svq {
+namespace {
+
+constexpr int64_t kMaxDim = int64_t(1) << 24;  // per dimension
+constexpr int kMaxDevices = 64;
+constexpr int kWideThreads = 256;              // threads per wide-kernel workgroup
+constexpr int kWideAccPerThread = 16;          // f32x4 accumulators per thread
+
+std::atomic<int> g_num_cus[kMaxDevices];
+
+}  // namespace
+
+// Compute units of the current device (cached per device).
+int device_cus() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+    int v = g_num_cus[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+        n = 256;
+    g_num_cus[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+
+static WidePlan make_plan(int64_t M, int64_t N, int64_t K, int num_cus) {
+    WidePlan p{};
+    if (M > 64) {
+        p.bm = 128;
+        p.bn = 128;
+    } else {
+        p.bm = 64;
+        p.bn = 256;
+    }
+    p.row_tiles = (int)((M + p.bm - 1) / p.bm);
+    p.col_tiles = (int)((N + p.bn - 1) / p.bn);
+    const int64_t KT = K / 128;
+    const int64_t tiles = (int64_t)p.row_tiles * p.col_tiles;
+    p.units = tiles * KT;
+    p.grid = (int)std::min<int64_t>(std::max(num_cus, 1), p.units);
+    int maxt = 1;
+    bool shared = false;
+    for (int w = 0; w < p.grid; ++w) {
+        const int64_t b = (int64_t)w * p.units / p.grid, e = (int64_t)(w + 1) * p.units / p.grid;
+        maxt = std::max<int>(maxt, (int)((e - 1) / KT - b / KT + 1));
+        if (b % KT != 0 || e % KT != 0) shared = true;
+    }
+    p.maxt = maxt;
+    if (shared) {
+        const size_t cnt_bytes = ((size_t)tiles * 4 + 255) & ~(size_t)255;
+        p.workspace_bytes = cnt_bytes + (size_t)p.grid * p.maxt * kWideAccPerThread * kWideThreads * 16;
+    }
+    return p;
+}
+
+WidePlan plan_w4a16_wide(int64_t M, int64_t N, int64_t K, int num_cus) {
+    return make_plan(M, N, K, num_cus);
+}
+WidePlan plan_mxfp8_wide(int64_t M, int64_t N, int64_t K, int num_cus) {
+    return make_plan(M, N, K, num_cus);
+}
+
+}  // namespace svq
+
+using namespace svq;
+
+namespace {
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+bool overlap(const void *a, size_t na, const void *b, size_t nb) {
+    const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
+    return pa < pb + nb && pb < pa + na;
+}
+
+bool dims_ok(int64_t M, int64_t N, int64_t K) {
+    return M > 0 && N > 0 && K > 0 && M <= kMaxDim && N <= kMaxDim && K <= kMaxDim &&
+           M * K <= (int64_t(1) << 40) && N * K <= (int64_t(1) << 40) &&
+           M * N <= (int64_t(1) << 40);
+}
+
+int resolve_kernel(int kernel, int64_t M, bool mxfp8) {
+    if (kernel != SVQ_KERNEL_AUTO) return kernel;
+    if (M <= (mxfp8 ? 2 : 1)) return SVQ_KERNEL_DOT2;
+    if (M <= 16) return SVQ_KERNEL_MFMA_SKINNY;
+    return SVQ_KERNEL_MFMA_WIDE;
+}
+
+int kernel_fits(int k, int64_t M) {
+    switch (k) {
+    case SVQ_KERNEL_DOT2: return M <= 8 ? SVQ_OK : SVQ_ERR_UNSUPPORTED;
+    case SVQ_KERNEL_MFMA_SKINNY: return M <= 16 ? SVQ_OK : SVQ_ERR_UNSUPPORTED;
+    case SVQ_KERNEL_MFMA_WIDE: return SVQ_OK;
+    default: return SVQ_ERR_UNSUPPORTED;
+    }
+}
+
+int check_w4a16_shape(int64_t M, int64_t N, int64_t K, int32_t G) {
+    if (!dims_ok(M, N, K)) return SVQ_ERR_DIM;
+    if (G != 32 && G != 64 && G != 128) return SVQ_ERR_GROUP;
+    if (N % 16 || K % 128 || K % G) return SVQ_ERR_DIVISIBILITY;
+    return SVQ_OK;
+}
+
+int check_mxfp8_shape(int64_t M, int64_t N, int64_t K, int32_t G) {
+    if (!dims_ok(M, N, K)) return SVQ_ERR_DIM;
+    if (G != 32) return SVQ_ERR_GROUP;
+    if (N < 128 || K % 32) return SVQ_ERR_MXFP8_SHAPE;
+    if (N % 16 || K % 128) return SVQ_ERR_DIVISIBILITY;
+    return SVQ_OK;
+}
+
+const char *w4a16_name(int k) {
+    switch (k) {
+    case SVQ_KERNEL_DOT2: return "w4a16_dot2_kernel";
+    case SVQ_KERNEL_MFMA_SKINNY: return "w4a16_skinny_kernel";
+    case SVQ_KERNEL_MFMA_WIDE: return "w4a16_wide_kernel";
+    default: return nullptr;
+    }
+}
+
+const char *mxfp8_name(int k) {
+    switch (k) {
+    case SVQ_KERNEL_DOT2: return "mxfp8_dot2_kernel";
+    case SVQ_KERNEL_MFMA_SKINNY: return "mxfp8_skinny_kernel";
+    case SVQ_KERNEL_MFMA_WIDE: return "mxfp8_wide_kernel";
+    default: return nullptr;
+    }
+}
+
+// Common buffer checks of a GEMM call; sizes in bytes.
+int check_gemm_buffers(const void *x, size_t x_bytes, const void *w, size_t w_bytes,
+                       const void *s, size_t s_bytes, const void *out, size_t out_bytes,
+                       const void *ws, size_t ws_bytes, size_t ws_needed, uintptr_t s_align) {
+    if (!x || !w || !s || !out) return SVQ_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(w, 16) || !aligned(s, s_align) || !aligned(out, 4))
+        return SVQ_ERR_ALIGN;
+    if (overlap(out, out_bytes, x, x_bytes) || overlap(out, out_bytes, w, w_bytes) ||
+        overlap(out, out_bytes, s, s_bytes))
+        return SVQ_ERR_OVERLAP;
+    if (ws_needed) {
+        if (!ws || ws_bytes < ws_needed || !aligned(ws, 256)) return SVQ_ERR_WORKSPACE;
+        if (overlap(ws, ws_needed, out, out_bytes) || overlap(ws, ws_needed, x, x_bytes) ||
+            overlap(ws, ws_needed, w, w_bytes) || overlap(ws, ws_needed, s, s_bytes))
+            return SVQ_ERR_OVERLAP;
+    }
+    return SVQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int svq_abi_version(void) { return SVQ_ABI_VERSION; }
+
+const char *svq_status_string(int status) {
+    switch (status) {
+    case SVQ_OK: return "ok";
+    case SVQ_ERR_NULL: return "a required pointer is NULL";
+    case SVQ_ERR_DIM: return "M, N or K out of range";
+    case SVQ_ERR_GROUP: return "unsupported group size";
+    case SVQ_ERR_DIVISIBILITY: return "N must be a multiple of 16 and K of 128 and of the group size";
+    case SVQ_ERR_MXFP8_SHAPE: return "MXFP8 needs N >= 128 and K % 32 == 0";
+    case SVQ_ERR_ALIGN: return "misaligned pointer";
+    case SVQ_ERR_OVERLAP: return "output or workspace overlaps another buffer";
+    case SVQ_ERR_WORKSPACE: return "workspace missing, too small or not 256-byte aligned";
+    case SVQ_ERR_HIP: return "HIP runtime error at launch";
+    case SVQ_ERR_UNSUPPORTED: return "the requested kernel cannot run this shape";
+    default: return "unknown status";
+    }
+}
+
+size_t svq_q4_repacked_bytes(int64_t N, int64_t K) {
+    if (N <= 0 || K <= 0 || N > kMaxDim || K > kMaxDim) return 0;
+    return (size_t)N * (size_t)K / 2;
+}
+
+int svq_q4_repack(const int32_t *src, int32_t *dst, int64_t N, int64_t K, void *stream) {
+    if (!src || !dst) return SVQ_ERR_NULL;
+    if (N <= 0 || K <= 0 || N > kMaxDim || K > kMaxDim || N * K > (int64_t(1) << 40)) return SVQ_ERR_DIM;
+    if (N % 16 || K % 128) return SVQ_ERR_DIVISIBILITY;
+    if (!aligned(src, 16) || !aligned(dst, 16)) return SVQ_ERR_ALIGN;
+    const size_t bytes = (size_t)N * (size_t)K / 2;
+    if (overlap(src, bytes, dst, bytes)) return SVQ_ERR_OVERLAP;
+    if (launch_q4_repack(src, dst, N, K, (hipStream_t)stream) != hipSuccess) return SVQ_ERR_HIP;
+    return SVQ_OK;
+}
+
+size_t svq_w4a16_workspace_bytes(int kernel, int64_t M, int64_t N, int64_t K, int32_t G) {
+    if (check_w4a16_shape(M, N, K, G) != SVQ_OK) return (size_t)-1;
+    const int k = resolve_kernel(kernel, M, false);
+    if (kernel_fits(k, M) != SVQ_OK) return (size_t)-1;
+    if (k != SVQ_KERNEL_MFMA_WIDE) return 0;
+    return plan_w4a16_wide(M, N, K, device_cus()).workspace_bytes;
+}
+
+const char *svq_w4a16_kernel_name(int kernel, int64_t M, int64_t N, int64_t K, int32_t G) {
+    if (check_w4a16_shape(M, N, K, G) != SVQ_OK) return nullptr;
+    const int k = resolve_kernel(kernel, M, false);
+    if (kernel_fits(k, M) != SVQ_OK) return nullptr;
+    return w4a16_name(k);
+}
+
+int svq_w4a16_gemm_with(int kernel, const void *x, const int32_t *wt, const void *scales, void *out,
+                        int64_t M, int64_t N, int64_t K, int32_t G, void *workspace,
+                        size_t workspace_bytes, void *stream) {
+    int st = check_w4a16_shape(M, N, K, G);
+    if (st != SVQ_OK) return st;
+    const int k = resolve_kernel(kernel, M, false);
+    if ((st = kernel_fits(k, M)) != SVQ_OK) return st;
+    WidePlan plan{};
+    if (k == SVQ_KERNEL_MFMA_WIDE) {
+        // the plan needs the device's compute-unit count; the buffers are
+        // checked first so that invalid pointers never reach the runtime
+        st = check_gemm_buffers(x, (size_t)M * K * 2, wt, (size_t)N * K / 2, scales,
+                                (size_t)(K / G) * N * 2, out, (size_t)M * N * 2, nullptr, 0, 0, 2);
+        if (st != SVQ_OK) return st;
+        plan = plan_w4a16_wide(M, N, K, device_cus());
+    }
+    st = check_gemm_buffers(x, (size_t)M * K * 2, wt, (size_t)N * K / 2, scales, (size_t)(K / G) * N * 2,
+                            out, (size_t)M * N * 2, workspace, workspace_bytes, plan.workspace_bytes, 2);
+    if (st != SVQ_OK) return st;
+    hipError_t e;
+    const hipStream_t s = (hipStream_t)stream;
+    switch (k) {
+    case SVQ_KERNEL_DOT2: e = launch_w4a16_dot2(x, wt, scales, out, (int)M, N, K, G, s); break;
+    case SVQ_KERNEL_MFMA_SKINNY: e = launch_w4a16_skinny(x, wt, scales, out, (int)M, N, K, G, s); break;
+    default: e = launch_w4a16_wide(plan, x, wt, scales, out, M, N, K, G, workspace, s); break;
+    }
+    return e == hipSuccess ? SVQ_OK : SVQ_ERR_HIP;
+}
+
+int svq_w4a16_gemm(const void *x, const int32_t *wt, const void *scales, void *out, int64_t M,
+                   int64_t N, int64_t K, int32_t G, void *workspace, size_t workspace_bytes,
+                   void *stream) {
+    return svq_w4a16_gemm_with(SVQ_KERNEL_AUTO, x, wt, scales, out, M, N, K, G, workspace,
+                               workspace_bytes, stream);
+}
+
+size_t svq_mxfp8_workspace_bytes(int kernel, int64_t M, int64_t N, int64_t K) {
+    if (check_mxfp8_shape(M, N, K, 32) != SVQ_OK) return (size_t)-1;
+    const int k = resolve_kernel(kernel, M, true);
+    if (kernel_fits(k, M) != SVQ_OK) return (size_t)-1;
+    if (k != SVQ_KERNEL_MFMA_WIDE) return 0;
+    return plan_mxfp8_wide(M, N, K, device_cus()).workspace_bytes;
+}
+
+const char *svq_mxfp8_kernel_name(int kernel, int64_t M, int64_t N, int64_t K) {
+    if (check_mxfp8_shape(M, N, K, 32) != SVQ_OK) return nullptr;
+    const int k = resolve_kernel(kernel, M, true);
+    if (kernel_fits(k, M) != SVQ_OK) return nullptr;
+    return mxfp8_name(k);
+}
+
+int svq_mxfp8_gemm_with(int kernel, const void *x, const uint8_t *w, const uint8_t *scales,
+                        void *out, int64_t M, int64_t N, int64_t K, int32_t G, void *workspace,
+                        size_t workspace_bytes, void *stream) {
+    int st = check_mxfp8_shape(M, N, K, G);
+    if (st != SVQ_OK) return st;
+    const int k = resolve_kernel(kernel, M, true);
+    if ((st = kernel_fits(k, M)) != SVQ_OK) return st;
+    const size_t xb = (size_t)M * K * 2, wb = (size_t)N * K, sb = (size_t)N * (K / 32), ob = (size_t)M * N * 2;
+    WidePlan plan{};
+    if (k == SVQ_KERNEL_MFMA_WIDE) {
+        st = check_gemm_buffers(x, xb, w, wb, scales, sb, out, ob, nullptr, 0, 0, 1);
+        if (st != SVQ_OK) return st;
+        plan = plan_mxfp8_wide(M, N, K, device_cus());
+    }
+    st = check_gemm_buffers(x, xb, w, wb, scales, sb, out, ob, workspace, workspace_bytes,
+                            plan.workspace_bytes, 1);
+    if (st != SVQ_OK) return st;
+    hipError_t e;
+    const hipStream_t s = (hipStream_t)stream;
+    switch (k) {
+    case SVQ_KERNEL_DOT2: e = launch_mxfp8_dot2(x, w, scales, out, (int)M, N, K, s); break;
+    case SVQ_KERNEL_MFMA_SKINNY: e = launch_mxfp8_skinny(x, w, scales, out, (int)M, N, K, s); break;
+    default: e = launch_mxfp8_wide(plan, x, w, scales, out, M, N, K, workspace, s); break;
+    }
+    return e == hipSuccess ? SVQ_OK : SVQ_ERR_HIP;
+}
+
+int svq_mxfp8_gemm(const void *x, const uint8_t *w, const uint8_t *scales, void *out, int64_t M,
+                   int64_t N, int64_t K, int32_t G, void *workspace, size_t workspace_bytes,
+                   void *stream) {
+    return svq_mxfp8_gemm_with(SVQ_KERNEL_AUTO, x, w, scales, out, M, N, K, G, workspace,
+                               workspace_bytes, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,112 @@
+// Device-side helpers shared by the gfx950 kernels of the quantized linear layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace svq {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// bf16 pattern of -136.0: the W4A16 kernels build each weight as the bf16 value
+// 128 + q (q = 0..15, exact) and subtract 136 * sum(x) per group, which gives
+// sum(x * (q - 8)) with zero point 8.
+constexpr uint32_t kBf16Neg136Pair = 0xC308C308u;
+constexpr uint32_t kBf16OnePair = 0x3F803F80u;
+constexpr uint32_t kMagic128Pair = 0x43004300u;  // two bf16 128.0
+constexpr uint32_t kNibblePairMask = 0x000F000Fu;
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte streaming load (non-temporal hint: weights are read exactly once).
+__device__ __forceinline__ uint4 load_stream16(const void *p) {
+    const u32x4 v = __builtin_nontemporal_load((const u32x4 *)p);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ float bits_f32(uint32_t u) { return __builtin_bit_cast(float, u); }
+__device__ __forceinline__ uint32_t f32_bits(float f) { return __builtin_bit_cast(uint32_t, f); }
+
+// fp32 -> bf16 bits, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+    uint32_t u = f32_bits(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float fp16_bits_to_f32(uint16_t h) {
+    return (float)__builtin_bit_cast(_Float16, h);
+}
+
+// Two bf16 weights (128 + q_lo, 128 + q_hi) from nibble slots s and s+4 of a
+// repacked word (the repack puts rows 2s and 2s+1 of an 8-row run there).
+template <int S>
+__device__ __forceinline__ uint32_t nibble_pair_bf16(uint32_t w) {
+    return ((w >> (4 * S)) & kNibblePairMask) | kMagic128Pair;
+}
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
+                                          __builtin_bit_cast(bf16x2, b), c, false);
+}
+
+// Sum over the 16 lanes of a DPP row; every lane of the row gets the sum.
+__device__ __forceinline__ float row16_sum(float v) {
+    v += bits_f32(__builtin_amdgcn_mov_dpp(f32_bits(v), 0xB1, 0xF, 0xF, true));   // quad_perm [1,0,3,2]
+    v += bits_f32(__builtin_amdgcn_mov_dpp(f32_bits(v), 0x4E, 0xF, 0xF, true));   // quad_perm [2,3,0,1]
+    v += bits_f32(__builtin_amdgcn_mov_dpp(f32_bits(v), 0x141, 0xF, 0xF, true));  // row_half_mirror
+    v += bits_f32(__builtin_amdgcn_mov_dpp(f32_bits(v), 0x140, 0xF, 0xF, true));  // row_mirror
+    return v;
+}
+
+// Sum of the four 16-lane rows, lane c of each row; every lane gets the sum of
+// its column position: (r0 + r1) + (r2 + r3), a fixed order.
+__device__ __forceinline__ float rows4_sum(float v) {
+    auto p = __builtin_amdgcn_permlane16_swap(f32_bits(v), f32_bits(v), false, false);
+    v = bits_f32(p[0]) + bits_f32(p[1]);
+    auto q = __builtin_amdgcn_permlane32_swap(f32_bits(v), f32_bits(v), false, false);
+    return bits_f32(q[0]) + bits_f32(q[1]);
+}
+
+// 4x4 transpose between the 16-lane row index and the word index of a 4-word
+// per-lane fragment: word j of row r becomes word r of row j.
+__device__ __forceinline__ void transpose_rows_words(uint32_t &w0, uint32_t &w1, uint32_t &w2,
+                                                     uint32_t &w3) {
+    auto a = __builtin_amdgcn_permlane32_swap(w0, w2, false, false);
+    auto b = __builtin_amdgcn_permlane32_swap(w1, w3, false, false);
+    auto c = __builtin_amdgcn_permlane16_swap(a[0], b[0], false, false);
+    auto d = __builtin_amdgcn_permlane16_swap(a[1], b[1], false, false);
+    w0 = c[0];
+    w1 = c[1];
+    w2 = d[0];
+    w3 = d[1];
+}
+
+__device__ __forceinline__ f32x4 mfma16x16x32(uint4 a, uint4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// Four bf16 pairs (one MFMA B operand: 8 rows x 1 column) from a repacked word.
+__device__ __forceinline__ uint4 word_to_bf16x8(uint32_t w) {
+    return make_uint4(nibble_pair_bf16<0>(w), nibble_pair_bf16<1>(w), nibble_pair_bf16<2>(w),
+                      nibble_pair_bf16<3>(w));
+}
+
+// E8M0 code -> fp32 scale 2^(b-127) (b = 0 gives the fp32 subnormal 2^-127).
+__device__ __forceinline__ float e8m0_to_f32(uint32_t b) {
+    return bits_f32(b == 0 ? 0x00400000u : (b << 23));
+}
+
+// Two E4M3FN codes (bytes 2*HI, 2*HI+1 of w) times `scale`, as a bf16 pair.
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3_pair_scaled(uint32_t w, float scale) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    bf16x2 r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, scale, HI);
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+}  // namespace svq

@@ -1,0 +1,47 @@
+// Internal launch interface between the C ABI (svq_api.cpp) and the kernels.
+// Every launcher assumes its arguments were validated by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "svq_device.h"
+
+namespace svq {
+
+hipError_t launch_q4_repack(const int32_t *src, int32_t *dst, int64_t N, int64_t K,
+                            hipStream_t stream);
+
+// Stream-K schedule of the wide MFMA kernels: output tiles of bm x bn, `units`
+// = row_tiles * col_tiles * (K/128) (tile, 128-row step) pairs split evenly over
+// `grid` persistent workgroups; a workgroup touches at most `maxt` tiles.
+struct WidePlan {
+    int bm, bn;
+    int row_tiles, col_tiles;
+    int64_t units;
+    int grid;
+    int maxt;
+    size_t workspace_bytes;  // arrival counters + fp32 partials (0 if no tile is shared)
+};
+
+WidePlan plan_w4a16_wide(int64_t M, int64_t N, int64_t K, int num_cus);
+WidePlan plan_mxfp8_wide(int64_t M, int64_t N, int64_t K, int num_cus);
+
+hipError_t launch_w4a16_dot2(const void *x, const int32_t *wt, const void *scales, void *out,
+                             int M, int64_t N, int64_t K, int G, hipStream_t stream);
+hipError_t launch_w4a16_skinny(const void *x, const int32_t *wt, const void *scales, void *out,
+                               int M, int64_t N, int64_t K, int G, hipStream_t stream);
+hipError_t launch_w4a16_wide(const WidePlan &plan, const void *x, const int32_t *wt,
+                             const void *scales, void *out, int64_t M, int64_t N, int64_t K,
+                             int G, void *workspace, hipStream_t stream);
+
+hipError_t launch_mxfp8_dot2(const void *x, const uint8_t *w, const uint8_t *scales, void *out,
+                             int M, int64_t N, int64_t K, hipStream_t stream);
+hipError_t launch_mxfp8_skinny(const void *x, const uint8_t *w, const uint8_t *scales, void *out,
+                               int M, int64_t N, int64_t K, hipStream_t stream);
+hipError_t launch_mxfp8_wide(const WidePlan &plan, const void *x, const uint8_t *w,
+                             const uint8_t *scales, void *out, int64_t M, int64_t N, int64_t K,
+                             void *workspace, hipStream_t stream);
+
+}  // namespace svq

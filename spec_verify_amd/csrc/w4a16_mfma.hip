@@ -1,0 +1,414 @@
+// W4A16 MFMA kernels for gfx950: v_mfma_f32_16x16x32_bf16 on weights dequantized
+// in registers from the 16-column x 128-row tile layout.
+//
+// What they compute: y[m][n] = sum_k x[m][k] * (q[k][n] - 8) * s[k/G][n], fp32
+// accumulation, bf16 (RNE) output. Format: GPTQ INT4 card
+// "Qwen3.8-27B-GPTQ-Int4-sym-G128-MTP-BF16", section "Quantization contract";
+// group sizes 32/64/128 per the Eole recipe "Qwen3.8-27B and native MTP
+// speculative decoding", section "Compressed-tensors INT4 layout". The batched
+// verify shape (32 streams x (1 + 3) tokens) comes from the autobench page
+// "Qwen3.8-27B · vLLM · FP8 + MTP" (concurrency 32, three speculative tokens).
+//
+// Operand mapping (16x16x32 bf16): lane l supplies row/column l%16 and 8 K-values
+// of K-group l/16 for both A (x) and B (weights); C holds rows 4*(l/16)+i of
+// column l%16. A tile word j of lane l covers rows 32*(l/16) + 8j + (0..7), so
+// for G = 128 MFMA step j simply takes word j, with x read at the same rows; for
+// G = 32/64 the four words and the four 16-lane rows are first transposed
+// (permlane swaps) so that step j covers the contiguous rows 32j.. of one group.
+//
+// Weights enter the MFMA as the exact bf16 values 128 + q; the bias is removed
+// per group by starting the group's accumulator at -136 * (sum of x over the
+// group), then the fp16 scale multiplies the group result into fp32 accumulators.
+#include "svq_launch.h"
+#include "svq_streamk.h"
+
+namespace svq {
+
+// ---------------------------------------------------------------------------
+// Skinny kernel: M <= 16, one 16-row MFMA tile (rows >= M are zero), the waves
+// of a workgroup split K over the tiles of one 16-column block. Memory-bound;
+// the MFMA pipe is mostly idle, so the -136 * sum(x) term is also computed on
+// it, by an MFMA against a constant -136 operand.
+// ---------------------------------------------------------------------------
+template <int NG>
+struct SkinnyStage {
+    uint4 w;
+    uint4 a[4];
+    uint16_t s[NG];
+};
+
+template <int WAVES, int D, int GSHIFT>
+__global__ __launch_bounds__(64 * WAVES) void w4a16_skinny_kernel(
+    const uint16_t *__restrict__ x, const uint4 *__restrict__ wt,
+    const uint16_t *__restrict__ sc, uint16_t *__restrict__ out, int M, int N, int K) {
+    constexpr int NG = 128 >> GSHIFT;
+    constexpr int SPG = 4 / NG;
+    constexpr bool kTrans = GSHIFT < 7;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int r = lane & 15, g = lane >> 4;
+    const int nb = blockIdx.x;
+    const int KT = K >> 7;
+    const int col = nb * 16 + r;
+    const uint4 *tp = wt + (size_t)nb * KT * 64 + lane;
+    const bool arow = r < M;
+    const uint16_t *xr = x + (size_t)(arow ? r : 0) * K;
+    const int ntile = wave < KT ? (KT - 1 - wave) / WAVES + 1 : 0;
+    const uint4 bneg = make_uint4(kBf16Neg136Pair, kBf16Neg136Pair, kBf16Neg136Pair, kBf16Neg136Pair);
+
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+
+    auto load = [&](SkinnyStage<NG>(&S)[D], int i0) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            int i = i0 + d;
+            i = i < ntile ? i : ntile - 1;
+            const int kt = wave + i * WAVES;
+            S[d].w = load_stream16(tp + (size_t)kt * 64);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int koff = kTrans ? (32 * j + 8 * g) : (32 * g + 8 * j);
+                S[d].a[j] = arow ? *(const uint4 *)(xr + (size_t)kt * 128 + koff) : make_uint4(0, 0, 0, 0);
+            }
+#pragma unroll
+            for (int q = 0; q < NG; ++q) S[d].s[q] = sc[(size_t)(kt * NG + q) * N + col];
+        }
+    };
+
+    auto compute = [&](const SkinnyStage<NG>(&S)[D], int i0) {
+        uint32_t wj[D][4];
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            wj[d][0] = S[d].w.x;
+            wj[d][1] = S[d].w.y;
+            wj[d][2] = S[d].w.z;
+            wj[d][3] = S[d].w.w;
+            if constexpr (kTrans) transpose_rows_words(wj[d][0], wj[d][1], wj[d][2], wj[d][3]);
+        }
+#pragma unroll
+        for (int q = 0; q < NG; ++q) {
+            f32x4 P[D];
+#pragma unroll
+            for (int d = 0; d < D; ++d) P[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int jj = 0; jj < SPG; ++jj) {
+                const int j = q * SPG + jj;
+#pragma unroll
+                for (int d = 0; d < D; ++d)
+                    if (i0 + d < ntile) P[d] = mfma16x16x32(S[d].a[j], bneg, P[d]);
+#pragma unroll
+                for (int d = 0; d < D; ++d)
+                    if (i0 + d < ntile) P[d] = mfma16x16x32(S[d].a[j], word_to_bf16x8(wj[d][j]), P[d]);
+            }
+#pragma unroll
+            for (int d = 0; d < D; ++d) {
+                if (i0 + d < ntile) {
+                    const float sf = fp16_bits_to_f32(S[d].s[q]);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(sf, P[d][i], acc[i]);
+                }
+            }
+        }
+    };
+
+    if (ntile > 0) {
+        SkinnyStage<NG> A[D], B[D];
+        load(A, 0);
+        for (int i0 = 0; i0 < ntile; i0 += 2 * D) {
+            load(B, i0 + D);
+            compute(A, i0);
+            load(A, i0 + 2 * D);
+            compute(B, i0 + D);
+        }
+    }
+
+    __shared__ float red[WAVES][16][17];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) red[wave][4 * g + i][r] = acc[i];
+    __syncthreads();
+    for (int t = threadIdx.x; t < M * 16; t += 64 * WAVES) {
+        const int m = t >> 4, c = t & 15;
+        float s = 0.f;
+#pragma unroll
+        for (int w = 0; w < WAVES; ++w) s += red[w][m][c];
+        out[(size_t)m * N + nb * 16 + c] = f32_to_bf16_rne(s);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Wide kernel: any M (tuned for M = 128). Persistent stream-K: the grid has one
+// workgroup per compute unit and each takes an equal contiguous share of the
+// (output tile, 128-row K step) units. A tile computed by several workgroups is
+// finished by the last to arrive, which adds the fp32 partials in workgroup
+// order (fixed order: deterministic) and clears the tile's arrival counter.
+//
+// Per step, the workgroup stages the x tile (BM rows x 128, bf16) in LDS with
+// -136 * (group sums of x) and the step's scales; each wave owns MBW 16-row
+// blocks x CT 16-column weight tiles, streams its weight tiles with 128-bit
+// loads one step ahead, and runs MBW*CT MFMA chains per group.
+// ---------------------------------------------------------------------------
+template <int MBW, int WR, int WC, int CT, int GSHIFT>
+struct WideCfg {
+    static constexpr int NT = 64 * WR * WC;
+    static constexpr int BM = 16 * MBW * WR;
+    static constexpr int BN = 16 * CT * WC;
+    static constexpr int NG = 128 >> GSHIFT;
+    static constexpr int SPG = 4 / NG;
+    static constexpr bool kTrans = GSHIFT < 7;
+    static constexpr int XROW = 128 + 8;        // bf16 per LDS row (16-byte pad)
+    static constexpr int UPT = BM * 16 / NT;    // 16-byte x chunks staged per thread
+    static constexpr int TPR = 16 / UPT;        // staging threads per x row
+    static constexpr int SPT = (NG * BN + NT - 1) / NT;  // scales staged per thread
+    static constexpr int NV = MBW * CT;         // f32x4 accumulators per lane
+    static_assert(UPT == 4 || UPT == 8, "staging assumes 1 or 2 32-row blocks per thread");
+};
+
+template <int MBW, int WR, int WC, int CT, int GSHIFT>
+__global__ __launch_bounds__(64 * WR * WC) void w4a16_wide_kernel(
+    const uint16_t *__restrict__ x, const uint4 *__restrict__ wt,
+    const uint16_t *__restrict__ sc, uint16_t *__restrict__ out, uint32_t *__restrict__ cnt,
+    f32x4 *__restrict__ part, int M, int N, int K, int col_tiles, int64_t units, int grid,
+    int maxt) {
+    using C = WideCfg<MBW, WR, WC, CT, GSHIFT>;
+    constexpr int NT = C::NT, BM = C::BM, BN = C::BN, NG = C::NG, SPG = C::SPG;
+    constexpr int XROW = C::XROW, UPT = C::UPT, TPR = C::TPR, SPT = C::SPT, NV = C::NV;
+    __shared__ __attribute__((aligned(16))) uint16_t xs[2][BM][XROW];
+    __shared__ __attribute__((aligned(16))) float xneg[2][NG][BM];
+    __shared__ uint16_t sl[2][NG][BN];
+    __shared__ int s_last;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wr = wave / WC, wc = wave % WC;
+    const int r = lane & 15, g = lane >> 4;
+    const int KT = K >> 7;
+    const int NB16 = N >> 4;
+    const int wg = blockIdx.x;
+    const int64_t u_begin = (int64_t)wg * units / grid;
+    const int64_t u_end = (int64_t)(wg + 1) * units / grid;
+    const int srow = tid / TPR, sseg = tid % TPR;
+
+    for (int64_t u = u_begin; u < u_end;) {
+        const int tile = (int)(u / KT);
+        const int s0 = (int)(u % KT);
+        const int s1 = (int)((u_end - u) < (int64_t)(KT - s0) ? s0 + (u_end - u) : KT);
+        const int rt = tile / col_tiles, cb = tile % col_tiles;
+        const int row0 = rt * BM;
+
+        // this wave's weight tiles (clamped to a valid tile past the last column)
+        const uint4 *tp[CT];
+        bool ctv[CT];
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+            const int nbg = cb * (BN / 16) + wc * CT + ct;
+            ctv[ct] = nbg < NB16;
+            tp[ct] = wt + (size_t)(ctv[ct] ? nbg : NB16 - 1) * KT * 64 + lane;
+        }
+        const bool srv = row0 + srow < M;
+        const uint4 *xsrc = (const uint4 *)(x + (size_t)(srv ? row0 + srow : 0) * K) + sseg * UPT;
+
+        f32x4 acc[NV];  // [rb * CT + ct]
+#pragma unroll
+        for (int v = 0; v < NV; ++v) acc[v] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+        uint4 xreg[UPT];
+        uint16_t sreg[SPT];
+        uint4 wcur[CT], wnext[CT];
+
+        auto load_x = [&](int s) {
+#pragma unroll
+            for (int v = 0; v < UPT; ++v) xreg[v] = srv ? xsrc[(size_t)s * 16 + v] : make_uint4(0, 0, 0, 0);
+#pragma unroll
+            for (int v = 0; v < SPT; ++v) {
+                const int i = tid + v * NT;
+                const int q = i / BN, c = i % BN;
+                int colg = cb * BN + c;
+                colg = colg < N ? colg : N - 1;
+                sreg[v] = (i < NG * BN) ? sc[(size_t)(s * NG + q) * N + colg] : (uint16_t)0;
+            }
+        };
+        auto load_w = [&](uint4(&W)[CT], int s) {
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) W[ct] = load_stream16(tp[ct] + (size_t)s * 64);
+        };
+        auto store_stage = [&](int buf) {
+#pragma unroll
+            for (int v = 0; v < UPT; ++v) *(uint4 *)&xs[buf][srow][(sseg * UPT + v) * 8] = xreg[v];
+            float bsum[UPT / 4];
+#pragma unroll
+            for (int b = 0; b < UPT / 4; ++b) {
+                float t = 0.f;
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const uint4 q4 = xreg[4 * b + v];
+                    t = dot2_bf16(q4.x, kBf16OnePair, t);
+                    t = dot2_bf16(q4.y, kBf16OnePair, t);
+                    t = dot2_bf16(q4.z, kBf16OnePair, t);
+                    t = dot2_bf16(q4.w, kBf16OnePair, t);
+                }
+                bsum[b] = t;
+            }
+            if constexpr (NG == 4) {  // G = 32: one group per 32-row block
+#pragma unroll
+                for (int b = 0; b < UPT / 4; ++b) xneg[buf][sseg * (UPT / 4) + b][srow] = -136.f * bsum[b];
+            } else if constexpr (NG == 2) {  // G = 64
+                if constexpr (UPT == 8) {
+                    xneg[buf][sseg][srow] = -136.f * (bsum[0] + bsum[1]);
+                } else {
+                    const float v = bsum[0] + __shfl_xor(bsum[0], 1);
+                    if ((sseg & 1) == 0) xneg[buf][sseg >> 1][srow] = -136.f * v;
+                }
+            } else {  // G = 128
+                float v = bsum[0];
+                if constexpr (UPT == 8) v += bsum[1];
+                v += __shfl_xor(v, 1);
+                if constexpr (TPR == 4) v += __shfl_xor(v, 2);
+                if (sseg == 0) xneg[buf][0][srow] = -136.f * v;
+            }
+#pragma unroll
+            for (int v = 0; v < SPT; ++v) {
+                const int i = tid + v * NT;
+                if (i < NG * BN) sl[buf][i / BN][i % BN] = sreg[v];
+            }
+        };
+        auto compute = [&](int buf, const uint4(&W)[CT]) {
+            uint32_t wj[CT][4];
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) {
+                wj[ct][0] = W[ct].x;
+                wj[ct][1] = W[ct].y;
+                wj[ct][2] = W[ct].z;
+                wj[ct][3] = W[ct].w;
+                if constexpr (C::kTrans) transpose_rows_words(wj[ct][0], wj[ct][1], wj[ct][2], wj[ct][3]);
+            }
+            const int rbase = wr * MBW * 16;
+#pragma unroll
+            for (int q = 0; q < NG; ++q) {
+                f32x4 P[MBW][CT];
+#pragma unroll
+                for (int rb = 0; rb < MBW; ++rb) {
+                    const f32x4 c = *(const f32x4 *)&xneg[buf][q][rbase + rb * 16 + 4 * g];
+#pragma unroll
+                    for (int ct = 0; ct < CT; ++ct) P[rb][ct] = c;
+                }
+#pragma unroll
+                for (int jj = 0; jj < SPG; ++jj) {
+                    const int j = q * SPG + jj;
+                    const int koff = C::kTrans ? (32 * j + 8 * g) : (32 * g + 8 * j);
+                    uint4 A[MBW];
+#pragma unroll
+                    for (int rb = 0; rb < MBW; ++rb) A[rb] = *(const uint4 *)&xs[buf][rbase + rb * 16 + r][koff];
+#pragma unroll
+                    for (int ct = 0; ct < CT; ++ct) {
+                        const uint4 B = word_to_bf16x8(wj[ct][j]);
+#pragma unroll
+                        for (int rb = 0; rb < MBW; ++rb) P[rb][ct] = mfma16x16x32(A[rb], B, P[rb][ct]);
+                    }
+                }
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) {
+                    const float sf = fp16_bits_to_f32(sl[buf][q][wc * CT * 16 + ct * 16 + r]);
+#pragma unroll
+                    for (int rb = 0; rb < MBW; ++rb)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) acc[rb * CT + ct][i] = __builtin_fmaf(sf, P[rb][ct][i], acc[rb * CT + ct][i]);
+                }
+            }
+        };
+
+        __syncthreads();  // LDS of a previous segment is no longer read
+        load_x(s0);
+        load_w(wcur, s0);
+        for (int s = s0; s < s1; ++s) {
+            const int buf = (s - s0) & 1;
+            store_stage(buf);
+            __syncthreads();
+            if (s + 1 < s1) {
+                load_x(s + 1);
+                load_w(wnext, s + 1);
+            }
+            compute(buf, wcur);
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) wcur[ct] = wnext[ct];
+        }
+
+        // ---- epilogue ----
+        const int rowb = row0 + wr * MBW * 16 + 4 * g;
+        auto store_out = [&]() {
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) {
+                if (!ctv[ct]) continue;
+                const int colg = (cb * (BN / 16) + wc * CT + ct) * 16 + r;
+#pragma unroll
+                for (int rb = 0; rb < MBW; ++rb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int row = rowb + rb * 16 + i;
+                        if (row < M) out[(size_t)row * N + colg] = f32_to_bf16_rne(acc[rb * CT + ct][i]);
+                    }
+            }
+        };
+        if ((s0 == 0 && s1 == KT) || sk_fixup<NV, NT>(acc, tile, KT, units, grid, maxt, cnt, part, &s_last))
+            store_out();
+        u += s1 - s0;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// host launchers
+// ---------------------------------------------------------------------------
+namespace {
+constexpr int kSkinnyWaves = 8;
+constexpr int kSkinnyDepth = 2;
+
+template <int GS>
+hipError_t skinny_launch(const void *x, const int32_t *wt, const void *sc, void *out, int M,
+                         int64_t N, int64_t K, hipStream_t stream) {
+    hipLaunchKernelGGL((w4a16_skinny_kernel<kSkinnyWaves, kSkinnyDepth, GS>), dim3((uint32_t)(N / 16)),
+                       dim3(64 * kSkinnyWaves), 0, stream, (const uint16_t *)x, (const uint4 *)wt,
+                       (const uint16_t *)sc, (uint16_t *)out, M, (int)N, (int)K);
+    return hipGetLastError();
+}
+
+template <int MBW, int WR, int WC, int CT, int GS>
+hipError_t wide_launch(const WidePlan &p, const void *x, const int32_t *wt, const void *sc,
+                       void *out, int64_t M, int64_t N, int64_t K, void *ws, hipStream_t stream) {
+    const size_t cnt_bytes = ((size_t)p.row_tiles * p.col_tiles * 4 + 255) & ~(size_t)255;
+    uint32_t *cnt = (uint32_t *)ws;
+    f32x4 *part = ws ? (f32x4 *)((char *)ws + cnt_bytes) : nullptr;
+    hipLaunchKernelGGL((w4a16_wide_kernel<MBW, WR, WC, CT, GS>), dim3((uint32_t)p.grid),
+                       dim3(64 * WR * WC), 0, stream, (const uint16_t *)x, (const uint4 *)wt,
+                       (const uint16_t *)sc, (uint16_t *)out, cnt, part, (int)M, (int)N, (int)K,
+                       p.col_tiles, p.units, p.grid, p.maxt);
+    return hipGetLastError();
+}
+
+template <int GS>
+hipError_t wide_by_shape(const WidePlan &p, const void *x, const int32_t *wt, const void *sc,
+                         void *out, int64_t M, int64_t N, int64_t K, void *ws, hipStream_t stream) {
+    if (p.bm == 128) return wide_launch<4, 2, 2, 4, GS>(p, x, wt, sc, out, M, N, K, ws, stream);
+    return wide_launch<4, 1, 4, 4, GS>(p, x, wt, sc, out, M, N, K, ws, stream);
+}
+}  // namespace
+
+hipError_t launch_w4a16_skinny(const void *x, const int32_t *wt, const void *scales, void *out,
+                               int M, int64_t N, int64_t K, int G, hipStream_t stream) {
+    switch (G) {
+    case 32: return skinny_launch<5>(x, wt, scales, out, M, N, K, stream);
+    case 64: return skinny_launch<6>(x, wt, scales, out, M, N, K, stream);
+    case 128: return skinny_launch<7>(x, wt, scales, out, M, N, K, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_w4a16_wide(const WidePlan &plan, const void *x, const int32_t *wt,
+                             const void *scales, void *out, int64_t M, int64_t N, int64_t K,
+                             int G, void *workspace, hipStream_t stream) {
+    switch (G) {
+    case 32: return wide_by_shape<5>(plan, x, wt, scales, out, M, N, K, workspace, stream);
+    case 64: return wide_by_shape<6>(plan, x, wt, scales, out, M, N, K, workspace, stream);
+    case 128: return wide_by_shape<7>(plan, x, wt, scales, out, M, N, K, workspace, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace svq

@@ -1,0 +1,127 @@
+"""The C ABI without a GPU: the library loads, exports every symbol declared in
+include/svq.h, and rejects every invalid argument on the host before anything
+reaches the HIP runtime (no compute call is made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    import spec_verify_amd as svq
+    if not os.path.exists(svq.library_path):
+        from spec_verify_amd import build
+        build.build()
+    return svq.lib()
+
+
+def _declared_symbols():
+    with open(os.path.join(ROOT, "include", "svq.h")) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"\b(svq_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(L):
+    import spec_verify_amd as svq
+    declared = _declared_symbols()
+    assert len(declared) >= 12
+    for name in declared:
+        assert hasattr(L, name), name
+    assert sorted(svq.EXPORTED_SYMBOLS) == declared
+    assert L.svq_abi_version() == 1
+
+
+def test_status_strings(L):
+    for code in range(0, 11):
+        assert L.svq_status_string(code)
+    assert L.svq_status_string(999) == b"unknown status"
+
+
+FAKE = 1 << 20          # aligned, never dereferenced: every call below fails validation first
+FAKE2 = 1 << 30
+FAKE3 = 1 << 34
+FAKE4 = 1 << 38
+
+
+def _w4(L, M=1, N=256, K=512, G=128, x=FAKE, w=FAKE2, s=FAKE3, o=FAKE4, kernel=0, ws=None, wsb=0):
+    return L.svq_w4a16_gemm_with(kernel, x, w, s, o, M, N, K, G, ws, wsb, None)
+
+
+def test_w4a16_validation(L):
+    assert _w4(L, x=None) == 1
+    assert _w4(L, o=None) == 1
+    assert _w4(L, M=0) == 2
+    assert _w4(L, N=-16) == 2
+    assert _w4(L, K=1 << 25) == 2
+    assert _w4(L, G=16) == 3
+    assert _w4(L, G=256) == 3
+    assert _w4(L, N=250) == 4
+    assert _w4(L, K=320, G=32) == 4          # K % 128
+    assert _w4(L, x=FAKE + 2) == 6            # x needs 16-byte alignment
+    assert _w4(L, w=FAKE2 + 8) == 6
+    assert _w4(L, s=FAKE3 + 1) == 6
+    assert _w4(L, o=FAKE4 + 2) == 6
+    assert _w4(L, o=FAKE + 64) == 7            # out overlaps x
+    assert _w4(L, M=9, kernel=1) == 10        # dot2 kernel takes M <= 8
+    assert _w4(L, M=17, kernel=2) == 10       # skinny kernel takes M <= 16
+    assert _w4(L, kernel=7) == 10
+
+
+def test_mxfp8_validation(L):
+    def mx(M=1, N=256, K=512, G=32, x=FAKE, w=FAKE2, s=FAKE3, o=FAKE4, kernel=0):
+        return L.svq_mxfp8_gemm_with(kernel, x, w, s, o, M, N, K, G, None, 0, None)
+    assert mx(w=None) == 1
+    assert mx(K=0) == 2
+    assert mx(G=128) == 3
+    assert mx(N=96) == 5                      # the N >= 128 constraint, as an error code
+    assert mx(K=520) == 5                     # K % 32
+    assert mx(K=160) == 4                     # K % 128 (this library's tile height)
+    assert mx(N=136) == 4
+    assert mx(x=FAKE + 8) == 6
+    assert mx(o=FAKE2 + 4) == 7
+    assert mx(M=9, kernel=1) == 10
+
+
+def test_repack_validation(L):
+    assert L.svq_q4_repack(None, FAKE2, 256, 512, None) == 1
+    assert L.svq_q4_repack(FAKE, FAKE2, 0, 512, None) == 2
+    assert L.svq_q4_repack(FAKE, FAKE2, 24, 512, None) == 4
+    assert L.svq_q4_repack(FAKE, FAKE2, 256, 192, None) == 4
+    assert L.svq_q4_repack(FAKE + 4, FAKE2, 256, 512, None) == 6
+    assert L.svq_q4_repack(FAKE, FAKE + 4096, 256, 512, None) == 7
+    assert L.svq_q4_repacked_bytes(5120, 17408) == 5120 * 17408 // 2
+    assert L.svq_q4_repacked_bytes(0, 5) == 0
+
+
+def test_kernel_selection_names(L):
+    name = lambda k, M: L.svq_w4a16_kernel_name(k, M, 5120, 5120, 128)
+    assert name(0, 1) == b"w4a16_dot2_kernel"
+    assert name(0, 5) == b"w4a16_skinny_kernel"
+    assert name(0, 128) == b"w4a16_wide_kernel"
+    assert name(1, 9) is None
+    assert L.svq_w4a16_kernel_name(0, 1, 5120, 5121, 128) is None
+    assert L.svq_mxfp8_kernel_name(0, 1, 5120, 5120) == b"mxfp8_dot2_kernel"
+    assert L.svq_mxfp8_kernel_name(0, 5, 5120, 5120) == b"mxfp8_skinny_kernel"
+    assert L.svq_mxfp8_kernel_name(0, 128, 5120, 5120) == b"mxfp8_wide_kernel"
+    assert L.svq_mxfp8_kernel_name(0, 1, 96, 5120) is None
+
+
+def test_workspace_query_rejects_bad_shapes(L):
+    bad = ctypes.c_size_t(-1).value
+    assert L.svq_w4a16_workspace_bytes(0, 1, 5120, 5121, 128) == bad
+    assert L.svq_w4a16_workspace_bytes(1, 9, 5120, 5120, 128) == bad
+    assert L.svq_w4a16_workspace_bytes(0, 1, 5120, 5120, 128) == 0      # dot2: no workspace
+    assert L.svq_w4a16_workspace_bytes(2, 5, 5120, 5120, 128) == 0      # skinny: no workspace
+    assert L.svq_mxfp8_workspace_bytes(0, 1, 96, 5120) == bad
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    import spec_verify_amd as svq
+    monkeypatch.setattr(svq, "_lib", None)
+    monkeypatch.setattr(svq, "library_path", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="libsvq.so not found"):
+        svq.lib()

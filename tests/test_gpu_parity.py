@@ -1,0 +1,279 @@
+"""GPU parity: every HIP kernel through the C ABI against the CPU oracle on the
+same seeded inputs.
+
+Tolerance (random inputs): max |fp32(out) - y_ref| <= 2e-2 * RMS(y_ref) against
+both the fp64-summed oracle and the fp32-sequential oracle. Integer-valued inputs
+have one exact answer: outputs must equal bf16_RNE(exact) bit for bit. Repack is
+bit-exact. Small shapes are compared element by element; the full-size
+workloads (in the launch configuration the benchmark times) on sampled outputs.
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a ROCm GPU (torch.cuda.is_available() is False)")
+    import spec_verify_amd as svq
+    if not os.path.exists(svq.library_path):
+        from spec_verify_amd import build
+        build.build()
+    svq.lib()
+    yield
+
+
+def _say(*a):
+    print("[gpu]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def dev(a):
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).cuda()
+
+
+def host_bits(t):
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def run_w4a16(inp, kernel=0, out=None):
+    import spec_verify_amd as svq
+    qw = dev(inp.qweight)
+    tiled = svq.q4_repack(qw)
+    o = svq.w4a16_gemm(dev(inp.x), tiled, dev(inp.scales), inp.N, inp.G, out=out, kernel=kernel)
+    torch.cuda.synchronize()
+    return host_bits(o), tiled
+
+
+def run_mxfp8(inp, kernel=0):
+    import spec_verify_amd as svq
+    o = svq.mxfp8_gemm(dev(inp.x), dev(inp.w), dev(inp.scales), kernel=kernel)
+    torch.cuda.synchronize()
+    return host_bits(o)
+
+
+def assert_gate(out, y64, y32, label):
+    ok64, e64, rms = oracle.gate(out, y64)
+    ok32, e32, _ = oracle.gate(out, y32.astype(np.float64))
+    assert ok64 and ok32, f"{label}: err64={e64:.4g} err32={e32:.4g} rms={rms:.4g} ratio={e64 / max(rms, 1e-30):.4g}"
+
+
+# ---- repack -------------------------------------------------------------------
+
+@pytest.mark.parametrize("N,K", [(16, 128), (48, 384), (256, 512), (5120, 5120), (1024, 17408)])
+def test_repack_bit_exact(N, K):
+    _say("repack", N, K)
+    inp = synth.gen_w4a16(7 + N, 1, K, N)
+    import spec_verify_amd as svq
+    got = svq.q4_repack(dev(inp.qweight)).cpu().numpy()
+    ref = oracle.q4_repack(inp.qweight)
+    np.testing.assert_array_equal(got, ref)
+    if N * K <= 1 << 20:
+        np.testing.assert_array_equal(oracle.q4_unrepack(got, N, K), inp.qweight)
+
+
+# ---- W4A16 small shapes, every kernel -------------------------------------------
+
+KNAME = {1: "dot2", 2: "skinny", 3: "wide"}
+
+
+def _ids(cases):
+    return ["-".join([KNAME[c[0]]] + [str(v) for v in c[1:]]) for c in cases]
+
+
+W4_CASES = (
+    [(1, m, K, N, G) for m in (1, 2, 3, 5, 8) for (K, N) in ((512, 48), (1280, 32)) for G in (32, 64, 128)]
+    + [(2, m, K, N, G) for m in (1, 3, 5, 11, 16) for (K, N) in ((512, 48), (1280, 32)) for G in (32, 64, 128)]
+    + [(3, m, K, N, G) for m in (1, 17, 64, 65, 128, 130) for (K, N) in ((1024, 272), (2560, 128)) for G in (32, 128)]
+    + [(3, 33, 640, 16, 64)]
+)
+
+
+@pytest.mark.parametrize("kernel,M,K,N,G", W4_CASES, ids=_ids(W4_CASES))
+def test_w4a16_random(kernel, M, K, N, G):
+    _say("w4a16 random kernel", kernel, "M K N G", M, K, N, G)
+    inp = synth.gen_w4a16(1000 + 7 * M + K + N + G, M, K, N, G)
+    out, _ = run_w4a16(inp, kernel)
+    y64, y32 = oracle.w4a16(inp.x, inp.qweight, inp.scales, G)
+    assert_gate(out, y64, y32, f"kernel {kernel} M{M} K{K} N{N} G{G}")
+
+
+W4_EXACT = [
+    (1, 1, 1024, 32, 128), (1, 5, 1024, 32, 32), (1, 8, 640, 48, 64),
+    (2, 1, 1024, 32, 128), (2, 7, 1024, 32, 32), (2, 16, 640, 48, 64),
+    (3, 128, 1024, 272, 128), (3, 40, 1024, 144, 32), (3, 130, 640, 128, 64),
+]
+
+
+@pytest.mark.parametrize("kernel,M,K,N,G", W4_EXACT, ids=_ids(W4_EXACT))
+def test_w4a16_integer_exact(kernel, M, K, N, G):
+    _say("w4a16 intexact kernel", kernel, "M K N G", M, K, N, G)
+    inp = synth.gen_w4a16(77 + M, M, K, N, G, kind="intexact", keep_q=True)
+    out, _ = run_w4a16(inp, kernel)
+    xi = oracle.bf16_bits_to_f64(inp.x).astype(np.int64)
+    exact = xi @ (inp.q.astype(np.int64) - 8)
+    np.testing.assert_array_equal(out, oracle.bf16_rne(exact.astype(np.float32)))
+
+
+# ---- W4A16 full-size workloads ---------------------------------------------------
+
+def _sample(M, N, n, seed):
+    rng = np.random.default_rng(seed)
+    rows = rng.integers(0, M, n)
+    cols = rng.integers(0, N, n)
+    rows[:4] = [0, M - 1, 0, M - 1]
+    cols[:4] = [0, 0, N - 1, N - 1]
+    return rows, cols
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode_n5120", "decode_n6144", "decode_n1024",
+                                  "verify5_up", "verify5_down", "verify3_up", "verify3_down",
+                                  "batch128_up", "batch128_down"])
+def test_w4a16_workloads(name):
+    w = synth.WORKLOADS[name]
+    _say("w4a16 workload", name, w)
+    inp = synth.gen_workload(name)
+    out, tiled = run_w4a16(inp)
+    if inp.M * inp.N * inp.K <= 5 * 17408 * 5120:
+        y64, y32 = oracle.w4a16(inp.x, inp.qweight, inp.scales)
+        assert_gate(out, y64, y32, name)
+    else:
+        rows, cols = _sample(inp.M, inp.N, 1500, w["seed"])
+        y64, y32 = oracle.w4a16_points(inp.x, inp.qweight, inp.scales, 128, rows, cols)
+        sel = out[rows, cols]
+        # the gate's RMS is that of the whole output; the sample estimates it
+        ok, err, rms = oracle.gate(sel, y64)
+        assert ok, f"{name}: err={err:.4g} rms={rms:.4g}"
+        assert oracle.gate(sel, y32.astype(np.float64))[0]
+        assert np.all(np.isfinite(oracle.bf16_bits_to_f64(out)))
+    # the repacked weights of the full-size run are the oracle's, bit for bit
+    np.testing.assert_array_equal(tiled.cpu().numpy(), oracle.q4_repack(inp.qweight))
+
+
+# ---- MXFP8 -------------------------------------------------------------------------
+
+MX_CASES = (
+    [(1, m, K, N) for m in (1, 2, 5, 8) for (K, N) in ((512, 128), (1280, 144))]
+    + [(2, m, K, N) for m in (1, 5, 16) for (K, N) in ((512, 128), (1280, 144))]
+    + [(3, m, K, N) for m in (1, 17, 64, 128, 130) for (K, N) in ((1024, 272), (640, 128))]
+)
+
+
+@pytest.mark.parametrize("kernel,M,K,N", MX_CASES, ids=_ids(MX_CASES))
+def test_mxfp8_random(kernel, M, K, N):
+    _say("mxfp8 random kernel", kernel, "M K N", M, K, N)
+    inp = synth.gen_mxfp8(2000 + M + K + N, M, K, N)
+    out = run_mxfp8(inp, kernel)
+    y64, y32 = oracle.mxfp8(inp.x, inp.w, inp.scales)
+    assert_gate(out, y64, y32, f"mxfp8 kernel {kernel} M{M} K{K} N{N}")
+
+
+MX_EXACT = [(1, 1), (1, 8), (2, 3), (2, 16), (3, 64), (3, 130)]
+
+
+@pytest.mark.parametrize("kernel,M", MX_EXACT, ids=_ids(MX_EXACT))
+def test_mxfp8_integer_exact(kernel, M):
+    _say("mxfp8 intexact kernel", kernel, "M", M)
+    inp = synth.gen_mxfp8(88 + M, M, 640, 272, kind="intexact")
+    out = run_mxfp8(inp, kernel)
+    table = oracle.e4m3_table()
+    exact = oracle.bf16_bits_to_f64(inp.x).astype(np.int64) @ table[inp.w].astype(np.int64).T
+    np.testing.assert_array_equal(out, oracle.bf16_rne(exact.astype(np.float32)))
+
+
+@pytest.mark.parametrize("kernel", [1, 2, 3], ids=["dot2", "skinny", "wide"])
+@pytest.mark.parametrize("scale_code", [127, 120, 131])
+def test_mxfp8_hardware_decode_all_codes(kernel, scale_code):
+    """Column n holds E4M3 code n at every K; x is one-hot, so y[0, n] is the
+    decoded value of code n times 2^(scale-127): all 254 finite codes through
+    the kernel's own conversion, against the oracle's decoder."""
+    _say("mxfp8 all codes kernel", kernel, "scale", scale_code)
+    N, K = 256, 128
+    codes = np.arange(256, dtype=np.uint8)
+    codes[[0x7F, 0xFF]] = 0                       # NaN codes are not inputs
+    w = np.repeat(codes[:, None], K, axis=1)
+    sc = np.full((N, K // 32), scale_code, dtype=np.uint8)
+    x = np.zeros((1, K), dtype=np.uint16)
+    x[0, 37] = 0x3F80                             # 1.0
+    inp = synth.MXFP8Inputs(1, K, N, x, w, sc)
+    out = run_mxfp8(inp, kernel)
+    vals = np.array([oracle.e4m3_to_f64(int(c)) for c in codes]) * oracle.e8m0_to_f64(scale_code)
+    vals = vals + 0.0    # a sum that starts from +0 turns the code 0x80 (-0) into +0
+    np.testing.assert_array_equal(out[0], oracle.bf16_rne(vals.astype(np.float32)))
+
+
+@pytest.mark.parametrize("name", ["mxfp8_m1", "mxfp8_m5", "mxfp8_m128"])
+def test_mxfp8_workloads(name):
+    w = synth.WORKLOADS[name]
+    _say("mxfp8 workload", name, w)
+    inp = synth.gen_workload(name)
+    out = run_mxfp8(inp)
+    if inp.M <= 5:
+        y64, y32 = oracle.mxfp8(inp.x, inp.w, inp.scales)
+        assert_gate(out, y64, y32, name)
+    else:
+        rows, cols = _sample(inp.M, inp.N, 1500, w["seed"])
+        y64, y32 = oracle.mxfp8_points(inp.x, inp.w, inp.scales, rows, cols)
+        ok, err, rms = oracle.gate(out[rows, cols], y64)
+        assert ok, f"{name}: err={err:.4g} rms={rms:.4g}"
+
+
+# ---- properties of the launch path -------------------------------------------------
+
+def test_wide_deterministic_and_counters_cleared():
+    import spec_verify_amd as svq
+    inp = synth.gen_w4a16(5, 128, 2560, 272)
+    x, qw, s = dev(inp.x), dev(inp.qweight), dev(inp.scales)
+    tiled = svq.q4_repack(qw)
+    nbytes = svq.w4a16_workspace_bytes(128, 272, 2560)
+    assert nbytes > 0                          # this shape splits tiles across workgroups
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    a = svq.w4a16_gemm(x, tiled, s, 272, workspace=ws)
+    b = svq.w4a16_gemm(x, tiled, s, 272, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    tiles = 1 * 3                              # 128-row x 128-column tiles
+    assert int(ws[: 4 * tiles].count_nonzero()) == 0
+
+
+def test_output_canaries_and_error_path_leave_memory_untouched():
+    import spec_verify_amd as svq
+    M, K, N = 5, 1024, 64
+    inp = synth.gen_w4a16(9, M, K, N)
+    x, s = dev(inp.x), dev(inp.scales)
+    tiled = svq.q4_repack(dev(inp.qweight))
+    guard = 64
+    buf = torch.full((M * N + 2 * guard,), 0x7A5A, dtype=torch.int16, device="cuda")
+    out = buf[guard:guard + M * N].view(M, N)
+    svq.w4a16_gemm(x, tiled, s, N, out=out)
+    torch.cuda.synchronize()
+    assert int((buf[:guard] != 0x7A5A).sum()) == 0 and int((buf[-guard:] != 0x7A5A).sum()) == 0
+    y64, y32 = oracle.w4a16(inp.x, inp.qweight, inp.scales)
+    assert_gate(host_bits(out), y64, y32, "canary run")
+    before = buf.clone()
+    bad_x = torch.zeros(M * K + 1, dtype=torch.int16, device="cuda")[1:].view(M, K)  # 2-byte offset
+    with pytest.raises(svq.SvqError) as e:
+        svq.w4a16_gemm(bad_x, tiled, s, N, out=out)
+    assert e.value.status == 6
+    torch.cuda.synchronize()
+    assert torch.equal(buf, before)
+
+
+def test_kernel_names_match_dispatch():
+    import spec_verify_amd as svq
+    assert svq.w4a16_kernel_name(1, 5120, 5120) == "w4a16_dot2_kernel"
+    assert svq.w4a16_kernel_name(5, 17408, 5120) == "w4a16_skinny_kernel"
+    assert svq.w4a16_kernel_name(128, 17408, 5120) == "w4a16_wide_kernel"

@@ -32,69 +32,63 @@ __device__ __forceinline__ uint4 cvt8_e4m3_bf16(uint32_t lo, uint32_t hi, float 
 // ---------------------------------------------------------------------------
 // dot2 kernel, M <= 8
 // ---------------------------------------------------------------------------
-template <int M>
-struct MxDot2Stage {
-    uint4 w0, w1;    // 32 codes: K-rows 32*(lane/16) + 0..31 of column lane%16
-    uint32_t x[M];   // bf16 pair (rows 2*lane, 2*lane+1 of the tile)
-    uint32_t s;      // E8M0 code of this lane's block
-};
-
 template <int M, int WAVES, int D>
 __global__ __launch_bounds__(64 * WAVES) void mxfp8_dot2_kernel(
     const uint32_t *__restrict__ x, const uint8_t *__restrict__ w,
-    const uint8_t *__restrict__ sc, uint16_t *__restrict__ out, int N, int K) {
+    const uint8_t *__restrict__ sc, uint16_t *__restrict__ out, uint32_t *__restrict__ cnt,
+    float *__restrict__ part, int N, int K, int splits, int S) {
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int rg = lane >> 4;
-    const int nb = blockIdx.x;
+    const int wave = wave_id();
+    const int r = lane & 15, rg = lane >> 4;
+    const int nb = blockIdx.x / splits, sp = blockIdx.x % splits;
     const int KT = K >> 7;
-    const int col = nb * 16 + (lane & 15);
-    const size_t KH = (size_t)K >> 1;
-    const uint8_t *wp = w + (size_t)col * K + rg * 32;
-    const uint8_t *sp = sc + (size_t)col * (K >> 5) + rg;
-    const uint32_t *xp = x + lane;
-    const int ntile = wave < KT ? (KT - 1 - wave) / WAVES + 1 : 0;
+    // this block's 16 weight rows ([N][K] layout) and their scale rows
+    const __amdgpu_buffer_rsrc_t wr = make_rsrc(w + (size_t)nb * 16 * K, (uint32_t)16 * K);
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, (uint32_t)M * K * 2);
+    const __amdgpu_buffer_rsrc_t sr = make_rsrc(sc + (size_t)nb * 16 * (K >> 5), (uint32_t)16 * (K >> 5));
+    const uint32_t w_vo = r * K + rg * 32;
+    const uint32_t x_vo = lane * 4;
+    const uint32_t s_vo = r * (K >> 5) + rg;
+    // this workgroup's K range: tiles [kbeg, kbeg + kcnt) of the column block
+    const int kbeg = sp * S;
+    const int kcnt = KT - kbeg < S ? KT - kbeg : S;
+    const int ntile = wave < kcnt ? (kcnt - 1 - wave) / WAVES + 1 : 0;
 
     float acc[M];
 #pragma unroll
     for (int m = 0; m < M; ++m) acc[m] = 0.f;
+    uint4 vA[D][2], vB[D][2];
+    uint32_t xA[D][M], xB[D][M], sA[D], sB[D];
 
-    auto load = [&](MxDot2Stage<M>(&S)[D], int i0) {
-#pragma unroll
-        for (int d = 0; d < D; ++d) {
-            int i = i0 + d;
-            i = i < ntile ? i : ntile - 1;
-            const int kt = wave + i * WAVES;
-            S[d].w0 = load_stream16(wp + (size_t)kt * 128);
-            S[d].w1 = load_stream16(wp + (size_t)kt * 128 + 16);
-#pragma unroll
-            for (int m = 0; m < M; ++m) S[d].x[m] = xp[m * KH + (size_t)kt * 64];
-            S[d].s = sp[(size_t)kt * 4];
-        }
-    };
-
-    auto tile = [&](const MxDot2Stage<M> &S) {
-        const float sf = e8m0_to_f32(S.s);
-        const uint32_t wd[8] = {S.w0.x, S.w0.y, S.w0.z, S.w0.w, S.w1.x, S.w1.y, S.w1.z, S.w1.w};
-        mxfp8_tile_dots<M>(acc, S.x, wd, sf);
-    };
-
-    auto compute = [&](const MxDot2Stage<M>(&S)[D], int i0) {
-#pragma unroll
-        for (int d = 0; d < D; ++d)
-            if (i0 + d < ntile) tile(S[d]);
-    };
+#define SVQ_LOAD(V, X, S, I0)                                                        \
+    _Pragma("unroll") for (int d = 0; d < D; ++d) if ((I0) + d < ntile) {            \
+        const int kt = kbeg + wave + ((I0) + d) * WAVES;                                    \
+        V[d][0] = bload16(wr, w_vo, kt * 128);                                       \
+        V[d][1] = bload16(wr, w_vo + 16, kt * 128);                                  \
+        _Pragma("unroll") for (int m = 0; m < M; ++m) X[d][m] = bload4(xr, x_vo, m * K * 2 + kt * 256); \
+        S[d] = bload1(sr, s_vo, kt * 4);                                             \
+    }
+#define SVQ_COMPUTE(V, X, S, I0)                                                     \
+    _Pragma("unroll") for (int d = 0; d < D; ++d) if ((I0) + d < ntile) {            \
+        const float sf = e8m0_to_f32(S[d]);                                          \
+        const uint32_t wd[8] = {V[d][0].x, V[d][0].y, V[d][0].z, V[d][0].w,          \
+                                V[d][1].x, V[d][1].y, V[d][1].z, V[d][1].w};         \
+        mxfp8_tile_dots<M>(acc, X[d], wd, sf);                                       \
+    }
 
     if (ntile > 0) {
-        MxDot2Stage<M> A[D], B[D];
-        load(A, 0);
-        for (int i0 = 0; i0 < ntile; i0 += 2 * D) {
-            load(B, i0 + D);
-            compute(A, i0);
-            load(A, i0 + 2 * D);
-            compute(B, i0 + D);
+        SVQ_LOAD(vA, xA, sA, 0)
+        for (int i0 = 0;; i0 += 2 * D) {
+            SVQ_LOAD(vB, xB, sB, i0 + D)
+            SVQ_COMPUTE(vA, xA, sA, i0)
+            if (i0 + D >= ntile) break;
+            SVQ_LOAD(vA, xA, sA, i0 + 2 * D)
+            SVQ_COMPUTE(vB, xB, sB, i0 + D)
+            if (i0 + 2 * D >= ntile) break;
         }
     }
+#undef SVQ_LOAD
+#undef SVQ_COMPUTE
 
     __shared__ float red[WAVES][M][16];
 #pragma unroll
@@ -103,91 +97,85 @@ __global__ __launch_bounds__(64 * WAVES) void mxfp8_dot2_kernel(
         if (lane < 16) red[wave][m][lane] = v;
     }
     __syncthreads();
-    for (int t = threadIdx.x; t < M * 16; t += 64 * WAVES) {
-        const int m = t >> 4, c = t & 15;
-        float s = 0.f;
+    __shared__ int s_flag;
+    float v = 0.f;
+    if (threadIdx.x < 16 * M) {
 #pragma unroll
-        for (int wv = 0; wv < WAVES; ++wv) s += red[wv][m][c];
-        out[(size_t)m * N + nb * 16 + c] = f32_to_bf16_rne(s);
+        for (int wv = 0; wv < WAVES; ++wv) v += red[wv][threadIdx.x >> 4][threadIdx.x & 15];
     }
+    smallm_finish(v, M, N, nb, sp, splits, out, cnt, part, &s_flag);
 }
 
 // ---------------------------------------------------------------------------
 // skinny MFMA kernel, M <= 16
 // ---------------------------------------------------------------------------
-struct MxSkinnyStage {
-    uint4 w0, w1;
-    uint4 a[4];
-    uint32_t s;
-};
-
 template <int WAVES, int D>
 __global__ __launch_bounds__(64 * WAVES) void mxfp8_skinny_kernel(
     const uint16_t *__restrict__ x, const uint8_t *__restrict__ w,
-    const uint8_t *__restrict__ sc, uint16_t *__restrict__ out, int M, int N, int K) {
+    const uint8_t *__restrict__ sc, uint16_t *__restrict__ out, uint32_t *__restrict__ cnt,
+    float *__restrict__ part, int M, int N, int K, int splits, int S) {
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = wave_id();
     const int r = lane & 15, g = lane >> 4;
-    const int nb = blockIdx.x;
+    const int nb = blockIdx.x / splits, sp = blockIdx.x % splits;
     const int KT = K >> 7;
-    const int col = nb * 16 + r;
-    const uint8_t *wp = w + (size_t)col * K + g * 32;
-    const uint8_t *sp = sc + (size_t)col * (K >> 5) + g;
-    const bool arow = r < M;
-    const uint16_t *xr = x + (size_t)(arow ? r : 0) * K + g * 32;
-    const int ntile = wave < KT ? (KT - 1 - wave) / WAVES + 1 : 0;
+    const __amdgpu_buffer_rsrc_t wr = make_rsrc(w + (size_t)nb * 16 * K, (uint32_t)16 * K);
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, (uint32_t)M * K * 2);
+    const __amdgpu_buffer_rsrc_t sr = make_rsrc(sc + (size_t)nb * 16 * (K >> 5), (uint32_t)16 * (K >> 5));
+    const uint32_t w_vo = r * K + g * 32;
+    const uint32_t x_vo = r * K * 2 + g * 64;     // rows >= M read as zero
+    const uint32_t s_vo = r * (K >> 5) + g;
+    // this workgroup's K range: tiles [kbeg, kbeg + kcnt) of the column block
+    const int kbeg = sp * S;
+    const int kcnt = KT - kbeg < S ? KT - kbeg : S;
+    const int ntile = wave < kcnt ? (kcnt - 1 - wave) / WAVES + 1 : 0;
 
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    uint4 vA[D][2], vB[D][2], aA[D][4], aB[D][4];
+    uint32_t sA[D], sB[D];
 
-    auto load = [&](MxSkinnyStage(&S)[D], int i0) {
-#pragma unroll
-        for (int d = 0; d < D; ++d) {
-            int i = i0 + d;
-            i = i < ntile ? i : ntile - 1;
-            const int kt = wave + i * WAVES;
-            S[d].w0 = load_stream16(wp + (size_t)kt * 128);
-            S[d].w1 = load_stream16(wp + (size_t)kt * 128 + 16);
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                S[d].a[j] = arow ? *(const uint4 *)(xr + (size_t)kt * 128 + 8 * j) : make_uint4(0, 0, 0, 0);
-            S[d].s = sp[(size_t)kt * 4];
-        }
-    };
-
-    auto compute = [&](const MxSkinnyStage(&S)[D], int i0) {
-#pragma unroll
-        for (int d = 0; d < D; ++d) {
-            if (i0 + d >= ntile) continue;
-            const float sf = e8m0_to_f32(S[d].s);
-            acc = mfma16x16x32(S[d].a[0], cvt8_e4m3_bf16(S[d].w0.x, S[d].w0.y, sf), acc);
-            acc = mfma16x16x32(S[d].a[1], cvt8_e4m3_bf16(S[d].w0.z, S[d].w0.w, sf), acc);
-            acc = mfma16x16x32(S[d].a[2], cvt8_e4m3_bf16(S[d].w1.x, S[d].w1.y, sf), acc);
-            acc = mfma16x16x32(S[d].a[3], cvt8_e4m3_bf16(S[d].w1.z, S[d].w1.w, sf), acc);
-        }
-    };
+#define SVQ_LOAD(V, A, S, I0)                                                        \
+    _Pragma("unroll") for (int d = 0; d < D; ++d) if ((I0) + d < ntile) {            \
+        const int kt = kbeg + wave + ((I0) + d) * WAVES;                                    \
+        V[d][0] = bload16(wr, w_vo, kt * 128);                                       \
+        V[d][1] = bload16(wr, w_vo + 16, kt * 128);                                  \
+        _Pragma("unroll") for (int j = 0; j < 4; ++j) A[d][j] = bload16(xr, x_vo + 16 * j, kt * 256); \
+        S[d] = bload1(sr, s_vo, kt * 4);                                             \
+    }
+#define SVQ_COMPUTE(V, A, S, I0)                                                     \
+    _Pragma("unroll") for (int d = 0; d < D; ++d) if ((I0) + d < ntile) {            \
+        const float sf = e8m0_to_f32(S[d]);                                          \
+        acc = mfma16x16x32(A[d][0], cvt8_e4m3_bf16(V[d][0].x, V[d][0].y, sf), acc);  \
+        acc = mfma16x16x32(A[d][1], cvt8_e4m3_bf16(V[d][0].z, V[d][0].w, sf), acc);  \
+        acc = mfma16x16x32(A[d][2], cvt8_e4m3_bf16(V[d][1].x, V[d][1].y, sf), acc);  \
+        acc = mfma16x16x32(A[d][3], cvt8_e4m3_bf16(V[d][1].z, V[d][1].w, sf), acc);  \
+    }
 
     if (ntile > 0) {
-        MxSkinnyStage A[D], B[D];
-        load(A, 0);
-        for (int i0 = 0; i0 < ntile; i0 += 2 * D) {
-            load(B, i0 + D);
-            compute(A, i0);
-            load(A, i0 + 2 * D);
-            compute(B, i0 + D);
+        SVQ_LOAD(vA, aA, sA, 0)
+        for (int i0 = 0;; i0 += 2 * D) {
+            SVQ_LOAD(vB, aB, sB, i0 + D)
+            SVQ_COMPUTE(vA, aA, sA, i0)
+            if (i0 + D >= ntile) break;
+            SVQ_LOAD(vA, aA, sA, i0 + 2 * D)
+            SVQ_COMPUTE(vB, aB, sB, i0 + D)
+            if (i0 + 2 * D >= ntile) break;
         }
     }
+#undef SVQ_LOAD
+#undef SVQ_COMPUTE
 
     __shared__ float red[WAVES][16][17];
 #pragma unroll
     for (int i = 0; i < 4; ++i) red[wave][4 * g + i][r] = acc[i];
     __syncthreads();
-    for (int t = threadIdx.x; t < M * 16; t += 64 * WAVES) {
-        const int m = t >> 4, c = t & 15;
-        float s = 0.f;
+    __shared__ int s_flag;
+    float v = 0.f;
+    if (threadIdx.x < 16 * M) {
 #pragma unroll
-        for (int wv = 0; wv < WAVES; ++wv) s += red[wv][m][c];
-        out[(size_t)m * N + nb * 16 + c] = f32_to_bf16_rne(s);
+        for (int wv = 0; wv < WAVES; ++wv) v += red[wv][threadIdx.x >> 4][threadIdx.x & 15];
     }
+    smallm_finish(v, M, N, nb, sp, splits, out, cnt, part, &s_flag);
 }
 
 // ---------------------------------------------------------------------------
@@ -324,25 +312,24 @@ __global__ __launch_bounds__(64 * WR * WC) void mxfp8_wide_kernel(
 // host launchers
 // ---------------------------------------------------------------------------
 namespace {
-constexpr int kMxWaves = 8;
+constexpr int kMxWaves = 4;
 constexpr int kMxDot2Depth = 4;
 constexpr int kMxSkinnyDepth = 2;
 
 template <int M>
-hipError_t mx_dot2_launch(const void *x, const uint8_t *w, const uint8_t *sc, void *out, int64_t N,
-                          int64_t K, hipStream_t stream) {
-    hipLaunchKernelGGL((mxfp8_dot2_kernel<M, kMxWaves, kMxDot2Depth>), dim3((uint32_t)(N / 16)),
+hipError_t mx_dot2_launch(const SmallPlan &p, const void *x, const uint8_t *w, const uint8_t *sc,
+                          void *out, int64_t N, int64_t K, void *ws, hipStream_t stream) {
+    hipLaunchKernelGGL((mxfp8_dot2_kernel<M, kMxWaves, kMxDot2Depth>), dim3((uint32_t)(N / 16 * p.splits)),
                        dim3(64 * kMxWaves), 0, stream, (const uint32_t *)x, w, sc, (uint16_t *)out,
-                       (int)N, (int)K);
+                       ws_counters(ws), (float *)ws_partials(ws), (int)N, (int)K, p.splits, p.S);
     return hipGetLastError();
 }
 
 template <int MBW, int WR, int WC, int CT>
 hipError_t mx_wide_launch(const WidePlan &p, const void *x, const uint8_t *w, const uint8_t *sc,
                           void *out, int64_t M, int64_t N, int64_t K, void *ws, hipStream_t stream) {
-    const size_t cnt_bytes = ((size_t)p.row_tiles * p.col_tiles * 4 + 255) & ~(size_t)255;
-    uint32_t *cnt = (uint32_t *)ws;
-    f32x4 *part = ws ? (f32x4 *)((char *)ws + cnt_bytes) : nullptr;
+    uint32_t *cnt = ws_counters(ws);
+    f32x4 *part = (f32x4 *)ws_partials(ws);
     hipLaunchKernelGGL((mxfp8_wide_kernel<MBW, WR, WC, CT>), dim3((uint32_t)p.grid),
                        dim3(64 * WR * WC), 0, stream, (const uint16_t *)x, w, sc, (uint16_t *)out,
                        cnt, part, (int)M, (int)N, (int)K, p.col_tiles, p.units, p.grid, p.maxt);
@@ -350,26 +337,29 @@ hipError_t mx_wide_launch(const WidePlan &p, const void *x, const uint8_t *w, co
 }
 }  // namespace
 
-hipError_t launch_mxfp8_dot2(const void *x, const uint8_t *w, const uint8_t *scales, void *out,
-                             int M, int64_t N, int64_t K, hipStream_t stream) {
+hipError_t launch_mxfp8_dot2(const SmallPlan &plan, const void *x, const uint8_t *w,
+                             const uint8_t *scales, void *out, int M, int64_t N, int64_t K,
+                             void *ws, hipStream_t stream) {
     switch (M) {
-    case 1: return mx_dot2_launch<1>(x, w, scales, out, N, K, stream);
-    case 2: return mx_dot2_launch<2>(x, w, scales, out, N, K, stream);
-    case 3: return mx_dot2_launch<3>(x, w, scales, out, N, K, stream);
-    case 4: return mx_dot2_launch<4>(x, w, scales, out, N, K, stream);
-    case 5: return mx_dot2_launch<5>(x, w, scales, out, N, K, stream);
-    case 6: return mx_dot2_launch<6>(x, w, scales, out, N, K, stream);
-    case 7: return mx_dot2_launch<7>(x, w, scales, out, N, K, stream);
-    case 8: return mx_dot2_launch<8>(x, w, scales, out, N, K, stream);
+    case 1: return mx_dot2_launch<1>(plan, x, w, scales, out, N, K, ws, stream);
+    case 2: return mx_dot2_launch<2>(plan, x, w, scales, out, N, K, ws, stream);
+    case 3: return mx_dot2_launch<3>(plan, x, w, scales, out, N, K, ws, stream);
+    case 4: return mx_dot2_launch<4>(plan, x, w, scales, out, N, K, ws, stream);
+    case 5: return mx_dot2_launch<5>(plan, x, w, scales, out, N, K, ws, stream);
+    case 6: return mx_dot2_launch<6>(plan, x, w, scales, out, N, K, ws, stream);
+    case 7: return mx_dot2_launch<7>(plan, x, w, scales, out, N, K, ws, stream);
+    case 8: return mx_dot2_launch<8>(plan, x, w, scales, out, N, K, ws, stream);
     default: return hipErrorInvalidValue;
     }
 }
 
-hipError_t launch_mxfp8_skinny(const void *x, const uint8_t *w, const uint8_t *scales, void *out,
-                               int M, int64_t N, int64_t K, hipStream_t stream) {
-    hipLaunchKernelGGL((mxfp8_skinny_kernel<kMxWaves, kMxSkinnyDepth>), dim3((uint32_t)(N / 16)),
+hipError_t launch_mxfp8_skinny(const SmallPlan &plan, const void *x, const uint8_t *w,
+                               const uint8_t *scales, void *out, int M, int64_t N, int64_t K,
+                               void *ws, hipStream_t stream) {
+    hipLaunchKernelGGL((mxfp8_skinny_kernel<kMxWaves, kMxSkinnyDepth>), dim3((uint32_t)(N / 16 * plan.splits)),
                        dim3(64 * kMxWaves), 0, stream, (const uint16_t *)x, w, scales,
-                       (uint16_t *)out, M, (int)N, (int)K);
+                       (uint16_t *)out, ws_counters(ws), (float *)ws_partials(ws), M, (int)N,
+                       (int)K, plan.splits, plan.S);
     return hipGetLastError();
 }
 

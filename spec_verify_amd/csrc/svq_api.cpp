@@ -59,10 +59,21 @@ static WidePlan make_plan(int64_t M, int64_t N, int64_t K, int num_cus) {
         if (b % KT != 0 || e % KT != 0) shared = true;
     }
     p.maxt = maxt;
-    if (shared) {
-        const size_t cnt_bytes = ((size_t)tiles * 4 + 255) & ~(size_t)255;
-        p.workspace_bytes = cnt_bytes + (size_t)p.grid * p.maxt * kWideAccPerThread * kWideThreads * 16;
-    }
+    if (shared) p.workspace_bytes = kCounterBytes + (size_t)p.grid * p.maxt * kWideAccPerThread * kWideThreads * 16;
+    return p;
+}
+
+SmallPlan plan_smallm(int64_t M, int64_t N, int64_t K, int num_cus) {
+    // about four 4-wave workgroups per compute unit: enough to balance the
+    // column blocks over the chip and keep every CU's loads in flight
+    const int64_t col_blocks = N / 16, KT = K / 128;
+    const int64_t target = 4 * (int64_t)std::max(num_cus, 1);
+    int64_t splits = std::min<int64_t>(std::max<int64_t>((target + col_blocks - 1) / col_blocks, 1), KT);
+    if (col_blocks > (int64_t)kMaxCounters) splits = 1;  // one counter per column block
+    const int64_t S = (KT + splits - 1) / splits;
+    splits = (KT + S - 1) / S;
+    SmallPlan p{(int)splits, (int)S, 0};
+    if (splits > 1) p.workspace_bytes = kCounterBytes + (size_t)col_blocks * splits * 16 * M * 4;
     return p;
 }
 
@@ -203,7 +214,7 @@ size_t svq_w4a16_workspace_bytes(int kernel, int64_t M, int64_t N, int64_t K, in
     if (check_w4a16_shape(M, N, K, G) != SVQ_OK) return (size_t)-1;
     const int k = resolve_kernel(kernel, M, false);
     if (kernel_fits(k, M) != SVQ_OK) return (size_t)-1;
-    if (k != SVQ_KERNEL_MFMA_WIDE) return 0;
+    if (k != SVQ_KERNEL_MFMA_WIDE) return plan_smallm(M, N, K, device_cus()).workspace_bytes;
     return plan_w4a16_wide(M, N, K, device_cus()).workspace_bytes;
 }
 
@@ -221,24 +232,32 @@ int svq_w4a16_gemm_with(int kernel, const void *x, const int32_t *wt, const void
     if (st != SVQ_OK) return st;
     const int k = resolve_kernel(kernel, M, false);
     if ((st = kernel_fits(k, M)) != SVQ_OK) return st;
-    WidePlan plan{};
+    // the plans need the device's compute-unit count; the buffers are checked
+    // first so that invalid pointers never reach the runtime
+    st = check_gemm_buffers(x, (size_t)M * K * 2, wt, (size_t)N * K / 2, scales,
+                            (size_t)(K / G) * N * 2, out, (size_t)M * N * 2, nullptr, 0, 0, 2);
+    if (st != SVQ_OK) return st;
+    const int cus = device_cus();
+    WidePlan wplan{};
+    SmallPlan splan{};
+    size_t need;
     if (k == SVQ_KERNEL_MFMA_WIDE) {
-        // the plan needs the device's compute-unit count; the buffers are
-        // checked first so that invalid pointers never reach the runtime
-        st = check_gemm_buffers(x, (size_t)M * K * 2, wt, (size_t)N * K / 2, scales,
-                                (size_t)(K / G) * N * 2, out, (size_t)M * N * 2, nullptr, 0, 0, 2);
-        if (st != SVQ_OK) return st;
-        plan = plan_w4a16_wide(M, N, K, device_cus());
+        wplan = plan_w4a16_wide(M, N, K, cus);
+        need = wplan.workspace_bytes;
+        if (need && (size_t)wplan.row_tiles * wplan.col_tiles > kMaxCounters) return SVQ_ERR_UNSUPPORTED;
+    } else {
+        splan = plan_smallm(M, N, K, cus);
+        need = splan.workspace_bytes;
     }
     st = check_gemm_buffers(x, (size_t)M * K * 2, wt, (size_t)N * K / 2, scales, (size_t)(K / G) * N * 2,
-                            out, (size_t)M * N * 2, workspace, workspace_bytes, plan.workspace_bytes, 2);
+                            out, (size_t)M * N * 2, workspace, workspace_bytes, need, 2);
     if (st != SVQ_OK) return st;
     hipError_t e;
     const hipStream_t s = (hipStream_t)stream;
     switch (k) {
-    case SVQ_KERNEL_DOT2: e = launch_w4a16_dot2(x, wt, scales, out, (int)M, N, K, G, s); break;
-    case SVQ_KERNEL_MFMA_SKINNY: e = launch_w4a16_skinny(x, wt, scales, out, (int)M, N, K, G, s); break;
-    default: e = launch_w4a16_wide(plan, x, wt, scales, out, M, N, K, G, workspace, s); break;
+    case SVQ_KERNEL_DOT2: e = launch_w4a16_dot2(splan, x, wt, scales, out, (int)M, N, K, G, workspace, s); break;
+    case SVQ_KERNEL_MFMA_SKINNY: e = launch_w4a16_skinny(splan, x, wt, scales, out, (int)M, N, K, G, workspace, s); break;
+    default: e = launch_w4a16_wide(wplan, x, wt, scales, out, M, N, K, G, workspace, s); break;
     }
     return e == hipSuccess ? SVQ_OK : SVQ_ERR_HIP;
 }
@@ -254,7 +273,7 @@ size_t svq_mxfp8_workspace_bytes(int kernel, int64_t M, int64_t N, int64_t K) {
     if (check_mxfp8_shape(M, N, K, 32) != SVQ_OK) return (size_t)-1;
     const int k = resolve_kernel(kernel, M, true);
     if (kernel_fits(k, M) != SVQ_OK) return (size_t)-1;
-    if (k != SVQ_KERNEL_MFMA_WIDE) return 0;
+    if (k != SVQ_KERNEL_MFMA_WIDE) return plan_smallm(M, N, K, device_cus()).workspace_bytes;
     return plan_mxfp8_wide(M, N, K, device_cus()).workspace_bytes;
 }
 
@@ -273,21 +292,28 @@ int svq_mxfp8_gemm_with(int kernel, const void *x, const uint8_t *w, const uint8
     const int k = resolve_kernel(kernel, M, true);
     if ((st = kernel_fits(k, M)) != SVQ_OK) return st;
     const size_t xb = (size_t)M * K * 2, wb = (size_t)N * K, sb = (size_t)N * (K / 32), ob = (size_t)M * N * 2;
-    WidePlan plan{};
+    st = check_gemm_buffers(x, xb, w, wb, scales, sb, out, ob, nullptr, 0, 0, 1);
+    if (st != SVQ_OK) return st;
+    const int cus = device_cus();
+    WidePlan wplan{};
+    SmallPlan splan{};
+    size_t need;
     if (k == SVQ_KERNEL_MFMA_WIDE) {
-        st = check_gemm_buffers(x, xb, w, wb, scales, sb, out, ob, nullptr, 0, 0, 1);
-        if (st != SVQ_OK) return st;
-        plan = plan_mxfp8_wide(M, N, K, device_cus());
+        wplan = plan_mxfp8_wide(M, N, K, cus);
+        need = wplan.workspace_bytes;
+        if (need && (size_t)wplan.row_tiles * wplan.col_tiles > kMaxCounters) return SVQ_ERR_UNSUPPORTED;
+    } else {
+        splan = plan_smallm(M, N, K, cus);
+        need = splan.workspace_bytes;
     }
-    st = check_gemm_buffers(x, xb, w, wb, scales, sb, out, ob, workspace, workspace_bytes,
-                            plan.workspace_bytes, 1);
+    st = check_gemm_buffers(x, xb, w, wb, scales, sb, out, ob, workspace, workspace_bytes, need, 1);
     if (st != SVQ_OK) return st;
     hipError_t e;
     const hipStream_t s = (hipStream_t)stream;
     switch (k) {
-    case SVQ_KERNEL_DOT2: e = launch_mxfp8_dot2(x, w, scales, out, (int)M, N, K, s); break;
-    case SVQ_KERNEL_MFMA_SKINNY: e = launch_mxfp8_skinny(x, w, scales, out, (int)M, N, K, s); break;
-    default: e = launch_mxfp8_wide(plan, x, w, scales, out, M, N, K, workspace, s); break;
+    case SVQ_KERNEL_DOT2: e = launch_mxfp8_dot2(splan, x, w, scales, out, (int)M, N, K, workspace, s); break;
+    case SVQ_KERNEL_MFMA_SKINNY: e = launch_mxfp8_skinny(splan, x, w, scales, out, (int)M, N, K, workspace, s); break;
+    default: e = launch_mxfp8_wide(wplan, x, w, scales, out, M, N, K, workspace, s); break;
     }
     return e == hipSuccess ? SVQ_OK : SVQ_ERR_HIP;
 }

@@ -28,18 +28,41 @@ struct WidePlan {
 WidePlan plan_w4a16_wide(int64_t M, int64_t N, int64_t K, int num_cus);
 WidePlan plan_mxfp8_wide(int64_t M, int64_t N, int64_t K, int num_cus);
 
-hipError_t launch_w4a16_dot2(const void *x, const int32_t *wt, const void *scales, void *out,
-                             int M, int64_t N, int64_t K, int G, hipStream_t stream);
-hipError_t launch_w4a16_skinny(const void *x, const int32_t *wt, const void *scales, void *out,
-                               int M, int64_t N, int64_t K, int G, hipStream_t stream);
+// Split-K schedule of the small-M kernels: one workgroup per (16-column block,
+// K range of S 128-row tiles); `splits` ranges per column block.
+struct SmallPlan {
+    int splits, S;
+    size_t workspace_bytes;  // arrival counters + fp32 partials (0 if splits == 1)
+};
+
+SmallPlan plan_smallm(int64_t M, int64_t N, int64_t K, int num_cus);
+
+hipError_t launch_w4a16_dot2(const SmallPlan &plan, const void *x, const int32_t *wt,
+                             const void *scales, void *out, int M, int64_t N, int64_t K, int G,
+                             void *workspace, hipStream_t stream);
+hipError_t launch_w4a16_skinny(const SmallPlan &plan, const void *x, const int32_t *wt,
+                               const void *scales, void *out, int M, int64_t N, int64_t K, int G,
+                               void *workspace, hipStream_t stream);
 hipError_t launch_w4a16_wide(const WidePlan &plan, const void *x, const int32_t *wt,
                              const void *scales, void *out, int64_t M, int64_t N, int64_t K,
                              int G, void *workspace, hipStream_t stream);
 
-hipError_t launch_mxfp8_dot2(const void *x, const uint8_t *w, const uint8_t *scales, void *out,
-                             int M, int64_t N, int64_t K, hipStream_t stream);
-hipError_t launch_mxfp8_skinny(const void *x, const uint8_t *w, const uint8_t *scales, void *out,
-                               int M, int64_t N, int64_t K, hipStream_t stream);
+hipError_t launch_mxfp8_dot2(const SmallPlan &plan, const void *x, const uint8_t *w,
+                             const uint8_t *scales, void *out, int M, int64_t N, int64_t K,
+                             void *workspace, hipStream_t stream);
+hipError_t launch_mxfp8_skinny(const SmallPlan &plan, const void *x, const uint8_t *w,
+                               const uint8_t *scales, void *out, int M, int64_t N, int64_t K,
+                               void *workspace, hipStream_t stream);
+
+// Workspace layout shared by every kernel that splits work across workgroups:
+// a fixed region of arrival counters (which every kernel leaves at zero) then
+// the fp32 partials. The counter region has the same size for all kernels so
+// that one kernel's partials never land on another kernel's counters when
+// callers reuse one workspace.
+constexpr size_t kCounterBytes = 256 * 1024;
+constexpr size_t kMaxCounters = kCounterBytes / 4;
+inline uint32_t *ws_counters(void *ws) { return (uint32_t *)ws; }
+inline void *ws_partials(void *ws) { return ws ? (void *)((char *)ws + kCounterBytes) : nullptr; }
 hipError_t launch_mxfp8_wide(const WidePlan &plan, const void *x, const uint8_t *w,
                              const uint8_t *scales, void *out, int64_t M, int64_t N, int64_t K,
                              void *workspace, hipStream_t stream);

@@ -1,18 +1,34 @@
-// Stream-K bookkeeping shared by the wide MFMA kernels.
+// Cross-workgroup reductions shared by the kernels that split work.
 //
-// The (output tile, 128-row K step) units are split evenly over `grid`
-// persistent workgroups: workgroup w owns [w*units/grid, (w+1)*units/grid).
-// A tile whose steps are spread over several workgroups is finished by the last
-// one to arrive: every contributor stores its fp32 partial in its own slot, then
-// bumps the tile's arrival counter; the one that sees the final count adds all
-// partials in workgroup order (a fixed order, so results are deterministic),
-// writes the bf16 output and clears the counter for the next call.
+// Handoff without fences: an agent-scope release/acquire fence on gfx950 writes
+// back / invalidates the XCD-local L2 caches and costs tens of microseconds per
+// workgroup when hundreds of workgroups do it, so partials travel with
+// coherent ("sc1") stores and loads that bypass the non-coherent L2 state
+// instead. A contributor stores its partial coherently, waits until its stores
+// have completed (s_waitcnt), and only then bumps the arrival counter with an
+// agent-scope atomic; the workgroup that observes the final count reads the
+// other partials with coherent loads. Partials are added in a fixed order, so
+// results are deterministic, and the last arriver clears the counter.
 #pragma once
 
 #include "svq_device.h"
 
 namespace svq {
 
+constexpr int kCoherent = 16;  // cache-policy bits of a buffer access: sc1
+
+// Wait until every outstanding memory access of this wave has completed.
+__device__ __forceinline__ void wait_all_memory() { __builtin_amdgcn_s_waitcnt(0); }
+
+__device__ __forceinline__ uint32_t arrive(uint32_t *cnt) {
+    return __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void clear_counter(uint32_t *cnt) {
+    __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Stream-K: the (output tile, 128-row K step) units are split evenly over
+// `grid` persistent workgroups: workgroup w owns [w*units/grid, (w+1)*units/grid).
 // The workgroup whose unit range holds unit a (units >= grid >= 1).
 __device__ __forceinline__ int sk_owner(int64_t a, int64_t units, int grid) {
     const int64_t w = ((a + 1) * grid - 1) / units;
@@ -32,22 +48,19 @@ __device__ __forceinline__ bool sk_fixup(f32x4 (&acc)[NV], int tile, int KT, int
                                          int *s_flag) {
     const int tid = threadIdx.x;
     const int wg = blockIdx.x;
+    const uint32_t slot_bytes = (uint32_t)NV * NT * 16;
     const int slot = tile - sk_first_tile(wg, units, grid, KT);
-    f32x4 *mine = part + ((size_t)(wg * maxt + slot) * NV) * NT + tid;
+    const __amdgpu_buffer_rsrc_t mine = make_rsrc(part + (size_t)(wg * maxt + slot) * NV * NT, slot_bytes);
 #pragma unroll
-    for (int v = 0; v < NV; ++v) mine[(size_t)v * NT] = acc[v];
+    for (int v = 0; v < NV; ++v)
+        __builtin_amdgcn_raw_buffer_store_b128(acc[v], mine, (uint32_t)(v * NT + tid) * 16, 0, kCoherent);
     const int fw = sk_owner((int64_t)tile * KT, units, grid);
     const int lw = sk_owner((int64_t)tile * KT + KT - 1, units, grid);
-    __threadfence();
+    wait_all_memory();
     __syncthreads();
-    if (tid == 0) {
-        const uint32_t prev = atomicAdd(&cnt[tile], 1u);
-        *s_flag = (prev == (uint32_t)(lw - fw));
-    }
+    if (tid == 0) *s_flag = (arrive(&cnt[tile]) == (uint32_t)(lw - fw));
     __syncthreads();
-    const bool last = *s_flag != 0;
-    if (!last) return false;
-    __threadfence();
+    if (*s_flag == 0) return false;
     f32x4 sum[NV];
 #pragma unroll
     for (int v = 0; v < NV; ++v) sum[v] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -57,15 +70,52 @@ __device__ __forceinline__ bool sk_fixup(f32x4 (&acc)[NV], int tile, int KT, int
             for (int v = 0; v < NV; ++v) sum[v] += acc[v];
         } else {
             const int wslot = tile - sk_first_tile(w, units, grid, KT);
-            const f32x4 *theirs = part + ((size_t)(w * maxt + wslot) * NV) * NT + tid;
+            const __amdgpu_buffer_rsrc_t theirs =
+                make_rsrc(part + (size_t)(w * maxt + wslot) * NV * NT, slot_bytes);
 #pragma unroll
-            for (int v = 0; v < NV; ++v) sum[v] += __builtin_nontemporal_load(theirs + (size_t)v * NT);
+            for (int v = 0; v < NV; ++v)
+                sum[v] += __builtin_amdgcn_raw_buffer_load_b128(theirs, (uint32_t)(v * NT + tid) * 16, 0, kCoherent);
         }
     }
 #pragma unroll
     for (int v = 0; v < NV; ++v) acc[v] = sum[v];
-    if (tid == 0) cnt[tile] = 0u;
+    if (tid == 0) clear_counter(&cnt[tile]);
     return true;
+}
+
+
+// Split-K finish of the small-M kernels. Workgroup (nb, sp) of `splits` holds,
+// in threads t < 16*M, the partial sum v of output (m = t/16, column 16*nb +
+// t%16). With one split it is the result. Otherwise every split stores its
+// partials in its own slot and bumps the column block's arrival counter; the
+// last to arrive adds the slots in split order (deterministic), writes bf16
+// and clears the counter. part: [N/16][splits][16*M] fp32; cnt: [N/16].
+__device__ __forceinline__ void smallm_finish(float v, int M, int N, int nb, int sp, int splits,
+                                              uint16_t *__restrict__ out, uint32_t *__restrict__ cnt,
+                                              float *__restrict__ part, int *s_flag) {
+    const int t = threadIdx.x;
+    const bool owner = t < 16 * M;
+    const int m = t >> 4, c = t & 15;
+    if (splits == 1) {
+        if (owner) out[(size_t)m * N + nb * 16 + c] = f32_to_bf16_rne(v);
+        return;
+    }
+    float *slots = part + (size_t)nb * splits * 16 * M;
+    if (owner) __hip_atomic_store(slots + (size_t)sp * 16 * M + t, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    wait_all_memory();
+    __syncthreads();
+    if (t == 0) *s_flag = (arrive(&cnt[nb]) == (uint32_t)(splits - 1));
+    __syncthreads();
+    if (*s_flag == 0) return;
+    if (owner) {
+        float s = 0.f;
+        for (int k = 0; k < splits; ++k)
+            s += (k == sp) ? v
+                           : __hip_atomic_load(slots + (size_t)k * 16 * M + t, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+        out[(size_t)m * N + nb * 16 + c] = f32_to_bf16_rne(s);
+    }
+    if (t == 0) clear_counter(&cnt[nb]);
 }
 
 }  // namespace svq

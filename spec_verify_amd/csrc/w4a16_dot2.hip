@@ -28,81 +28,77 @@
 //    swaps (a wavefront reduction), the waves through LDS, in a fixed order.
 #include "svq_launch.h"
 #include "dot2_asm.h"
+#include "svq_streamk.h"
 
 namespace svq {
-
-template <int M>
-struct Dot2Stage {
-    uint4 w;         // this lane's 16 bytes of the tile
-    uint32_t x[M];   // bf16 pair (rows 2*lane, 2*lane+1 of the tile) of each x row
-    uint16_t s;      // fp16 scale of this lane's group and column
-};
 
 template <int M, int WAVES, int D, int GSHIFT>
 __global__ __launch_bounds__(64 * WAVES) void w4a16_dot2_kernel(
     const uint32_t *__restrict__ x, const uint4 *__restrict__ wt,
-    const uint16_t *__restrict__ sc, uint16_t *__restrict__ out, int N, int K) {
+    const uint16_t *__restrict__ sc, uint16_t *__restrict__ out, uint32_t *__restrict__ cnt,
+    float *__restrict__ part, int N, int K, int splits, int S) {
     constexpr int NG = 128 >> GSHIFT;  // groups per 128-row tile
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = wave_id();
     const int rg = lane >> 4;
-    const int nb = blockIdx.x;
+    const int nb = blockIdx.x / splits, sp = blockIdx.x % splits;
     const int KT = K >> 7;
-    const int col = nb * 16 + (lane & 15);
-    const size_t KH = (size_t)K >> 1;
-    const uint4 *tp = wt + (size_t)nb * KT * 64 + lane;
-    const uint32_t *xp = x + lane;
-    const uint16_t *sp = sc + col;
-    const int gsub = (rg * 32) >> GSHIFT;
-    const int ntile = wave < KT ? (KT - 1 - wave) / WAVES + 1 : 0;
+    // buffer views rebased on this workgroup's column block; tile kt of the
+    // block is at byte kt*1024 of `wr`, x row m at byte m*2K of `xr`, and the
+    // scale of group g for this lane's column at byte g*2N + 2*(lane%16) of `sr`
+    const __amdgpu_buffer_rsrc_t wr = make_rsrc(wt + (size_t)nb * KT * 64, (uint32_t)KT * 1024);
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, (uint32_t)M * K * 2);
+    const __amdgpu_buffer_rsrc_t sr = make_rsrc(sc + nb * 16, (uint32_t)(((size_t)(K >> GSHIFT) * N - nb * 16) * 2));
+    const uint32_t w_vo = lane * 16;
+    const uint32_t x_vo = lane * 4;
+    const uint32_t s_vo = ((rg * 32) >> GSHIFT) * N * 2 + (lane & 15) * 2;
+    // this workgroup's K range: tiles [kbeg, kbeg + kcnt) of the column block
+    const int kbeg = sp * S;
+    const int kcnt = KT - kbeg < S ? KT - kbeg : S;
+    const int ntile = wave < kcnt ? (kcnt - 1 - wave) / WAVES + 1 : 0;
 
     float acc[M];
 #pragma unroll
     for (int m = 0; m < M; ++m) acc[m] = 0.f;
 
-    // Loads are unconditional (tile index clamped to the wave's last tile) so
-    // the compiler can count outstanding loads statically; out-of-range tiles
-    // are loaded again and skipped.
-    auto load = [&](Dot2Stage<M>(&S)[D], int i0) {
-#pragma unroll
-        for (int d = 0; d < D; ++d) {
-            int i = i0 + d;
-            i = i < ntile ? i : ntile - 1;
-            const int kt = wave + i * WAVES;
-            S[d].w = load_stream16(tp + (size_t)kt * 64);
-#pragma unroll
-            for (int m = 0; m < M; ++m) S[d].x[m] = xp[m * KH + (size_t)kt * 64];
-            S[d].s = sp[(size_t)(kt * NG + gsub) * N];
-        }
-    };
+    uint4 wA[D], wB[D];
+    uint32_t xA[D][M], xB[D][M], sA[D], sB[D];
 
-    auto tile = [&](const Dot2Stage<M> &S) {
-        float p[M];
-#pragma unroll
-        for (int m = 0; m < M; ++m) p[m] = -136.f * row16_sum(dot2_bf16(S.x[m], kBf16OnePair, 0.f));
-        const uint32_t wj[4] = {S.w.x, S.w.y, S.w.z, S.w.w};
-        w4a16_tile_dots<M>(p, S.x, wj, kNibblePairMask, kMagic128Pair);
-        const float sf = fp16_bits_to_f32(S.s);
-#pragma unroll
-        for (int m = 0; m < M; ++m) acc[m] = __builtin_fmaf(sf, p[m], acc[m]);
-    };
-
-    auto compute = [&](const Dot2Stage<M>(&S)[D], int i0) {
-#pragma unroll
-        for (int d = 0; d < D; ++d)
-            if (i0 + d < ntile) tile(S[d]);
-    };
+    // Two register stages of D tiles each: the loads of one stage are in flight
+    // while the other is computed. Every branch below is wave-uniform.
+#define SVQ_LOAD(W, X, S, I0)                                                        \
+    _Pragma("unroll") for (int d = 0; d < D; ++d) if ((I0) + d < ntile) {            \
+        const int kt = kbeg + wave + ((I0) + d) * WAVES;                                    \
+        W[d] = bload16(wr, w_vo, kt * 1024);                                         \
+        _Pragma("unroll") for (int m = 0; m < M; ++m) X[d][m] = bload4(xr, x_vo, m * K * 2 + kt * 256); \
+        S[d] = bload2(sr, s_vo, kt * NG * N * 2);                                    \
+    }
+#define SVQ_COMPUTE(W, X, S, I0)                                                     \
+    _Pragma("unroll") for (int d = 0; d < D; ++d) {                                  \
+        float p[M];                                                                  \
+        _Pragma("unroll") for (int m = 0; m < M; ++m)                                \
+            p[m] = -136.f * row16_sum(dot2_bf16(X[d][m], kBf16OnePair, 0.f));        \
+        const uint32_t wj[4] = {W[d].x, W[d].y, W[d].z, W[d].w};                     \
+        w4a16_tile_dots<M>(p, X[d], wj, kNibblePairMask, kMagic128Pair);             \
+        if ((I0) + d < ntile) {                                                      \
+            const float sf = fp16_bits_to_f32((uint16_t)S[d]);                       \
+            _Pragma("unroll") for (int m = 0; m < M; ++m) acc[m] = __builtin_fmaf(sf, p[m], acc[m]); \
+        }                                                                            \
+    }
 
     if (ntile > 0) {
-        Dot2Stage<M> A[D], B[D];
-        load(A, 0);
-        for (int i0 = 0; i0 < ntile; i0 += 2 * D) {
-            load(B, i0 + D);
-            compute(A, i0);
-            load(A, i0 + 2 * D);
-            compute(B, i0 + D);
+        SVQ_LOAD(wA, xA, sA, 0)
+        for (int i0 = 0;; i0 += 2 * D) {
+            SVQ_LOAD(wB, xB, sB, i0 + D)
+            SVQ_COMPUTE(wA, xA, sA, i0)
+            if (i0 + D >= ntile) break;
+            SVQ_LOAD(wA, xA, sA, i0 + 2 * D)
+            SVQ_COMPUTE(wB, xB, sB, i0 + D)
+            if (i0 + 2 * D >= ntile) break;
         }
     }
+#undef SVQ_LOAD
+#undef SVQ_COMPUTE
 
     __shared__ float red[WAVES][M][16];
 #pragma unroll
@@ -111,51 +107,53 @@ __global__ __launch_bounds__(64 * WAVES) void w4a16_dot2_kernel(
         if (lane < 16) red[wave][m][lane] = v;
     }
     __syncthreads();
-    for (int t = threadIdx.x; t < M * 16; t += 64 * WAVES) {
-        const int m = t >> 4, c = t & 15;
-        float s = 0.f;
+    __shared__ int s_flag;
+    float v = 0.f;
+    if (threadIdx.x < 16 * M) {
 #pragma unroll
-        for (int w = 0; w < WAVES; ++w) s += red[w][m][c];
-        out[(size_t)m * N + nb * 16 + c] = f32_to_bf16_rne(s);
+        for (int w = 0; w < WAVES; ++w) v += red[w][threadIdx.x >> 4][threadIdx.x & 15];
     }
+    smallm_finish(v, M, N, nb, sp, splits, out, cnt, part, &s_flag);
 }
 
 namespace {
-constexpr int kDot2Waves = 8;
+constexpr int kDot2Waves = 4;
 constexpr int kDot2Depth = 4;
 
 template <int M, int GS>
-hipError_t dot2_launch(const void *x, const int32_t *wt, const void *sc, void *out, int64_t N,
-                       int64_t K, hipStream_t stream) {
-    hipLaunchKernelGGL((w4a16_dot2_kernel<M, kDot2Waves, kDot2Depth, GS>), dim3((uint32_t)(N / 16)),
-                       dim3(64 * kDot2Waves), 0, stream, (const uint32_t *)x, (const uint4 *)wt,
-                       (const uint16_t *)sc, (uint16_t *)out, (int)N, (int)K);
+hipError_t dot2_launch(const SmallPlan &p, const void *x, const int32_t *wt, const void *sc, void *out,
+                       int64_t N, int64_t K, void *ws, hipStream_t stream) {
+    hipLaunchKernelGGL((w4a16_dot2_kernel<M, kDot2Waves, kDot2Depth, GS>),
+                       dim3((uint32_t)(N / 16 * p.splits)), dim3(64 * kDot2Waves), 0, stream,
+                       (const uint32_t *)x, (const uint4 *)wt, (const uint16_t *)sc, (uint16_t *)out,
+                       ws_counters(ws), (float *)ws_partials(ws), (int)N, (int)K, p.splits, p.S);
     return hipGetLastError();
 }
 
 template <int GS>
-hipError_t dot2_by_m(int M, const void *x, const int32_t *wt, const void *sc, void *out,
-                     int64_t N, int64_t K, hipStream_t stream) {
+hipError_t dot2_by_m(const SmallPlan &p, int M, const void *x, const int32_t *wt, const void *sc,
+                     void *out, int64_t N, int64_t K, void *ws, hipStream_t stream) {
     switch (M) {
-    case 1: return dot2_launch<1, GS>(x, wt, sc, out, N, K, stream);
-    case 2: return dot2_launch<2, GS>(x, wt, sc, out, N, K, stream);
-    case 3: return dot2_launch<3, GS>(x, wt, sc, out, N, K, stream);
-    case 4: return dot2_launch<4, GS>(x, wt, sc, out, N, K, stream);
-    case 5: return dot2_launch<5, GS>(x, wt, sc, out, N, K, stream);
-    case 6: return dot2_launch<6, GS>(x, wt, sc, out, N, K, stream);
-    case 7: return dot2_launch<7, GS>(x, wt, sc, out, N, K, stream);
-    case 8: return dot2_launch<8, GS>(x, wt, sc, out, N, K, stream);
+    case 1: return dot2_launch<1, GS>(p, x, wt, sc, out, N, K, ws, stream);
+    case 2: return dot2_launch<2, GS>(p, x, wt, sc, out, N, K, ws, stream);
+    case 3: return dot2_launch<3, GS>(p, x, wt, sc, out, N, K, ws, stream);
+    case 4: return dot2_launch<4, GS>(p, x, wt, sc, out, N, K, ws, stream);
+    case 5: return dot2_launch<5, GS>(p, x, wt, sc, out, N, K, ws, stream);
+    case 6: return dot2_launch<6, GS>(p, x, wt, sc, out, N, K, ws, stream);
+    case 7: return dot2_launch<7, GS>(p, x, wt, sc, out, N, K, ws, stream);
+    case 8: return dot2_launch<8, GS>(p, x, wt, sc, out, N, K, ws, stream);
     default: return hipErrorInvalidValue;
     }
 }
 }  // namespace
 
-hipError_t launch_w4a16_dot2(const void *x, const int32_t *wt, const void *scales, void *out,
-                             int M, int64_t N, int64_t K, int G, hipStream_t stream) {
+hipError_t launch_w4a16_dot2(const SmallPlan &plan, const void *x, const int32_t *wt,
+                             const void *scales, void *out, int M, int64_t N, int64_t K, int G,
+                             void *workspace, hipStream_t stream) {
     switch (G) {
-    case 32: return dot2_by_m<5>(M, x, wt, scales, out, N, K, stream);
-    case 64: return dot2_by_m<6>(M, x, wt, scales, out, N, K, stream);
-    case 128: return dot2_by_m<7>(M, x, wt, scales, out, N, K, stream);
+    case 32: return dot2_by_m<5>(plan, M, x, wt, scales, out, N, K, workspace, stream);
+    case 64: return dot2_by_m<6>(plan, M, x, wt, scales, out, N, K, workspace, stream);
+    case 128: return dot2_by_m<7>(plan, M, x, wt, scales, out, N, K, workspace, stream);
     default: return hipErrorInvalidValue;
     }
 }

@@ -30,109 +30,95 @@ namespace svq {
 // the MFMA pipe is mostly idle, so the -136 * sum(x) term is also computed on
 // it, by an MFMA against a constant -136 operand.
 // ---------------------------------------------------------------------------
-template <int NG>
-struct SkinnyStage {
-    uint4 w;
-    uint4 a[4];
-    uint16_t s[NG];
-};
-
 template <int WAVES, int D, int GSHIFT>
 __global__ __launch_bounds__(64 * WAVES) void w4a16_skinny_kernel(
     const uint16_t *__restrict__ x, const uint4 *__restrict__ wt,
-    const uint16_t *__restrict__ sc, uint16_t *__restrict__ out, int M, int N, int K) {
+    const uint16_t *__restrict__ sc, uint16_t *__restrict__ out, uint32_t *__restrict__ cnt,
+    float *__restrict__ part, int M, int N, int K, int splits, int S) {
     constexpr int NG = 128 >> GSHIFT;
     constexpr int SPG = 4 / NG;
     constexpr bool kTrans = GSHIFT < 7;
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = wave_id();
     const int r = lane & 15, g = lane >> 4;
-    const int nb = blockIdx.x;
+    const int nb = blockIdx.x / splits, sp = blockIdx.x % splits;
     const int KT = K >> 7;
-    const int col = nb * 16 + r;
-    const uint4 *tp = wt + (size_t)nb * KT * 64 + lane;
-    const bool arow = r < M;
-    const uint16_t *xr = x + (size_t)(arow ? r : 0) * K;
-    const int ntile = wave < KT ? (KT - 1 - wave) / WAVES + 1 : 0;
+    const __amdgpu_buffer_rsrc_t wr = make_rsrc(wt + (size_t)nb * KT * 64, (uint32_t)KT * 1024);
+    // x rows >= M lie past the end of the view and load as zero (padding rows)
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, (uint32_t)M * K * 2);
+    const __amdgpu_buffer_rsrc_t sr = make_rsrc(sc + nb * 16, (uint32_t)(((size_t)(K >> GSHIFT) * N - nb * 16) * 2));
+    const uint32_t w_vo = lane * 16;
+    // A operand of MFMA step j: x[r][128 kt + koff(j)], 8 bf16 = 16 bytes
+    const uint32_t x_vo = r * K * 2 + (kTrans ? 16 * g : 64 * g);
+    constexpr uint32_t kXStep = kTrans ? 64 : 16;   // byte distance between steps j
+    const uint32_t s_vo = r * 2;
+    // this workgroup's K range: tiles [kbeg, kbeg + kcnt) of the column block
+    const int kbeg = sp * S;
+    const int kcnt = KT - kbeg < S ? KT - kbeg : S;
+    const int ntile = wave < kcnt ? (kcnt - 1 - wave) / WAVES + 1 : 0;
     const uint4 bneg = make_uint4(kBf16Neg136Pair, kBf16Neg136Pair, kBf16Neg136Pair, kBf16Neg136Pair);
 
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    uint4 wA[D], wB[D], aA[D][4], aB[D][4];
+    uint32_t sA[D][NG], sB[D][NG];
 
-    auto load = [&](SkinnyStage<NG>(&S)[D], int i0) {
-#pragma unroll
-        for (int d = 0; d < D; ++d) {
-            int i = i0 + d;
-            i = i < ntile ? i : ntile - 1;
-            const int kt = wave + i * WAVES;
-            S[d].w = load_stream16(tp + (size_t)kt * 64);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int koff = kTrans ? (32 * j + 8 * g) : (32 * g + 8 * j);
-                S[d].a[j] = arow ? *(const uint4 *)(xr + (size_t)kt * 128 + koff) : make_uint4(0, 0, 0, 0);
-            }
-#pragma unroll
-            for (int q = 0; q < NG; ++q) S[d].s[q] = sc[(size_t)(kt * NG + q) * N + col];
-        }
-    };
-
-    auto compute = [&](const SkinnyStage<NG>(&S)[D], int i0) {
-        uint32_t wj[D][4];
-#pragma unroll
-        for (int d = 0; d < D; ++d) {
-            wj[d][0] = S[d].w.x;
-            wj[d][1] = S[d].w.y;
-            wj[d][2] = S[d].w.z;
-            wj[d][3] = S[d].w.w;
-            if constexpr (kTrans) transpose_rows_words(wj[d][0], wj[d][1], wj[d][2], wj[d][3]);
-        }
-#pragma unroll
-        for (int q = 0; q < NG; ++q) {
-            f32x4 P[D];
-#pragma unroll
-            for (int d = 0; d < D; ++d) P[d] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int jj = 0; jj < SPG; ++jj) {
-                const int j = q * SPG + jj;
-#pragma unroll
-                for (int d = 0; d < D; ++d)
-                    if (i0 + d < ntile) P[d] = mfma16x16x32(S[d].a[j], bneg, P[d]);
-#pragma unroll
-                for (int d = 0; d < D; ++d)
-                    if (i0 + d < ntile) P[d] = mfma16x16x32(S[d].a[j], word_to_bf16x8(wj[d][j]), P[d]);
-            }
-#pragma unroll
-            for (int d = 0; d < D; ++d) {
-                if (i0 + d < ntile) {
-                    const float sf = fp16_bits_to_f32(S[d].s[q]);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(sf, P[d][i], acc[i]);
-                }
-            }
-        }
-    };
+#define SVQ_LOAD(W, A, S, I0)                                                        \
+    _Pragma("unroll") for (int d = 0; d < D; ++d) if ((I0) + d < ntile) {            \
+        const int kt = kbeg + wave + ((I0) + d) * WAVES;                                    \
+        W[d] = bload16(wr, w_vo, kt * 1024);                                         \
+        _Pragma("unroll") for (int j = 0; j < 4; ++j) A[d][j] = bload16(xr, x_vo + j * kXStep, kt * 256); \
+        _Pragma("unroll") for (int q = 0; q < NG; ++q) S[d][q] = bload2(sr, s_vo, (kt * NG + q) * N * 2); \
+    }
+#define SVQ_COMPUTE(W, A, S, I0)                                                     \
+    {                                                                                \
+        uint32_t wj[D][4];                                                           \
+        _Pragma("unroll") for (int d = 0; d < D; ++d) {                              \
+            wj[d][0] = W[d].x; wj[d][1] = W[d].y; wj[d][2] = W[d].z; wj[d][3] = W[d].w; \
+            if constexpr (kTrans) transpose_rows_words(wj[d][0], wj[d][1], wj[d][2], wj[d][3]); \
+        }                                                                            \
+        _Pragma("unroll") for (int q = 0; q < NG; ++q) {                             \
+            f32x4 P[D];                                                              \
+            _Pragma("unroll") for (int d = 0; d < D; ++d) P[d] = f32x4{0.f, 0.f, 0.f, 0.f}; \
+            _Pragma("unroll") for (int jj = 0; jj < SPG; ++jj) {                     \
+                const int j = q * SPG + jj;                                          \
+                _Pragma("unroll") for (int d = 0; d < D; ++d) P[d] = mfma16x16x32(A[d][j], bneg, P[d]); \
+                _Pragma("unroll") for (int d = 0; d < D; ++d)                        \
+                    P[d] = mfma16x16x32(A[d][j], word_to_bf16x8(wj[d][j]), P[d]);     \
+            }                                                                        \
+            _Pragma("unroll") for (int d = 0; d < D; ++d) {                          \
+                if ((I0) + d < ntile) {                                              \
+                    const float sf = fp16_bits_to_f32((uint16_t)S[d][q]);            \
+                    _Pragma("unroll") for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(sf, P[d][i], acc[i]); \
+                }                                                                    \
+            }                                                                        \
+        }                                                                            \
+    }
 
     if (ntile > 0) {
-        SkinnyStage<NG> A[D], B[D];
-        load(A, 0);
-        for (int i0 = 0; i0 < ntile; i0 += 2 * D) {
-            load(B, i0 + D);
-            compute(A, i0);
-            load(A, i0 + 2 * D);
-            compute(B, i0 + D);
+        SVQ_LOAD(wA, aA, sA, 0)
+        for (int i0 = 0;; i0 += 2 * D) {
+            SVQ_LOAD(wB, aB, sB, i0 + D)
+            SVQ_COMPUTE(wA, aA, sA, i0)
+            if (i0 + D >= ntile) break;
+            SVQ_LOAD(wA, aA, sA, i0 + 2 * D)
+            SVQ_COMPUTE(wB, aB, sB, i0 + D)
+            if (i0 + 2 * D >= ntile) break;
         }
     }
+#undef SVQ_LOAD
+#undef SVQ_COMPUTE
 
     __shared__ float red[WAVES][16][17];
 #pragma unroll
     for (int i = 0; i < 4; ++i) red[wave][4 * g + i][r] = acc[i];
     __syncthreads();
-    for (int t = threadIdx.x; t < M * 16; t += 64 * WAVES) {
-        const int m = t >> 4, c = t & 15;
-        float s = 0.f;
+    __shared__ int s_flag;
+    float v = 0.f;
+    if (threadIdx.x < 16 * M) {
 #pragma unroll
-        for (int w = 0; w < WAVES; ++w) s += red[w][m][c];
-        out[(size_t)m * N + nb * 16 + c] = f32_to_bf16_rne(s);
+        for (int w = 0; w < WAVES; ++w) v += red[w][threadIdx.x >> 4][threadIdx.x & 15];
     }
+    smallm_finish(v, M, N, nb, sp, splits, out, cnt, part, &s_flag);
 }
 
 // ---------------------------------------------------------------------------
@@ -357,24 +343,24 @@ __global__ __launch_bounds__(64 * WR * WC) void w4a16_wide_kernel(
 // host launchers
 // ---------------------------------------------------------------------------
 namespace {
-constexpr int kSkinnyWaves = 8;
+constexpr int kSkinnyWaves = 4;
 constexpr int kSkinnyDepth = 2;
 
 template <int GS>
-hipError_t skinny_launch(const void *x, const int32_t *wt, const void *sc, void *out, int M,
-                         int64_t N, int64_t K, hipStream_t stream) {
-    hipLaunchKernelGGL((w4a16_skinny_kernel<kSkinnyWaves, kSkinnyDepth, GS>), dim3((uint32_t)(N / 16)),
-                       dim3(64 * kSkinnyWaves), 0, stream, (const uint16_t *)x, (const uint4 *)wt,
-                       (const uint16_t *)sc, (uint16_t *)out, M, (int)N, (int)K);
+hipError_t skinny_launch(const SmallPlan &p, const void *x, const int32_t *wt, const void *sc, void *out,
+                         int M, int64_t N, int64_t K, void *ws, hipStream_t stream) {
+    hipLaunchKernelGGL((w4a16_skinny_kernel<kSkinnyWaves, kSkinnyDepth, GS>),
+                       dim3((uint32_t)(N / 16 * p.splits)), dim3(64 * kSkinnyWaves), 0, stream,
+                       (const uint16_t *)x, (const uint4 *)wt, (const uint16_t *)sc, (uint16_t *)out,
+                       ws_counters(ws), (float *)ws_partials(ws), M, (int)N, (int)K, p.splits, p.S);
     return hipGetLastError();
 }
 
 template <int MBW, int WR, int WC, int CT, int GS>
 hipError_t wide_launch(const WidePlan &p, const void *x, const int32_t *wt, const void *sc,
                        void *out, int64_t M, int64_t N, int64_t K, void *ws, hipStream_t stream) {
-    const size_t cnt_bytes = ((size_t)p.row_tiles * p.col_tiles * 4 + 255) & ~(size_t)255;
-    uint32_t *cnt = (uint32_t *)ws;
-    f32x4 *part = ws ? (f32x4 *)((char *)ws + cnt_bytes) : nullptr;
+    uint32_t *cnt = ws_counters(ws);
+    f32x4 *part = (f32x4 *)ws_partials(ws);
     hipLaunchKernelGGL((w4a16_wide_kernel<MBW, WR, WC, CT, GS>), dim3((uint32_t)p.grid),
                        dim3(64 * WR * WC), 0, stream, (const uint16_t *)x, (const uint4 *)wt,
                        (const uint16_t *)sc, (uint16_t *)out, cnt, part, (int)M, (int)N, (int)K,
@@ -390,12 +376,13 @@ hipError_t wide_by_shape(const WidePlan &p, const void *x, const int32_t *wt, co
 }
 }  // namespace
 
-hipError_t launch_w4a16_skinny(const void *x, const int32_t *wt, const void *scales, void *out,
-                               int M, int64_t N, int64_t K, int G, hipStream_t stream) {
+hipError_t launch_w4a16_skinny(const SmallPlan &plan, const void *x, const int32_t *wt,
+                               const void *scales, void *out, int M, int64_t N, int64_t K, int G,
+                               void *workspace, hipStream_t stream) {
     switch (G) {
-    case 32: return skinny_launch<5>(x, wt, scales, out, M, N, K, stream);
-    case 64: return skinny_launch<6>(x, wt, scales, out, M, N, K, stream);
-    case 128: return skinny_launch<7>(x, wt, scales, out, M, N, K, stream);
+    case 32: return skinny_launch<5>(plan, x, wt, scales, out, M, N, K, workspace, stream);
+    case 64: return skinny_launch<6>(plan, x, wt, scales, out, M, N, K, workspace, stream);
+    case 128: return skinny_launch<7>(plan, x, wt, scales, out, M, N, K, workspace, stream);
     default: return hipErrorInvalidValue;
     }
 }

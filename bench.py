@@ -125,26 +125,43 @@ class Problem:
         self.ws_w = self.ws_s = None
 
 
-def time_kernel(torch, prob, launches, warmup):
-    """Mean per-launch kernel time (µs) from event pairs around each launch, and
-    the mean time per launch of a back-to-back sequence."""
-    for _ in range(warmup):
-        prob.launch()
+def graph_of(torch, fn, n):
+    """Capture n calls fn(i) into one HIP graph (no host launch overhead on replay)."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for i in range(3):          # warm the allocator/caches outside the capture
+            fn(i)
+    torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(launches)]
-    for a, b in ev:
-        a.record()
-        prob.launch()
-        b.record()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(n):
+            fn(i)
     torch.cuda.synchronize()
-    per = np.array([a.elapsed_time(b) * 1e3 for a, b in ev])
-    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    s.record()
-    for _ in range(launches):
-        prob.launch()
-    e.record()
+    return g
+
+
+def time_graph(torch, g, reps):
+    """Mean seconds per replay of g over reps replays (events on the replay stream)."""
+    g.replay()
     torch.cuda.synchronize()
-    return float(np.mean(per)), float(np.median(per)), s.elapsed_time(e) * 1e3 / launches
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1e-3 / reps
+
+
+def time_kernel(torch, prob, launches=100, reps=5):
+    """Mean µs per launch of one kernel: a graph of `launches` launches that
+    rotate over the weight pool, replayed `reps` times."""
+    g = graph_of(torch, lambda i: prob.launch(i % len(prob.ws_w)), launches)
+    t = time_graph(torch, g, reps)
+    del g
+    return t / launches * 1e6
 
 
 def cpu_baseline(budget_s=12.0):
@@ -199,29 +216,26 @@ def main():
         p.check(oracle)
     bytes_step = sum(algo_bytes(p.w) for p in probs)
     dom = probs[DECODE.index(DOMINANT)]
-    for _ in range(args.warmup):
+    # one graph = `chunk` decode steps (3 launches each, weights rotating over the
+    # pool); it is replayed until `steps` steps have run, after `warmup` steps
+    chunk = next(c for c in range(min(args.steps, 100), 0, -1) if args.steps % c == 0)
+    reps = args.steps // chunk
+
+    def step(i):
         for p in probs:
-            p.launch()
+            p.launch(i % len(p.ws_w))
+    g = graph_of(torch, step, chunk)
+    for _ in range(max(1, -(-args.warmup // chunk))):
+        g.replay()
     torch.cuda.synchronize()
-    dom_ev = []
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record()
-    for _ in range(args.steps):
-        for p in probs:
-            if p is dom:
-                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                a.record()
-                p.launch()
-                b.record()
-                dom_ev.append((a, b))
-            else:
-                p.launch()
-    end.record()
-    torch.cuda.synchronize()
-    ms_step = start.elapsed_time(end) / args.steps
-    dom_us = float(np.mean([a.elapsed_time(b) * 1e3 for a, b in dom_ev]))
+    sec = time_graph(torch, g, reps)
+    steps_run = chunk * reps
+    ms_step = sec / chunk * 1e3
+    del g
+    dom_us = time_kernel(torch, dom, launches=100, reps=5)
     value = bytes_step / (ms_step * 1e-3) / 1e9
     dom_gbs = algo_bytes(dom.w) / (dom_us * 1e-6) / 1e9
+    dom.check(oracle)
     log(f"decode step: {ms_step * 1e3:.2f} µs/step, {value:.1f} GB/s; {DOMINANT} ({dom.kernel}) "
         f"{dom_us:.2f} µs/launch = {dom_gbs:.1f} GB/s ({100 * dom_gbs / HBM_PEAK_GBS:.1f}% of HBM peak)")
     for p in probs:
@@ -234,22 +248,23 @@ def main():
         names = ["decode_n5120", "decode_n6144", "decode_n1024", "verify3_up", "verify3_down",
                  "verify5_up", "verify5_down", "batch128_up", "batch128_down", "mxfp8_m1", "mxfp8_m5",
                  "mxfp8_m128"]
-        log(f"{'workload':15s} {'kernel':22s} {'µs(ev)':>8s} {'µs(b2b)':>8s} {'GB/s':>8s} {'%HBM':>6s} "
+        log(f"{'workload':15s} {'kernel':22s} {'µs':>8s} {'GB/s':>8s} {'%HBM':>6s} "
             f"{'TFLOP/s':>8s} {'%MFMA':>6s}")
         for n in names:
             p = Problem(torch, svq, n, POOL_BYTES)
             p.check(oracle)
-            us, med, b2b = time_kernel(torch, p, 200, 20)
+            us = time_kernel(torch, p, launches=100, reps=3)
+            p.check(oracle)
             w = p.w
             gbs = algo_bytes(w) / (us * 1e-6) / 1e9
             tfl = 2.0 * w["M"] * w["N"] * w["K"] / (us * 1e-6) / 1e12
             row = {"workload": n, "op": w["op"], "M": w["M"], "K": w["K"], "N": w["N"], "kernel": p.kernel,
-                   "us": round(us, 3), "us_median": round(med, 3), "us_back_to_back": round(b2b, 3),
+                   "us": round(us, 3),
                    "GBps": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
                    "weight_GBps": round(weight_bytes(w) / (us * 1e-6) / 1e9, 1),
                    "TFLOPs": round(tfl, 2), "mfma_frac": round(tfl / MFMA_BF16_PEAK_TFLOPS, 4)}
             detail.append(row)
-            log(f"{n:15s} {p.kernel:22s} {us:8.2f} {b2b:8.2f} {gbs:8.1f} {100 * gbs / HBM_PEAK_GBS:6.1f} "
+            log(f"{n:15s} {p.kernel:22s} {us:8.2f} {gbs:8.1f} {100 * gbs / HBM_PEAK_GBS:6.1f} "
                 f"{tfl:8.2f} {100 * tfl / MFMA_BF16_PEAK_TFLOPS:6.2f}")
             p.release()
             del p
@@ -269,7 +284,7 @@ def main():
 
     line = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms_step, 6), "higher_is_better": True, "scaling": "weak",
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 6), "steps_timed": steps_run, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "single-stream decode step: three W4A16 g128 GEMVs, M=1, K=5120, "
                                "N=5120/6144/1024, weights rotated over >1 GiB of copies",

@@ -13,6 +13,7 @@ M=3/5 verify chunks, M=128 batched verify, MXFP8 at M=1/5/128), and the CPU
 oracle's throughput on a bounded sample (``cpu_baseline``).
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--quick] [--no-cpu]
+    python bench.py --copy-probe    # a plain 1 GiB device copy, to calibrate HBM counters
 """
 from __future__ import annotations
 
@@ -185,6 +186,22 @@ def cpu_baseline(budget_s=12.0):
             "ms_per_step": round(dt / steps * 1e3, 3)}
 
 
+def copy_probe(nbytes=1 << 30, reps=5):
+    """Plain device-to-device copies of known size: what FETCH_SIZE / WRITE_SIZE
+    read for exactly nbytes read and nbytes written per dispatch."""
+    import torch
+    a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").uniform_()
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / reps
+    log(f"copy probe: {nbytes} bytes read + {nbytes} written per copy, {dt * 1e6:.1f} µs, "
+        f"{2 * nbytes / dt / 1e9:.1f} GB/s")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -192,11 +209,16 @@ def main():
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--quick", action="store_true", help="decode step only, no per-workload table")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run 5 copies of a 1 GiB device buffer (known bytes for counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)",
               file=sys.stderr)
         sys.exit(2)
+    if args.copy_probe:
+        copy_probe()
+        return
 
     import torch
     import spec_verify_amd as svq
@@ -300,14 +322,19 @@ def main():
     print(json.dumps(line), flush=True)
 
 
+# sources the dominant kernel is built from: traffic counters taken on other
+# sources do not describe it
+DOMINANT_SOURCES = ["w4a16_dot2.hip", "dot2_asm.h", "svq_device.h", "svq_streamk.h", "svq_launch.h",
+                    "svq_api.cpp"]
+
+
 def _kernel_source_sha():
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "spec_verify_amd", "csrc")
-    for n in sorted(os.listdir(csrc)):
-        if n.endswith((".hip", ".h", ".cpp")):
-            with open(os.path.join(csrc, n), "rb") as f:
-                h.update(f.read())
+    for n in DOMINANT_SOURCES:
+        with open(os.path.join(csrc, n), "rb") as f:
+            h.update(f.read())
     return h.hexdigest()[:16]
 
 

@@ -40,7 +40,8 @@ __global__ __launch_bounds__(64 * WAVES) void mxfp8_dot2_kernel(
     const int lane = threadIdx.x & 63;
     const int wave = wave_id();
     const int r = lane & 15, rg = lane >> 4;
-    const int nb = blockIdx.x / splits, sp = blockIdx.x % splits;
+    const int lb = xcd_contiguous(blockIdx.x, gridDim.x);
+    const int nb = lb / splits, sp = lb % splits;
     const int KT = K >> 7;
     // this block's 16 weight rows ([N][K] layout) and their scale rows
     const __amdgpu_buffer_rsrc_t wr = make_rsrc(w + (size_t)nb * 16 * K, (uint32_t)16 * K);
@@ -117,7 +118,8 @@ __global__ __launch_bounds__(64 * WAVES) void mxfp8_skinny_kernel(
     const int lane = threadIdx.x & 63;
     const int wave = wave_id();
     const int r = lane & 15, g = lane >> 4;
-    const int nb = blockIdx.x / splits, sp = blockIdx.x % splits;
+    const int lb = xcd_contiguous(blockIdx.x, gridDim.x);
+    const int nb = lb / splits, sp = lb % splits;
     const int KT = K >> 7;
     const __amdgpu_buffer_rsrc_t wr = make_rsrc(w + (size_t)nb * 16 * K, (uint32_t)16 * K);
     const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, (uint32_t)M * K * 2);
@@ -312,16 +314,37 @@ __global__ __launch_bounds__(64 * WR * WC) void mxfp8_wide_kernel(
 // host launchers
 // ---------------------------------------------------------------------------
 namespace {
-constexpr int kMxWaves = 4;
 constexpr int kMxDot2Depth = 4;
 constexpr int kMxSkinnyDepth = 2;
+
+template <int M, int WAVES>
+hipError_t mx_dot2_launch_w(const SmallPlan &p, const void *x, const uint8_t *w, const uint8_t *sc,
+                            void *out, int64_t N, int64_t K, void *ws, hipStream_t stream) {
+    hipLaunchKernelGGL((mxfp8_dot2_kernel<M, WAVES, kMxDot2Depth>), dim3((uint32_t)(N / 16 * p.splits)),
+                       dim3(64 * WAVES), 0, stream, (const uint32_t *)x, w, sc, (uint16_t *)out,
+                       ws_counters(ws), (float *)ws_partials(ws), (int)N, (int)K, p.splits, p.S);
+    return hipGetLastError();
+}
 
 template <int M>
 hipError_t mx_dot2_launch(const SmallPlan &p, const void *x, const uint8_t *w, const uint8_t *sc,
                           void *out, int64_t N, int64_t K, void *ws, hipStream_t stream) {
-    hipLaunchKernelGGL((mxfp8_dot2_kernel<M, kMxWaves, kMxDot2Depth>), dim3((uint32_t)(N / 16 * p.splits)),
-                       dim3(64 * kMxWaves), 0, stream, (const uint32_t *)x, w, sc, (uint16_t *)out,
-                       ws_counters(ws), (float *)ws_partials(ws), (int)N, (int)K, p.splits, p.S);
+    static const int r16 = resident_blocks(mxfp8_dot2_kernel<M, 16, kMxDot2Depth>, 1024);
+    static const int r8 = resident_blocks(mxfp8_dot2_kernel<M, 8, kMxDot2Depth>, 512);
+    switch (pick_waves(N / 16 * p.splits, p.cus, r16, r8)) {
+    case 16: return mx_dot2_launch_w<M, 16>(p, x, w, sc, out, N, K, ws, stream);
+    case 8: return mx_dot2_launch_w<M, 8>(p, x, w, sc, out, N, K, ws, stream);
+    default: return mx_dot2_launch_w<M, 4>(p, x, w, sc, out, N, K, ws, stream);
+    }
+}
+
+template <int WAVES>
+hipError_t mx_skinny_launch_w(const SmallPlan &p, const void *x, const uint8_t *w, const uint8_t *sc,
+                              void *out, int M, int64_t N, int64_t K, void *ws, hipStream_t stream) {
+    hipLaunchKernelGGL((mxfp8_skinny_kernel<WAVES, kMxSkinnyDepth>), dim3((uint32_t)(N / 16 * p.splits)),
+                       dim3(64 * WAVES), 0, stream, (const uint16_t *)x, w, sc,
+                       (uint16_t *)out, ws_counters(ws), (float *)ws_partials(ws), M, (int)N,
+                       (int)K, p.splits, p.S);
     return hipGetLastError();
 }
 
@@ -356,11 +379,13 @@ hipError_t launch_mxfp8_dot2(const SmallPlan &plan, const void *x, const uint8_t
 hipError_t launch_mxfp8_skinny(const SmallPlan &plan, const void *x, const uint8_t *w,
                                const uint8_t *scales, void *out, int M, int64_t N, int64_t K,
                                void *ws, hipStream_t stream) {
-    hipLaunchKernelGGL((mxfp8_skinny_kernel<kMxWaves, kMxSkinnyDepth>), dim3((uint32_t)(N / 16 * plan.splits)),
-                       dim3(64 * kMxWaves), 0, stream, (const uint16_t *)x, w, scales,
-                       (uint16_t *)out, ws_counters(ws), (float *)ws_partials(ws), M, (int)N,
-                       (int)K, plan.splits, plan.S);
-    return hipGetLastError();
+    static const int r16 = resident_blocks(mxfp8_skinny_kernel<16, kMxSkinnyDepth>, 1024);
+    static const int r8 = resident_blocks(mxfp8_skinny_kernel<8, kMxSkinnyDepth>, 512);
+    switch (pick_waves(N / 16 * plan.splits, plan.cus, r16, r8)) {
+    case 16: return mx_skinny_launch_w<16>(plan, x, w, scales, out, M, N, K, ws, stream);
+    case 8: return mx_skinny_launch_w<8>(plan, x, w, scales, out, M, N, K, ws, stream);
+    default: return mx_skinny_launch_w<4>(plan, x, w, scales, out, M, N, K, ws, stream);
+    }
 }
 
 hipError_t launch_mxfp8_wide(const WidePlan &plan, const void *x, const uint8_t *w,

@@ -64,15 +64,20 @@ static WidePlan make_plan(int64_t M, int64_t N, int64_t K, int num_cus) {
 }
 
 SmallPlan plan_smallm(int64_t M, int64_t N, int64_t K, int num_cus) {
-    // about four 4-wave workgroups per compute unit: enough to balance the
-    // column blocks over the chip and keep every CU's loads in flight
+    // A column block's K range is best handled inside one workgroup: its waves
+    // split the K tiles and reduce through LDS, with no cross-workgroup
+    // handoff. K is split across workgroups only when there are fewer column
+    // blocks than a quarter of the CUs.
+    (void)M;
     const int64_t col_blocks = N / 16, KT = K / 128;
-    const int64_t target = 4 * (int64_t)std::max(num_cus, 1);
-    int64_t splits = std::min<int64_t>(std::max<int64_t>((target + col_blocks - 1) / col_blocks, 1), KT);
-    if (col_blocks > (int64_t)kMaxCounters) splits = 1;  // one counter per column block
+    const int64_t cus = std::max(num_cus, 1);
+    const int64_t quarter = std::max<int64_t>(cus / 4, 1);
+    int64_t splits = 1;
+    if (col_blocks < quarter && KT >= 2 && col_blocks <= (int64_t)kMaxCounters)
+        splits = std::min<int64_t>((quarter + col_blocks - 1) / col_blocks, KT / 2);
     const int64_t S = (KT + splits - 1) / splits;
     splits = (KT + S - 1) / S;
-    SmallPlan p{(int)splits, (int)S, 0};
+    SmallPlan p{(int)splits, (int)S, (int)cus, 0};
     if (splits > 1) p.workspace_bytes = kCounterBytes + (size_t)col_blocks * splits * 16 * M * 4;
     return p;
 }

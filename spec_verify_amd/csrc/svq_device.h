@@ -113,6 +113,15 @@ __device__ __forceinline__ f32x4 mfma16x16x32(uint4 a, uint4 b, f32x4 c) {
                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+// Workgroups are dispatched round-robin over the 8 XCDs (workgroup b runs on
+// XCD b % 8). Returns a logical index such that each XCD receives one
+// contiguous range of [0, n): neighbouring column blocks, which share 128-byte
+// scale lines and x, then share one XCD's L2.
+__device__ __forceinline__ int xcd_contiguous(int b, int n) {
+    const int q = n >> 3, r = n & 7, x = b & 7, i = b >> 3;
+    return x * q + (x < r ? x : r) + i;
+}
+
 // Four bf16 pairs (one MFMA B operand: 8 rows x 1 column) from a repacked word.
 __device__ __forceinline__ uint4 word_to_bf16x8(uint32_t w) {
     return make_uint4(nibble_pair_bf16<0>(w), nibble_pair_bf16<1>(w), nibble_pair_bf16<2>(w),

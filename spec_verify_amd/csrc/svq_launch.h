@@ -28,12 +28,31 @@ struct WidePlan {
 WidePlan plan_w4a16_wide(int64_t M, int64_t N, int64_t K, int num_cus);
 WidePlan plan_mxfp8_wide(int64_t M, int64_t N, int64_t K, int num_cus);
 
-// Split-K schedule of the small-M kernels: one workgroup per (16-column block,
-// K range of S 128-row tiles); `splits` ranges per column block.
+// Schedule of the small-M kernels: one workgroup per (16-column block, K range
+// of S 128-row tiles); `splits` ranges per column block (1 unless the matrix has
+// too few column blocks to occupy the chip). The launcher picks the workgroup
+// size: the largest of 16, 8 or 4 waves for which the whole grid is resident at
+// once on `cus` compute units.
 struct SmallPlan {
-    int splits, S;
+    int splits, S, cus;
     size_t workspace_bytes;  // arrival counters + fp32 partials (0 if splits == 1)
 };
+
+// Workgroups of `threads` threads of `kernel` that fit on one CU at once.
+template <typename F>
+int resident_blocks(F kernel, int threads) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, threads, 0) != hipSuccess) return 1;
+    return n > 0 ? n : 1;
+}
+
+// Waves per workgroup for `wgs` workgroups given the resident counts of the 16-
+// and 8-wave instantiations.
+inline int pick_waves(int64_t wgs, int cus, int res16, int res8) {
+    if (wgs <= (int64_t)res16 * cus) return 16;
+    if (wgs <= (int64_t)res8 * cus) return 8;
+    return 4;
+}
 
 SmallPlan plan_smallm(int64_t M, int64_t N, int64_t K, int num_cus);
 

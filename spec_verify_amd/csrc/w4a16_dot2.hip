@@ -41,7 +41,8 @@ __global__ __launch_bounds__(64 * WAVES) void w4a16_dot2_kernel(
     const int lane = threadIdx.x & 63;
     const int wave = wave_id();
     const int rg = lane >> 4;
-    const int nb = blockIdx.x / splits, sp = blockIdx.x % splits;
+    const int lb = xcd_contiguous(blockIdx.x, gridDim.x);
+    const int nb = lb / splits, sp = lb % splits;
     const int KT = K >> 7;
     // buffer views rebased on this workgroup's column block; tile kt of the
     // block is at byte kt*1024 of `wr`, x row m at byte m*2K of `xr`, and the
@@ -117,17 +118,28 @@ __global__ __launch_bounds__(64 * WAVES) void w4a16_dot2_kernel(
 }
 
 namespace {
-constexpr int kDot2Waves = 4;
 constexpr int kDot2Depth = 4;
+
+template <int M, int WAVES, int GS>
+hipError_t dot2_launch_w(const SmallPlan &p, const void *x, const int32_t *wt, const void *sc, void *out,
+                         int64_t N, int64_t K, void *ws, hipStream_t stream) {
+    hipLaunchKernelGGL((w4a16_dot2_kernel<M, WAVES, kDot2Depth, GS>),
+                       dim3((uint32_t)(N / 16 * p.splits)), dim3(64 * WAVES), 0, stream,
+                       (const uint32_t *)x, (const uint4 *)wt, (const uint16_t *)sc, (uint16_t *)out,
+                       ws_counters(ws), (float *)ws_partials(ws), (int)N, (int)K, p.splits, p.S);
+    return hipGetLastError();
+}
 
 template <int M, int GS>
 hipError_t dot2_launch(const SmallPlan &p, const void *x, const int32_t *wt, const void *sc, void *out,
                        int64_t N, int64_t K, void *ws, hipStream_t stream) {
-    hipLaunchKernelGGL((w4a16_dot2_kernel<M, kDot2Waves, kDot2Depth, GS>),
-                       dim3((uint32_t)(N / 16 * p.splits)), dim3(64 * kDot2Waves), 0, stream,
-                       (const uint32_t *)x, (const uint4 *)wt, (const uint16_t *)sc, (uint16_t *)out,
-                       ws_counters(ws), (float *)ws_partials(ws), (int)N, (int)K, p.splits, p.S);
-    return hipGetLastError();
+    static const int r16 = resident_blocks(w4a16_dot2_kernel<M, 16, kDot2Depth, GS>, 1024);
+    static const int r8 = resident_blocks(w4a16_dot2_kernel<M, 8, kDot2Depth, GS>, 512);
+    switch (pick_waves(N / 16 * p.splits, p.cus, r16, r8)) {
+    case 16: return dot2_launch_w<M, 16, GS>(p, x, wt, sc, out, N, K, ws, stream);
+    case 8: return dot2_launch_w<M, 8, GS>(p, x, wt, sc, out, N, K, ws, stream);
+    default: return dot2_launch_w<M, 4, GS>(p, x, wt, sc, out, N, K, ws, stream);
+    }
 }
 
 template <int GS>

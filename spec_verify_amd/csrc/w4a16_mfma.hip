@@ -41,7 +41,8 @@ __global__ __launch_bounds__(64 * WAVES) void w4a16_skinny_kernel(
     const int lane = threadIdx.x & 63;
     const int wave = wave_id();
     const int r = lane & 15, g = lane >> 4;
-    const int nb = blockIdx.x / splits, sp = blockIdx.x % splits;
+    const int lb = xcd_contiguous(blockIdx.x, gridDim.x);
+    const int nb = lb / splits, sp = lb % splits;
     const int KT = K >> 7;
     const __amdgpu_buffer_rsrc_t wr = make_rsrc(wt + (size_t)nb * KT * 64, (uint32_t)KT * 1024);
     // x rows >= M lie past the end of the view and load as zero (padding rows)
@@ -343,17 +344,28 @@ __global__ __launch_bounds__(64 * WR * WC) void w4a16_wide_kernel(
 // host launchers
 // ---------------------------------------------------------------------------
 namespace {
-constexpr int kSkinnyWaves = 4;
 constexpr int kSkinnyDepth = 2;
+
+template <int WAVES, int GS>
+hipError_t skinny_launch_w(const SmallPlan &p, const void *x, const int32_t *wt, const void *sc, void *out,
+                           int M, int64_t N, int64_t K, void *ws, hipStream_t stream) {
+    hipLaunchKernelGGL((w4a16_skinny_kernel<WAVES, kSkinnyDepth, GS>),
+                       dim3((uint32_t)(N / 16 * p.splits)), dim3(64 * WAVES), 0, stream,
+                       (const uint16_t *)x, (const uint4 *)wt, (const uint16_t *)sc, (uint16_t *)out,
+                       ws_counters(ws), (float *)ws_partials(ws), M, (int)N, (int)K, p.splits, p.S);
+    return hipGetLastError();
+}
 
 template <int GS>
 hipError_t skinny_launch(const SmallPlan &p, const void *x, const int32_t *wt, const void *sc, void *out,
                          int M, int64_t N, int64_t K, void *ws, hipStream_t stream) {
-    hipLaunchKernelGGL((w4a16_skinny_kernel<kSkinnyWaves, kSkinnyDepth, GS>),
-                       dim3((uint32_t)(N / 16 * p.splits)), dim3(64 * kSkinnyWaves), 0, stream,
-                       (const uint16_t *)x, (const uint4 *)wt, (const uint16_t *)sc, (uint16_t *)out,
-                       ws_counters(ws), (float *)ws_partials(ws), M, (int)N, (int)K, p.splits, p.S);
-    return hipGetLastError();
+    static const int r16 = resident_blocks(w4a16_skinny_kernel<16, kSkinnyDepth, GS>, 1024);
+    static const int r8 = resident_blocks(w4a16_skinny_kernel<8, kSkinnyDepth, GS>, 512);
+    switch (pick_waves(N / 16 * p.splits, p.cus, r16, r8)) {
+    case 16: return skinny_launch_w<16, GS>(p, x, wt, sc, out, M, N, K, ws, stream);
+    case 8: return skinny_launch_w<8, GS>(p, x, wt, sc, out, M, N, K, ws, stream);
+    default: return skinny_launch_w<4, GS>(p, x, wt, sc, out, M, N, K, ws, stream);
+    }
 }
 
 template <int MBW, int WR, int WC, int CT, int GS>

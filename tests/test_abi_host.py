@@ -116,8 +116,10 @@ def test_workspace_query_rejects_bad_shapes(L):
     assert L.svq_w4a16_workspace_bytes(1, 9, 5120, 5120, 128) == bad
     # enough 16-column blocks to fill the chip: no split of K, no workspace
     assert L.svq_w4a16_workspace_bytes(2, 5, 17408, 5120, 128) == 0
+    assert L.svq_w4a16_workspace_bytes(0, 1, 1024, 5120, 128) == 0
     # few column blocks: K is split and the split partials need a workspace
-    assert 0 < L.svq_w4a16_workspace_bytes(0, 1, 5120, 5120, 128) < (1 << 22)
+    assert 0 < L.svq_w4a16_workspace_bytes(0, 1, 256, 17408, 128) < (1 << 22)
+    assert 0 < L.svq_mxfp8_workspace_bytes(0, 3, 256, 4096) < (1 << 22)
     assert L.svq_mxfp8_workspace_bytes(0, 1, 96, 5120) == bad
 
 

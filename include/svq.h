@@ -107,7 +107,7 @@ size_t svq_w4a16_workspace_bytes(int kernel, int64_t M, int64_t N, int64_t K,
  * y = x . ((q - 8) * s)^T
  *   x             bf16 [M][K], 16-byte aligned
  *   qweight_tiled output of svq_q4_repack, 16-byte aligned
- *   scales        fp16 [K/G][N], 2-byte aligned
+ *   scales        fp16 [K/G][N], 4-byte aligned (read as aligned 32-bit words)
  *   out           bf16 [M][N], 4-byte aligned, fully overwritten, must not
  *                 overlap any input or the workspace
  *   group_size    G in {32, 64, 128}; K % 128 == 0, N % 16 == 0
@@ -141,7 +141,8 @@ size_t svq_mxfp8_workspace_bytes(int kernel, int64_t M, int64_t N, int64_t K);
  *   x       bf16 [M][K], 16-byte aligned
  *   w       E4M3FN codes [N][K] (row n holds the K elements of output column n),
  *           16-byte aligned
- *   scales  E8M0 codes [N][K/32], one per 32 consecutive K-elements of a row
+ *   scales  E8M0 codes [N][K/32], one per 32 consecutive K-elements of a row,
+ *           4-byte aligned (read as aligned 32-bit words)
  *   out     bf16 [M][N], 4-byte aligned, fully overwritten, no overlap
  *   group_size must be 32. Requires N >= 128, N % 16 == 0, K % 128 == 0.
  *   workspace as for svq_w4a16_gemm.

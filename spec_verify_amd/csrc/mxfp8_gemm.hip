@@ -49,7 +49,9 @@ __global__ __launch_bounds__(64 * WAVES) void mxfp8_dot2_kernel(
     const __amdgpu_buffer_rsrc_t sr = make_rsrc(sc + (size_t)nb * 16 * (K >> 5), (uint32_t)16 * (K >> 5));
     const uint32_t w_vo = r * K + rg * 32;
     const uint32_t x_vo = lane * 4;
-    const uint32_t s_vo = r * (K >> 5) + rg;
+    // the dword holding the tile's four block scales; s_sh selects this lane's
+    const uint32_t s_vo = r * (K >> 5);
+    const int s_sh = rg * 8;
     // this workgroup's K range: tiles [kbeg, kbeg + kcnt) of the column block
     const int kbeg = sp * S;
     const int kcnt = KT - kbeg < S ? KT - kbeg : S;
@@ -67,11 +69,11 @@ __global__ __launch_bounds__(64 * WAVES) void mxfp8_dot2_kernel(
         V[d][0] = bload16(wr, w_vo, kt * 128);                                       \
         V[d][1] = bload16(wr, w_vo + 16, kt * 128);                                  \
         _Pragma("unroll") for (int m = 0; m < M; ++m) X[d][m] = bload4(xr, x_vo, m * K * 2 + kt * 256); \
-        S[d] = bload1(sr, s_vo, kt * 4);                                             \
+        S[d] = bload4(sr, s_vo, kt * 4);                                             \
     }
 #define SVQ_COMPUTE(V, X, S, I0)                                                     \
     _Pragma("unroll") for (int d = 0; d < D; ++d) if ((I0) + d < ntile) {            \
-        const float sf = e8m0_to_f32(S[d]);                                          \
+        const float sf = e8m0_to_f32((uint8_t)(S[d] >> s_sh));                                          \
         const uint32_t wd[8] = {V[d][0].x, V[d][0].y, V[d][0].z, V[d][0].w,          \
                                 V[d][1].x, V[d][1].y, V[d][1].z, V[d][1].w};         \
         mxfp8_tile_dots<M>(acc, X[d], wd, sf);                                       \
@@ -126,7 +128,9 @@ __global__ __launch_bounds__(64 * WAVES) void mxfp8_skinny_kernel(
     const __amdgpu_buffer_rsrc_t sr = make_rsrc(sc + (size_t)nb * 16 * (K >> 5), (uint32_t)16 * (K >> 5));
     const uint32_t w_vo = r * K + g * 32;
     const uint32_t x_vo = r * K * 2 + g * 64;     // rows >= M read as zero
-    const uint32_t s_vo = r * (K >> 5) + g;
+    // the dword holding the tile's four block scales; s_sh selects this lane's
+    const uint32_t s_vo = r * (K >> 5);
+    const int s_sh = g * 8;
     // this workgroup's K range: tiles [kbeg, kbeg + kcnt) of the column block
     const int kbeg = sp * S;
     const int kcnt = KT - kbeg < S ? KT - kbeg : S;
@@ -142,11 +146,11 @@ __global__ __launch_bounds__(64 * WAVES) void mxfp8_skinny_kernel(
         V[d][0] = bload16(wr, w_vo, kt * 128);                                       \
         V[d][1] = bload16(wr, w_vo + 16, kt * 128);                                  \
         _Pragma("unroll") for (int j = 0; j < 4; ++j) A[d][j] = bload16(xr, x_vo + 16 * j, kt * 256); \
-        S[d] = bload1(sr, s_vo, kt * 4);                                             \
+        S[d] = bload4(sr, s_vo, kt * 4);                                             \
     }
 #define SVQ_COMPUTE(V, A, S, I0)                                                     \
     _Pragma("unroll") for (int d = 0; d < D; ++d) if ((I0) + d < ntile) {            \
-        const float sf = e8m0_to_f32(S[d]);                                          \
+        const float sf = e8m0_to_f32((uint8_t)(S[d] >> s_sh));                                          \
         acc = mfma16x16x32(A[d][0], cvt8_e4m3_bf16(V[d][0].x, V[d][0].y, sf), acc);  \
         acc = mfma16x16x32(A[d][1], cvt8_e4m3_bf16(V[d][0].z, V[d][0].w, sf), acc);  \
         acc = mfma16x16x32(A[d][2], cvt8_e4m3_bf16(V[d][1].x, V[d][1].y, sf), acc);  \

@@ -63,7 +63,7 @@ static WidePlan make_plan(int64_t M, int64_t N, int64_t K, int num_cus) {
     return p;
 }
 
-SmallPlan plan_smallm(int64_t M, int64_t N, int64_t K, int num_cus) {
+SmallPlan plan_smallm(int64_t M, int64_t N, int64_t K, int num_cus, int64_t max_tiles) {
     // A column block's K range is best handled inside one workgroup: its waves
     // split the K tiles and reduce through LDS, with no cross-workgroup
     // handoff. K is split across workgroups only when there are fewer column
@@ -75,6 +75,7 @@ SmallPlan plan_smallm(int64_t M, int64_t N, int64_t K, int num_cus) {
     int64_t splits = 1;
     if (col_blocks < quarter && KT >= 2 && col_blocks <= (int64_t)kMaxCounters)
         splits = std::min<int64_t>((quarter + col_blocks - 1) / col_blocks, KT / 2);
+    if (max_tiles > 0) splits = std::max(splits, (KT + max_tiles - 1) / max_tiles);
     const int64_t S = (KT + splits - 1) / splits;
     splits = (KT + S - 1) / S;
     SmallPlan p{(int)splits, (int)S, (int)cus, 0};
@@ -215,11 +216,18 @@ int svq_q4_repack(const int32_t *src, int32_t *dst, int64_t N, int64_t K, void *
     return SVQ_OK;
 }
 
+namespace {
+// the skinny kernel stages its x range in LDS, which bounds its K range
+SmallPlan w4a16_small_plan(int k, int64_t M, int64_t N, int64_t K, int cus) {
+    return plan_smallm(M, N, K, cus, k == SVQ_KERNEL_MFMA_SKINNY ? skinny_max_tiles(M) : 0);
+}
+}  // namespace
+
 size_t svq_w4a16_workspace_bytes(int kernel, int64_t M, int64_t N, int64_t K, int32_t G) {
     if (check_w4a16_shape(M, N, K, G) != SVQ_OK) return (size_t)-1;
     const int k = resolve_kernel(kernel, M, false);
     if (kernel_fits(k, M) != SVQ_OK) return (size_t)-1;
-    if (k != SVQ_KERNEL_MFMA_WIDE) return plan_smallm(M, N, K, device_cus()).workspace_bytes;
+    if (k != SVQ_KERNEL_MFMA_WIDE) return w4a16_small_plan(k, M, N, K, device_cus()).workspace_bytes;
     return plan_w4a16_wide(M, N, K, device_cus()).workspace_bytes;
 }
 
@@ -240,7 +248,7 @@ int svq_w4a16_gemm_with(int kernel, const void *x, const int32_t *wt, const void
     // the plans need the device's compute-unit count; the buffers are checked
     // first so that invalid pointers never reach the runtime
     st = check_gemm_buffers(x, (size_t)M * K * 2, wt, (size_t)N * K / 2, scales,
-                            (size_t)(K / G) * N * 2, out, (size_t)M * N * 2, nullptr, 0, 0, 2);
+                            (size_t)(K / G) * N * 2, out, (size_t)M * N * 2, nullptr, 0, 0, 4);
     if (st != SVQ_OK) return st;
     const int cus = device_cus();
     WidePlan wplan{};
@@ -251,11 +259,12 @@ int svq_w4a16_gemm_with(int kernel, const void *x, const int32_t *wt, const void
         need = wplan.workspace_bytes;
         if (need && (size_t)wplan.row_tiles * wplan.col_tiles > kMaxCounters) return SVQ_ERR_UNSUPPORTED;
     } else {
-        splan = plan_smallm(M, N, K, cus);
+        splan = w4a16_small_plan(k, M, N, K, cus);
         need = splan.workspace_bytes;
+        if (splan.splits > 1 && N / 16 > (int64_t)kMaxCounters) return SVQ_ERR_UNSUPPORTED;
     }
     st = check_gemm_buffers(x, (size_t)M * K * 2, wt, (size_t)N * K / 2, scales, (size_t)(K / G) * N * 2,
-                            out, (size_t)M * N * 2, workspace, workspace_bytes, need, 2);
+                            out, (size_t)M * N * 2, workspace, workspace_bytes, need, 4);
     if (st != SVQ_OK) return st;
     hipError_t e;
     const hipStream_t s = (hipStream_t)stream;
@@ -297,7 +306,7 @@ int svq_mxfp8_gemm_with(int kernel, const void *x, const uint8_t *w, const uint8
     const int k = resolve_kernel(kernel, M, true);
     if ((st = kernel_fits(k, M)) != SVQ_OK) return st;
     const size_t xb = (size_t)M * K * 2, wb = (size_t)N * K, sb = (size_t)N * (K / 32), ob = (size_t)M * N * 2;
-    st = check_gemm_buffers(x, xb, w, wb, scales, sb, out, ob, nullptr, 0, 0, 1);
+    st = check_gemm_buffers(x, xb, w, wb, scales, sb, out, ob, nullptr, 0, 0, 4);
     if (st != SVQ_OK) return st;
     const int cus = device_cus();
     WidePlan wplan{};
@@ -310,8 +319,9 @@ int svq_mxfp8_gemm_with(int kernel, const void *x, const uint8_t *w, const uint8
     } else {
         splan = plan_smallm(M, N, K, cus);
         need = splan.workspace_bytes;
+        if (splan.splits > 1 && N / 16 > (int64_t)kMaxCounters) return SVQ_ERR_UNSUPPORTED;
     }
-    st = check_gemm_buffers(x, xb, w, wb, scales, sb, out, ob, workspace, workspace_bytes, need, 1);
+    st = check_gemm_buffers(x, xb, w, wb, scales, sb, out, ob, workspace, workspace_bytes, need, 4);
     if (st != SVQ_OK) return st;
     hipError_t e;
     const hipStream_t s = (hipStream_t)stream;

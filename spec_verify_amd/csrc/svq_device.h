@@ -38,10 +38,13 @@ __device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff
 __device__ __forceinline__ uint32_t bload4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
     return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
 }
-__device__ __forceinline__ uint32_t bload2(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+// The 16- and 8-bit loads return their own width: widening the result at the
+// load would make the compiler wait for the load right there (it masks the
+// high bits), which serializes a prefetch.
+__device__ __forceinline__ uint16_t bload2(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
     return __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
 }
-__device__ __forceinline__ uint32_t bload1(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+__device__ __forceinline__ uint8_t bload1(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
     return __builtin_amdgcn_raw_buffer_load_b8(r, voff, soff, 0);
 }
 
@@ -113,6 +116,30 @@ __device__ __forceinline__ f32x4 mfma16x16x32(uint4 a, uint4 b, f32x4 c) {
                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+// s_waitcnt immediate that waits until at most k vector-memory loads of this
+// wave are outstanding (gfx9 encoding; expcnt and lgkmcnt left at their max).
+constexpr int vmcnt_imm(int k) { return (k & 15) | (7 << 4) | (15 << 8) | (((k >> 4) & 3) << 14); }
+
+// Wait until at most n (wave-uniform, 0 <= n <= K) loads are outstanding:
+// s_waitcnt takes an immediate, so n selects one of K+1 waits. Loads complete
+// in issue order, so this waits for everything issued before the last n.
+template <int K>
+__device__ __forceinline__ void wait_vmcnt_at_most(int n) {
+    if constexpr (K == 0) {
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    } else {
+        if (n >= K) __builtin_amdgcn_s_waitcnt(vmcnt_imm(K));
+        else wait_vmcnt_at_most<K - 1>(n);
+    }
+}
+
+// One 16-byte-per-lane LDS-DMA load: lane l's 16 bytes from gptr land at
+// lds_base + 16*l (lds_base wave-uniform); inactive lanes write nothing.
+__device__ __forceinline__ void dma16(const void *gptr, void *lds_base) {
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)gptr,
+                                     (__attribute__((address_space(3))) void *)lds_base, 16, 0, 0);
+}
+
 // Workgroups are dispatched round-robin over the 8 XCDs (workgroup b runs on
 // XCD b % 8). Returns a logical index such that each XCD receives one
 // contiguous range of [0, n): neighbouring column blocks, which share 128-byte
@@ -124,8 +151,21 @@ __device__ __forceinline__ int xcd_contiguous(int b, int n) {
 
 // Four bf16 pairs (one MFMA B operand: 8 rows x 1 column) from a repacked word.
 __device__ __forceinline__ uint4 word_to_bf16x8(uint32_t w) {
-    return make_uint4(nibble_pair_bf16<0>(w), nibble_pair_bf16<1>(w), nibble_pair_bf16<2>(w),
-                      nibble_pair_bf16<3>(w));
+    // one v_and_or_b32 per pair (the compiler would emit v_and + v_or); the
+    // trailing s_nop covers the wait states between these VALU writes and an
+    // MFMA that reads them
+    uint32_t a, b, c, d, t1, t2, t3;
+    asm("v_and_or_b32 %0, %7, %8, %9\n\t"
+        "v_lshrrev_b32 %4, 4, %7\n\t"
+        "v_lshrrev_b32 %5, 8, %7\n\t"
+        "v_lshrrev_b32 %6, 12, %7\n\t"
+        "v_and_or_b32 %1, %4, %8, %9\n\t"
+        "v_and_or_b32 %2, %5, %8, %9\n\t"
+        "v_and_or_b32 %3, %6, %8, %9\n\t"
+        "s_nop 1"
+        : "=&v"(a), "=&v"(b), "=&v"(c), "=&v"(d), "=&v"(t1), "=&v"(t2), "=&v"(t3)
+        : "v"(w), "s"(kNibblePairMask), "v"(kMagic128Pair));
+    return make_uint4(a, b, c, d);
 }
 
 // E8M0 code -> fp32 scale 2^(b-127) (b = 0 gives the fp32 subnormal 2^-127).

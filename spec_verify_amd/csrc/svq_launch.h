@@ -38,6 +38,20 @@ struct SmallPlan {
     size_t workspace_bytes;  // arrival counters + fp32 partials (0 if splits == 1)
 };
 
+// LDS of one compute unit, and the most a skinny workgroup may take for its
+// stage of x (M rows x 128*S bf16, rows padded by 16 bytes).
+constexpr size_t kLdsPerCu = 160 * 1024;
+constexpr size_t kSkinnyLdsMax = 64 * 1024;
+inline size_t skinny_lds_bytes(int M, int S, int waves) {
+    const size_t stage = (size_t)M * ((size_t)S * 256 + 16);
+    const size_t red = (size_t)waves * M * 16 * 4;
+    return stage > red ? stage : red;
+}
+// Largest K range (in 128-row tiles) whose x stage fits kSkinnyLdsMax.
+inline int64_t skinny_max_tiles(int64_t M) {
+    return ((int64_t)kSkinnyLdsMax / M - 16) / 256;
+}
+
 // Workgroups of `threads` threads of `kernel` that fit on one CU at once.
 template <typename F>
 int resident_blocks(F kernel, int threads) {
@@ -54,7 +68,8 @@ inline int pick_waves(int64_t wgs, int cus, int res16, int res8) {
     return 4;
 }
 
-SmallPlan plan_smallm(int64_t M, int64_t N, int64_t K, int num_cus);
+// max_tiles: the most K tiles one workgroup may take (0: no limit).
+SmallPlan plan_smallm(int64_t M, int64_t N, int64_t K, int num_cus, int64_t max_tiles = 0);
 
 hipError_t launch_w4a16_dot2(const SmallPlan &plan, const void *x, const int32_t *wt,
                              const void *scales, void *out, int M, int64_t N, int64_t K, int G,

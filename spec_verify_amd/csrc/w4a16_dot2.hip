@@ -52,7 +52,10 @@ __global__ __launch_bounds__(64 * WAVES) void w4a16_dot2_kernel(
     const __amdgpu_buffer_rsrc_t sr = make_rsrc(sc + nb * 16, (uint32_t)(((size_t)(K >> GSHIFT) * N - nb * 16) * 2));
     const uint32_t w_vo = lane * 16;
     const uint32_t x_vo = lane * 4;
-    const uint32_t s_vo = ((rg * 32) >> GSHIFT) * N * 2 + (lane & 15) * 2;
+    // scales are loaded as the aligned dword holding this lane's fp16 and the
+    // neighbouring column's; s_sh selects the half
+    const uint32_t s_vo = ((rg * 32) >> GSHIFT) * N * 2 + (lane & 14) * 2;
+    const int s_sh = (lane & 1) * 16;
     // this workgroup's K range: tiles [kbeg, kbeg + kcnt) of the column block
     const int kbeg = sp * S;
     const int kcnt = KT - kbeg < S ? KT - kbeg : S;
@@ -72,7 +75,7 @@ __global__ __launch_bounds__(64 * WAVES) void w4a16_dot2_kernel(
         const int kt = kbeg + wave + ((I0) + d) * WAVES;                                    \
         W[d] = bload16(wr, w_vo, kt * 1024);                                         \
         _Pragma("unroll") for (int m = 0; m < M; ++m) X[d][m] = bload4(xr, x_vo, m * K * 2 + kt * 256); \
-        S[d] = bload2(sr, s_vo, kt * NG * N * 2);                                    \
+        S[d] = bload4(sr, s_vo, kt * NG * N * 2);                                    \
     }
 #define SVQ_COMPUTE(W, X, S, I0)                                                     \
     _Pragma("unroll") for (int d = 0; d < D; ++d) {                                  \
@@ -82,7 +85,7 @@ __global__ __launch_bounds__(64 * WAVES) void w4a16_dot2_kernel(
         const uint32_t wj[4] = {W[d].x, W[d].y, W[d].z, W[d].w};                     \
         w4a16_tile_dots<M>(p, X[d], wj, kNibblePairMask, kMagic128Pair);             \
         if ((I0) + d < ntile) {                                                      \
-            const float sf = fp16_bits_to_f32((uint16_t)S[d]);                       \
+            const float sf = fp16_bits_to_f32((uint16_t)(S[d] >> s_sh));                       \
             _Pragma("unroll") for (int m = 0; m < M; ++m) acc[m] = __builtin_fmaf(sf, p[m], acc[m]); \
         }                                                                            \
     }

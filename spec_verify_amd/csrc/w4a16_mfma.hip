@@ -19,22 +19,29 @@
 // Weights enter the MFMA as the exact bf16 values 128 + q; the bias is removed
 // per group by starting the group's accumulator at -136 * (sum of x over the
 // group), then the fp16 scale multiplies the group result into fp32 accumulators.
+#include <algorithm>
+
 #include "svq_launch.h"
 #include "svq_streamk.h"
 
 namespace svq {
 
 // ---------------------------------------------------------------------------
-// Skinny kernel: M <= 16, one 16-row MFMA tile (rows >= M are zero), the waves
-// of a workgroup split K over the tiles of one 16-column block. Memory-bound;
-// the MFMA pipe is mostly idle, so the -136 * sum(x) term is also computed on
-// it, by an MFMA against a constant -136 operand.
+// Skinny kernel: M <= 16, one 16-row MFMA tile (MFMA rows >= M repeat row M-1
+// and their results are dropped). A workgroup owns one 16-column block and a
+// range of S K-tiles; its waves take the tiles round-robin. The workgroup's
+// x rows (M x 128*S bf16) are staged once in LDS, so the A operands come from
+// LDS and the vector-memory path carries only weights and scales, which each
+// wave prefetches 2*D tiles deep behind the staging loads. Memory-bound; the
+// MFMA pipe is mostly idle, so the -136 * sum(x) term is also computed on it,
+// by an MFMA against a constant -136 operand.
 // ---------------------------------------------------------------------------
 template <int WAVES, int D, int GSHIFT>
 __global__ __launch_bounds__(64 * WAVES) void w4a16_skinny_kernel(
     const uint16_t *__restrict__ x, const uint4 *__restrict__ wt,
     const uint16_t *__restrict__ sc, uint16_t *__restrict__ out, uint32_t *__restrict__ cnt,
     float *__restrict__ part, int M, int N, int K, int splits, int S) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     constexpr int NG = 128 >> GSHIFT;
     constexpr int SPG = 4 / NG;
     constexpr bool kTrans = GSHIFT < 7;
@@ -45,79 +52,108 @@ __global__ __launch_bounds__(64 * WAVES) void w4a16_skinny_kernel(
     const int nb = lb / splits, sp = lb % splits;
     const int KT = K >> 7;
     const __amdgpu_buffer_rsrc_t wr = make_rsrc(wt + (size_t)nb * KT * 64, (uint32_t)KT * 1024);
-    // x rows >= M lie past the end of the view and load as zero (padding rows)
-    const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, (uint32_t)M * K * 2);
     const __amdgpu_buffer_rsrc_t sr = make_rsrc(sc + nb * 16, (uint32_t)(((size_t)(K >> GSHIFT) * N - nb * 16) * 2));
     const uint32_t w_vo = lane * 16;
-    // A operand of MFMA step j: x[r][128 kt + koff(j)], 8 bf16 = 16 bytes
-    const uint32_t x_vo = r * K * 2 + (kTrans ? 16 * g : 64 * g);
-    constexpr uint32_t kXStep = kTrans ? 64 : 16;   // byte distance between steps j
-    const uint32_t s_vo = r * 2;
+    // the aligned dword holding this lane's fp16 scale; s_sh selects the half
+    const uint32_t s_vo = (r & 14) * 2;
+    const int s_sh = (r & 1) * 16;
     // this workgroup's K range: tiles [kbeg, kbeg + kcnt) of the column block
     const int kbeg = sp * S;
     const int kcnt = KT - kbeg < S ? KT - kbeg : S;
     const int ntile = wave < kcnt ? (kcnt - 1 - wave) / WAVES + 1 : 0;
     const uint4 bneg = make_uint4(kBf16Neg136Pair, kBf16Neg136Pair, kBf16Neg136Pair, kBf16Neg136Pair);
 
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    uint4 wA[D], wB[D], aA[D][4], aB[D][4];
+    uint4 wA[D], wB[D];
     uint32_t sA[D][NG], sB[D][NG];
-
-#define SVQ_LOAD(W, A, S, I0)                                                        \
+#define SVQ_LOAD(W, SS, I0)                                                          \
     _Pragma("unroll") for (int d = 0; d < D; ++d) if ((I0) + d < ntile) {            \
-        const int kt = kbeg + wave + ((I0) + d) * WAVES;                                    \
+        const int kt = kbeg + wave + ((I0) + d) * WAVES;                             \
         W[d] = bload16(wr, w_vo, kt * 1024);                                         \
-        _Pragma("unroll") for (int j = 0; j < 4; ++j) A[d][j] = bload16(xr, x_vo + j * kXStep, kt * 256); \
-        _Pragma("unroll") for (int q = 0; q < NG; ++q) S[d][q] = bload2(sr, s_vo, (kt * NG + q) * N * 2); \
+        _Pragma("unroll") for (int q = 0; q < NG; ++q) SS[d][q] = bload4(sr, s_vo, (kt * NG + q) * N * 2); \
     }
-#define SVQ_COMPUTE(W, A, S, I0)                                                     \
+    // stage x[0..M)[128*kbeg, 128*(kbeg+kcnt)) in LDS by DMA (one 64-chunk
+    // segment of a row per instruction); rows padded by 16 bytes so that the
+    // 16-byte A reads of different rows fall in different banks. The weight
+    // prefetch is issued behind it, and only the x loads are waited for.
+    const int xs_stride = kcnt * 256 + 16;
+    {
+        const int row_chunks = kcnt * 16;
+        const int nseg = (row_chunks + 63) >> 6;
+        for (int i = wave; i < M * nseg; i += WAVES) {
+            const int m = i / nseg, c = ((i - m * nseg) << 6) + lane;
+            if (c < row_chunks)
+                dma16(x + (size_t)m * K + (size_t)kbeg * 128 + c * 8, smem + m * xs_stride + ((c - lane) << 4));
+        }
+    }
+    // two stages of D tiles (weights and scales) in flight behind the x loads
+    if (ntile > 0) SVQ_LOAD(wA, sA, 0)
+    if (ntile > D) SVQ_LOAD(wB, sB, D)
+    {
+        const int na = ntile < D ? ntile : D;
+        const int nb2 = ntile - D < 0 ? 0 : (ntile - D < D ? ntile - D : D);
+        wait_vmcnt_at_most<2 * D * (1 + NG)>((na + nb2) * (1 + NG));
+    }
+    // a bare barrier: __syncthreads() would also wait for the weight prefetch
+    __builtin_amdgcn_s_barrier();
+
+    // A operand of MFMA step j for tile i of the range: row min(r, M-1), 8 bf16
+    // at K offset 32j + 8g (transposed words) or 32g + 8j
+    const int arow = r < M ? r : M - 1;
+    const uint8_t *abase = smem + arow * xs_stride + (kTrans ? 16 * g : 64 * g);
+    constexpr int kXStep = kTrans ? 64 : 16;
+
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#define SVQ_COMPUTE(W, SS, I0)                                                       \
     {                                                                                \
         uint32_t wj[D][4];                                                           \
         _Pragma("unroll") for (int d = 0; d < D; ++d) {                              \
             wj[d][0] = W[d].x; wj[d][1] = W[d].y; wj[d][2] = W[d].z; wj[d][3] = W[d].w; \
             if constexpr (kTrans) transpose_rows_words(wj[d][0], wj[d][1], wj[d][2], wj[d][3]); \
         }                                                                            \
-        _Pragma("unroll") for (int q = 0; q < NG; ++q) {                             \
-            f32x4 P[D];                                                              \
-            _Pragma("unroll") for (int d = 0; d < D; ++d) P[d] = f32x4{0.f, 0.f, 0.f, 0.f}; \
-            _Pragma("unroll") for (int jj = 0; jj < SPG; ++jj) {                     \
-                const int j = q * SPG + jj;                                          \
-                _Pragma("unroll") for (int d = 0; d < D; ++d) P[d] = mfma16x16x32(A[d][j], bneg, P[d]); \
-                _Pragma("unroll") for (int d = 0; d < D; ++d)                        \
-                    P[d] = mfma16x16x32(A[d][j], word_to_bf16x8(wj[d][j]), P[d]);     \
-            }                                                                        \
-            _Pragma("unroll") for (int d = 0; d < D; ++d) {                          \
-                if ((I0) + d < ntile) {                                              \
-                    const float sf = fp16_bits_to_f32((uint16_t)S[d][q]);            \
-                    _Pragma("unroll") for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(sf, P[d][i], acc[i]); \
+        _Pragma("unroll") for (int d = 0; d < D; ++d) {                              \
+            if ((I0) + d < ntile) {                                                  \
+                const uint8_t *ap = abase + (wave + ((I0) + d) * WAVES) * 256;       \
+                _Pragma("unroll") for (int q = 0; q < NG; ++q) {                     \
+                    f32x4 P = {0.f, 0.f, 0.f, 0.f};                                  \
+                    _Pragma("unroll") for (int jj = 0; jj < SPG; ++jj) {             \
+                        const int j = q * SPG + jj;                                  \
+                        const uint4 A = *(const uint4 *)(ap + j * kXStep);           \
+                        P = mfma16x16x32(A, bneg, P);                                \
+                        P = mfma16x16x32(A, word_to_bf16x8(wj[d][j]), P);            \
+                    }                                                                \
+                    const float sf = fp16_bits_to_f32((uint16_t)(SS[d][q] >> s_sh));           \
+                    _Pragma("unroll") for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(sf, P[i], acc[i]); \
                 }                                                                    \
             }                                                                        \
         }                                                                            \
     }
 
     if (ntile > 0) {
-        SVQ_LOAD(wA, aA, sA, 0)
         for (int i0 = 0;; i0 += 2 * D) {
-            SVQ_LOAD(wB, aB, sB, i0 + D)
-            SVQ_COMPUTE(wA, aA, sA, i0)
+            SVQ_COMPUTE(wA, sA, i0)
             if (i0 + D >= ntile) break;
-            SVQ_LOAD(wA, aA, sA, i0 + 2 * D)
-            SVQ_COMPUTE(wB, aB, sB, i0 + D)
+            SVQ_LOAD(wA, sA, i0 + 2 * D)
+            SVQ_COMPUTE(wB, sB, i0 + D)
             if (i0 + 2 * D >= ntile) break;
+            SVQ_LOAD(wB, sB, i0 + 3 * D)
         }
     }
 #undef SVQ_LOAD
 #undef SVQ_COMPUTE
 
-    __shared__ float red[WAVES][16][17];
+    // cross-wave sum of the valid rows through LDS (the x stage is dead now)
+    __syncthreads();
+    float *red = (float *)smem;  // [WAVES][M][16]
 #pragma unroll
-    for (int i = 0; i < 4; ++i) red[wave][4 * g + i][r] = acc[i];
+    for (int i = 0; i < 4; ++i) {
+        const int row = 4 * g + i;
+        if (row < M) red[(wave * M + row) * 16 + r] = acc[i];
+    }
     __syncthreads();
     __shared__ int s_flag;
     float v = 0.f;
     if (threadIdx.x < 16 * M) {
-#pragma unroll
-        for (int w = 0; w < WAVES; ++w) v += red[w][threadIdx.x >> 4][threadIdx.x & 15];
+        for (int w = 0; w < WAVES; ++w) v += red[w * M * 16 + threadIdx.x];
     }
     smallm_finish(v, M, N, nb, sp, splits, out, cnt, part, &s_flag);
 }
@@ -350,7 +386,8 @@ template <int WAVES, int GS>
 hipError_t skinny_launch_w(const SmallPlan &p, const void *x, const int32_t *wt, const void *sc, void *out,
                            int M, int64_t N, int64_t K, void *ws, hipStream_t stream) {
     hipLaunchKernelGGL((w4a16_skinny_kernel<WAVES, kSkinnyDepth, GS>),
-                       dim3((uint32_t)(N / 16 * p.splits)), dim3(64 * WAVES), 0, stream,
+                       dim3((uint32_t)(N / 16 * p.splits)), dim3(64 * WAVES),
+                       skinny_lds_bytes(M, p.S, WAVES), stream,
                        (const uint16_t *)x, (const uint4 *)wt, (const uint16_t *)sc, (uint16_t *)out,
                        ws_counters(ws), (float *)ws_partials(ws), M, (int)N, (int)K, p.splits, p.S);
     return hipGetLastError();
@@ -361,7 +398,8 @@ hipError_t skinny_launch(const SmallPlan &p, const void *x, const int32_t *wt, c
                          int M, int64_t N, int64_t K, void *ws, hipStream_t stream) {
     static const int r16 = resident_blocks(w4a16_skinny_kernel<16, kSkinnyDepth, GS>, 1024);
     static const int r8 = resident_blocks(w4a16_skinny_kernel<8, kSkinnyDepth, GS>, 512);
-    switch (pick_waves(N / 16 * p.splits, p.cus, r16, r8)) {
+    const int by_lds = (int)(kLdsPerCu / skinny_lds_bytes(M, p.S, 16));
+    switch (pick_waves(N / 16 * p.splits, p.cus, std::min(r16, by_lds), std::min(r8, by_lds))) {
     case 16: return skinny_launch_w<16, GS>(p, x, wt, sc, out, M, N, K, ws, stream);
     case 8: return skinny_launch_w<8, GS>(p, x, wt, sc, out, M, N, K, ws, stream);
     default: return skinny_launch_w<4, GS>(p, x, wt, sc, out, M, N, K, ws, stream);

@@ -64,6 +64,7 @@ def test_w4a16_validation(L):
     assert _w4(L, x=FAKE + 2) == 6            # x needs 16-byte alignment
     assert _w4(L, w=FAKE2 + 8) == 6
     assert _w4(L, s=FAKE3 + 1) == 6
+    assert _w4(L, s=FAKE3 + 2) == 6
     assert _w4(L, o=FAKE4 + 2) == 6
     assert _w4(L, o=FAKE + 64) == 7            # out overlaps x
     assert _w4(L, M=9, kernel=1) == 10        # dot2 kernel takes M <= 8
@@ -82,6 +83,7 @@ def test_mxfp8_validation(L):
     assert mx(K=160) == 4                     # K % 128 (this library's tile height)
     assert mx(N=136) == 4
     assert mx(x=FAKE + 8) == 6
+    assert mx(s=FAKE3 + 2) == 6                # scales are read as aligned 32-bit words
     assert mx(o=FAKE2 + 4) == 7
     assert mx(M=9, kernel=1) == 10
 

@@ -36,15 +36,10 @@ int device_cus() {
     return n;
 }
 
-static WidePlan make_plan(int64_t M, int64_t N, int64_t K, int num_cus) {
+static WidePlan make_plan(int64_t M, int64_t N, int64_t K, int num_cus, int bm, int bn, size_t slot_bytes) {
     WidePlan p{};
-    if (M > 64) {
-        p.bm = 128;
-        p.bn = 128;
-    } else {
-        p.bm = 64;
-        p.bn = 256;
-    }
+    p.bm = bm;
+    p.bn = bn;
     p.row_tiles = (int)((M + p.bm - 1) / p.bm);
     p.col_tiles = (int)((N + p.bn - 1) / p.bn);
     const int64_t KT = K / 128;
@@ -59,7 +54,7 @@ static WidePlan make_plan(int64_t M, int64_t N, int64_t K, int num_cus) {
         if (b % KT != 0 || e % KT != 0) shared = true;
     }
     p.maxt = maxt;
-    if (shared) p.workspace_bytes = kCounterBytes + (size_t)p.grid * p.maxt * kWideAccPerThread * kWideThreads * 16;
+    if (shared) p.workspace_bytes = kCounterBytes + (size_t)p.grid * p.maxt * slot_bytes;
     return p;
 }
 
@@ -84,10 +79,12 @@ SmallPlan plan_smallm(int64_t M, int64_t N, int64_t K, int num_cus, int64_t max_
 }
 
 WidePlan plan_w4a16_wide(int64_t M, int64_t N, int64_t K, int num_cus) {
-    return make_plan(M, N, K, num_cus);
+    // 128 x 256 output tiles; a stream-K partial is one fp32 tile
+    return make_plan(M, N, K, num_cus, 128, 256, (size_t)128 * 256 * 4);
 }
 WidePlan plan_mxfp8_wide(int64_t M, int64_t N, int64_t K, int num_cus) {
-    return make_plan(M, N, K, num_cus);
+    const int bm = M > 64 ? 128 : 64, bn = M > 64 ? 128 : 256;
+    return make_plan(M, N, K, num_cus, bm, bn, (size_t)kWideAccPerThread * kWideThreads * 16);
 }
 
 }  // namespace svq
@@ -258,6 +255,10 @@ int svq_w4a16_gemm_with(int kernel, const void *x, const int32_t *wt, const void
         wplan = plan_w4a16_wide(M, N, K, cus);
         need = wplan.workspace_bytes;
         if (need && (size_t)wplan.row_tiles * wplan.col_tiles > kMaxCounters) return SVQ_ERR_UNSUPPORTED;
+        // the kernel addresses x (padded to whole row tiles), the weights and
+        // the scales with 32-bit buffer offsets
+        if ((uint64_t)wplan.row_tiles * wplan.bm * K * 2 >= (1ull << 32) || (uint64_t)N * K / 2 >= (1ull << 32))
+            return SVQ_ERR_UNSUPPORTED;
     } else {
         splan = w4a16_small_plan(k, M, N, K, cus);
         need = splan.workspace_bytes;

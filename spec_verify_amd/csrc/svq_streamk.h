@@ -60,25 +60,41 @@ __device__ __forceinline__ bool sk_fixup(f32x4 (&acc)[NV], int tile, int KT, int
     __syncthreads();
     if (tid == 0) *s_flag = (arrive(&cnt[tile]) == (uint32_t)(lw - fw));
     __syncthreads();
-    if (*s_flag == 0) return false;
-    f32x4 sum[NV];
+    // read as a wave-uniform value: the code below is then uniform control
+    // flow with scalar buffer descriptors
+    if (__builtin_amdgcn_readfirstlane(*s_flag) == 0) return false;
+    // every contributor, this one included, stored its partial above: add
+    // them all from memory in workgroup order, so that `acc` need not stay
+    // live next to the running sum
 #pragma unroll
-    for (int v = 0; v < NV; ++v) sum[v] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int w = fw; w <= lw; ++w) {
-        if (w == wg) {
+    for (int v = 0; v < NV; ++v) acc[v] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int fwu = __builtin_amdgcn_readfirstlane(fw), lwu = __builtin_amdgcn_readfirstlane(lw);
+    // uniform by construction; readfirstlane lets the compiler keep the buffer
+    // descriptors in scalar registers
+    auto view = [&](int w) {
+        const int wslot = __builtin_amdgcn_readfirstlane(tile - sk_first_tile(w, units, grid, KT));
+        return make_rsrc(part + (size_t)(w * maxt + wslot) * NV * NT, slot_bytes);
+    };
+    // two contributors' loads in flight at a time (each load is a round trip
+    // to the device-coherent level), added in workgroup order
+    for (int w = fwu; w <= lwu; w += 2) {
+        f32x4 a[NV], b[NV];
+        const __amdgpu_buffer_rsrc_t ra = view(w);
 #pragma unroll
-            for (int v = 0; v < NV; ++v) sum[v] += acc[v];
-        } else {
-            const int wslot = tile - sk_first_tile(w, units, grid, KT);
-            const __amdgpu_buffer_rsrc_t theirs =
-                make_rsrc(part + (size_t)(w * maxt + wslot) * NV * NT, slot_bytes);
+        for (int v = 0; v < NV; ++v) a[v] = __builtin_amdgcn_raw_buffer_load_b128(ra, (uint32_t)(v * NT + tid) * 16, 0, kCoherent);
+        const bool two = w + 1 <= lwu;
+        if (two) {
+            const __amdgpu_buffer_rsrc_t rb = view(w + 1);
 #pragma unroll
-            for (int v = 0; v < NV; ++v)
-                sum[v] += __builtin_amdgcn_raw_buffer_load_b128(theirs, (uint32_t)(v * NT + tid) * 16, 0, kCoherent);
+            for (int v = 0; v < NV; ++v) b[v] = __builtin_amdgcn_raw_buffer_load_b128(rb, (uint32_t)(v * NT + tid) * 16, 0, kCoherent);
+        }
+#pragma unroll
+        for (int v = 0; v < NV; ++v) acc[v] += a[v];
+        if (two) {
+#pragma unroll
+            for (int v = 0; v < NV; ++v) acc[v] += b[v];
         }
     }
-#pragma unroll
-    for (int v = 0; v < NV; ++v) acc[v] = sum[v];
     if (tid == 0) clear_counter(&cnt[tile]);
     return true;
 }
@@ -106,7 +122,7 @@ __device__ __forceinline__ void smallm_finish(float v, int M, int N, int nb, int
     __syncthreads();
     if (t == 0) *s_flag = (arrive(&cnt[nb]) == (uint32_t)(splits - 1));
     __syncthreads();
-    if (*s_flag == 0) return;
+    if (__builtin_amdgcn_readfirstlane(*s_flag) == 0) return;
     if (owner) {
         float s = 0.f;
         for (int k = 0; k < splits; ++k)

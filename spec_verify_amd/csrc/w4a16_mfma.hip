@@ -20,6 +20,7 @@
 // per group by starting the group's accumulator at -136 * (sum of x over the
 // group), then the fp16 scale multiplies the group result into fp32 accumulators.
 #include <algorithm>
+#include <type_traits>
 
 #include "svq_launch.h"
 #include "svq_streamk.h"
@@ -159,32 +160,106 @@ __global__ __launch_bounds__(64 * WAVES) void w4a16_skinny_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Wide kernel: any M (tuned for M = 128). Persistent stream-K: the grid has one
-// workgroup per compute unit and each takes an equal contiguous share of the
-// (output tile, 128-row K step) units. A tile computed by several workgroups is
-// finished by the last to arrive, which adds the fp32 partials in workgroup
-// order (fixed order: deterministic) and clears the tile's arrival counter.
+// Wide kernel: any M (built for M = 128). Persistent stream-K: one workgroup
+// per compute unit, each taking an equal contiguous share of the (output tile,
+// 128-row K step) units. A tile computed by several workgroups is finished by
+// the last to arrive, which adds the fp32 partials in workgroup order (fixed
+// order: deterministic) and clears the tile's arrival counter.
 //
-// Per step, the workgroup stages the x tile (BM rows x 128, bf16) in LDS with
-// -136 * (group sums of x) and the step's scales; each wave owns MBW 16-row
-// blocks x CT 16-column weight tiles, streams its weight tiles with 128-bit
-// loads one step ahead, and runs MBW*CT MFMA chains per group.
+// Workgroup: WR x WC waves (two per SIMD, so one wave's MFMAs cover the other's
+// VALU work), output tile BM x BN; a wave owns MBW 16-row blocks x CT 16-column
+// tiles. With MBW = 8 every converted weight operand feeds eight MFMAs, which
+// keeps the dequant VALU work under the MFMA issue budget.
+//
+// Pipeline: a ring of three LDS stages, each one K step: x (BM rows x 128,
+// 16-byte chunks XOR-swizzled by row so that the MFMA A reads are
+// bank-conflict free), the BN/16 weight tiles, the fp16 scales, and
+// -136 * (group sums of x). Stages are filled by LDS-DMA (buffer loads that
+// write LDS directly; rows past M and columns past N read as zero), two steps
+// ahead; the group sums of step i+1 are computed during step i. Each slot is
+// its own LDS object, so the compiler can tell a DMA into one slot from reads
+// of another and does not wait for in-flight DMAs before every LDS read.
+//
+// MFMA step j of a K step covers rows 32j..32j+31; lane (r, g) supplies
+// K-rows 32j+8g.. of x row r and of column r, and its weight word is word g of
+// lane 16j+r of the repacked tile (a transposed read from LDS), so every
+// group size uses the same mapping.
 // ---------------------------------------------------------------------------
 template <int MBW, int WR, int WC, int CT, int GSHIFT>
 struct WideCfg {
-    static constexpr int NT = 64 * WR * WC;
+    static constexpr int WAVES = WR * WC;
+    static constexpr int NT = 64 * WAVES;
     static constexpr int BM = 16 * MBW * WR;
     static constexpr int BN = 16 * CT * WC;
     static constexpr int NG = 128 >> GSHIFT;
     static constexpr int SPG = 4 / NG;
-    static constexpr bool kTrans = GSHIFT < 7;
-    static constexpr int XROW = 128 + 8;        // bf16 per LDS row (16-byte pad)
-    static constexpr int UPT = BM * 16 / NT;    // 16-byte x chunks staged per thread
-    static constexpr int TPR = 16 / UPT;        // staging threads per x row
-    static constexpr int SPT = (NG * BN + NT - 1) / NT;  // scales staged per thread
-    static constexpr int NV = MBW * CT;         // f32x4 accumulators per lane
-    static_assert(UPT == 4 || UPT == 8, "staging assumes 1 or 2 32-row blocks per thread");
+    static constexpr int NV = MBW * CT;          // f32x4 accumulators per lane
+    // one LDS stage (slot): x, weight tiles, fp16 scales [NG][BN], -136 *
+    // group sums of x [NG][BM]
+    static constexpr int XB = BM * 256;
+    static constexpr int WB = (BN / 16) * 1024;
+    static constexpr int SB = NG * BN * 2;
+    static constexpr int OFF_W = XB, OFF_S = XB + WB, OFF_N = XB + WB + SB;
+    static constexpr int SLOT = OFF_N + NG * BM * 4;
+    static constexpr int XI = BM / 4 / WAVES;    // x DMAs per wave per stage (1 KiB = 4 rows each)
+    static constexpr int WI = BN / 16 / WAVES;   // weight DMAs per wave per stage (one tile each)
+    static constexpr int SI = NG * BN / 128;     // scale DMAs per stage (128 fp16 each), waves 0..SI-1
+    static_assert(XI * 4 * WAVES == BM && WI * 16 * WAVES == BN, "stage split over the waves");
+    static_assert(SI <= WAVES, "one scale DMA per wave at most");
+    static_assert(BM == 16 * WAVES, "each wave sums x over 16 rows");
+    static_assert(SLOT % 16 == 0 && SLOT < 65536, "slot offsets fit a ds immediate");
+    static_assert(MBW % 2 == 0, "row blocks go in pairs");
 };
+
+// LDS-DMA loads (buffer_load ... lds: lane l's bytes land at M0 + size*l, and
+// offsets past num_records read as zero). Written in asm so that the compiler
+// does not track them: it cannot tell the ring's slots apart and would wait
+// for every DMA in flight before each LDS read. The asm has no output
+// registers; every wait for these loads is an explicit s_waitcnt vmcnt, and
+// the "memory" clobber keeps LDS accesses in order with them. s_nop 0 covers
+// the wait state between writing M0 and the DMA reading it.
+struct BufDesc {
+    u32x4 v;
+};
+__device__ __forceinline__ BufDesc buf_desc(const void *base, uint32_t bytes) {
+    const uint64_t a = (uint64_t)base;
+    return BufDesc{u32x4{(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, bytes, 0x00020000u}};
+}
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
+__device__ __forceinline__ void dma_b128(const BufDesc &d, uint32_t lds, uint32_t voff, uint32_t soff) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %3 offen lds"
+                 :
+                 : "v"(voff), "s"(d.v), "s"(lds), "s"(soff)
+                 : "memory", "m0");
+}
+__device__ __forceinline__ void dma_b32(const BufDesc &d, uint32_t lds, uint32_t voff, uint32_t soff) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dword %0, %1, %3 offen lds"
+                 :
+                 : "v"(voff), "s"(d.v), "s"(lds), "s"(soff)
+                 : "memory", "m0");
+}
+// Barrier after this wave's LDS writes have completed; unlike __syncthreads()
+// it does not also wait for the DMAs in flight.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() { __builtin_amdgcn_s_waitcnt(vmcnt_imm(N)); }
+
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+// An LDS address the compiler must treat as unknown at this point: every
+// address derived from it is then base + per-lane offset + immediate, instead
+// of dozens of precomputed addresses held in registers across the loop.
+__device__ __forceinline__ const lds_u8 *lds_opaque(uint32_t a) {
+    asm volatile("" : "+v"(a));
+    return (const lds_u8 *)(uintptr_t)a;
+}
+template <typename T>
+__device__ __forceinline__ T lds_ld(const lds_u8 *p) { return *(const __attribute__((address_space(3))) T *)p; }
+__device__ __forceinline__ uint4 lds_ld16(const lds_u8 *p) {
+    const u32x4 v = lds_ld<u32x4>(p);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
 
 template <int MBW, int WR, int WC, int CT, int GSHIFT>
 __global__ __launch_bounds__(64 * WR * WC) void w4a16_wide_kernel(
@@ -193,14 +268,12 @@ __global__ __launch_bounds__(64 * WR * WC) void w4a16_wide_kernel(
     f32x4 *__restrict__ part, int M, int N, int K, int col_tiles, int64_t units, int grid,
     int maxt) {
     using C = WideCfg<MBW, WR, WC, CT, GSHIFT>;
-    constexpr int NT = C::NT, BM = C::BM, BN = C::BN, NG = C::NG, SPG = C::SPG;
-    constexpr int XROW = C::XROW, UPT = C::UPT, TPR = C::TPR, SPT = C::SPT, NV = C::NV;
-    __shared__ __attribute__((aligned(16))) uint16_t xs[2][BM][XROW];
-    __shared__ __attribute__((aligned(16))) float xneg[2][NG][BM];
-    __shared__ uint16_t sl[2][NG][BN];
+    constexpr int BM = C::BM, BN = C::BN, NG = C::NG, SPG = C::SPG, NV = C::NV;
+    __shared__ __attribute__((aligned(16))) uint8_t ring[3 * C::SLOT];
     __shared__ int s_last;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wave = wave_id();
     const int wr = wave / WC, wc = wave % WC;
     const int r = lane & 15, g = lane >> 4;
     const int KT = K >> 7;
@@ -208,171 +281,233 @@ __global__ __launch_bounds__(64 * WR * WC) void w4a16_wide_kernel(
     const int wg = blockIdx.x;
     const int64_t u_begin = (int64_t)wg * units / grid;
     const int64_t u_end = (int64_t)(wg + 1) * units / grid;
-    const int srow = tid / TPR, sseg = tid % TPR;
+    const uint32_t ring_lds = lds_addr(ring);
+    // buffer views: reads past the end return zero (rows >= M, columns >= N)
+    const BufDesc xr = buf_desc(x, (uint32_t)((size_t)M * K * 2));
+    const BufDesc wrs = buf_desc(wt, (uint32_t)((size_t)N * K / 2));
+    const BufDesc sr = buf_desc(sc, (uint32_t)((size_t)(K >> GSHIFT) * N * 2));
 
-    for (int64_t u = u_begin; u < u_end;) {
-        const int tile = (int)(u / KT);
-        const int s0 = (int)(u % KT);
-        const int s1 = (int)((u_end - u) < (int64_t)(KT - s0) ? s0 + (u_end - u) : KT);
-        const int rt = tile / col_tiles, cb = tile % col_tiles;
-        const int row0 = rt * BM;
-
-        // this wave's weight tiles (clamped to a valid tile past the last column)
-        const uint4 *tp[CT];
-        bool ctv[CT];
+    // per-lane LDS offsets within a slot (constant for the whole kernel)
+    uint32_t offA[4];  // A operand of MFMA step j: row r of the block, K-rows 32j+8g..
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct) {
-            const int nbg = cb * (BN / 16) + wc * CT + ct;
-            ctv[ct] = nbg < NB16;
-            tp[ct] = wt + (size_t)(ctv[ct] ? nbg : NB16 - 1) * KT * 64 + lane;
-        }
-        const bool srv = row0 + srow < M;
-        const uint4 *xsrc = (const uint4 *)(x + (size_t)(srv ? row0 + srow : 0) * K) + sseg * UPT;
+    for (int j = 0; j < 4; ++j) offA[j] = r * 256 + (((4 * j + g) ^ r) << 4);
+    const uint32_t offW = C::OFF_W + wc * CT * 1024 + (r << 4) + (g << 2);  // word g of lane 16j+r
+    const uint32_t offS = C::OFF_S + (wc * CT * 16 + r) * 2;
+    const uint32_t offN = C::OFF_N + 16 * g;
+    const int srow = 16 * wave + (lane >> 2), q4 = lane & 3;  // group-sum rows of this wave
+    uint32_t offX[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) offX[c] = srow * 256 + (((4 * q4 + c) ^ (srow & 15)) << 4);
+    const uint32_t offNw = C::OFF_N + srow * 4;
 
-        f32x4 acc[NV];  // [rb * CT + ct]
+    // A segment is a run of K steps of one tile. Its stages use consecutive
+    // ring slots; the next segment's first two stages are issued during the
+    // last step of the current one, so their latency hides behind that step
+    // and the epilogue.
+    struct Seg {
+        int tile, s0, n, rt, cb;
+    };
+    auto seg_at = [&](int64_t u) {
+        Seg g;
+        g.tile = (int)(u / KT);
+        g.s0 = (int)(u % KT);
+        g.n = (int)((u_end - u) < (int64_t)(KT - g.s0) ? (u_end - u) : (KT - g.s0));
+        g.rt = g.tile / col_tiles;
+        g.cb = g.tile % col_tiles;
+        return g;
+    };
+    // DMA of K step kt of segment g into slot st: x, then scales, then
+    // weights (the order the waits below rely on)
+    auto issue = [&](const Seg &sg, int st, int kt) {
+        const uint32_t base = ring_lds + st * C::SLOT;
+#pragma unroll
+        for (int v = 0; v < C::XI; ++v) {
+            const int rl = 4 * (wave * C::XI + v) + (lane >> 4);
+            const uint32_t vx = (uint32_t)(sg.rt * BM + rl) * (uint32_t)K * 2u + (uint32_t)(((lane & 15) ^ (rl & 15)) * 16);
+            dma_b128(xr, base + (wave * C::XI + v) * 1024, vx, (uint32_t)kt * 256u);
+        }
+        if (wave < C::SI) {
+            const int q = wave / (BN / 128), prt = wave % (BN / 128);
+            dma_b32(sr, base + C::OFF_S + (q * BN + prt * 128) * 2, lane * 4,
+                    ((uint32_t)(kt * NG + q) * (uint32_t)N + (uint32_t)(sg.cb * BN + prt * 128)) * 2u);
+        }
+#pragma unroll
+        for (int v = 0; v < C::WI; ++v) {
+            const int t = wave * C::WI + v;
+            dma_b128(wrs, base + C::OFF_W + t * 1024, lane * 16,
+                     ((uint32_t)(sg.cb * (BN / 16) + t) * (uint32_t)KT + (uint32_t)kt) * 1024u);
+        }
+    };
+    int slot0 = 0;         // ring slot of the segment's first stage
+    bool issued = false;   // the segment's first stages were issued ahead
+    for (int64_t u = u_begin; u < u_end;) {
+        const Seg sg = seg_at(u);
+        const int tile = sg.tile, s0 = sg.s0, n = sg.n, rt = sg.rt, cb = sg.cb;
+        const int s1 = s0 + n;
+        // -136 * (sum of x over each group) for rows 16*wave.. of slot st
+        auto sums = [&](int st) {
+            const lds_u8 *b = lds_opaque(ring_lds + st * C::SLOT);
+            float t = 0.f;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const uint4 v = lds_ld16(b + offX[c]);
+                t = dot2_bf16(v.x, kBf16OnePair, t);
+                t = dot2_bf16(v.y, kBf16OnePair, t);
+                t = dot2_bf16(v.z, kBf16OnePair, t);
+                t = dot2_bf16(v.w, kBf16OnePair, t);
+            }
+            __attribute__((address_space(3))) float *xn =
+                (__attribute__((address_space(3))) float *)(b + offNw);
+            // the four K quarters of a row sit in adjacent lanes: quad DPP sums
+            if constexpr (NG == 4) {
+                xn[q4 * BM] = -136.f * t;
+            } else if constexpr (NG == 2) {
+                t += bits_f32(__builtin_amdgcn_mov_dpp(f32_bits(t), 0xB1, 0xF, 0xF, true));  // quad_perm [1,0,3,2]
+                if ((q4 & 1) == 0) xn[(q4 >> 1) * BM] = -136.f * t;
+            } else {
+                t += bits_f32(__builtin_amdgcn_mov_dpp(f32_bits(t), 0xB1, 0xF, 0xF, true));  // quad_perm [1,0,3,2]
+                t += bits_f32(__builtin_amdgcn_mov_dpp(f32_bits(t), 0x4E, 0xF, 0xF, true));  // quad_perm [2,3,0,1]
+                if (q4 == 0) xn[0] = -136.f * t;
+            }
+        };
+
+        f32x4 acc[NV];
 #pragma unroll
         for (int v = 0; v < NV; ++v) acc[v] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-        uint4 xreg[UPT];
-        uint16_t sreg[SPT];
-        uint4 wcur[CT], wnext[CT];
-
-        auto load_x = [&](int s) {
-#pragma unroll
-            for (int v = 0; v < UPT; ++v) xreg[v] = srv ? xsrc[(size_t)s * 16 + v] : make_uint4(0, 0, 0, 0);
-#pragma unroll
-            for (int v = 0; v < SPT; ++v) {
-                const int i = tid + v * NT;
-                const int q = i / BN, c = i % BN;
-                int colg = cb * BN + c;
-                colg = colg < N ? colg : N - 1;
-                sreg[v] = (i < NG * BN) ? sc[(size_t)(s * NG + q) * N + colg] : (uint16_t)0;
-            }
-        };
-        auto load_w = [&](uint4(&W)[CT], int s) {
-#pragma unroll
-            for (int ct = 0; ct < CT; ++ct) W[ct] = load_stream16(tp[ct] + (size_t)s * 64);
-        };
-        auto store_stage = [&](int buf) {
-#pragma unroll
-            for (int v = 0; v < UPT; ++v) *(uint4 *)&xs[buf][srow][(sseg * UPT + v) * 8] = xreg[v];
-            float bsum[UPT / 4];
-#pragma unroll
-            for (int b = 0; b < UPT / 4; ++b) {
-                float t = 0.f;
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const uint4 q4 = xreg[4 * b + v];
-                    t = dot2_bf16(q4.x, kBf16OnePair, t);
-                    t = dot2_bf16(q4.y, kBf16OnePair, t);
-                    t = dot2_bf16(q4.z, kBf16OnePair, t);
-                    t = dot2_bf16(q4.w, kBf16OnePair, t);
-                }
-                bsum[b] = t;
-            }
-            if constexpr (NG == 4) {  // G = 32: one group per 32-row block
-#pragma unroll
-                for (int b = 0; b < UPT / 4; ++b) xneg[buf][sseg * (UPT / 4) + b][srow] = -136.f * bsum[b];
-            } else if constexpr (NG == 2) {  // G = 64
-                if constexpr (UPT == 8) {
-                    xneg[buf][sseg][srow] = -136.f * (bsum[0] + bsum[1]);
-                } else {
-                    const float v = bsum[0] + __shfl_xor(bsum[0], 1);
-                    if ((sseg & 1) == 0) xneg[buf][sseg >> 1][srow] = -136.f * v;
-                }
-            } else {  // G = 128
-                float v = bsum[0];
-                if constexpr (UPT == 8) v += bsum[1];
-                v += __shfl_xor(v, 1);
-                if constexpr (TPR == 4) v += __shfl_xor(v, 2);
-                if (sseg == 0) xneg[buf][0][srow] = -136.f * v;
-            }
-#pragma unroll
-            for (int v = 0; v < SPT; ++v) {
-                const int i = tid + v * NT;
-                if (i < NG * BN) sl[buf][i / BN][i % BN] = sreg[v];
-            }
-        };
-        auto compute = [&](int buf, const uint4(&W)[CT]) {
-            uint32_t wj[CT][4];
-#pragma unroll
-            for (int ct = 0; ct < CT; ++ct) {
-                wj[ct][0] = W[ct].x;
-                wj[ct][1] = W[ct].y;
-                wj[ct][2] = W[ct].z;
-                wj[ct][3] = W[ct].w;
-                if constexpr (C::kTrans) transpose_rows_words(wj[ct][0], wj[ct][1], wj[ct][2], wj[ct][3]);
-            }
-            const int rbase = wr * MBW * 16;
+        // The MFMA work of a step, in two halves of the (group, row-block pair)
+        // items, so that the step's DMA issue and group sums can sit between
+        // them and overlap MFMAs.
+        auto compute = [&](int st, auto H) {
+            constexpr int half = decltype(H)::value;
+            constexpr int NP = MBW / 2;
+            constexpr int NI = NG * NP;
+            const lds_u8 *b = lds_opaque(ring_lds + st * C::SLOT);
 #pragma unroll
             for (int q = 0; q < NG; ++q) {
-                f32x4 P[MBW][CT];
-#pragma unroll
-                for (int rb = 0; rb < MBW; ++rb) {
-                    const f32x4 c = *(const f32x4 *)&xneg[buf][q][rbase + rb * 16 + 4 * g];
-#pragma unroll
-                    for (int ct = 0; ct < CT; ++ct) P[rb][ct] = c;
-                }
-#pragma unroll
-                for (int jj = 0; jj < SPG; ++jj) {
-                    const int j = q * SPG + jj;
-                    const int koff = C::kTrans ? (32 * j + 8 * g) : (32 * g + 8 * j);
-                    uint4 A[MBW];
-#pragma unroll
-                    for (int rb = 0; rb < MBW; ++rb) A[rb] = *(const uint4 *)&xs[buf][rbase + rb * 16 + r][koff];
-#pragma unroll
-                    for (int ct = 0; ct < CT; ++ct) {
-                        const uint4 B = word_to_bf16x8(wj[ct][j]);
-#pragma unroll
-                        for (int rb = 0; rb < MBW; ++rb) P[rb][ct] = mfma16x16x32(A[rb], B, P[rb][ct]);
-                    }
-                }
+                constexpr int pb = 0;
+                (void)pb;
+                const int i0 = q * NP;  // first item of group q
+                if ((i0 + NP <= half * NI / 2) || (i0 >= (half + 1) * NI / 2)) continue;
+                const int pa = (i0 < half * NI / 2 ? half * NI / 2 - i0 : 0);
+                const int pe = (i0 + NP > (half + 1) * NI / 2 ? (half + 1) * NI / 2 - i0 : NP);
+                float sf[CT];
+                uint4 B[SPG][CT];
 #pragma unroll
                 for (int ct = 0; ct < CT; ++ct) {
-                    const float sf = fp16_bits_to_f32(sl[buf][q][wc * CT * 16 + ct * 16 + r]);
+                    sf[ct] = fp16_bits_to_f32(lds_ld<uint16_t>(b + offS + (q * BN + ct * 16) * 2));
+#pragma unroll
+                    for (int jj = 0; jj < SPG; ++jj)
+                        B[jj][ct] = word_to_bf16x8(lds_ld<uint32_t>(b + offW + ct * 1024 + (q * SPG + jj) * 256));
+                }
+                // Row blocks go in pairs (2*CT independent MFMA chains); the
+                // next pair's A operands are read while this pair's MFMAs run,
+                // and a pair's scale FMAs wait until the next pair's MFMAs are
+                // issued, so that neither an MFMA nor an FMA waits on its input.
+                uint4 A[2][2][SPG];
+                f32x4 I[2][2];
+                f32x4 P[2][2][CT];
+                auto load_pair = [&](int p, uint4 (&Ap)[2][SPG], f32x4 (&Ip)[2]) {
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const int rb = 2 * p + h;
+#pragma unroll
+                        for (int jj = 0; jj < SPG; ++jj)
+                            Ap[h][jj] = lds_ld16(b + offA[q * SPG + jj] + (wr * MBW + rb) * 4096);
+                        Ip[h] = lds_ld<f32x4>(b + offN + (q * BM + (wr * MBW + rb) * 16) * 4);
+                    }
+                };
+                auto fma_pair = [&](int p, const f32x4 (&Pp)[2][CT]) {
+#pragma unroll
+                    for (int h = 0; h < 2; ++h)
+#pragma unroll
+                        for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+                            for (int i = 0; i < 4; ++i)
+                                acc[(2 * p + h) * CT + ct][i] =
+                                    __builtin_fmaf(sf[ct], Pp[h][ct][i], acc[(2 * p + h) * CT + ct][i]);
+                };
+                load_pair(pa, A[pa & 1], I[pa & 1]);
+#pragma unroll
+                for (int p = 0; p < NP; ++p) {
+                    if (p < pa || p >= pe) continue;
+                    if (p + 1 < pe) load_pair(p + 1, A[(p + 1) & 1], I[(p + 1) & 1]);
+                    uint4 (&Ac)[2][SPG] = A[p & 1];
+                    f32x4 (&Pc)[2][CT] = P[p & 1];
+#pragma unroll
+                    for (int jj = 0; jj < SPG; ++jj)
+#pragma unroll
+                        for (int h = 0; h < 2; ++h)
+#pragma unroll
+                            for (int ct = 0; ct < CT; ++ct)
+                                Pc[h][ct] = mfma16x16x32(Ac[h][jj], B[jj][ct], jj == 0 ? I[p & 1][h] : Pc[h][ct]);
+                    if (p > pa) fma_pair(p - 1, P[(p - 1) & 1]);
+                }
+                fma_pair(pe - 1, P[(pe - 1) & 1]);
+            }
+        };
+
+        const int slot1 = slot0 == 2 ? 0 : slot0 + 1;
+        if (!issued) {
+            lds_barrier();  // the previous segment is done with every slot
+            issue(sg, slot0, s0);
+            if (n > 1) issue(sg, slot1, s0 + 1);
+        }
+        // stage 0 has landed (at most stage 1's DMAs are outstanding)
+        if (n > 1) wait_vmcnt_at_most<C::XI + 1 + C::WI>(C::XI + (wave < C::SI ? 1 : 0) + C::WI);
+        else wait_vmcnt<0>();
+        lds_barrier();
+        sums(slot0);
+        int st = slot0;
+        for (int i = 0; i < n; ++i, st = (st == 2 ? 0 : st + 1)) {
+            // this wave's DMAs: all but the weights of step i+1 have landed
+            if (i + 1 < n) wait_vmcnt<C::WI>();
+            else wait_vmcnt<0>();
+            lds_barrier();  // every wave's slot st and x of slot st+1 are in; slot st+2 is free
+            const int st1 = st == 2 ? 0 : st + 1, st2 = st1 == 2 ? 0 : st1 + 1;
+            compute(st, std::integral_constant<int, 0>{});
+            if (i + 2 < n) issue(sg, st2, s0 + i + 2);
+            if (i + 1 < n) sums(st1);
+            if (i + 1 == n && u + n < u_end) {
+                // the next segment's first two stages go into the two slots
+                // this step does not use
+                const Seg nx = seg_at(u + n);
+                issue(nx, st1, nx.s0);
+                if (nx.n > 1) issue(nx, st2, nx.s0 + 1);
+            }
+            compute(st, std::integral_constant<int, 1>{});
+        }
+        slot0 = st;  // one past the last stage's slot
+        issued = true;
+
+        // ---- epilogue ----
+        auto store_out = [&]() {
+            // a row tile inside M needs no per-element row check
+            const bool full = rt * BM + BM <= M;
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) {
+                const int nbg = cb * (BN / 16) + wc * CT + ct;
+                if (nbg >= NB16) continue;
+                uint16_t *o = out + (size_t)(rt * BM + wr * MBW * 16 + 4 * g) * N + nbg * 16 + r;
+                if (full) {
 #pragma unroll
                     for (int rb = 0; rb < MBW; ++rb)
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) acc[rb * CT + ct][i] = __builtin_fmaf(sf, P[rb][ct][i], acc[rb * CT + ct][i]);
+                        for (int i = 0; i < 4; ++i) o[(size_t)(rb * 16 + i) * N] = f32_to_bf16_rne(acc[rb * CT + ct][i]);
+                } else {
+#pragma unroll
+                    for (int rb = 0; rb < MBW; ++rb)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const int row = rt * BM + (wr * MBW + rb) * 16 + 4 * g + i;
+                            if (row < M) o[(size_t)(rb * 16 + i) * N] = f32_to_bf16_rne(acc[rb * CT + ct][i]);
+                        }
                 }
             }
         };
-
-        __syncthreads();  // LDS of a previous segment is no longer read
-        load_x(s0);
-        load_w(wcur, s0);
-        for (int s = s0; s < s1; ++s) {
-            const int buf = (s - s0) & 1;
-            store_stage(buf);
-            __syncthreads();
-            if (s + 1 < s1) {
-                load_x(s + 1);
-                load_w(wnext, s + 1);
-            }
-            compute(buf, wcur);
-#pragma unroll
-            for (int ct = 0; ct < CT; ++ct) wcur[ct] = wnext[ct];
-        }
-
-        // ---- epilogue ----
-        const int rowb = row0 + wr * MBW * 16 + 4 * g;
-        auto store_out = [&]() {
-#pragma unroll
-            for (int ct = 0; ct < CT; ++ct) {
-                if (!ctv[ct]) continue;
-                const int colg = (cb * (BN / 16) + wc * CT + ct) * 16 + r;
-#pragma unroll
-                for (int rb = 0; rb < MBW; ++rb)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int row = rowb + rb * 16 + i;
-                        if (row < M) out[(size_t)row * N + colg] = f32_to_bf16_rne(acc[rb * CT + ct][i]);
-                    }
-            }
-        };
-        if ((s0 == 0 && s1 == KT) || sk_fixup<NV, NT>(acc, tile, KT, units, grid, maxt, cnt, part, &s_last))
+        if ((s0 == 0 && s1 == KT) || sk_fixup<NV, C::NT>(acc, tile, KT, units, grid, maxt, cnt, part, &s_last))
             store_out();
-        u += s1 - s0;
+        u += n;
     }
 }
 
@@ -421,8 +556,8 @@ hipError_t wide_launch(const WidePlan &p, const void *x, const int32_t *wt, cons
 template <int GS>
 hipError_t wide_by_shape(const WidePlan &p, const void *x, const int32_t *wt, const void *sc,
                          void *out, int64_t M, int64_t N, int64_t K, void *ws, hipStream_t stream) {
-    if (p.bm == 128) return wide_launch<4, 2, 2, 4, GS>(p, x, wt, sc, out, M, N, K, ws, stream);
-    return wide_launch<4, 1, 4, 4, GS>(p, x, wt, sc, out, M, N, K, ws, stream);
+    // 8 waves of 128 rows x 32 columns: a 128 x 256 tile
+    return wide_launch<8, 1, 8, 2, GS>(p, x, wt, sc, out, M, N, K, ws, stream);
 }
 }  // namespace
 

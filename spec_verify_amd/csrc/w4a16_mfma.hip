@@ -378,6 +378,20 @@ __global__ __launch_bounds__(64 * WR * WC) void w4a16_wide_kernel(
         // The MFMA work of a step, in two halves of the (group, row-block pair)
         // items, so that the step's DMA issue and group sums can sit between
         // them and overlap MFMAs.
+        // dequantized weight operands and scales of a step: converted once
+        // and shared by both halves of the MFMA work
+        uint4 B[4][CT];
+        float sfa[NG][CT];
+        auto prep = [&](int st) {
+            const lds_u8 *b = lds_opaque(ring_lds + st * C::SLOT);
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) {
+#pragma unroll
+                for (int q = 0; q < NG; ++q) sfa[q][ct] = fp16_bits_to_f32(lds_ld<uint16_t>(b + offS + (q * BN + ct * 16) * 2));
+#pragma unroll
+                for (int j = 0; j < 4; ++j) B[j][ct] = word_to_bf16x8(lds_ld<uint32_t>(b + offW + ct * 1024 + j * 256));
+            }
+        };
         auto compute = [&](int st, auto H) {
             constexpr int half = decltype(H)::value;
             constexpr int NP = MBW / 2;
@@ -385,21 +399,11 @@ __global__ __launch_bounds__(64 * WR * WC) void w4a16_wide_kernel(
             const lds_u8 *b = lds_opaque(ring_lds + st * C::SLOT);
 #pragma unroll
             for (int q = 0; q < NG; ++q) {
-                constexpr int pb = 0;
-                (void)pb;
                 const int i0 = q * NP;  // first item of group q
                 if ((i0 + NP <= half * NI / 2) || (i0 >= (half + 1) * NI / 2)) continue;
                 const int pa = (i0 < half * NI / 2 ? half * NI / 2 - i0 : 0);
                 const int pe = (i0 + NP > (half + 1) * NI / 2 ? (half + 1) * NI / 2 - i0 : NP);
-                float sf[CT];
-                uint4 B[SPG][CT];
-#pragma unroll
-                for (int ct = 0; ct < CT; ++ct) {
-                    sf[ct] = fp16_bits_to_f32(lds_ld<uint16_t>(b + offS + (q * BN + ct * 16) * 2));
-#pragma unroll
-                    for (int jj = 0; jj < SPG; ++jj)
-                        B[jj][ct] = word_to_bf16x8(lds_ld<uint32_t>(b + offW + ct * 1024 + (q * SPG + jj) * 256));
-                }
+                const float (&sf)[CT] = sfa[q];
                 // Row blocks go in pairs (2*CT independent MFMA chains); the
                 // next pair's A operands are read while this pair's MFMAs run,
                 // and a pair's scale FMAs wait until the next pair's MFMAs are
@@ -440,7 +444,7 @@ __global__ __launch_bounds__(64 * WR * WC) void w4a16_wide_kernel(
                         for (int h = 0; h < 2; ++h)
 #pragma unroll
                             for (int ct = 0; ct < CT; ++ct)
-                                Pc[h][ct] = mfma16x16x32(Ac[h][jj], B[jj][ct], jj == 0 ? I[p & 1][h] : Pc[h][ct]);
+                                Pc[h][ct] = mfma16x16x32(Ac[h][jj], B[q * SPG + jj][ct], jj == 0 ? I[p & 1][h] : Pc[h][ct]);
                     if (p > pa) fma_pair(p - 1, P[(p - 1) & 1]);
                 }
                 fma_pair(pe - 1, P[(pe - 1) & 1]);
@@ -465,6 +469,7 @@ __global__ __launch_bounds__(64 * WR * WC) void w4a16_wide_kernel(
             else wait_vmcnt<0>();
             lds_barrier();  // every wave's slot st and x of slot st+1 are in; slot st+2 is free
             const int st1 = st == 2 ? 0 : st + 1, st2 = st1 == 2 ? 0 : st1 + 1;
+            prep(st);
             compute(st, std::integral_constant<int, 0>{});
             if (i + 2 < n) issue(sg, st2, s0 + i + 2);
             if (i + 1 < n) sums(st1);

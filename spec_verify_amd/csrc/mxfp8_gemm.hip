@@ -201,7 +201,7 @@ __global__ __launch_bounds__(64 * WR * WC) void mxfp8_wide_kernel(
     constexpr int TPR = 16 / UPT;
     constexpr int NV = MBW * CT;
     __shared__ __attribute__((aligned(16))) uint16_t xs[2][BM][XROW];
-    __shared__ int s_last;
+    __shared__ int s_sk[3];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wr = wave / WC, wc = wave % WC;
@@ -294,22 +294,24 @@ __global__ __launch_bounds__(64 * WR * WC) void mxfp8_wide_kernel(
         }
 
         const int rowb = row0 + wr * MBW * 16 + 4 * g;
-        auto store_out = [&]() {
+        // accumulator v = (row block v / CT, column tile v % CT) of this thread
+        auto store_v = [&](int v, const f32x4 &val) {
+            const int rb = v / CT, ct = v % CT;
+            const int nbg = cb * (BN / 16) + wc * CT + ct;
+            if (nbg >= NB16) return;
+            const int colg = nbg * 16 + r;
 #pragma unroll
-            for (int ct = 0; ct < CT; ++ct) {
-                if (!ctv[ct]) continue;
-                const int colg = (cb * (BN / 16) + wc * CT + ct) * 16 + r;
-#pragma unroll
-                for (int rb = 0; rb < MBW; ++rb)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int row = rowb + rb * 16 + i;
-                        if (row < M) out[(size_t)row * N + colg] = f32_to_bf16_rne(acc[rb * CT + ct][i]);
-                    }
+            for (int i = 0; i < 4; ++i) {
+                const int row = rowb + rb * 16 + i;
+                if (row < M) out[(size_t)row * N + colg] = f32_to_bf16_rne(val[i]);
             }
         };
-        if ((s0 == 0 && s1 == KT) || sk_fixup<NV, NT>(acc, tile, KT, units, grid, maxt, cnt, part, &s_last))
-            store_out();
+        if (s0 == 0 && s1 == KT) {
+#pragma unroll
+            for (int v = 0; v < NV; ++v) store_v(v, acc[v]);
+        } else {
+            sk_reduce<NV, NT>(acc, tile, KT, units, grid, maxt, cnt, part, s_sk, store_v);
+        }
         u += s1 - s0;
     }
 }

@@ -254,7 +254,7 @@ int svq_w4a16_gemm_with(int kernel, const void *x, const int32_t *wt, const void
     if (k == SVQ_KERNEL_MFMA_WIDE) {
         wplan = plan_w4a16_wide(M, N, K, cus);
         need = wplan.workspace_bytes;
-        if (need && (size_t)wplan.row_tiles * wplan.col_tiles > kMaxCounters) return SVQ_ERR_UNSUPPORTED;
+        if (need && (size_t)wplan.row_tiles * wplan.col_tiles * kSkCountersPerTile > kMaxCounters) return SVQ_ERR_UNSUPPORTED;
         // the kernel addresses x (padded to whole row tiles), the weights and
         // the scales with 32-bit buffer offsets
         if ((uint64_t)wplan.row_tiles * wplan.bm * K * 2 >= (1ull << 32) || (uint64_t)N * K / 2 >= (1ull << 32))
@@ -316,7 +316,7 @@ int svq_mxfp8_gemm_with(int kernel, const void *x, const uint8_t *w, const uint8
     if (k == SVQ_KERNEL_MFMA_WIDE) {
         wplan = plan_mxfp8_wide(M, N, K, cus);
         need = wplan.workspace_bytes;
-        if (need && (size_t)wplan.row_tiles * wplan.col_tiles > kMaxCounters) return SVQ_ERR_UNSUPPORTED;
+        if (need && (size_t)wplan.row_tiles * wplan.col_tiles * kSkCountersPerTile > kMaxCounters) return SVQ_ERR_UNSUPPORTED;
     } else {
         splan = plan_smallm(M, N, K, cus);
         need = splan.workspace_bytes;

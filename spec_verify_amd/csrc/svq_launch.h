@@ -95,6 +95,8 @@ hipError_t launch_mxfp8_skinny(const SmallPlan &plan, const void *x, const uint8
 // callers reuse one workspace.
 constexpr size_t kCounterBytes = 256 * 1024;
 constexpr size_t kMaxCounters = kCounterBytes / 4;
+// counters a stream-K tile shared by several workgroups uses (wide kernels)
+constexpr size_t kSkCountersPerTile = 3;
 inline uint32_t *ws_counters(void *ws) { return (uint32_t *)ws; }
 inline void *ws_partials(void *ws) { return ws ? (void *)((char *)ws + kCounterBytes) : nullptr; }
 hipError_t launch_mxfp8_wide(const WidePlan &plan, const void *x, const uint8_t *w,

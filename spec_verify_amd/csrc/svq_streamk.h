@@ -12,6 +12,7 @@
 #pragma once
 
 #include "svq_device.h"
+#include "svq_launch.h"
 
 namespace svq {
 
@@ -39,64 +40,128 @@ __device__ __forceinline__ int sk_first_tile(int w, int64_t units, int grid, int
     return (int)(((int64_t)w * units / grid) / KT);
 }
 
-// Returns true in every thread of the workgroup that must write the tile's
-// output; `acc` then holds the full sum. NV f32x4 accumulators per thread, NT
-// threads; `part` slots are laid out [workgroup][slot][NV][NT] (f32x4).
-template <int NV, int NT>
-__device__ __forceinline__ bool sk_fixup(f32x4 (&acc)[NV], int tile, int KT, int64_t units,
-                                         int grid, int maxt, uint32_t *cnt, f32x4 *part,
-                                         int *s_flag) {
+// Finish of a tile shared by several workgroups. Counters of tile t (at
+// cnt[3t..3t+2]): arrivals, a bit mask of reduced chunk ranges, departures.
+//
+// Every contributor stores its partial tile (NV f32x4 per thread, NT threads;
+// slots laid out [workgroup][slot][NV][NT]) and arrives. The tile is reduced
+// per accumulator index v (all contributors added in workgroup order, so the
+// result does not depend on which workgroup reduces it). The contributors for
+// which this tile is the last piece of work (the "finishing group", known
+// from the schedule) split the NV indices into ranges, one each: a member
+// waits, for a bounded time, until every partial is in, reduces its range and
+// sets its bit. The last arriver reduces its own range if it has one, waits
+// (bounded) for the other bits, and reduces every range whose bit is still
+// missing, so the tile is complete whether or not the members were resident
+// at the same time; a range reduced twice is written twice with the same
+// values. The last contributor to depart clears the three counters.
+constexpr uint64_t kSkArriveWaitTicks = 2000;  // s_memrealtime runs at 100 MHz: 20 us
+constexpr uint64_t kSkRangeWaitTicks = 1000;   // 10 us
+constexpr int kSkMaxRanges = 32;               // one bit each
+
+// Spin (thread 0) until (*p & mask) == mask, or at least `want` for mask 0,
+// for at most `ticks`; returns whether it happened.
+__device__ __forceinline__ bool sk_wait(uint32_t *p, uint32_t want, uint32_t mask, uint64_t ticks) {
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    for (;;) {
+        const uint32_t v = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (mask ? (v & mask) == mask : v >= want) return true;
+        if (__builtin_amdgcn_s_memrealtime() - t0 > ticks) return false;
+        __builtin_amdgcn_s_sleep(2);
+    }
+}
+
+template <int NV, int NT, typename StoreV>
+__device__ __forceinline__ void sk_reduce(const f32x4 (&acc)[NV], int tile, int KT, int64_t units,
+                                          int grid, int maxt, uint32_t *cnt, f32x4 *part,
+                                          int *s_sk, StoreV store_v) {
     const int tid = threadIdx.x;
     const int wg = blockIdx.x;
+    uint32_t *c = cnt + kSkCountersPerTile * tile;
     const uint32_t slot_bytes = (uint32_t)NV * NT * 16;
     const int slot = tile - sk_first_tile(wg, units, grid, KT);
     const __amdgpu_buffer_rsrc_t mine = make_rsrc(part + (size_t)(wg * maxt + slot) * NV * NT, slot_bytes);
 #pragma unroll
     for (int v = 0; v < NV; ++v)
         __builtin_amdgcn_raw_buffer_store_b128(acc[v], mine, (uint32_t)(v * NT + tid) * 16, 0, kCoherent);
-    const int fw = sk_owner((int64_t)tile * KT, units, grid);
-    const int lw = sk_owner((int64_t)tile * KT + KT - 1, units, grid);
+    const int64_t tend = (int64_t)tile * KT + KT;  // one past the tile's last unit
+    const int fw = __builtin_amdgcn_readfirstlane(sk_owner((int64_t)tile * KT, units, grid));
+    const int lw = __builtin_amdgcn_readfirstlane(sk_owner(tend - 1, units, grid));
+    const uint32_t nc = (uint32_t)(lw - fw + 1);
+    // finishing group: fw..lw-1 (their ranges end inside the tile) and lw if
+    // its range ends with the tile
+    const int nf0 = lw - fw + ((int64_t)(lw + 1) * units / grid <= tend ? 1 : 0);
+    const int nf = nf0 < kSkMaxRanges ? nf0 : kSkMaxRanges;
+    const int me = wg - fw;  // my range, if me < nf (the ranges cover all NV indices)
+    const uint32_t all = nf == 32 ? 0xffffffffu : ((1u << nf) - 1u);
     wait_all_memory();
     __syncthreads();
-    if (tid == 0) *s_flag = (arrive(&cnt[tile]) == (uint32_t)(lw - fw));
+    if (tid == 0) s_sk[0] = (int)arrive(&c[0]);
     __syncthreads();
-    // read as a wave-uniform value: the code below is then uniform control
-    // flow with scalar buffer descriptors
-    if (__builtin_amdgcn_readfirstlane(*s_flag) == 0) return false;
-    // every contributor, this one included, stored its partial above: add
-    // them all from memory in workgroup order, so that `acc` need not stay
-    // live next to the running sum
-#pragma unroll
-    for (int v = 0; v < NV; ++v) acc[v] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const int fwu = __builtin_amdgcn_readfirstlane(fw), lwu = __builtin_amdgcn_readfirstlane(lw);
-    // uniform by construction; readfirstlane lets the compiler keep the buffer
-    // descriptors in scalar registers
+    const bool owner = (uint32_t)__builtin_amdgcn_readfirstlane(s_sk[0]) == nc - 1;
+
     auto view = [&](int w) {
         const int wslot = __builtin_amdgcn_readfirstlane(tile - sk_first_tile(w, units, grid, KT));
         return make_rsrc(part + (size_t)(w * maxt + wslot) * NV * NT, slot_bytes);
     };
-    // two contributors' loads in flight at a time (each load is a round trip
-    // to the device-coherent level), added in workgroup order
-    for (int w = fwu; w <= lwu; w += 2) {
-        f32x4 a[NV], b[NV];
-        const __amdgpu_buffer_rsrc_t ra = view(w);
+    // reduce accumulator indices [v0, v1), two at a time with eight
+    // contributors' loads each in flight (every load is a round trip to the
+    // device-coherent level)
+    auto reduce = [&](int v0, int v1) {
+        for (int v = v0; v < v1; v += 2) {
+            const bool two = v + 1 < v1;
+            f32x4 sa = f32x4{0.f, 0.f, 0.f, 0.f}, sb = sa;
+            for (int w0 = fw; w0 <= lw; w0 += 8) {
+                f32x4 a[8], b[8];
 #pragma unroll
-        for (int v = 0; v < NV; ++v) a[v] = __builtin_amdgcn_raw_buffer_load_b128(ra, (uint32_t)(v * NT + tid) * 16, 0, kCoherent);
-        const bool two = w + 1 <= lwu;
-        if (two) {
-            const __amdgpu_buffer_rsrc_t rb = view(w + 1);
+                for (int k = 0; k < 8; ++k) {
+                    if (w0 + k > lw) continue;
+                    const __amdgpu_buffer_rsrc_t rs = view(w0 + k);
+                    a[k] = __builtin_amdgcn_raw_buffer_load_b128(rs, (uint32_t)(v * NT + tid) * 16, 0, kCoherent);
+                    if (two) b[k] = __builtin_amdgcn_raw_buffer_load_b128(rs, (uint32_t)((v + 1) * NT + tid) * 16, 0, kCoherent);
+                }
 #pragma unroll
-            for (int v = 0; v < NV; ++v) b[v] = __builtin_amdgcn_raw_buffer_load_b128(rb, (uint32_t)(v * NT + tid) * 16, 0, kCoherent);
+                for (int k = 0; k < 8; ++k) {
+                    if (w0 + k > lw) continue;
+                    sa += a[k];
+                    if (two) sb += b[k];
+                }
+            }
+            store_v(v, sa);
+            if (two) store_v(v + 1, sb);
         }
-#pragma unroll
-        for (int v = 0; v < NV; ++v) acc[v] += a[v];
-        if (two) {
-#pragma unroll
-            for (int v = 0; v < NV; ++v) acc[v] += b[v];
-        }
+    };
+    auto range_lo = [&](int e) { return e * NV / nf; };
+
+    bool mine_ready = owner;
+    if (!owner && me < nf) {
+        if (tid == 0) s_sk[1] = sk_wait(&c[0], nc, 0u, kSkArriveWaitTicks) ? 1 : 0;
+        __syncthreads();
+        mine_ready = __builtin_amdgcn_readfirstlane(s_sk[1]) != 0;
     }
-    if (tid == 0) clear_counter(&cnt[tile]);
-    return true;
+    if (mine_ready && me < nf) {
+        reduce(range_lo(me), range_lo(me + 1));
+        __syncthreads();
+        if (tid == 0) __hip_atomic_fetch_or(&c[1], 1u << me, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (owner) {
+        // the other members' ranges: wait a bounded time for their bits, then
+        // reduce whatever is still missing
+        if (tid == 0) {
+            sk_wait(&c[1], 0u, all, kSkRangeWaitTicks);
+            s_sk[2] = (int)__hip_atomic_load(&c[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __syncthreads();
+        const uint32_t done = (uint32_t)__builtin_amdgcn_readfirstlane(s_sk[2]);
+        for (int e = 0; e < nf; ++e)
+            if (!((done >> e) & 1u)) reduce(range_lo(e), range_lo(e + 1));
+    }
+    __syncthreads();
+    if (tid == 0 && arrive(&c[2]) == nc - 1) {
+        clear_counter(&c[0]);
+        clear_counter(&c[1]);
+        clear_counter(&c[2]);
+    }
 }
 
 

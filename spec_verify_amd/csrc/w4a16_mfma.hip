@@ -270,7 +270,7 @@ __global__ __launch_bounds__(64 * WR * WC) void w4a16_wide_kernel(
     using C = WideCfg<MBW, WR, WC, CT, GSHIFT>;
     constexpr int BM = C::BM, BN = C::BN, NG = C::NG, SPG = C::SPG, NV = C::NV;
     __shared__ __attribute__((aligned(16))) uint8_t ring[3 * C::SLOT];
-    __shared__ int s_last;
+    __shared__ int s_sk[3];
 
     const int lane = threadIdx.x & 63;
     const int wave = wave_id();
@@ -486,32 +486,28 @@ __global__ __launch_bounds__(64 * WR * WC) void w4a16_wide_kernel(
         issued = true;
 
         // ---- epilogue ----
-        auto store_out = [&]() {
-            // a row tile inside M needs no per-element row check
-            const bool full = rt * BM + BM <= M;
+        // accumulator v = (row block v / CT, column tile v % CT) of this thread
+        auto store_v = [&](int v, const f32x4 &val) {
+            const int rb = v / CT, ct = v % CT;
+            const int nbg = cb * (BN / 16) + wc * CT + ct;
+            if (nbg >= NB16) return;
+            const int row0 = rt * BM + (wr * MBW + rb) * 16 + 4 * g;
+            uint16_t *o = out + (size_t)row0 * N + nbg * 16 + r;
+            if (row0 + 4 <= M) {
 #pragma unroll
-            for (int ct = 0; ct < CT; ++ct) {
-                const int nbg = cb * (BN / 16) + wc * CT + ct;
-                if (nbg >= NB16) continue;
-                uint16_t *o = out + (size_t)(rt * BM + wr * MBW * 16 + 4 * g) * N + nbg * 16 + r;
-                if (full) {
+                for (int i = 0; i < 4; ++i) o[(size_t)i * N] = f32_to_bf16_rne(val[i]);
+            } else {
 #pragma unroll
-                    for (int rb = 0; rb < MBW; ++rb)
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) o[(size_t)(rb * 16 + i) * N] = f32_to_bf16_rne(acc[rb * CT + ct][i]);
-                } else {
-#pragma unroll
-                    for (int rb = 0; rb < MBW; ++rb)
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            const int row = rt * BM + (wr * MBW + rb) * 16 + 4 * g + i;
-                            if (row < M) o[(size_t)(rb * 16 + i) * N] = f32_to_bf16_rne(acc[rb * CT + ct][i]);
-                        }
-                }
+                for (int i = 0; i < 4; ++i)
+                    if (row0 + i < M) o[(size_t)i * N] = f32_to_bf16_rne(val[i]);
             }
         };
-        if ((s0 == 0 && s1 == KT) || sk_fixup<NV, C::NT>(acc, tile, KT, units, grid, maxt, cnt, part, &s_last))
-            store_out();
+        if (s0 == 0 && s1 == KT) {
+#pragma unroll
+            for (int v = 0; v < NV; ++v) store_v(v, acc[v]);
+        } else {
+            sk_reduce<NV, C::NT>(acc, tile, KT, units, grid, maxt, cnt, part, s_sk, store_v);
+        }
         u += n;
     }
 }

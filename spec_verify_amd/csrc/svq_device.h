@@ -133,6 +133,10 @@ __device__ __forceinline__ void wait_vmcnt_at_most(int n) {
     }
 }
 
+// Barrier after this wave's LDS accesses have completed; unlike
+// __syncthreads() it does not also wait for the vector memory loads in flight.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // One 16-byte-per-lane LDS-DMA load: lane l's 16 bytes from gptr land at
 // lds_base + 16*l (lds_base wave-uniform); inactive lanes write nothing.
 __device__ __forceinline__ void dma16(const void *gptr, void *lds_base) {

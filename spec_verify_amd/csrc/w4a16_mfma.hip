@@ -240,9 +240,6 @@ __device__ __forceinline__ void dma_b32(const BufDesc &d, uint32_t lds, uint32_t
                  : "v"(voff), "s"(d.v), "s"(lds), "s"(soff)
                  : "memory", "m0");
 }
-// Barrier after this wave's LDS writes have completed; unlike __syncthreads()
-// it does not also wait for the DMAs in flight.
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() { __builtin_amdgcn_s_waitcnt(vmcnt_imm(N)); }
 

@@ -99,6 +99,9 @@ W4_CASES = (
     + [(2, m, K, N, G) for m in (1, 3, 5, 11, 16) for (K, N) in ((512, 48), (1280, 32)) for G in (32, 64, 128)]
     + [(3, m, K, N, G) for m in (1, 17, 64, 65, 128, 130) for (K, N) in ((1024, 272), (2560, 128)) for G in (32, 128)]
     + [(3, 33, 640, 16, 64)]
+    # dot2 with more column blocks than compute units (456, 336 and 576 blocks)
+    + [(1, m, K, N, G) for (m, K, N, G) in ((1, 1280, 7296, 128), (3, 1280, 7296, 32), (2, 1280, 5376, 128),
+                                            (8, 640, 5376, 64), (5, 1280, 9216, 128), (1, 1280, 9216, 32))]
 )
 
 
@@ -245,8 +248,24 @@ def test_wide_deterministic_and_counters_cleared():
     b = svq.w4a16_gemm(x, tiled, s, 272, workspace=ws)
     torch.cuda.synchronize()
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
-    tiles = 1 * 3                              # 128-row x 128-column tiles
-    assert int(ws[: 4 * tiles].count_nonzero()) == 0
+    assert int(ws[: 256 * 1024].count_nonzero()) == 0   # the arrival counters
+
+
+def test_dot2_deterministic_and_counters_cleared():
+    import spec_verify_amd as svq
+    M, K, N = 3, 1280, 5376                    # 336 column blocks
+    inp = synth.gen_w4a16(6, M, K, N)
+    x, qw, s = dev(inp.x), dev(inp.qweight), dev(inp.scales)
+    tiled = svq.q4_repack(qw)
+    nbytes = svq.w4a16_workspace_bytes(M, N, K, 128, 1)
+    ws = torch.zeros(max(nbytes, 256 * 1024), dtype=torch.uint8, device="cuda")
+    a = svq.w4a16_gemm(x, tiled, s, N, kernel=1, workspace=ws)
+    b = svq.w4a16_gemm(x, tiled, s, N, kernel=1, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    assert int(ws[: 256 * 1024].count_nonzero()) == 0
+    y64, y32 = oracle.w4a16(inp.x, inp.qweight, inp.scales, 128)
+    assert_gate(host_bits(a), y64, y32, "dot2 repeated")
 
 
 def test_output_canaries_and_error_path_leave_memory_untouched():

@@ -162,9 +162,9 @@ __global__ __launch_bounds__(64 * WAVES) void w4a16_skinny_kernel(
 // ---------------------------------------------------------------------------
 // Wide kernel: any M (built for M = 128). Persistent stream-K: one workgroup
 // per compute unit, each taking an equal contiguous share of the (output tile,
-// 128-row K step) units. A tile computed by several workgroups is finished by
-// the last to arrive, which adds the fp32 partials in workgroup order (fixed
-// order: deterministic) and clears the tile's arrival counter.
+// 128-row K step) units. A tile computed by several workgroups is reduced by
+// the ones that finish it together (sk_reduce): fp32 partials added in
+// workgroup order, so the result is deterministic.
 //
 // Workgroup: WR x WC waves (two per SIMD, so one wave's MFMAs cover the other's
 // VALU work), output tile BM x BN; a wave owns MBW 16-row blocks x CT 16-column

@@ -7,9 +7,12 @@ product package. The arithmetic lives in ``oracle.c`` (plain C, built with gcc,
 OpenMP over output columns); every function there writes out the plain
 definition of the quantized matmul with k ascending.
 
+The load-time round-to-nearest quantizer of the vocabulary head
+(``rtn_quantize``) is written here in numpy, in fp32 arithmetic step by step.
+
 Functions with no pin (see tests/test_oracle_pins.py): none -- every exported
-computation is checked against closed forms, brute force, library routines or
-the pages' stated format rules. The conventions themselves (zero point 8, nibble
+computation is checked against closed forms, brute force, library routines,
+hand-worked values or the pages' stated format rules. The conventions themselves (zero point 8, nibble
 order, scale layout) are readings of the pages and are not pinned against a real
 checkpoint, of which there is none here.
 """
@@ -61,6 +64,10 @@ def _load():
     lib.oracle_mxfp8.argtypes = [_p, _p, _p, _i64, _i64, _i64, _p, _p]
     lib.oracle_mxfp8_points.restype = _int
     lib.oracle_mxfp8_points.argtypes = [_p, _p, _p, _i64, _i64, _i64, _p, _p, _i64, _p, _p]
+    lib.oracle_w8a16.restype = _int
+    lib.oracle_w8a16.argtypes = [_p, _p, _p, _i64, _i64, _i64, _int, _p, _p]
+    lib.oracle_w8a16_points.restype = _int
+    lib.oracle_w8a16_points.argtypes = [_p, _p, _p, _i64, _i64, _i64, _int, _p, _p, _i64, _p, _p]
     lib.oracle_q4_repack.restype = _int
     lib.oracle_q4_repack.argtypes = [_p, _p, _i64, _i64]
     lib.oracle_q4_unrepack.restype = _int
@@ -206,6 +213,84 @@ def mxfp8_points(x, w, scales, rows, cols):
     if rc:
         raise ValueError("oracle_mxfp8_points rejected its arguments")
     return y64, y32
+
+
+# ---- W8A16 (quantized vocabulary head) ---------------------------------------
+
+def w8a16(x: np.ndarray, w: np.ndarray, scales: np.ndarray, group_size: int = 128):
+    """(y64, y32) for bf16 x [M,K], int8 codes [N,K], fp16 scales [K/G,N]."""
+    x = _c(x, np.uint16)
+    w = _c(w, np.int8)
+    scales = _c(scales, np.uint16)
+    M, K = x.shape
+    N = w.shape[0]
+    if w.shape != (N, K) or scales.shape != (K // group_size, N):
+        raise ValueError("shape mismatch")
+    y64 = np.empty((M, N), dtype=np.float64)
+    y32 = np.empty((M, N), dtype=np.float32)
+    rc = _load().oracle_w8a16(_ptr(x), _ptr(w), _ptr(scales), M, N, K, group_size,
+                              _ptr(y64), _ptr(y32))
+    if rc:
+        raise ValueError("oracle_w8a16 rejected its arguments")
+    return y64, y32
+
+
+def w8a16_points(x, w, scales, group_size, rows, cols):
+    x = _c(x, np.uint16)
+    w = _c(w, np.int8)
+    scales = _c(scales, np.uint16)
+    rows = _c(np.asarray(rows, dtype=np.int64), np.int64)
+    cols = _c(np.asarray(cols, dtype=np.int64), np.int64)
+    M, K = x.shape
+    N = w.shape[0]
+    if w.shape != (N, K) or scales.shape != (K // group_size, N) or rows.shape != cols.shape:
+        raise ValueError("shape mismatch")
+    y64 = np.empty(rows.shape, dtype=np.float64)
+    y32 = np.empty(rows.shape, dtype=np.float32)
+    rc = _load().oracle_w8a16_points(_ptr(x), _ptr(w), _ptr(scales), M, N, K, group_size,
+                                     _ptr(rows), _ptr(cols), rows.size, _ptr(y64), _ptr(y32))
+    if rc:
+        raise ValueError("oracle_w8a16_points rejected its arguments")
+    return y64, y32
+
+
+def rtn_quantize(w_bits: np.ndarray, bits: int, group_size: int):
+    """Load-time symmetric group-wise round-to-nearest of a dense bf16 weight [N, K].
+
+    Eole recipe "Qwen3.8-27B and native MTP speculative decoding", section
+    "Optional vocabulary-head quantization" (int8 or int4, groups of 32/64/128
+    along K, symmetric, round to nearest). Per group (n, g), in fp32:
+        amax = max |w|,  s = fp16(amax / qmax)  with qmax = 2^(bits-1) - 1,
+        q = clamp(rint(w / s), -qmax - 1, qmax)      (rint: nearest, ties to even)
+    where s is used as stored (fp16 -> fp32) and a group with s == 0 gets q = 0.
+    Returns (codes, scales): int8 codes [N, K] for bits = 8, GPTQ words
+    [K/8, N] holding q + 8 for bits = 4; fp16 scale bits [K/G, N].
+    """
+    w_bits = _c(w_bits, np.uint16)
+    if bits not in (4, 8):
+        raise ValueError("bits must be 4 or 8")
+    N, K = w_bits.shape
+    G = group_size
+    if K % G:
+        raise ValueError("K must be a multiple of the group size")
+    W = (w_bits.astype(np.uint32) << 16).view(np.float32)       # bf16 -> fp32, exact
+    Wg = W.reshape(N, K // G, G)
+    qmax = np.float32(2 ** (bits - 1) - 1)
+    amax = np.abs(Wg).max(axis=2)                                 # exact
+    s16 = (amax / qmax).astype(np.float32).astype(np.float16)    # fp32 division, then RNE
+    s = s16.astype(np.float32)
+    safe = np.where(s > 0, s, np.float32(1.0))
+    qf = (Wg / safe[:, :, None]).astype(np.float32)               # fp32 division
+    q = np.clip(np.rint(qf), -qmax - 1, qmax)
+    q = np.where((s > 0)[:, :, None], q, 0).astype(np.int32).reshape(N, K)
+    scales = np.ascontiguousarray(s16.T).view(np.uint16)
+    if bits == 8:
+        return q.astype(np.int8), scales
+    u = (q + 8).T.astype(np.uint32).reshape(K // 8, 8, N)           # [K, N] codes 0..15
+    words = np.zeros((K // 8, N), dtype=np.uint32)
+    for i in range(8):
+        words |= u[:, i, :] << np.uint32(4 * i)
+    return words.view(np.int32), scales
 
 
 # ---- device layout of packed INT4 weights ------------------------------------

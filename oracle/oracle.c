@@ -150,7 +150,9 @@ static void dot_column(const uint16_t *x, int64_t m, int64_t K, const double *wc
     for (int64_t k = 0; k < K; ++k) {
         double a = oracle_bf16_to_f64(xr[k]);
         acc += a * wcol[k];
-        float p = (float)a * (float)wcol[k]; /* exact: 8 x 14 significant bits */
+        /* exact for W4A16 (8 x 14 significant bits) and MXFP8; rounded to
+           fp32 for W8A16, whose weights carry up to 19 */
+        float p = (float)a * (float)wcol[k];
         acc32 = acc32 + p;
     }
     *y64 = acc;
@@ -267,6 +269,77 @@ int oracle_mxfp8_points(const uint16_t *x, const uint8_t *w, const uint8_t *scal
                     continue;
                 }
                 mxfp8_column(w, scales, K, cols[i], wcol);
+                dot_column(x, rows[i], K, wcol, &y64[i], &y32[i]);
+            }
+            free(wcol);
+        }
+    }
+    return bad ? -1 : 0;
+}
+
+/* ---- W8A16 (quantized vocabulary head) ------------------------------------- */
+/*
+ * Eole recipe "Qwen3.8-27B and native MTP speculative decoding", section
+ * "Optional vocabulary-head quantization": the dense vocabulary projection is
+ * quantized at load time to int8 (or int4) by symmetric group-wise
+ * round-to-nearest, groups of 32, 64 or 128 along K. Stored for the GPU path as
+ * int8 two's-complement codes [N][K] row-major and fp16 scales [K/G][N]:
+ *     w[n][k] = q[n][k] * fp16(scales[k/G][n])      (exact: 8 + 11 significant bits)
+ *     y[m][n] = sum_k bf16(x[m][k]) * w[n][k]
+ * y64 is exact up to the fp64 running sum; y32 also rounds each product to fp32
+ * (a product can carry 8 + 19 significant bits).
+ */
+static void w8a16_column(const int8_t *w, const uint16_t *scales, int64_t N, int64_t K,
+                         int G, int64_t n, double *wcol) {
+    for (int64_t k = 0; k < K; ++k)
+        wcol[k] = (double)w[n * K + k] * oracle_fp16_to_f64(scales[(k / G) * N + n]);
+}
+
+int oracle_w8a16(const uint16_t *x, const int8_t *w, const uint16_t *scales, int64_t M,
+                 int64_t N, int64_t K, int G, double *y64, float *y32) {
+    if (M < 0 || N < 0 || K < 0 || G <= 0 || K % G)
+        return -1;
+    int bad = 0;
+#pragma omp parallel
+    {
+        double *wcol = (double *)malloc(sizeof(double) * (size_t)(K > 0 ? K : 1));
+        if (!wcol) {
+#pragma omp atomic write
+            bad = 1;
+        } else {
+#pragma omp for schedule(static)
+            for (int64_t n = 0; n < N; ++n) {
+                w8a16_column(w, scales, N, K, G, n, wcol);
+                for (int64_t m = 0; m < M; ++m)
+                    dot_column(x, m, K, wcol, &y64[m * N + n], &y32[m * N + n]);
+            }
+            free(wcol);
+        }
+    }
+    return bad ? -1 : 0;
+}
+
+int oracle_w8a16_points(const uint16_t *x, const int8_t *w, const uint16_t *scales,
+                        int64_t M, int64_t N, int64_t K, int G, const int64_t *rows,
+                        const int64_t *cols, int64_t npts, double *y64, float *y32) {
+    if (M < 0 || N < 0 || K < 0 || G <= 0 || K % G)
+        return -1;
+    int bad = 0;
+#pragma omp parallel
+    {
+        double *wcol = (double *)malloc(sizeof(double) * (size_t)(K > 0 ? K : 1));
+        if (!wcol) {
+#pragma omp atomic write
+            bad = 1;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t i = 0; i < npts; ++i) {
+                if (rows[i] < 0 || rows[i] >= M || cols[i] < 0 || cols[i] >= N) {
+#pragma omp atomic write
+                    bad = 1;
+                    continue;
+                }
+                w8a16_column(w, scales, N, K, G, cols[i], wcol);
                 dot_column(x, rows[i], K, wcol, &y64[i], &y32[i]);
             }
             free(wcol);

@@ -20,6 +20,12 @@ Formats produced (readings of the pages):
   without calibration. Elements are E4M3FN, blocks run along K within a row n,
   weights are stored [N, K] and scales [N, K/32].
 
+* W8A16, the quantized vocabulary head -- Eole recipe "Qwen3.8-27B and native
+  MTP speculative decoding", section "Optional vocabulary-head quantization"
+  (int8, symmetric group-wise round to nearest, groups along K): int8 codes
+  stored [N, K], fp16 scales [K/G, N]. Dense bf16 weights [N, K] feed the
+  load-time quantizer.
+
 Value distributions: x ~ N(0, 1) rounded to bf16; q uniform on [0, 15]; scales
 uniform on [0.002, 0.02] rounded to fp16; MXFP8 weights come from an N(0, 1)
 matrix. Draw order from one ``numpy.random.default_rng(seed)``: x, then q (or the
@@ -34,7 +40,8 @@ import numpy as np
 
 __all__ = [
     "bf16_bits", "fp16_bits", "pack_gptq", "e4m3_encode_rne", "mxfp8_quantize_rtn",
-    "gen_w4a16", "gen_mxfp8", "W4A16Inputs", "MXFP8Inputs", "WORKLOADS", "sha256",
+    "gen_w4a16", "gen_mxfp8", "gen_w8a16", "gen_dense_bf16", "W4A16Inputs", "MXFP8Inputs",
+    "W8A16Inputs", "WORKLOADS", "sha256",
 ]
 
 
@@ -138,6 +145,20 @@ class W4A16Inputs:
 
 
 @dataclass
+class W8A16Inputs:
+    M: int
+    K: int
+    N: int
+    G: int
+    x: np.ndarray       # uint16 bf16 bits [M, K]
+    w: np.ndarray       # int8 codes [N, K]
+    scales: np.ndarray  # uint16 fp16 bits [K/G, N]
+
+    def digest(self) -> str:
+        return sha256(self.x, self.w, self.scales)
+
+
+@dataclass
 class MXFP8Inputs:
     M: int
     K: int
@@ -197,6 +218,31 @@ def gen_mxfp8(seed: int, M: int, K: int, N: int, kind: str = "random") -> MXFP8I
     return MXFP8Inputs(M, K, N, x, w, sc)
 
 
+def gen_w8a16(seed: int, M: int, K: int, N: int, G: int = 128, kind: str = "random") -> W8A16Inputs:
+    """Seeded W8A16 inputs.
+
+    kind="random":   x ~ N(0,1) in bf16, q ~ U{-128..127}, s ~ U[2e-4, 2e-3] in fp16
+                     (the scale range of int8 round-to-nearest of N(0, 0.02) weights).
+    kind="intexact": x ~ U{-4..4}, s = 1.0: integer partial sums below 2^24.
+    """
+    if K % G:
+        raise ValueError("K must be a multiple of G")
+    rng = np.random.default_rng(seed)
+    x = _x(rng, M, K, kind)
+    w = rng.integers(-128, 128, size=(N, K), dtype=np.int8)
+    if kind == "intexact":
+        s = fp16_bits(np.ones((K // G, N), dtype=np.float32))
+    else:
+        s = fp16_bits(rng.uniform(2e-4, 2e-3, size=(K // G, N)).astype(np.float32))
+    return W8A16Inputs(M, K, N, G, x, w, s)
+
+
+def gen_dense_bf16(seed: int, N: int, K: int, std: float = 0.02) -> np.ndarray:
+    """Seeded dense weights [N, K] ~ N(0, std^2) as bf16 bits (input of the quantizer)."""
+    rng = np.random.default_rng(seed)
+    return bf16_bits(rng.standard_normal((N, K), dtype=np.float32) * np.float32(std))
+
+
 # Named workloads: single-stream decode (M=1), MTP verify chunks (M = 1 + drafts),
 # and batched verify (32 streams x (1 + 3) tokens). K = 5120 is the hidden size in
 # the GPTQ card's "Model facts"; 17408 is a synthetic MLP width.
@@ -214,6 +260,9 @@ WORKLOADS = {
     "mxfp8_m1":      dict(op="mxfp8", M=1,   K=5120,  N=5120,  seed=501),
     "mxfp8_m5":      dict(op="mxfp8", M=5,   K=5120,  N=5120,  seed=502),
     "mxfp8_m128":    dict(op="mxfp8", M=128, K=5120,  N=5120,  seed=503),
+    # quantized vocabulary head: N = 248320 (about 248k entries, a multiple of 256)
+    "vocab_w8_m1":   dict(op="w8a16", M=1,   K=5120,  N=248320, seed=601),
+    "vocab_w4_m1":   dict(op="w4a16", M=1,   K=5120,  N=248320, seed=602),
 }
 
 
@@ -221,4 +270,6 @@ def gen_workload(name: str, kind: str = "random"):
     w = WORKLOADS[name]
     if w["op"] == "w4a16":
         return gen_w4a16(w["seed"], w["M"], w["K"], w["N"], 128, kind)
+    if w["op"] == "w8a16":
+        return gen_w8a16(w["seed"], w["M"], w["K"], w["N"], 128, kind)
     return gen_mxfp8(w["seed"], w["M"], w["K"], w["N"], kind)

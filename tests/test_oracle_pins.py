@@ -343,3 +343,128 @@ def test_gate_accepts_rounding_and_rejects_a_wrong_weight():
     assert ok and err <= 2 ** -8 * np.max(np.abs(y64))
     bad = oracle.bf16_rne((y64 + 0.05 * rms).astype(np.float32))
     assert not oracle.gate(bad, y64)[0]
+
+
+# ---- W8A16 (quantized vocabulary head) and its load-time RTN quantizer --------
+
+def _w8_inputs(seed, M, K, N, G, xlo=-4, xhi=5):
+    rng = np.random.default_rng(seed)
+    x = rng.integers(xlo, xhi, (M, K)).astype(np.float32)
+    w = rng.integers(-128, 128, (N, K)).astype(np.int8)
+    return synth.bf16_bits(x), w, rng
+
+
+@pytest.mark.parametrize("M,K,N,G", [(1, 128, 16, 128), (3, 512, 48, 32), (5, 1024, 32, 64)])
+def test_w8a16_integer_exact_matches_int64_matmul(M, K, N, G):
+    xb, w, _ = _w8_inputs(11 + M, M, K, N, G)
+    scales = np.full((K // G, N), 0x3C00, dtype=np.uint16)       # fp16 1.0
+    y64, y32 = oracle.w8a16(xb, w, scales, G)
+    xi = oracle.bf16_bits_to_f64(xb).astype(np.int64)
+    exact = xi @ w.astype(np.int64).T                                # |y| < 2^24: exact in fp32 too
+    np.testing.assert_array_equal(y64, exact.astype(np.float64))
+    np.testing.assert_array_equal(y32, exact.astype(np.float32))
+
+
+def test_w8a16_against_blas_and_one_hot_group():
+    M, K, N, G = 4, 512, 32, 128
+    rng = np.random.default_rng(5)
+    xb = synth.bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
+    w = rng.integers(-128, 128, (N, K)).astype(np.int8)
+    s16 = rng.uniform(2e-4, 2e-3, (K // G, N)).astype(np.float16)
+    y64, _ = oracle.w8a16(xb, w, s16.view(np.uint16), G)
+    deq = w.astype(np.float64) * np.repeat(s16.astype(np.float64).T, G, axis=1)   # [N, K]
+    ref = oracle.bf16_bits_to_f64(xb) @ deq.T
+    rms = np.sqrt(np.mean(ref ** 2))
+    assert np.max(np.abs(y64 - ref)) <= 1e-12 * rms
+    # only group 2 has a nonzero scale: y = s * sum over that group's K range
+    one = np.zeros((K // G, N), dtype=np.float16)
+    one[2, :] = np.float16(0.5)
+    y1, _ = oracle.w8a16(xb, w, one.view(np.uint16), G)
+    xs = oracle.bf16_bits_to_f64(xb)[:, 2 * G:3 * G]
+    np.testing.assert_allclose(y1, 0.5 * xs @ w[:, 2 * G:3 * G].astype(np.float64).T, rtol=0, atol=1e-12 * rms)
+
+
+def test_rtn_handworked_cases():
+    n = 0
+    for case, bits, G, sbits, vals, shift, codes in _rows("rtn_handworked.txt"):
+        bits, G, shift = int(bits), int(G), int(shift)
+        v = np.array([int(t) for t in vals.split(",")], dtype=np.float64) * 2.0 ** shift
+        want = np.array([int(t) for t in codes.split(",")], dtype=np.int64)
+        wb = synth.bf16_bits(v.astype(np.float32)).reshape(1, -1)
+        assert np.array_equal(oracle.bf16_bits_to_f64(wb).ravel(), v), case   # exact in bf16
+        q, s = oracle.rtn_quantize(wb, bits, G)
+        assert s.shape == (v.size // G, 1) and int(s[0, 0]) == int(sbits, 16), (case, hex(int(s[0, 0])))
+        if bits == 8:
+            np.testing.assert_array_equal(q.ravel().astype(np.int64), want, err_msg=case)
+        else:
+            np.testing.assert_array_equal(oracle.q4_unpack(q)[:, 0].astype(np.int64), want + 8, err_msg=case)
+        n += 1
+    assert n == 5
+
+
+@pytest.mark.parametrize("bits,G", [(8, 128), (8, 32), (4, 128), (4, 64)])
+def test_rtn_error_bound_extremes_and_scaling(bits, G):
+    N, K = 24, 512
+    rng = np.random.default_rng(40 + bits + G)
+    W = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    wb = synth.bf16_bits(W)
+    Wf = oracle.bf16_bits_to_f64(wb)
+    q, s = oracle.rtn_quantize(wb, bits, G)
+    if bits == 4:
+        q = oracle.q4_unpack(q).astype(np.int64).T - 8                 # GPTQ words -> q [N, K]
+    q = q.astype(np.int64)
+    sf = np.repeat(s.view(np.float16).astype(np.float64).T, G, axis=1)  # [N, K]
+    qmax = 2 ** (bits - 1) - 1
+    assert q.min() >= -qmax - 1 and q.max() <= qmax
+    # round to nearest: every weight within half a step of its code
+    assert np.all(np.abs(Wf - q * sf) <= 0.5 * sf * (1 + 2.0 ** -20))
+    # the largest |w| of each group lands on +-qmax (the scale is amax / qmax up to fp16 rounding)
+    Wg, qg = np.abs(Wf).reshape(N, K // G, G), np.abs(q).reshape(N, K // G, G)
+    top = np.take_along_axis(qg, np.argmax(Wg, axis=2)[:, :, None], axis=2)
+    assert np.all(top == qmax)
+    # a power-of-two factor on the weights moves only the scales
+    q2, s2 = oracle.rtn_quantize(synth.bf16_bits(W * np.float32(8.0)), bits, G)
+    if bits == 4:
+        q2 = oracle.q4_unpack(q2).astype(np.int64).T - 8
+    np.testing.assert_array_equal(q2.astype(np.int64), q)
+    np.testing.assert_array_equal(s2.view(np.float16).astype(np.float64), 8.0 * s.view(np.float16).astype(np.float64))
+
+
+def _f32(fr):
+    """Nearest binary32 to a Fraction (ties to even), for normal magnitudes."""
+    if fr == 0:
+        return Fraction(0)
+    sgn = -1 if fr < 0 else 1
+    a = abs(fr)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    ulp = Fraction(2) ** (e - 23)
+    m = a / ulp
+    r = math.floor(m)
+    if m - r > Fraction(1, 2) or (m - r == Fraction(1, 2) and r % 2):
+        r += 1
+    return sgn * r * ulp
+
+
+def test_rtn_int8_bruteforce_rationals():
+    # exact-rational re-derivation on small groups: fp32 quotient rounded by
+    # hand, fp16 scale from numpy's own conversion of that fp32 value
+    rng = np.random.default_rng(3)
+    W = (rng.standard_normal((3, 64)) * 0.05).astype(np.float32)
+    wb = synth.bf16_bits(W)
+    q, s = oracle.rtn_quantize(wb, 8, 32)
+    vals = oracle.bf16_bits_to_f64(wb)
+    for n in range(3):
+        for g in range(2):
+            grp = [Fraction(float(v)) for v in vals[n, 32 * g:32 * g + 32]]
+            amax = max(abs(v) for v in grp)
+            s32 = _f32(amax / 127)
+            s16 = Fraction(float(np.float32(float(s32)).astype(np.float16)))
+            assert s16 == Fraction(float(s.view(np.float16)[g, n]))
+            for i, v in enumerate(grp):
+                r = _f32(v / s16)
+                k = math.floor(r)
+                if r - k > Fraction(1, 2) or (r - k == Fraction(1, 2) and k % 2):
+                    k += 1
+                assert int(q[n, 32 * g + i]) == max(-128, min(127, k)), (n, g, i)

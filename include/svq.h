@@ -14,6 +14,10 @@
  *    card "Qwen3.8-27B-MXFP8-CT-AutoRound-mtp", opening summary, sections
  *    "2. Precision plan" (N >= 128, K % 32 == 0) and "8. License and
  *    attribution" (OCP MX, E8M0 scale per 32-element block).
+ *  - W8A16, the quantized vocabulary head: symmetric int8 codes with one fp16
+ *    scale per group of G K-rows, produced at load time from the dense bf16
+ *    projection by svq_rtn_quantize (which also produces W4A16 weights). Eole
+ *    recipe, section "Optional vocabulary-head quantization".
  *
  * M is the number of tokens verified per call: streams x (1 + draft tokens)
  * (Eole recipe, opening paragraph: the main model verifies a chunk of drafted
@@ -158,6 +162,48 @@ int svq_mxfp8_gemm_with(int kernel, const void *x, const uint8_t *w, const uint8
                         void *workspace, size_t workspace_bytes, void *stream);
 
 const char *svq_mxfp8_kernel_name(int kernel, int64_t M, int64_t N, int64_t K);
+
+/* ---- quantized vocabulary head (W8A16) and the load-time quantizer --------- */
+
+/*
+ * Symmetric group-wise round-to-nearest quantization of a dense projection,
+ * done once when the model loads (Eole recipe, section "Optional
+ * vocabulary-head quantization": int8 or int4, groups of 32, 64 or 128 along
+ * K, symmetric, round to nearest). Per group of G consecutive K-elements of
+ * row n, in fp32 with IEEE division:
+ *     amax = max |w|,  s = fp16_rne(amax / qmax),  qmax = 127 (int8) or 7 (int4)
+ *     q    = clamp(rint(w / s), -qmax - 1, qmax)   (rint: nearest, ties to even)
+ * with s used as stored; a group whose stored s is 0 gets q = 0.
+ *   w           bf16 [N][K] (row n = output column n), 16-byte aligned; finite values
+ *   bits        8: codes = int8 [N][K] (two's complement), 16-byte aligned
+ *               4: codes = GPTQ int32 words [K/8][N] holding q + 8, the W4A16
+ *                  input of svq_q4_repack; 4-byte aligned
+ *   scales      fp16 [K/G][N], 2-byte aligned
+ *   group_size  G in {32, 64, 128}; K % G == 0
+ * codes and scales must not overlap w or each other. Errors as for the GEMMs.
+ */
+int svq_rtn_quantize(const void *w, int32_t bits, int32_t group_size, void *codes, void *scales,
+                     int64_t N, int64_t K, void *stream);
+
+/* Workspace bytes needed by svq_w8a16_gemm; 0 if none, (size_t)-1 if invalid. */
+size_t svq_w8a16_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group_size);
+
+/*
+ * y = x . (q * s)^T for the int8 codes of svq_rtn_quantize, M <= 16
+ * (SVQ_ERR_UNSUPPORTED above).
+ *   x       bf16 [M][K], 16-byte aligned
+ *   w       int8 codes [N][K], 16-byte aligned
+ *   scales  fp16 [K/G][N], 4-byte aligned (read as aligned 32-bit words)
+ *   out     bf16 [M][N], 4-byte aligned, fully overwritten, no overlap
+ *   group_size G in {32, 64, 128}; K % 128 == 0, N % 16 == 0
+ *   workspace as for svq_w4a16_gemm.
+ */
+int svq_w8a16_gemm(const void *x, const int8_t *w, const void *scales, void *out, int64_t M,
+                   int64_t N, int64_t K, int32_t group_size, void *workspace,
+                   size_t workspace_bytes, void *stream);
+
+/* Name of the kernel svq_w8a16_gemm would launch (static text), or NULL. */
+const char *svq_w8a16_kernel_name(int64_t M, int64_t N, int64_t K, int32_t group_size);
 
 #ifdef __cplusplus
 }

@@ -21,7 +21,7 @@ __all__ = [
     "SvqError", "KERNEL_AUTO", "KERNEL_DOT2", "KERNEL_MFMA_SKINNY", "KERNEL_MFMA_WIDE",
     "lib", "library_path", "q4_repack", "w4a16_gemm", "mxfp8_gemm", "w4a16_kernel_name",
     "mxfp8_kernel_name", "w4a16_workspace_bytes", "mxfp8_workspace_bytes", "Workspace",
-    "EXPORTED_SYMBOLS",
+    "EXPORTED_SYMBOLS", "rtn_quantize", "w8a16_gemm", "w8a16_workspace_bytes", "w8a16_kernel_name",
 ]
 
 KERNEL_AUTO, KERNEL_DOT2, KERNEL_MFMA_SKINNY, KERNEL_MFMA_WIDE = 0, 1, 2, 3
@@ -33,7 +33,8 @@ EXPORTED_SYMBOLS = (
     "svq_abi_version", "svq_status_string", "svq_q4_repacked_bytes", "svq_q4_repack",
     "svq_w4a16_workspace_bytes", "svq_w4a16_gemm", "svq_w4a16_gemm_with",
     "svq_w4a16_kernel_name", "svq_mxfp8_workspace_bytes", "svq_mxfp8_gemm",
-    "svq_mxfp8_gemm_with", "svq_mxfp8_kernel_name",
+    "svq_mxfp8_gemm_with", "svq_mxfp8_kernel_name", "svq_rtn_quantize",
+    "svq_w8a16_workspace_bytes", "svq_w8a16_gemm", "svq_w8a16_kernel_name",
 )
 
 _i64, _i32, _p, _sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t
@@ -83,6 +84,14 @@ def lib():
         L.svq_mxfp8_gemm_with.argtypes = [ctypes.c_int, _p, _p, _p, _p, _i64, _i64, _i64, _i32, _p, _sz, _p]
         L.svq_mxfp8_kernel_name.restype = ctypes.c_char_p
         L.svq_mxfp8_kernel_name.argtypes = [ctypes.c_int, _i64, _i64, _i64]
+        L.svq_rtn_quantize.restype = ctypes.c_int
+        L.svq_rtn_quantize.argtypes = [_p, _i32, _i32, _p, _p, _i64, _i64, _p]
+        L.svq_w8a16_workspace_bytes.restype = _sz
+        L.svq_w8a16_workspace_bytes.argtypes = [_i64, _i64, _i64, _i32]
+        L.svq_w8a16_gemm.restype = ctypes.c_int
+        L.svq_w8a16_gemm.argtypes = [_p, _p, _p, _p, _i64, _i64, _i64, _i32, _p, _sz, _p]
+        L.svq_w8a16_kernel_name.restype = ctypes.c_char_p
+        L.svq_w8a16_kernel_name.argtypes = [_i64, _i64, _i64, _i32]
         _lib = L
         return L
 
@@ -235,4 +244,65 @@ def mxfp8_gemm(x, w, scales, out=None, kernel=KERNEL_AUTO, workspace=None):
     _check(lib().svq_mxfp8_gemm_with(kernel, _dev_ptr(x, "x"), _dev_ptr(w, "w"), _dev_ptr(scales, "scales"),
                                      _dev_ptr(out, "out"), M, N, K, 32, ws_ptr, ws_bytes, stream),
            "svq_mxfp8_gemm")
+    return out
+
+
+# ---- quantized vocabulary head ----------------------------------------------------
+
+def rtn_quantize(w, bits=8, group_size=128, codes=None, scales=None):
+    """Load-time symmetric group-wise RTN of bf16 w [N, K] (device).
+
+    Returns (codes, scales): int8 codes [N, K] for bits=8, GPTQ int32 words
+    [K/8, N] (the svq_q4_repack input) for bits=4; fp16 scales [K/G, N].
+    """
+    torch = _torch()
+    N, K = w.shape
+    _check_elem(w, "w", 2)
+    if codes is None:
+        codes = (torch.empty((N, K), dtype=torch.int8, device=w.device) if bits == 8
+                 else torch.empty((K // 8, N), dtype=torch.int32, device=w.device))
+    if scales is None:
+        scales = torch.empty((K // group_size, N), dtype=torch.float16, device=w.device)
+    _check_elem(scales, "scales", 2)
+    if codes.numel() * codes.element_size() != N * K * bits // 8 or scales.numel() != (K // group_size) * N:
+        raise ValueError("codes or scales have the wrong size")
+    _check(lib().svq_rtn_quantize(_dev_ptr(w, "w"), bits, group_size, _dev_ptr(codes, "codes"),
+                                  _dev_ptr(scales, "scales"), N, K, _stream_ptr(w)), "svq_rtn_quantize")
+    return codes, scales
+
+
+def w8a16_workspace_bytes(M, N, K, group_size=128) -> int:
+    v = lib().svq_w8a16_workspace_bytes(M, N, K, group_size)
+    if v == ctypes.c_size_t(-1).value:
+        raise SvqError(10, "svq_w8a16_workspace_bytes")
+    return v
+
+
+def w8a16_kernel_name(M, N, K, group_size=128):
+    r = lib().svq_w8a16_kernel_name(M, N, K, group_size)
+    return r.decode() if r else None
+
+
+def w8a16_gemm(x, w, scales, group_size=128, out=None, workspace=None):
+    """bf16 x [M, K] . (int8 w [N, K] * fp16 scales [K/G, N])^T -> bf16 [M, N], M <= 16."""
+    torch = _torch()
+    M, K = x.shape
+    N = w.shape[0]
+    _check_elem(x, "x", 2)
+    _check_elem(w, "w", 1)
+    _check_elem(scales, "scales", 2)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    _check_elem(out, "out", 2)
+    if tuple(out.shape) != (M, N):
+        raise ValueError(f"out must have shape {(M, N)}")
+    stream = _stream_ptr(x)
+    if workspace is None:
+        nbytes = w8a16_workspace_bytes(M, N, K, group_size)
+        workspace = Workspace.get(nbytes, x.device, stream.value or 0)
+    ws_ptr = _dev_ptr(workspace, "workspace") if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().svq_w8a16_gemm(_dev_ptr(x, "x"), _dev_ptr(w, "w"), _dev_ptr(scales, "scales"),
+                                _dev_ptr(out, "out"), M, N, K, group_size, ws_ptr, ws_bytes, stream),
+           "svq_w8a16_gemm")
     return out

@@ -341,4 +341,51 @@ int svq_mxfp8_gemm(const void *x, const uint8_t *w, const uint8_t *scales, void 
                                workspace_bytes, stream);
 }
 
+// ---- quantized vocabulary head -------------------------------------------------
+
+int svq_rtn_quantize(const void *w, int32_t bits, int32_t G, void *codes, void *scales, int64_t N,
+                     int64_t K, void *stream) {
+    if (!w || !codes || !scales) return SVQ_ERR_NULL;
+    if (N <= 0 || K <= 0 || N > kMaxDim || K > kMaxDim || N * K > (int64_t(1) << 40)) return SVQ_ERR_DIM;
+    if (bits != 4 && bits != 8) return SVQ_ERR_UNSUPPORTED;
+    if (G != 32 && G != 64 && G != 128) return SVQ_ERR_GROUP;
+    if (K % G) return SVQ_ERR_DIVISIBILITY;
+    if (!aligned(w, 16) || !aligned(codes, bits == 8 ? 16 : 4) || !aligned(scales, 2)) return SVQ_ERR_ALIGN;
+    const size_t wb = (size_t)N * K * 2, cb = (size_t)N * K * bits / 8, sb = (size_t)(K / G) * N * 2;
+    if (overlap(codes, cb, w, wb) || overlap(scales, sb, w, wb) || overlap(codes, cb, scales, sb))
+        return SVQ_ERR_OVERLAP;
+    if (launch_rtn_quantize(w, bits, G, codes, scales, N, K, (hipStream_t)stream) != hipSuccess)
+        return SVQ_ERR_HIP;
+    return SVQ_OK;
+}
+
+size_t svq_w8a16_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t G) {
+    if (check_w4a16_shape(M, N, K, G) != SVQ_OK || M > 16) return (size_t)-1;
+    return plan_smallm(M, N, K, device_cus()).workspace_bytes;
+}
+
+const char *svq_w8a16_kernel_name(int64_t M, int64_t N, int64_t K, int32_t G) {
+    if (check_w4a16_shape(M, N, K, G) != SVQ_OK || M > 16) return nullptr;
+    return "w8a16_skinny_kernel";
+}
+
+int svq_w8a16_gemm(const void *x, const int8_t *w, const void *scales, void *out, int64_t M,
+                   int64_t N, int64_t K, int32_t G, void *workspace, size_t workspace_bytes,
+                   void *stream) {
+    int st = check_w4a16_shape(M, N, K, G);  // same shape rules as W4A16
+    if (st != SVQ_OK) return st;
+    if (M > 16) return SVQ_ERR_UNSUPPORTED;
+    const size_t xb = (size_t)M * K * 2, wb = (size_t)N * K, sb = (size_t)(K / G) * N * 2, ob = (size_t)M * N * 2;
+    st = check_gemm_buffers(x, xb, w, wb, scales, sb, out, ob, nullptr, 0, 0, 4);
+    if (st != SVQ_OK) return st;
+    const SmallPlan plan = plan_smallm(M, N, K, device_cus());
+    if (plan.splits > 1 && N / 16 > (int64_t)kMaxCounters) return SVQ_ERR_UNSUPPORTED;
+    st = check_gemm_buffers(x, xb, w, wb, scales, sb, out, ob, workspace, workspace_bytes,
+                            plan.workspace_bytes, 4);
+    if (st != SVQ_OK) return st;
+    return launch_w8a16_skinny(plan, x, w, scales, out, (int)M, N, K, G, workspace, (hipStream_t)stream) == hipSuccess
+               ? SVQ_OK
+               : SVQ_ERR_HIP;
+}
+
 }  // extern "C"

@@ -88,6 +88,12 @@ hipError_t launch_mxfp8_skinny(const SmallPlan &plan, const void *x, const uint8
                                const uint8_t *scales, void *out, int M, int64_t N, int64_t K,
                                void *workspace, hipStream_t stream);
 
+hipError_t launch_w8a16_skinny(const SmallPlan &plan, const void *x, const int8_t *w,
+                               const void *scales, void *out, int M, int64_t N, int64_t K, int G,
+                               void *workspace, hipStream_t stream);
+hipError_t launch_rtn_quantize(const void *w, int bits, int G, void *codes, void *scales, int64_t N,
+                               int64_t K, hipStream_t stream);
+
 // Workspace layout shared by every kernel that splits work across workgroups:
 // a fixed region of arrival counters (which every kernel leaves at zero) then
 // the fp32 partials. The counter region has the same size for all kernels so

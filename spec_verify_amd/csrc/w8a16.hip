@@ -1,0 +1,274 @@
+// Quantized vocabulary head for gfx950: the W8A16 GEMM for small M and the
+// load-time round-to-nearest quantizer that produces its weights (and the INT4
+// weights of the W4A16 path).
+//
+// Format: Eole recipe "Qwen3.8-27B and native MTP speculative decoding",
+// section "Optional vocabulary-head quantization": the dense vocabulary
+// projection is quantized when the model loads, to int8 or int4, symmetric,
+// group-wise (32, 64 or 128 elements along K), round to nearest. Stored here as
+//   int8:  codes q [N][K] row-major (two's complement), fp16 scales [K/G][N]
+//   int4:  GPTQ words [K/8][N] holding q + 8 (the W4A16 format), fp16 scales [K/G][N]
+// with w[n][k] = q[n][k] * s[k/G][n].
+//
+// W8A16 kernel (M <= 16): the W4A16 skinny design on one byte per weight. A
+// workgroup owns one 16-column block; its waves take the 16 x 128 K-tiles
+// round-robin. Lane l owns column l%16 and K-rows 32*(l/16).. of a tile: two
+// 128-bit loads of its row of W. x comes straight from L2 per tile (rows >= M
+// read past the buffer's end as zeros). MFMA 16x16x32 bf16; the MFMA pipe is
+// idle enough that the offset of the byte decode is also removed on it.
+//
+// Byte decode: b ^ 0x80 is q + 128 as an unsigned byte, which v_cvt_f32_ubyte
+// turns into an exact float; its upper half is the exact bf16 (integers below
+// 256 need 8 significant bits). The -128 comes back per 32-row step as an MFMA
+// of x against a constant -128 operand, and the fp16 group scale multiplies
+// each group's fp32 MFMA result into the accumulator, as in W4A16.
+#include <hip/hip_fp16.h>
+
+#include "svq_launch.h"
+#include "svq_streamk.h"
+
+namespace svq {
+
+constexpr uint32_t kBf16Neg128Pair = 0xC300C300u;
+
+// Two bf16 values (q + 128 of bytes 2p, 2p+1 of a flipped dword) in one dword.
+__device__ __forceinline__ uint32_t u8pair_bf16(uint32_t u, int p) {
+    const float a = (float)((u >> (16 * p)) & 0xffu);
+    const float b = (float)((u >> (16 * p + 8)) & 0xffu);
+    // upper halves of the two floats: bytes 2,3 of a then bytes 2,3 of b
+    return __builtin_amdgcn_perm(f32_bits(b), f32_bits(a), 0x07060302u);
+}
+
+// Eight codes (dwords lo, hi: K-rows e = 0..7) -> the bf16x8 B operand of q + 128.
+__device__ __forceinline__ uint4 i8x8_to_bf16(uint32_t lo, uint32_t hi) {
+    const uint32_t a = lo ^ 0x80808080u, b = hi ^ 0x80808080u;
+    return make_uint4(u8pair_bf16(a, 0), u8pair_bf16(a, 1), u8pair_bf16(b, 0), u8pair_bf16(b, 1));
+}
+
+// ---------------------------------------------------------------------------
+// W8A16 skinny MFMA kernel, M <= 16
+// ---------------------------------------------------------------------------
+template <int WAVES, int D, int GSHIFT>
+__global__ __launch_bounds__(64 * WAVES) void w8a16_skinny_kernel(
+    const uint16_t *__restrict__ x, const int8_t *__restrict__ w,
+    const uint16_t *__restrict__ sc, uint16_t *__restrict__ out, uint32_t *__restrict__ cnt,
+    float *__restrict__ part, int M, int N, int K, int splits, int S) {
+    constexpr int NG = 128 >> GSHIFT;  // groups per 128-row tile
+    constexpr int SPG = 4 / NG;        // MFMA steps per group
+    constexpr bool kTrans = GSHIFT < 7;
+    const int lane = threadIdx.x & 63;
+    const int wave = wave_id();
+    const int r = lane & 15, g = lane >> 4;
+    const int lb = xcd_contiguous(blockIdx.x, gridDim.x);
+    const int nb = lb / splits, sp = lb % splits;
+    const int KT = K >> 7;
+    const __amdgpu_buffer_rsrc_t wr = make_rsrc(w + (size_t)nb * 16 * K, (uint32_t)16 * K);
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, (uint32_t)M * K * 2);
+    const __amdgpu_buffer_rsrc_t sr = make_rsrc(sc + nb * 16, (uint32_t)(((size_t)(K >> GSHIFT) * N - nb * 16) * 2));
+    const uint32_t w_vo = r * K + g * 32;
+    // A operand of MFMA step j: x row r (rows >= M read as zero), K-rows
+    // 32j + 8g.. for every group size below 128 (the weight words are
+    // transposed to match) or 32g + 8j.. for 128
+    const uint32_t x_vo = r * K * 2 + (kTrans ? 16 * g : 64 * g);
+    constexpr int kXStep = kTrans ? 64 : 16;
+    // the aligned dword holding this lane's fp16 scale; s_sh selects the half
+    const uint32_t s_vo = (r & 14) * 2;
+    const int s_sh = (r & 1) * 16;
+    // this workgroup's K range: tiles [kbeg, kbeg + kcnt) of the column block
+    const int kbeg = sp * S;
+    const int kcnt = KT - kbeg < S ? KT - kbeg : S;
+    const int ntile = wave < kcnt ? (kcnt - 1 - wave) / WAVES + 1 : 0;
+    const uint4 bneg = make_uint4(kBf16Neg128Pair, kBf16Neg128Pair, kBf16Neg128Pair, kBf16Neg128Pair);
+
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    uint4 vA[D][2], vB[D][2], aA[D][4], aB[D][4];
+    uint32_t sA[D][NG], sB[D][NG];
+
+#define SVQ_LOAD(V, A, SS, I0)                                                       \
+    _Pragma("unroll") for (int d = 0; d < D; ++d) if ((I0) + d < ntile) {            \
+        const int kt = kbeg + wave + ((I0) + d) * WAVES;                             \
+        V[d][0] = bload16(wr, w_vo, kt * 128);                                       \
+        V[d][1] = bload16(wr, w_vo + 16, kt * 128);                                  \
+        _Pragma("unroll") for (int j = 0; j < 4; ++j) A[d][j] = bload16(xr, x_vo + kXStep * j, kt * 256); \
+        _Pragma("unroll") for (int q = 0; q < NG; ++q) SS[d][q] = bload4(sr, s_vo, (kt * NG + q) * N * 2); \
+    }
+#define SVQ_COMPUTE(V, A, SS, I0)                                                    \
+    _Pragma("unroll") for (int d = 0; d < D; ++d) if ((I0) + d < ntile) {            \
+        uint32_t lo[4] = {V[d][0].x, V[d][0].z, V[d][1].x, V[d][1].z};               \
+        uint32_t hi[4] = {V[d][0].y, V[d][0].w, V[d][1].y, V[d][1].w};               \
+        if constexpr (kTrans) {                                                      \
+            transpose_rows_words(lo[0], lo[1], lo[2], lo[3]);                        \
+            transpose_rows_words(hi[0], hi[1], hi[2], hi[3]);                        \
+        }                                                                            \
+        _Pragma("unroll") for (int q = 0; q < NG; ++q) {                             \
+            f32x4 P = {0.f, 0.f, 0.f, 0.f};                                          \
+            _Pragma("unroll") for (int jj = 0; jj < SPG; ++jj) {                     \
+                const int j = q * SPG + jj;                                          \
+                P = mfma16x16x32(A[d][j], bneg, P);                                  \
+                P = mfma16x16x32(A[d][j], i8x8_to_bf16(lo[j], hi[j]), P);            \
+            }                                                                        \
+            const float sf = fp16_bits_to_f32((uint16_t)(SS[d][q] >> s_sh));         \
+            _Pragma("unroll") for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(sf, P[i], acc[i]); \
+        }                                                                            \
+    }
+
+    if (ntile > 0) {
+        SVQ_LOAD(vA, aA, sA, 0)
+        for (int i0 = 0;; i0 += 2 * D) {
+            SVQ_LOAD(vB, aB, sB, i0 + D)
+            SVQ_COMPUTE(vA, aA, sA, i0)
+            if (i0 + D >= ntile) break;
+            SVQ_LOAD(vA, aA, sA, i0 + 2 * D)
+            SVQ_COMPUTE(vB, aB, sB, i0 + D)
+            if (i0 + 2 * D >= ntile) break;
+        }
+    }
+#undef SVQ_LOAD
+#undef SVQ_COMPUTE
+
+    // cross-wave sum of the valid rows through LDS, in wave order
+    __shared__ float red[WAVES][16][17];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) red[wave][4 * g + i][r] = acc[i];
+    __syncthreads();
+    __shared__ int s_flag;
+    float v = 0.f;
+    if (threadIdx.x < 16 * M) {
+#pragma unroll
+        for (int wv = 0; wv < WAVES; ++wv) v += red[wv][threadIdx.x >> 4][threadIdx.x & 15];
+    }
+    smallm_finish(v, M, N, nb, sp, splits, out, cnt, part, &s_flag);
+}
+
+// ---------------------------------------------------------------------------
+// Load-time quantizer: dense bf16 W [N][K] -> codes + fp16 scales [K/G][N].
+// Thread (n, group): lanes of a wave take consecutive rows n, the waves of a
+// workgroup consecutive groups, so the scale and GPTQ-word stores of a wave
+// are contiguous. Per group, in fp32 with IEEE division:
+//   amax = max |w|, s = fp16_rne(amax / qmax), q = clamp(rint(w / s), -qmax-1, qmax)
+// with s used as stored; a group whose stored scale is zero gets q = 0.
+// ---------------------------------------------------------------------------
+template <int BITS, int GSHIFT>
+__global__ __launch_bounds__(256) void rtn_quantize_kernel(const uint16_t *__restrict__ w,
+                                                           void *__restrict__ codes,
+                                                           uint16_t *__restrict__ scales, int N,
+                                                           int K) {
+    constexpr int G = 1 << GSHIFT;
+    constexpr float kQmax = (float)((1 << (BITS - 1)) - 1);
+    const int n = blockIdx.x * 64 + (threadIdx.x & 63);
+    const int grp = blockIdx.y * 4 + (threadIdx.x >> 6);
+    if (n >= N || grp >= (K >> GSHIFT)) return;
+    const uint4 *src = (const uint4 *)(w + (size_t)n * K + (size_t)grp * G);
+    uint4 v[G / 8];
+#pragma unroll
+    for (int i = 0; i < G / 8; ++i) v[i] = src[i];
+    auto elem = [&](int e) {  // bf16 -> fp32, exact
+        const uint4 &c = v[e >> 3];
+        const uint32_t word = ((e >> 1) & 3) == 0 ? c.x : ((e >> 1) & 3) == 1 ? c.y : ((e >> 1) & 3) == 2 ? c.z : c.w;
+        return bits_f32((e & 1) ? (word & 0xffff0000u) : (word << 16));
+    };
+    float amax = 0.f;
+#pragma unroll
+    for (int e = 0; e < G; ++e) amax = fmaxf(amax, fabsf(elem(e)));
+    const __half s16 = __float2half_rn(__fdiv_rn(amax, kQmax));
+    const float s = __half2float(s16);
+    scales[(size_t)grp * N + n] = __half_as_ushort(s16);
+    auto code = [&](int e) -> int {
+        if (!(s > 0.f)) return 0;
+        const float t = rintf(__fdiv_rn(elem(e), s));
+        return (int)fminf(fmaxf(t, -kQmax - 1.f), kQmax);
+    };
+    if constexpr (BITS == 8) {
+        uint4 *dst = (uint4 *)((int8_t *)codes + (size_t)n * K + (size_t)grp * G);
+#pragma unroll
+        for (int i = 0; i < G / 16; ++i) {
+            uint32_t d[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                uint32_t word = 0;
+#pragma unroll
+                for (int b = 0; b < 4; ++b) word |= ((uint32_t)code(16 * i + 4 * c + b) & 0xffu) << (8 * b);
+                d[c] = word;
+            }
+            dst[i] = make_uint4(d[0], d[1], d[2], d[3]);
+        }
+    } else {
+        // GPTQ words [K/8][N]: nibble i of word k/8 is row k (least significant first)
+        int32_t *dst = (int32_t *)codes + (size_t)grp * (G / 8) * N + n;
+#pragma unroll
+        for (int j = 0; j < G / 8; ++j) {
+            uint32_t word = 0;
+#pragma unroll
+            for (int b = 0; b < 8; ++b) word |= (uint32_t)(code(8 * j + b) + 8) << (4 * b);
+            dst[(size_t)j * N] = (int32_t)word;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// host launchers
+// ---------------------------------------------------------------------------
+namespace {
+constexpr int kW8SkinnyDepth = 2;
+
+template <int WAVES, int GS>
+hipError_t w8_skinny_launch_w(const SmallPlan &p, const void *x, const int8_t *w, const void *sc,
+                              void *out, int M, int64_t N, int64_t K, void *ws, hipStream_t stream) {
+    hipLaunchKernelGGL((w8a16_skinny_kernel<WAVES, kW8SkinnyDepth, GS>), dim3((uint32_t)(N / 16 * p.splits)),
+                       dim3(64 * WAVES), 0, stream, (const uint16_t *)x, w, (const uint16_t *)sc,
+                       (uint16_t *)out, ws_counters(ws), (float *)ws_partials(ws), M, (int)N, (int)K,
+                       p.splits, p.S);
+    return hipGetLastError();
+}
+
+template <int GS>
+hipError_t w8_skinny_launch(const SmallPlan &p, const void *x, const int8_t *w, const void *sc,
+                            void *out, int M, int64_t N, int64_t K, void *ws, hipStream_t stream) {
+    static const int r16 = resident_blocks(w8a16_skinny_kernel<16, kW8SkinnyDepth, GS>, 1024);
+    static const int r8 = resident_blocks(w8a16_skinny_kernel<8, kW8SkinnyDepth, GS>, 512);
+    switch (pick_waves(N / 16 * p.splits, p.cus, r16, r8)) {
+    case 16: return w8_skinny_launch_w<16, GS>(p, x, w, sc, out, M, N, K, ws, stream);
+    case 8: return w8_skinny_launch_w<8, GS>(p, x, w, sc, out, M, N, K, ws, stream);
+    default: return w8_skinny_launch_w<4, GS>(p, x, w, sc, out, M, N, K, ws, stream);
+    }
+}
+
+template <int BITS, int GS>
+hipError_t rtn_launch(const void *w, void *codes, void *scales, int64_t N, int64_t K, hipStream_t stream) {
+    const dim3 grid((uint32_t)((N + 63) / 64), (uint32_t)(((K >> GS) + 3) / 4));
+    hipLaunchKernelGGL((rtn_quantize_kernel<BITS, GS>), grid, dim3(256), 0, stream,
+                       (const uint16_t *)w, codes, (uint16_t *)scales, (int)N, (int)K);
+    return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_w8a16_skinny(const SmallPlan &plan, const void *x, const int8_t *w,
+                               const void *scales, void *out, int M, int64_t N, int64_t K, int G,
+                               void *workspace, hipStream_t stream) {
+    switch (G) {
+    case 32: return w8_skinny_launch<5>(plan, x, w, scales, out, M, N, K, workspace, stream);
+    case 64: return w8_skinny_launch<6>(plan, x, w, scales, out, M, N, K, workspace, stream);
+    case 128: return w8_skinny_launch<7>(plan, x, w, scales, out, M, N, K, workspace, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_rtn_quantize(const void *w, int bits, int G, void *codes, void *scales, int64_t N,
+                               int64_t K, hipStream_t stream) {
+    if (bits == 8) {
+        switch (G) {
+        case 32: return rtn_launch<8, 5>(w, codes, scales, N, K, stream);
+        case 64: return rtn_launch<8, 6>(w, codes, scales, N, K, stream);
+        case 128: return rtn_launch<8, 7>(w, codes, scales, N, K, stream);
+        default: return hipErrorInvalidValue;
+        }
+    }
+    switch (G) {
+    case 32: return rtn_launch<4, 5>(w, codes, scales, N, K, stream);
+    case 64: return rtn_launch<4, 6>(w, codes, scales, N, K, stream);
+    case 128: return rtn_launch<4, 7>(w, codes, scales, N, K, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace svq

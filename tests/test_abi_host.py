@@ -125,6 +125,42 @@ def test_workspace_query_rejects_bad_shapes(L):
     assert L.svq_mxfp8_workspace_bytes(0, 1, 96, 5120) == bad
 
 
+def test_w8a16_validation_and_names(L):
+    def w8(M=1, N=256, K=512, G=128, x=FAKE, w=FAKE2, s=FAKE3, o=FAKE4):
+        return L.svq_w8a16_gemm(x, w, s, o, M, N, K, G, None, 0, None)
+    assert w8(w=None) == 1
+    assert w8(M=0) == 2
+    assert w8(G=96) == 3
+    assert w8(N=24) == 4
+    assert w8(K=192, G=64) == 4               # K % 128
+    assert w8(M=17) == 10                     # one MFMA tile of rows: M <= 16
+    assert w8(w=FAKE2 + 8) == 6
+    assert w8(s=FAKE3 + 2) == 6
+    assert w8(o=FAKE2 + 64) == 7               # out overlaps w
+    assert L.svq_w8a16_kernel_name(1, 248320, 5120, 128) == b"w8a16_skinny_kernel"
+    assert L.svq_w8a16_kernel_name(17, 256, 512, 128) is None
+    bad = ctypes.c_size_t(-1).value
+    assert L.svq_w8a16_workspace_bytes(17, 256, 512, 128) == bad
+    assert L.svq_w8a16_workspace_bytes(1, 248320, 5120, 128) == 0
+
+
+def test_rtn_quantize_validation(L):
+    def q(w=FAKE, bits=8, G=128, c=FAKE2, s=FAKE3, N=256, K=512):
+        return L.svq_rtn_quantize(w, bits, G, c, s, N, K, None)
+    assert q(w=None) == 1
+    assert q(s=None) == 1
+    assert q(N=0) == 2
+    assert q(bits=2) == 10
+    assert q(G=16) == 3
+    assert q(K=96, G=64) == 4
+    assert q(w=FAKE + 8) == 6
+    assert q(c=FAKE2 + 4) == 6                 # int8 codes are written 16 bytes at a time
+    assert q(bits=4, c=FAKE2 + 4, N=0) == 2    # dimensions are checked first
+    assert q(s=FAKE3 + 1) == 6
+    assert q(c=FAKE + 1024) == 7               # codes overlap w
+    assert q(s=FAKE2 + 4096) == 7              # scales overlap codes
+
+
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     import spec_verify_amd as svq
     monkeypatch.setattr(svq, "_lib", None)

@@ -234,6 +234,91 @@ def test_mxfp8_workloads(name):
         assert ok, f"{name}: err={err:.4g} rms={rms:.4g}"
 
 
+# ---- quantized vocabulary head: W8A16 and the load-time RTN quantizer --------------
+
+W8_CASES = [(m, K, N, G) for m in (1, 3, 5, 8, 16) for (K, N) in ((512, 48), (1280, 32)) for G in (32, 64, 128)]
+
+
+@pytest.mark.parametrize("M,K,N,G", W8_CASES, ids=["-".join(map(str, c)) for c in W8_CASES])
+def test_w8a16_random(M, K, N, G):
+    import spec_verify_amd as svq
+    _say("w8a16 random M K N G", M, K, N, G)
+    inp = synth.gen_w8a16(2000 + 7 * M + K + N + G, M, K, N, G)
+    out = svq.w8a16_gemm(dev(inp.x), dev(inp.w), dev(inp.scales), G)
+    torch.cuda.synchronize()
+    y64, y32 = oracle.w8a16(inp.x, inp.w, inp.scales, G)
+    assert_gate(host_bits(out), y64, y32, f"w8a16 M{M} K{K} N{N} G{G}")
+
+
+@pytest.mark.parametrize("M,K,N,G", [(1, 1024, 32, 128), (5, 1024, 48, 32), (16, 640, 32, 64)])
+def test_w8a16_integer_exact(M, K, N, G):
+    import spec_verify_amd as svq
+    _say("w8a16 intexact M K N G", M, K, N, G)
+    inp = synth.gen_w8a16(91 + M, M, K, N, G, kind="intexact")
+    out = svq.w8a16_gemm(dev(inp.x), dev(inp.w), dev(inp.scales), G)
+    torch.cuda.synchronize()
+    xi = oracle.bf16_bits_to_f64(inp.x).astype(np.int64)
+    exact = xi @ inp.w.astype(np.int64).T
+    np.testing.assert_array_equal(host_bits(out), oracle.bf16_rne(exact.astype(np.float32)))
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+@pytest.mark.parametrize("G", [32, 64, 128])
+def test_rtn_quantize_bit_exact(bits, G):
+    import spec_verify_amd as svq
+    N, K = 80, 1024
+    _say("rtn bits G", bits, G)
+    wb = synth.gen_dense_bf16(700 + bits + G, N, K)
+    wb[3, :G] = 0                                  # an all-zero group: scale 0, codes 0
+    q, s = svq.rtn_quantize(dev(wb), bits, G)
+    torch.cuda.synchronize()
+    q_ref, s_ref = oracle.rtn_quantize(wb, bits, G)
+    np.testing.assert_array_equal(s.view(torch.int16).cpu().numpy().view(np.uint16), s_ref)
+    np.testing.assert_array_equal(q.cpu().numpy(), q_ref)
+
+
+def test_rtn_then_gemm_end_to_end():
+    import spec_verify_amd as svq
+    M, K, N, G = 3, 2560, 512, 128
+    _say("rtn -> gemm M K N", M, K, N)
+    rng = np.random.default_rng(77)
+    x = synth.bf16_bits(rng.standard_normal((M, K), dtype=np.float32))
+    wb = synth.gen_dense_bf16(78, N, K)
+    # int8: codes on the GPU, the W8A16 kernel on them
+    q8, s8 = svq.rtn_quantize(dev(wb), 8, G)
+    y8 = svq.w8a16_gemm(dev(x), q8, s8, G)
+    # int4: GPTQ words on the GPU, repacked, through the W4A16 path
+    q4, s4 = svq.rtn_quantize(dev(wb), 4, G)
+    y4 = svq.w4a16_gemm(dev(x), svq.q4_repack(q4), s4, N, G)
+    torch.cuda.synchronize()
+    c8, t8 = oracle.rtn_quantize(wb, 8, G)
+    c4, t4 = oracle.rtn_quantize(wb, 4, G)
+    np.testing.assert_array_equal(q8.cpu().numpy(), c8)
+    np.testing.assert_array_equal(q4.cpu().numpy(), c4)
+    assert_gate(host_bits(y8), *oracle.w8a16(x, c8, t8, G), "rtn int8 -> w8a16")
+    assert_gate(host_bits(y4), *oracle.w4a16(x, c4, t4, G), "rtn int4 -> w4a16")
+
+
+@pytest.mark.parametrize("name", ["vocab_w8_m1", "vocab_w4_m1"])
+def test_vocab_head_workloads(name):
+    import spec_verify_amd as svq
+    w = synth.WORKLOADS[name]
+    _say("vocab workload", name, w)
+    inp = synth.gen_workload(name)
+    rows, cols = _sample(inp.M, inp.N, 1500, w["seed"])
+    if w["op"] == "w8a16":
+        out = host_bits(svq.w8a16_gemm(dev(inp.x), dev(inp.w), dev(inp.scales), 128))
+        y64, y32 = oracle.w8a16_points(inp.x, inp.w, inp.scales, 128, rows, cols)
+    else:
+        out, _ = run_w4a16(inp)
+        y64, y32 = oracle.w4a16_points(inp.x, inp.qweight, inp.scales, 128, rows, cols)
+    torch.cuda.synchronize()
+    ok, err, rms = oracle.gate(out[rows, cols], y64)
+    assert ok, f"{name}: err={err:.4g} rms={rms:.4g}"
+    assert oracle.gate(out[rows, cols], y32.astype(np.float64))[0]
+    assert np.all(np.isfinite(oracle.bf16_bits_to_f64(out)))
+
+
 # ---- properties of the launch path -------------------------------------------------
 
 def test_wide_deterministic_and_counters_cleared():

@@ -43,18 +43,17 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def algo_bytes(w):
-    M, K, N = w["M"], w["K"], w["N"]
-    if w["op"] == "w4a16":
-        return K * N // 2 + (K // 128) * N * 2 + 2 * M * K + 2 * M * N
-    return K * N + (K // 32) * N + 2 * M * K + 2 * M * N
-
-
 def weight_bytes(w):
     K, N = w["K"], w["N"]
     if w["op"] == "w4a16":
         return K * N // 2 + (K // 128) * N * 2
+    if w["op"] == "w8a16":
+        return K * N + (K // 128) * N * 2
     return K * N + (K // 32) * N
+
+
+def algo_bytes(w):
+    return weight_bytes(w) + 2 * w["M"] * w["K"] + 2 * w["M"] * w["N"]
 
 
 class Problem:
@@ -83,6 +82,11 @@ class Problem:
             base_s = d(inp.scales)
             self.kernel = svq.w4a16_kernel_name(M, N, K)
             nb = svq.w4a16_workspace_bytes(M, N, K)
+        elif self.w["op"] == "w8a16":
+            base_w = torch.from_numpy(np.ascontiguousarray(inp.w)).to(dev)
+            base_s = d(inp.scales)
+            self.kernel = svq.w8a16_kernel_name(M, N, K)
+            nb = svq.w8a16_workspace_bytes(M, N, K)
         else:
             base_w = d(inp.w)
             base_s = d(inp.scales)
@@ -100,6 +104,8 @@ class Problem:
         if w["op"] == "w4a16":
             self.svq.w4a16_gemm(self.x, self.ws_w[i], self.ws_s[i], w["N"], 128, out=self.out,
                                 workspace=self.ws)
+        elif w["op"] == "w8a16":
+            self.svq.w8a16_gemm(self.x, self.ws_w[i], self.ws_s[i], 128, out=self.out, workspace=self.ws)
         else:
             self.svq.mxfp8_gemm(self.x, self.ws_w[i], self.ws_s[i], out=self.out, workspace=self.ws)
 
@@ -116,6 +122,8 @@ class Problem:
             bits = self.out.view(torch.int16).cpu().numpy().view(np.uint16)[rows, cols]
             if w["op"] == "w4a16":
                 y64, _ = oracle.w4a16_points(inp.x, inp.qweight, inp.scales, 128, rows, cols)
+            elif w["op"] == "w8a16":
+                y64, _ = oracle.w8a16_points(inp.x, inp.w, inp.scales, 128, rows, cols)
             else:
                 y64, _ = oracle.mxfp8_points(inp.x, inp.w, inp.scales, rows, cols)
             ok, err, rms = oracle.gate(bits, y64)
@@ -186,6 +194,62 @@ def cpu_baseline(budget_s=12.0):
             "ms_per_step": round(dt / steps * 1e3, 3)}
 
 
+def workload_table(torch, svq, oracle, names):
+    """µs per launch (graph of 100 rotating launches, parity checked before and
+    after) and the derived rates of each named workload."""
+    log(f"{'workload':15s} {'kernel':22s} {'µs':>8s} {'GB/s':>8s} {'%HBM':>6s} "
+        f"{'TFLOP/s':>8s} {'%MFMA':>6s}")
+    detail = []
+    for n in names:
+        p = Problem(torch, svq, n, POOL_BYTES)
+        p.check(oracle)
+        us = time_kernel(torch, p, launches=100, reps=3)
+        p.check(oracle)
+        w = p.w
+        gbs = algo_bytes(w) / (us * 1e-6) / 1e9
+        tfl = 2.0 * w["M"] * w["N"] * w["K"] / (us * 1e-6) / 1e12
+        detail.append({"workload": n, "op": w["op"], "M": w["M"], "K": w["K"], "N": w["N"], "kernel": p.kernel,
+                       "us": round(us, 3),
+                       "GBps": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+                       "weight_GBps": round(weight_bytes(w) / (us * 1e-6) / 1e9, 1),
+                       "TFLOPs": round(tfl, 2), "mfma_frac": round(tfl / MFMA_BF16_PEAK_TFLOPS, 4)})
+        log(f"{n:15s} {p.kernel:22s} {us:8.2f} {gbs:8.1f} {100 * gbs / HBM_PEAK_GBS:6.1f} "
+            f"{tfl:8.2f} {100 * tfl / MFMA_BF16_PEAK_TFLOPS:6.2f}")
+        p.release()
+        del p
+        torch.cuda.empty_cache()
+    return detail
+
+
+def time_quantizer(torch, svq, oracle, N=24832, K=5120, G=128, reps=20):
+    """The load-time RTN quantizer on a tenth of the vocabulary head (bf16 [N, K]):
+    µs per call and GB/s over its bytes (bf16 read, codes and fp16 scales written);
+    the codes of the first call are checked against the oracle on sampled rows."""
+    wb = synth.gen_dense_bf16(611, N, K)
+    w = torch.from_numpy(wb.view(np.int16)).to("cuda:0")
+    res = {"N": N, "K": K, "G": G}
+    for bits in (8, 4):
+        q, s = svq.rtn_quantize(w, bits, G)
+        torch.cuda.synchronize()
+        rows = np.arange(0, N, 997)
+        q_ref, s_ref = oracle.rtn_quantize(wb[rows], bits, G)
+        got_s = s.view(torch.int16).cpu().numpy().view(np.uint16)[:, rows]
+        got_q = q.cpu().numpy()[rows] if bits == 8 else q.cpu().numpy()[:, rows]
+        if not (np.array_equal(got_s, s_ref) and np.array_equal(got_q, q_ref)):
+            raise SystemExit(f"quantizer parity failure (int{bits})")
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            svq.rtn_quantize(w, bits, G, codes=q, scales=s)
+        b.record()
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) * 1e3 / reps
+        nbytes = N * K * 2 + N * K * bits // 8 + (K // G) * N * 2
+        res[f"us_int{bits}"] = round(us, 2)
+        res[f"GBps_int{bits}"] = round(nbytes / (us * 1e-6) / 1e9, 1)
+    return res
+
+
 def copy_probe(nbytes=1 << 30, reps=5):
     """Plain device-to-device copies of known size: what FETCH_SIZE / WRITE_SIZE
     read for exactly nbytes read and nbytes written per dispatch."""
@@ -209,6 +273,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--quick", action="store_true", help="decode step only, no per-workload table")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--only", default="",
+                    help="comma-separated workloads: time just these (per-workload table, no decode "
+                         "step, no CPU leg) and print their rows as JSON; for profiling runs")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run 5 copies of a 1 GiB device buffer (known bytes for counter calibration)")
     args = ap.parse_args()
@@ -231,6 +298,10 @@ def main():
     props = torch.cuda.get_device_properties(0)
     log(f"device: {props.name} ({getattr(props, 'gcnArchName', '?')}), CUs {props.multi_processor_count}, "
         f"torch {torch.__version__}, hip {torch.version.hip}")
+    if args.only:
+        rows = workload_table(torch, svq, oracle, [n for n in args.only.split(",") if n])
+        print(json.dumps({"workloads": rows}), flush=True)
+        return
 
     # ---- the decode step ----------------------------------------------------
     probs = [Problem(torch, svq, n, POOL_BYTES / len(DECODE)) for n in DECODE]
@@ -267,30 +338,16 @@ def main():
     # ---- per-workload table ------------------------------------------------------
     detail = []
     if not args.quick:
-        names = ["decode_n5120", "decode_n6144", "decode_n1024", "verify3_up", "verify3_down",
-                 "verify5_up", "verify5_down", "batch128_up", "batch128_down", "mxfp8_m1", "mxfp8_m5",
-                 "mxfp8_m128"]
-        log(f"{'workload':15s} {'kernel':22s} {'µs':>8s} {'GB/s':>8s} {'%HBM':>6s} "
-            f"{'TFLOP/s':>8s} {'%MFMA':>6s}")
-        for n in names:
-            p = Problem(torch, svq, n, POOL_BYTES)
-            p.check(oracle)
-            us = time_kernel(torch, p, launches=100, reps=3)
-            p.check(oracle)
-            w = p.w
-            gbs = algo_bytes(w) / (us * 1e-6) / 1e9
-            tfl = 2.0 * w["M"] * w["N"] * w["K"] / (us * 1e-6) / 1e12
-            row = {"workload": n, "op": w["op"], "M": w["M"], "K": w["K"], "N": w["N"], "kernel": p.kernel,
-                   "us": round(us, 3),
-                   "GBps": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
-                   "weight_GBps": round(weight_bytes(w) / (us * 1e-6) / 1e9, 1),
-                   "TFLOPs": round(tfl, 2), "mfma_frac": round(tfl / MFMA_BF16_PEAK_TFLOPS, 4)}
-            detail.append(row)
-            log(f"{n:15s} {p.kernel:22s} {us:8.2f} {gbs:8.1f} {100 * gbs / HBM_PEAK_GBS:6.1f} "
-                f"{tfl:8.2f} {100 * tfl / MFMA_BF16_PEAK_TFLOPS:6.2f}")
-            p.release()
-            del p
-            torch.cuda.empty_cache()
+        detail = workload_table(torch, svq, oracle, [
+            "decode_n5120", "decode_n6144", "decode_n1024", "verify3_up", "verify3_down", "verify5_up",
+            "verify5_down", "batch128_up", "batch128_down", "mxfp8_m1", "mxfp8_m5", "mxfp8_m128",
+            "vocab_w8_m1", "vocab_w4_m1"])
+
+    quant = None
+    if not args.quick:
+        quant = time_quantizer(torch, svq, oracle)
+        log(f"load-time RTN quantizer, bf16 [{quant['N']}, {quant['K']}]: int8 {quant['us_int8']:.1f} µs "
+            f"({quant['GBps_int8']:.1f} GB/s), int4 {quant['us_int4']:.1f} µs ({quant['GBps_int4']:.1f} GB/s)")
 
     cpu = None if args.no_cpu else cpu_baseline()
     if cpu:
@@ -318,6 +375,7 @@ def main():
                      "bytes_per_launch": algo_bytes(dom.w)},
         "cpu_baseline": cpu,
         "workloads": detail,
+        "quantizer": quant,
     }
     print(json.dumps(line), flush=True)
 

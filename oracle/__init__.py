@@ -8,7 +8,10 @@ OpenMP over output columns); every function there writes out the plain
 definition of the quantized matmul with k ascending.
 
 The load-time round-to-nearest quantizer of the vocabulary head
-(``rtn_quantize``) is written here in numpy, in fp32 arithmetic step by step.
+(``rtn_quantize``) is written here in numpy, in fp32 arithmetic step by step,
+and so are the setup-time layout steps that involve no arithmetic: projection
+fusion (``fuse_projections``, concatenation along N) and the compressed-tensors
+ingest (``ct_to_gptq``, a transpose of words and scales).
 
 Functions with no pin (see tests/test_oracle_pins.py): none -- every exported
 computation is checked against closed forms, brute force, library routines,
@@ -313,6 +316,79 @@ def q4_unrepack(tiled: np.ndarray, N: int, K: int) -> np.ndarray:
     if _load().oracle_q4_unrepack(_ptr(tiled), _ptr(out), N, K):
         raise ValueError("unrepack needs N % 16 == 0 and K % 128 == 0")
     return out
+
+
+# ---- setup-time projection fusion and compressed-tensors ingest ----------------
+
+def fuse_incompatibility(parts, bits: int, group_size: int):
+    """Why a list of quantized projections cannot be fused, or None if it can.
+
+    Eole recipe "Qwen3.8-27B and native MTP speculative decoding", section
+    "Pack inference projections": projections that read the same input are
+    packed together at setup, before the kernel repack, without requantizing;
+    pairs that do not fit keep their own projections. Read here as: same
+    weight format (bits), same K, same group size, and every width a multiple
+    of the 16-column tile of the packed layout. ``parts`` holds
+    (weights, scales) pairs in the formats of ``fuse_projections``.
+    """
+    if bits not in (4, 8):
+        return "bits must be 4 or 8"
+    if not parts:
+        return "no projections"
+    Ks, Ns = [], []
+    for w, s in parts:
+        w, s = np.asarray(w), np.asarray(s)
+        if bits == 4:
+            K, N = w.shape[0] * 8, w.shape[1]
+        else:
+            N, K = w.shape
+        if s.shape[1] != N or K % group_size or s.shape[0] != K // group_size:
+            return "scales do not match the weights or the group size"
+        Ks.append(K)
+        Ns.append(N)
+    if len(set(Ks)) != 1:
+        return "projections read inputs of different K"
+    if any(n % 16 for n in Ns):
+        return "a width is not a multiple of 16"
+    return None
+
+
+def fuse_projections(parts, bits: int, group_size: int):
+    """Concatenate quantized projections along N, in the order given.
+
+    Eole recipe, section "Pack inference projections" (K/V/Q and gate/up
+    packed before the repack, no requantization). Output column n of the
+    fused layer is column n - off_p of part p, where off_p is the sum of the
+    widths before it, so y_fused = [y_0 | y_1 | ...] exactly.
+      bits 4: GPTQ words [K/8, N_p] -> [K/8, sum N_p]   (columns appended)
+      bits 8: int8 codes [N_p, K]   -> [sum N_p, K]     (rows appended)
+      scales fp16 [K/G, N_p]       -> [K/G, sum N_p]   (columns appended)
+    """
+    why = fuse_incompatibility(parts, bits, group_size)
+    if why:
+        raise ValueError(why)
+    ws = [np.asarray(w) for w, _ in parts]
+    ss = [_c(s, np.uint16) for _, s in parts]
+    wf = np.concatenate([_c(w, np.int32) for w in ws], axis=1) if bits == 4 else \
+        np.concatenate([_c(w, np.int8) for w in ws], axis=0)
+    return wf, np.concatenate(ss, axis=1)
+
+
+def ct_to_gptq(weight_packed: np.ndarray, weight_scale: np.ndarray):
+    """Compressed-tensors W4A16 [N, K/8] words and [N, K/G] scales -> GPTQ layout.
+
+    Eole recipe, section "Compressed-tensors INT4 layout": the converter
+    transposes the packed INT4 words and the scales into the GPTQ layout and
+    does not dequantize. The words themselves are unchanged, so nibble i of
+    compressed-tensors word [n][j] is the code of row 8j + i, column n, as in
+    GPTQ word [j][n]. Returns (qweight int32 [K/8, N], scales fp16 bits
+    [K/G, N]).
+    """
+    wp = _c(weight_packed, np.int32)
+    sc = _c(weight_scale, np.uint16)
+    if wp.ndim != 2 or sc.ndim != 2 or sc.shape[0] != wp.shape[0]:
+        raise ValueError("weight_packed [N, K/8] and weight_scale [N, K/G] expected")
+    return np.ascontiguousarray(wp.T), np.ascontiguousarray(sc.T)
 
 
 # ---- the parity gate ---------------------------------------------------------

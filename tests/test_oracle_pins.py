@@ -468,3 +468,119 @@ def test_rtn_int8_bruteforce_rationals():
                 if r - k > Fraction(1, 2) or (r - k == Fraction(1, 2) and k % 2):
                     k += 1
                 assert int(q[n, 32 * g + i]) == max(-128, min(127, k)), (n, g, i)
+
+
+# ---- setup-time projection fusion and compressed-tensors ingest ---------------
+
+def _parts4(seed, K, widths, G):
+    rng = np.random.default_rng(seed)
+    parts = []
+    for n in widths:
+        q = rng.integers(0, 16, (K, n))
+        s = rng.uniform(2e-3, 2e-2, (K // G, n)).astype(np.float16).view(np.uint16)
+        parts.append((synth.pack_gptq(q), s))
+    return parts
+
+
+def test_fused_w4_columns_are_the_parts_exactly():
+    K, G, widths = 256, 64, [32, 16, 48]
+    parts = _parts4(21, K, widths, G)
+    wf, sf = oracle.fuse_projections(parts, 4, G)
+    assert wf.shape == (K // 8, sum(widths)) and sf.shape == (K // G, sum(widths))
+    xb = synth.bf16_bits(np.random.default_rng(22).standard_normal((3, K)).astype(np.float32))
+    y64, y32 = oracle.w4a16(xb, wf, sf, G)
+    off = 0
+    for (w, s), n in zip(parts, widths):
+        p64, p32 = oracle.w4a16(xb, w, s, G)
+        # each output column is its own sum: fusion changes no bit of it
+        np.testing.assert_array_equal(y64[:, off:off + n], p64)
+        np.testing.assert_array_equal(y32[:, off:off + n], p32)
+        off += n
+
+
+def test_fused_w8_columns_are_the_parts_exactly():
+    K, G, widths = 256, 32, [16, 64]
+    rng = np.random.default_rng(23)
+    parts = [(rng.integers(-128, 128, (n, K)).astype(np.int8),
+              rng.uniform(2e-4, 2e-3, (K // G, n)).astype(np.float16).view(np.uint16)) for n in widths]
+    wf, sf = oracle.fuse_projections(parts, 8, G)
+    assert wf.shape == (sum(widths), K) and wf.dtype == np.int8
+    xb = synth.bf16_bits(rng.standard_normal((2, K)).astype(np.float32))
+    y64, _ = oracle.w8a16(xb, wf, sf, G)
+    off = 0
+    for (w, s), n in zip(parts, widths):
+        np.testing.assert_array_equal(y64[:, off:off + n], oracle.w8a16(xb, w, s, G)[0])
+        off += n
+
+
+def test_fused_closed_form_and_tile_layout():
+    # part a: every code 1; part b: every code 14 -> words 0x11111111 / 0xeeeeeeee
+    K, G = 128, 128
+    a = (np.full((K // 8, 16), 0x11111111, dtype=np.uint32).view(np.int32),
+         np.full((1, 16), 0x3c00, dtype=np.uint16))
+    b = (np.full((K // 8, 32), 0xEEEEEEEE, dtype=np.uint32).view(np.int32),
+         np.full((1, 32), 0x4000, dtype=np.uint16))
+    wf, sf = oracle.fuse_projections([a, b], 4, G)
+    u = wf.view(np.uint32)
+    assert np.all(u[:, :16] == 0x11111111) and np.all(u[:, 16:] == 0xEEEEEEEE)
+    assert np.all(sf[:, :16] == 0x3c00) and np.all(sf[:, 16:] == 0x4000)
+    # x = 1: column sums are K * (q - 8) * s = 128 * -7 * 1 and 128 * 6 * 2
+    y64, _ = oracle.w4a16(synth.bf16_bits(np.ones((1, K), np.float32)), wf, sf, G)
+    np.testing.assert_array_equal(y64[0], np.r_[np.full(16, -896.0), np.full(32, 1536.0)])
+    # the tile layout is column-block-major, so fused tiles are the parts' tiles end to end
+    parts = _parts4(24, 256, [16, 48, 32], 128)
+    wf, _ = oracle.fuse_projections(parts, 4, 128)
+    np.testing.assert_array_equal(oracle.q4_repack(wf),
+                                  np.concatenate([oracle.q4_repack(w) for w, _ in parts]))
+
+
+def test_fuse_rejects_incompatible_projections():
+    p = _parts4(25, 256, [16, 32], 64)
+    assert oracle.fuse_incompatibility(p, 4, 64) is None
+    other_k = _parts4(26, 128, [16], 64)
+    assert "different K" in oracle.fuse_incompatibility(p + other_k, 4, 64)
+    odd = _parts4(27, 256, [24], 64)
+    assert "multiple of 16" in oracle.fuse_incompatibility(p + odd, 4, 64)
+    assert "group size" in oracle.fuse_incompatibility(p, 4, 128)     # scales are [K/64, N]
+    assert oracle.fuse_incompatibility(p, 5, 64) is not None
+    assert oracle.fuse_incompatibility([], 4, 64) is not None
+    with pytest.raises(ValueError):
+        oracle.fuse_projections(p + odd, 4, 64)
+
+
+def test_ct_ingest_handworked():
+    ct = np.zeros((2, 2), dtype=np.uint32)
+    sc = np.zeros((2, 1), dtype=np.uint16)
+    gq = np.zeros((2, 2), dtype=np.uint32)
+    w = np.full((16, 2), np.nan)
+    for row in _rows("ct_handworked.txt"):
+        if row[0] == "ct":
+            ct[int(row[1]), int(row[2])] = int(row[3], 16)
+        elif row[0] == "sc":
+            sc[int(row[1]), int(row[2])] = int(row[3], 16)
+        elif row[0] == "gptq":
+            gq[int(row[1]), int(row[2])] = int(row[3], 16)
+        else:
+            w[int(row[1]), int(row[2])] = float(row[3])
+    assert not np.isnan(w).any()
+    qw, s = oracle.ct_to_gptq(ct.view(np.int32), sc)
+    np.testing.assert_array_equal(qw.view(np.uint32), gq)
+    np.testing.assert_array_equal(s, sc.T)
+    deq = (oracle.q4_unpack(qw).astype(np.float64) - 8) * s.view(np.float16).astype(np.float64)
+    np.testing.assert_array_equal(deq, w)
+
+
+def test_ct_ingest_gemm_matches_the_ct_definition():
+    # dequantize straight from the [N, K/8] words (shifts along the word axis)
+    # and multiply with BLAS; the oracle GEMM on the converted tensors must agree
+    N, K, G = 48, 512, 128
+    rng = np.random.default_rng(28)
+    wp = rng.integers(0, 2 ** 32, (N, K // 8), dtype=np.uint64).astype(np.uint32)
+    ws = rng.uniform(2e-3, 2e-2, (N, K // G)).astype(np.float16)
+    q = np.stack([(wp >> np.uint32(4 * i)) & np.uint32(15) for i in range(8)], axis=2)   # [N, K/8, 8]
+    deq = (q.reshape(N, K).astype(np.float64) - 8) * np.repeat(ws.astype(np.float64), G, axis=1)
+    xb = synth.bf16_bits(rng.standard_normal((4, K)).astype(np.float32))
+    ref = oracle.bf16_bits_to_f64(xb) @ deq.T
+    qw, s = oracle.ct_to_gptq(wp.view(np.int32), ws.view(np.uint16))
+    y64, _ = oracle.w4a16(xb, qw, s, G)
+    assert np.max(np.abs(y64 - ref)) <= 1e-12 * np.sqrt(np.mean(ref ** 2))

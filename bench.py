@@ -10,7 +10,9 @@ each once) per second.
 Also reported (stderr table and the JSON line's "workloads" list): per-kernel
 time, GB/s, TFLOP/s and roofline fraction for every named workload (decode,
 M=3/5 verify chunks, M=128 batched verify, MXFP8 at M=1/5/128), and the CPU
-oracle's throughput on a bounded sample (``cpu_baseline``).
+oracle's throughput on a bounded sample (``cpu_baseline``), the fused K/V/Q and
+gate/up projections against the same projections launched one by one
+(``fusion``), and the setup-time steps (``quantizer``, ``ct_ingest``).
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--quick] [--no-cpu]
     python bench.py --copy-probe    # a plain 1 GiB device copy, to calibrate HBM counters
@@ -250,6 +252,120 @@ def time_quantizer(torch, svq, oracle, N=24832, K=5120, G=128, reps=20):
     return res
 
 
+def time_fusion(torch, svq, oracle, names):
+    """Projections fused at setup against the same projections launched one by
+    one: µs per fused GEMM and per sequence of separate GEMMs (each a graph of
+    100 steps rotating over >1 GiB of weight copies), plus the one-off fusion
+    call itself; sampled outputs of both forms are checked against the oracle
+    on the concatenated weights."""
+    dev = torch.device("cuda:0")
+
+    def d(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            a = a.view(np.int16)
+        return torch.from_numpy(a).to(dev)
+
+    rows_out = []
+    for name in names:
+        f = synth.FUSIONS[name]
+        M, K, widths = f["M"], f["K"], f["widths"]
+        Nt = sum(widths)
+        inp = synth.gen_fusion(f["seed"], M, K, widths, 128, 4)
+        parts = [(d(w), d(sc)) for w, sc in inp.parts]
+        x = d(inp.x)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        wf, sf = svq.fuse_projections(parts, 4, 128)
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(5):
+            svq.fuse_projections(parts, 4, 128, weight_fused=wf, scales_fused=sf)
+        b.record()
+        torch.cuda.synchronize()
+        us_setup = a.elapsed_time(b) * 1e3 / 5
+        wbytes = K * Nt // 2 + (K // 128) * Nt * 2
+        ncopy = max(2, int(POOL_BYTES // wbytes))
+        fused_pool = [(wf, sf)] + [(wf.clone(), sf.clone()) for _ in range(ncopy - 1)]
+        sep0 = [(svq.q4_repack(w), sc) for w, sc in parts]
+        sep_pool = [sep0] + [[(w.clone(), sc.clone()) for w, sc in sep0] for _ in range(ncopy - 1)]
+        del parts
+        out_f = torch.empty((M, Nt), dtype=torch.bfloat16, device=dev)
+        outs = [torch.empty((M, n), dtype=torch.bfloat16, device=dev) for n in widths]
+        nb = max([svq.w4a16_workspace_bytes(M, Nt, K)] + [svq.w4a16_workspace_bytes(M, n, K) for n in widths])
+        ws = torch.zeros(max(nb, 256), dtype=torch.uint8, device=dev) if nb else None
+
+        def fused(i):
+            w, sc = fused_pool[i % ncopy]
+            svq.w4a16_gemm(x, w, sc, Nt, 128, out=out_f, workspace=ws)
+
+        def separate(i):
+            for (w, sc), n, o in zip(sep_pool[i % ncopy], widths, outs):
+                svq.w4a16_gemm(x, w, sc, n, 128, out=o, workspace=ws)
+
+        wf_ref, sf_ref = oracle.fuse_projections(inp.parts, 4, 128)
+        rng = np.random.default_rng(2)
+        rr, cc = rng.integers(0, M, 256), rng.integers(0, Nt, 256)
+        y64, _ = oracle.w4a16_points(inp.x, wf_ref, sf_ref, 128, rr, cc)
+
+        def check(label):
+            for i in (0, ncopy - 1):
+                fused(i)
+                separate(i)
+                torch.cuda.synchronize()
+                yf = out_f.view(torch.int16).cpu().numpy().view(np.uint16)
+                ys = np.concatenate([o.view(torch.int16).cpu().numpy().view(np.uint16) for o in outs], axis=1)
+                for got, form in ((yf, "fused"), (ys, "separate")):
+                    ok, err, rms = oracle.gate(got[rr, cc], y64)
+                    if not ok:
+                        raise SystemExit(f"parity failure in {name} ({form}, {label}, copy {i}): err {err} rms {rms}")
+
+        check("before")
+        g = graph_of(torch, fused, 100)
+        us_f = time_graph(torch, g, 3) / 100 * 1e6
+        del g
+        g = graph_of(torch, separate, 100)
+        us_s = time_graph(torch, g, 3) / 100 * 1e6
+        del g
+        check("after")
+        ab = wbytes + 2 * M * K + 2 * M * Nt
+        gbs = ab / (us_f * 1e-6) / 1e9
+        kern = svq.w4a16_kernel_name(M, Nt, K)
+        rows_out.append({"fusion": name, "M": M, "K": K, "widths": widths, "kernel": kern,
+                         "us_fused": round(us_f, 3), "us_separate": round(us_s, 3),
+                         "speedup": round(us_s / us_f, 3), "GBps_fused": round(gbs, 1),
+                         "hbm_frac_fused": round(gbs / HBM_PEAK_GBS, 4), "us_fuse_setup": round(us_setup, 1)})
+        log(f"fusion {name:11s} {kern:22s} fused {us_f:8.2f} µs ({gbs:7.1f} GB/s, "
+            f"{100 * gbs / HBM_PEAK_GBS:4.1f}%)  separate {us_s:8.2f} µs  x{us_s / us_f:.2f}  "
+            f"(fusion call {us_setup:.1f} µs)")
+        del fused_pool, sep_pool, sep0, wf, sf, ws
+        torch.cuda.empty_cache()
+    return rows_out
+
+
+def time_ct_ingest(torch, svq, oracle, N=17408, K=5120, G=128, reps=20):
+    """The compressed-tensors ingest (a transpose of words and scales) on one
+    MLP-sized projection: µs per call and GB/s over its bytes (read + write),
+    the output checked bit for bit against the oracle."""
+    wp, ws = synth.gen_ct_w4a16(961, N, K, G)
+    d_wp = torch.from_numpy(wp).to("cuda:0")
+    d_ws = torch.from_numpy(ws.view(np.int16)).to("cuda:0")
+    qw, s = svq.ct_to_gptq(d_wp, d_ws, G)
+    torch.cuda.synchronize()
+    q_ref, s_ref = oracle.ct_to_gptq(wp, ws)
+    if not (np.array_equal(qw.cpu().numpy(), q_ref) and
+            np.array_equal(s.view(torch.int16).cpu().numpy().view(np.uint16), s_ref)):
+        raise SystemExit("compressed-tensors ingest parity failure")
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        svq.ct_to_gptq(d_wp, d_ws, G, qweight=qw, scales=s)
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / reps
+    nbytes = 2 * (N * K // 2 + N * (K // G) * 2)
+    return {"N": N, "K": K, "G": G, "us": round(us, 2), "GBps": round(nbytes / (us * 1e-6) / 1e9, 1)}
+
+
 def copy_probe(nbytes=1 << 30, reps=5):
     """Plain device-to-device copies of known size: what FETCH_SIZE / WRITE_SIZE
     read for exactly nbytes read and nbytes written per dispatch."""
@@ -299,8 +415,10 @@ def main():
     log(f"device: {props.name} ({getattr(props, 'gcnArchName', '?')}), CUs {props.multi_processor_count}, "
         f"torch {torch.__version__}, hip {torch.version.hip}")
     if args.only:
-        rows = workload_table(torch, svq, oracle, [n for n in args.only.split(",") if n])
-        print(json.dumps({"workloads": rows}), flush=True)
+        names = [n for n in args.only.split(",") if n]
+        rows = workload_table(torch, svq, oracle, [n for n in names if n in synth.WORKLOADS])
+        fus = time_fusion(torch, svq, oracle, [n for n in names if n in synth.FUSIONS])
+        print(json.dumps({"workloads": rows, "fusion": fus}), flush=True)
         return
 
     # ---- the decode step ----------------------------------------------------
@@ -349,6 +467,12 @@ def main():
         log(f"load-time RTN quantizer, bf16 [{quant['N']}, {quant['K']}]: int8 {quant['us_int8']:.1f} µs "
             f"({quant['GBps_int8']:.1f} GB/s), int4 {quant['us_int4']:.1f} µs ({quant['GBps_int4']:.1f} GB/s)")
 
+    fusion = ct = None
+    if not args.quick:
+        fusion = time_fusion(torch, svq, oracle, list(synth.FUSIONS))
+        ct = time_ct_ingest(torch, svq, oracle)
+        log(f"compressed-tensors ingest [{ct['N']}, {ct['K']}]: {ct['us']:.1f} µs ({ct['GBps']:.1f} GB/s)")
+
     cpu = None if args.no_cpu else cpu_baseline()
     if cpu:
         log(f"cpu oracle: {cpu['value']} GB/s on {cpu['cores']} threads ({cpu['sample']})")
@@ -376,6 +500,8 @@ def main():
         "cpu_baseline": cpu,
         "workloads": detail,
         "quantizer": quant,
+        "fusion": fusion,
+        "ct_ingest": ct,
     }
     print(json.dumps(line), flush=True)
 

@@ -101,6 +101,54 @@ size_t svq_q4_repacked_bytes(int64_t N, int64_t K);
 int svq_q4_repack(const int32_t *qweight_gptq, int32_t *qweight_tiled, int64_t N,
                   int64_t K, void *stream);
 
+/* Most projections svq_fuse_projections takes in one call. */
+#define SVQ_MAX_FUSED_PARTS 16
+
+/*
+ * Setup-time projection fusion: `parts` quantized projections that read the
+ * same x (same K, same format, same group size) become one projection whose
+ * output columns are the parts' columns in the order given, so a single GEMM
+ * call replaces `parts` calls and y_fused = [y_0 | y_1 | ...] (Eole recipe
+ * "Qwen3.8-27B and native MTP speculative decoding", section "Pack inference
+ * projections": K/V/Q and gate/up are packed at setup, before the repack, with
+ * no requantization; projections that do not fit stay separate -- here the
+ * call returns an error and changes nothing, and the caller keeps them).
+ *   bits 4: weights[p]   GPTQ int32 words [K/8][widths[p]], 4-byte aligned;
+ *           weight_fused the REPACKED fused weight (the svq_q4_repack layout of
+ *                        the concatenated words), K*N/2 bytes, 16-byte aligned,
+ *                        ready for svq_w4a16_gemm with N = sum of widths
+ *   bits 8: weights[p]   int8 codes [widths[p]][K], 16-byte aligned;
+ *           weight_fused int8 [N][K], 16-byte aligned (svq_w8a16_gemm input)
+ *   scales[p]     fp16 [K/G][widths[p]], 2-byte aligned
+ *   scales_fused  fp16 [K/G][N]; 4-byte aligned if it feeds a GEMM
+ *   weights, scales, widths: host arrays of `parts` entries (device pointers
+ *   and column counts), 1 <= parts <= SVQ_MAX_FUSED_PARTS, read during the
+ *   call only. Requires every width % 16 == 0, K % 128 == 0, G in {32, 64,
+ *   128}, K % G == 0. The outputs must not overlap any input or each other
+ *   (inputs may overlap one another). Reads and writes every byte once, in one
+ *   launch.
+ */
+int svq_fuse_projections(int32_t bits, const void *const *weights, const void *const *scales,
+                         const int64_t *widths, int32_t parts, int64_t K, int32_t group_size,
+                         void *weight_fused, void *scales_fused, void *stream);
+
+/*
+ * Compressed-tensors W4A16 ingest: words [N][K/8] and scales [N][K/G] become
+ * the GPTQ layout [K/8][N] and [K/G][N] by transposition, every word and scale
+ * unchanged (Eole recipe, section "Compressed-tensors INT4 layout": the
+ * converter transposes packed words and scales and does not requantize). The
+ * nibble order is the GPTQ one: nibble i of word [n][j] is the code of row
+ * 8j + i of column n.
+ *   weight_packed int32 [N][K/8], 4-byte aligned
+ *   weight_scale  fp16 [N][K/G], 2-byte aligned
+ *   qweight       int32 [K/8][N], 4-byte aligned (the svq_q4_repack input)
+ *   scales        fp16 [K/G][N], 2-byte aligned
+ *   group_size    G in {32, 64, 128}; K % G == 0 (any N >= 1)
+ * Outputs must not overlap the inputs or each other.
+ */
+int svq_ct_to_gptq(const int32_t *weight_packed, const void *weight_scale, int32_t *qweight,
+                   void *scales, int64_t N, int64_t K, int32_t group_size, void *stream);
+
 /* Workspace bytes needed by svq_w4a16_gemm (kernel = SVQ_KERNEL_AUTO) or by
  * svq_w4a16_gemm_with for the given kernel; 0 if none. (size_t)-1 if the
  * arguments are invalid or the kernel cannot run the shape. */

@@ -22,6 +22,7 @@ __all__ = [
     "lib", "library_path", "q4_repack", "w4a16_gemm", "mxfp8_gemm", "w4a16_kernel_name",
     "mxfp8_kernel_name", "w4a16_workspace_bytes", "mxfp8_workspace_bytes", "Workspace",
     "EXPORTED_SYMBOLS", "rtn_quantize", "w8a16_gemm", "w8a16_workspace_bytes", "w8a16_kernel_name",
+    "fuse_projections", "fuse_or_keep", "ct_to_gptq", "MAX_FUSED_PARTS",
 ]
 
 KERNEL_AUTO, KERNEL_DOT2, KERNEL_MFMA_SKINNY, KERNEL_MFMA_WIDE = 0, 1, 2, 3
@@ -35,7 +36,10 @@ EXPORTED_SYMBOLS = (
     "svq_w4a16_kernel_name", "svq_mxfp8_workspace_bytes", "svq_mxfp8_gemm",
     "svq_mxfp8_gemm_with", "svq_mxfp8_kernel_name", "svq_rtn_quantize",
     "svq_w8a16_workspace_bytes", "svq_w8a16_gemm", "svq_w8a16_kernel_name",
+    "svq_fuse_projections", "svq_ct_to_gptq",
 )
+
+MAX_FUSED_PARTS = 16
 
 _i64, _i32, _p, _sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t
 _lib = None
@@ -92,6 +96,10 @@ def lib():
         L.svq_w8a16_gemm.argtypes = [_p, _p, _p, _p, _i64, _i64, _i64, _i32, _p, _sz, _p]
         L.svq_w8a16_kernel_name.restype = ctypes.c_char_p
         L.svq_w8a16_kernel_name.argtypes = [_i64, _i64, _i64, _i32]
+        L.svq_fuse_projections.restype = ctypes.c_int
+        L.svq_fuse_projections.argtypes = [_i32, _p, _p, _p, _i32, _i64, _i32, _p, _p, _p]
+        L.svq_ct_to_gptq.restype = ctypes.c_int
+        L.svq_ct_to_gptq.argtypes = [_p, _p, _p, _p, _i64, _i64, _i32, _p]
         _lib = L
         return L
 
@@ -306,3 +314,93 @@ def w8a16_gemm(x, w, scales, group_size=128, out=None, workspace=None):
                                 _dev_ptr(out, "out"), M, N, K, group_size, ws_ptr, ws_bytes, stream),
            "svq_w8a16_gemm")
     return out
+
+
+# ---- setup-time projection fusion and compressed-tensors ingest --------------------
+
+def _part_shape(w, s, bits):
+    """(K, N) of one quantized projection, from its weights and fp16 scales."""
+    if bits == 4:
+        _check_elem(w, "weights", 4)
+        K, N = w.shape[0] * 8, w.shape[1]
+    else:
+        _check_elem(w, "weights", 1)
+        N, K = w.shape
+    _check_elem(s, "scales", 2)
+    return K, N
+
+
+def fuse_projections(parts, bits=4, group_size=128, weight_fused=None, scales_fused=None):
+    """Concatenate quantized projections that read the same x along N (device).
+
+    parts: [(weights, scales), ...] with GPTQ int32 words [K/8, N_p] (bits=4)
+    or int8 codes [N_p, K] (bits=8) and fp16 scales [K/G, N_p]. Returns
+    (weight_fused, scales_fused): the repacked tiles of the fused int4 weight
+    (flat int32, ready for w4a16_gemm) or int8 codes [N, K]; fp16 [K/G, N].
+    Raises SvqError if the projections cannot be fused.
+    """
+    torch = _torch()
+    if not 1 <= len(parts) <= MAX_FUSED_PARTS:
+        raise SvqError(2, "svq_fuse_projections")
+    shapes = [_part_shape(w, s, bits) for w, s in parts]
+    K = shapes[0][0]
+    if any(k != K for k, _ in shapes):
+        raise ValueError("projections with different K cannot be fused")
+    Nt = sum(n for _, n in shapes)
+    dev = parts[0][0].device
+    if weight_fused is None:
+        weight_fused = (torch.empty(K * Nt // 8, dtype=torch.int32, device=dev) if bits == 4
+                        else torch.empty((Nt, K), dtype=torch.int8, device=dev))
+    if scales_fused is None:
+        scales_fused = torch.empty((K // group_size, Nt), dtype=torch.float16, device=dev)
+    if weight_fused.numel() * weight_fused.element_size() != Nt * K * bits // 8 or \
+            scales_fused.numel() * scales_fused.element_size() != (K // group_size) * Nt * 2:
+        raise ValueError("weight_fused or scales_fused has the wrong size")
+    P = len(parts)
+    wp = (ctypes.c_void_p * P)(*[_dev_ptr(w, "weights").value for w, _ in parts])
+    sp = (ctypes.c_void_p * P)(*[_dev_ptr(s, "scales").value for _, s in parts])
+    nn = (ctypes.c_int64 * P)(*[n for _, n in shapes])
+    _check(lib().svq_fuse_projections(bits, wp, sp, nn, P, K, group_size,
+                                      _dev_ptr(weight_fused, "weight_fused"),
+                                      _dev_ptr(scales_fused, "scales_fused"),
+                                      _stream_ptr(parts[0][0])), "svq_fuse_projections")
+    return weight_fused, scales_fused
+
+
+def fuse_or_keep(parts, bits=4, group_size=128):
+    """fuse_projections, or None with a warning when the projections do not fit.
+
+    Projections that cannot be fused (different K, a width that is not a
+    multiple of 16, scales of another group size) keep their own weights: the
+    caller then runs one GEMM per projection.
+    """
+    import warnings
+    try:
+        return fuse_projections(parts, bits, group_size)
+    except (SvqError, ValueError) as e:
+        warnings.warn(f"projections not fused, kept separate: {e}", RuntimeWarning, stacklevel=2)
+        return None
+
+
+def ct_to_gptq(weight_packed, weight_scale, group_size=128, qweight=None, scales=None):
+    """Compressed-tensors int32 [N, K/8] words and fp16 [N, K/G] scales (device)
+    -> GPTQ int32 [K/8, N] and fp16 [K/G, N] (a transpose; no value changes)."""
+    torch = _torch()
+    N, K8 = weight_packed.shape
+    K = K8 * 8
+    _check_elem(weight_packed, "weight_packed", 4)
+    _check_elem(weight_scale, "weight_scale", 2)
+    if tuple(weight_scale.shape) != (N, K // group_size):
+        raise ValueError(f"weight_scale must have shape {(N, K // group_size)}")
+    if qweight is None:
+        qweight = torch.empty((K8, N), dtype=torch.int32, device=weight_packed.device)
+    if scales is None:
+        scales = torch.empty((K // group_size, N), dtype=torch.float16, device=weight_packed.device)
+    _check_elem(qweight, "qweight", 4)
+    _check_elem(scales, "scales", 2)
+    if qweight.numel() != K8 * N or scales.numel() != (K // group_size) * N:
+        raise ValueError("qweight or scales has the wrong size")
+    _check(lib().svq_ct_to_gptq(_dev_ptr(weight_packed, "weight_packed"), _dev_ptr(weight_scale, "weight_scale"),
+                                _dev_ptr(qweight, "qweight"), _dev_ptr(scales, "scales"), N, K, group_size,
+                                _stream_ptr(weight_packed)), "svq_ct_to_gptq")
+    return qweight, scales

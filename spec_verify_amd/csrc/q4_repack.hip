@@ -1,5 +1,5 @@
-// One-time repack of GPTQ INT4 words into the 16-column x 128-row tile layout
-// read by the W4A16 kernels. A pure bit permutation: each GPTQ word [j][n]
+// Setup-time layout kernels. One-time repack of GPTQ INT4 words into the
+// 16-column x 128-row tile layout read by the W4A16 kernels. A pure bit permutation: each GPTQ word [j][n]
 // (rows 8j..8j+7 of column n) becomes exactly one tile word, with its nibbles
 // reordered so that rows (2s, 2s+1) land in nibble slots (s, s+4).
 // The Eole recipe "Qwen3.8-27B and native MTP speculative decoding" repacks
@@ -42,6 +42,111 @@ hipError_t launch_q4_repack(const int32_t *src, int32_t *dst, int64_t N, int64_t
     const int64_t blocks = (total + 255) / 256;
     hipLaunchKernelGGL(q4_repack_kernel, dim3((uint32_t)blocks), dim3(256), 0, stream,
                        (const uint32_t *)src, (uint32_t *)dst, N, K / 8, K / 128);
+    return hipGetLastError();
+}
+
+// ---- projection fusion at setup ----------------------------------------------
+// Projections that read the same x are concatenated along N before the repack
+// (Eole recipe, section "Pack inference projections"; no requantization). Part p
+// covers fused columns [col_off[p], col_off[p+1]). Because the tile layout is
+// column-block-major and every width is a multiple of 16, part p's tiles are
+// its own repack placed at word col_off[p]*K/8; its scales are columns
+// col_off[p].. of the fused [K/G][N] array. One launch covers all parts: part p
+// owns workgroups [blk_off[p], blk_off[p+1]), one thread per GPTQ word (int4)
+// or per 16 bytes of int8 codes, the threads below (K/G)*N_p also moving one
+// scale each.
+struct FuseTable {
+    const void *w[kMaxFuseParts];
+    const uint16_t *s[kMaxFuseParts];
+    int64_t col_off[kMaxFuseParts + 1];
+    int64_t blk_off[kMaxFuseParts + 1];
+    int parts;
+};
+
+template <int BITS>
+__global__ __launch_bounds__(256) void fuse_pack_kernel(FuseTable t, void *__restrict__ dst_w,
+                                                        uint16_t *__restrict__ dst_s, int64_t K,
+                                                        int G) {
+    const int64_t b = blockIdx.x;
+    int p = 0;
+    while (p + 1 < t.parts && b >= t.blk_off[p + 1]) ++p;   // wave-uniform
+    const int64_t n0 = t.col_off[p], Np = t.col_off[p + 1] - n0, Nt = t.col_off[t.parts];
+    const int64_t idx = (b - t.blk_off[p]) * 256 + threadIdx.x;
+    if (BITS == 4) {
+        const int64_t K8 = K / 8, KT = K / 128;
+        if (idx < K8 * Np) {
+            const int64_t j = idx / Np, n = idx - j * Np;
+            const int64_t nf = n0 + n, r = j & 15, kt = j >> 4;
+            const int64_t lane = (r >> 2) * 16 + (nf & 15);
+            const int64_t w = (((nf >> 4) * KT + kt) * 64 + lane) * 4 + (r & 3);
+            ((uint32_t *)dst_w)[w] = gptq_to_slot_order(((const uint32_t *)t.w[p])[idx]);
+        }
+    } else {
+        if (idx < Np * (K / 16))
+            ((uint4 *)dst_w)[n0 * (K / 16) + idx] = ((const uint4 *)t.w[p])[idx];
+    }
+    if (idx < (K / G) * Np) {
+        const int64_t g = idx / Np, n = idx - g * Np;
+        dst_s[g * Nt + n0 + n] = t.s[p][idx];
+    }
+}
+
+hipError_t launch_fuse_pack(int bits, const void *const *w, const void *const *s,
+                            const int64_t *widths, int parts, int64_t K, int G, void *dst_w,
+                            void *dst_s, hipStream_t stream) {
+    FuseTable t{};
+    t.parts = parts;
+    t.col_off[0] = t.blk_off[0] = 0;
+    for (int p = 0; p < parts; ++p) {
+        t.w[p] = w[p];
+        t.s[p] = (const uint16_t *)s[p];
+        const int64_t items = bits == 4 ? (K / 8) * widths[p] : widths[p] * (K / 16);
+        t.col_off[p + 1] = t.col_off[p] + widths[p];
+        t.blk_off[p + 1] = t.blk_off[p] + (items + 255) / 256;
+    }
+    const dim3 grid((uint32_t)t.blk_off[parts]);
+    if (bits == 4)
+        hipLaunchKernelGGL(fuse_pack_kernel<4>, grid, dim3(256), 0, stream, t, dst_w,
+                           (uint16_t *)dst_s, K, G);
+    else
+        hipLaunchKernelGGL(fuse_pack_kernel<8>, grid, dim3(256), 0, stream, t, dst_w,
+                           (uint16_t *)dst_s, K, G);
+    return hipGetLastError();
+}
+
+// ---- compressed-tensors ingest -----------------------------------------------
+// Compressed-tensors stores a W4A16 projection as words [N][K/8] and scales
+// [N][K/G]; the GPTQ layout is their transpose, with each word unchanged (Eole
+// recipe, section "Compressed-tensors INT4 layout"). A 64 x 64 tile transpose
+// through LDS: reads run along a source row, writes along a destination row,
+// and the padded LDS rows keep both phases free of bank conflicts.
+template <typename T>
+__global__ __launch_bounds__(256) void transpose_kernel(const T *__restrict__ src,
+                                                        T *__restrict__ dst, int64_t rows,
+                                                        int64_t cols) {
+    __shared__ uint32_t tile[64][65];
+    const int64_t r0 = (int64_t)blockIdx.x * 64, c0 = (int64_t)blockIdx.y * 64;
+    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+    for (int i = ty; i < 64; i += 4) {
+        const int64_t r = r0 + i, c = c0 + tx;
+        if (r < rows && c < cols) tile[i][tx] = (uint32_t)src[r * cols + c];
+    }
+    __syncthreads();
+    for (int i = ty; i < 64; i += 4) {
+        const int64_t c = c0 + i, r = r0 + tx;
+        if (c < cols && r < rows) dst[c * rows + r] = (T)tile[tx][i];
+    }
+}
+
+hipError_t launch_ct_to_gptq(const int32_t *wp, const void *ws, int32_t *qw, void *s, int64_t N,
+                             int64_t K, int G, hipStream_t stream) {
+    const int64_t K8 = K / 8, KG = K / G;
+    hipLaunchKernelGGL(transpose_kernel<uint32_t>, dim3((uint32_t)((N + 63) / 64), (uint32_t)((K8 + 63) / 64)),
+                       dim3(256), 0, stream, (const uint32_t *)wp, (uint32_t *)qw, N, K8);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(transpose_kernel<uint16_t>, dim3((uint32_t)((N + 63) / 64), (uint32_t)((KG + 63) / 64)),
+                       dim3(256), 0, stream, (const uint16_t *)ws, (uint16_t *)s, N, KG);
     return hipGetLastError();
 }
 

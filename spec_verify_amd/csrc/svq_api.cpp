@@ -213,6 +213,65 @@ int svq_q4_repack(const int32_t *src, int32_t *dst, int64_t N, int64_t K, void *
     return SVQ_OK;
 }
 
+static_assert(SVQ_MAX_FUSED_PARTS == kMaxFuseParts, "fusion table size");
+
+int svq_fuse_projections(int32_t bits, const void *const *weights, const void *const *scales,
+                         const int64_t *widths, int32_t parts, int64_t K, int32_t G,
+                         void *weight_fused, void *scales_fused, void *stream) {
+    if (!weights || !scales || !widths || !weight_fused || !scales_fused) return SVQ_ERR_NULL;
+    if (bits != 4 && bits != 8) return SVQ_ERR_UNSUPPORTED;
+    if (parts < 1 || parts > kMaxFuseParts || K <= 0 || K > kMaxDim) return SVQ_ERR_DIM;
+    int64_t Nt = 0;
+    for (int p = 0; p < parts; ++p) {
+        if (!weights[p] || !scales[p]) return SVQ_ERR_NULL;
+        if (widths[p] <= 0 || widths[p] > kMaxDim) return SVQ_ERR_DIM;
+        Nt += widths[p];
+    }
+    if (Nt > kMaxDim || Nt * K > (int64_t(1) << 40)) return SVQ_ERR_DIM;
+    if (G != 32 && G != 64 && G != 128) return SVQ_ERR_GROUP;
+    if (K % 128 || K % G) return SVQ_ERR_DIVISIBILITY;
+    for (int p = 0; p < parts; ++p)
+        if (widths[p] % 16) return SVQ_ERR_DIVISIBILITY;
+    const uintptr_t wa = bits == 4 ? 4 : 16;
+    if (!aligned(weight_fused, 16) || !aligned(scales_fused, 2)) return SVQ_ERR_ALIGN;
+    for (int p = 0; p < parts; ++p)
+        if (!aligned(weights[p], wa) || !aligned(scales[p], 2)) return SVQ_ERR_ALIGN;
+    const size_t wf_bytes = (size_t)Nt * (size_t)K * (size_t)bits / 8;
+    const size_t sf_bytes = (size_t)Nt * (size_t)(K / G) * 2;
+    if (overlap(weight_fused, wf_bytes, scales_fused, sf_bytes)) return SVQ_ERR_OVERLAP;
+    for (int p = 0; p < parts; ++p) {
+        const size_t wb = (size_t)widths[p] * (size_t)K * (size_t)bits / 8;
+        const size_t sb = (size_t)widths[p] * (size_t)(K / G) * 2;
+        if (overlap(weight_fused, wf_bytes, weights[p], wb) || overlap(weight_fused, wf_bytes, scales[p], sb) ||
+            overlap(scales_fused, sf_bytes, weights[p], wb) || overlap(scales_fused, sf_bytes, scales[p], sb))
+            return SVQ_ERR_OVERLAP;
+    }
+    if (launch_fuse_pack(bits, weights, scales, widths, parts, K, G, weight_fused, scales_fused,
+                         (hipStream_t)stream) != hipSuccess)
+        return SVQ_ERR_HIP;
+    return SVQ_OK;
+}
+
+int svq_ct_to_gptq(const int32_t *weight_packed, const void *weight_scale, int32_t *qweight,
+                   void *scales, int64_t N, int64_t K, int32_t G, void *stream) {
+    if (!weight_packed || !weight_scale || !qweight || !scales) return SVQ_ERR_NULL;
+    if (N <= 0 || K <= 0 || N > kMaxDim || K > kMaxDim || N * K > (int64_t(1) << 40)) return SVQ_ERR_DIM;
+    if (G != 32 && G != 64 && G != 128) return SVQ_ERR_GROUP;
+    if (K % G) return SVQ_ERR_DIVISIBILITY;
+    if (!aligned(weight_packed, 4) || !aligned(qweight, 4) || !aligned(weight_scale, 2) ||
+        !aligned(scales, 2))
+        return SVQ_ERR_ALIGN;
+    const size_t wb = (size_t)N * (size_t)K / 2, sb = (size_t)N * (size_t)(K / G) * 2;
+    if (overlap(qweight, wb, weight_packed, wb) || overlap(qweight, wb, weight_scale, sb) ||
+        overlap(scales, sb, weight_packed, wb) || overlap(scales, sb, weight_scale, sb) ||
+        overlap(qweight, wb, scales, sb))
+        return SVQ_ERR_OVERLAP;
+    if (launch_ct_to_gptq(weight_packed, weight_scale, qweight, scales, N, K, G,
+                          (hipStream_t)stream) != hipSuccess)
+        return SVQ_ERR_HIP;
+    return SVQ_OK;
+}
+
 namespace {
 // the skinny kernel stages its x range in LDS, which bounds its K range
 SmallPlan w4a16_small_plan(int k, int64_t M, int64_t N, int64_t K, int cus) {

@@ -13,6 +13,16 @@ namespace svq {
 hipError_t launch_q4_repack(const int32_t *src, int32_t *dst, int64_t N, int64_t K,
                             hipStream_t stream);
 
+// Setup-time projection fusion (bits 4: GPTQ words -> fused tiles; bits 8: int8
+// codes [N_p][K] -> [sum N_p][K]) and fp16 scale concatenation, one launch.
+constexpr int kMaxFuseParts = 16;
+hipError_t launch_fuse_pack(int bits, const void *const *w, const void *const *s,
+                            const int64_t *widths, int parts, int64_t K, int G, void *dst_w,
+                            void *dst_s, hipStream_t stream);
+// Compressed-tensors [N][K/8] words and [N][K/G] scales -> GPTQ [K/8][N], [K/G][N].
+hipError_t launch_ct_to_gptq(const int32_t *wp, const void *ws, int32_t *qw, void *s, int64_t N,
+                             int64_t K, int G, hipStream_t stream);
+
 // Stream-K schedule of the wide MFMA kernels: output tiles of bm x bn, `units`
 // = row_tiles * col_tiles * (K/128) (tile, 128-row step) pairs split evenly over
 // `grid` persistent workgroups; a workgroup touches at most `maxt` tiles.

@@ -41,7 +41,7 @@ import numpy as np
 __all__ = [
     "bf16_bits", "fp16_bits", "pack_gptq", "e4m3_encode_rne", "mxfp8_quantize_rtn",
     "gen_w4a16", "gen_mxfp8", "gen_w8a16", "gen_dense_bf16", "W4A16Inputs", "MXFP8Inputs",
-    "W8A16Inputs", "WORKLOADS", "sha256",
+    "W8A16Inputs", "WORKLOADS", "sha256", "FusionInputs", "gen_fusion", "gen_ct_w4a16", "FUSIONS",
 ]
 
 
@@ -241,6 +241,58 @@ def gen_dense_bf16(seed: int, N: int, K: int, std: float = 0.02) -> np.ndarray:
     """Seeded dense weights [N, K] ~ N(0, std^2) as bf16 bits (input of the quantizer)."""
     rng = np.random.default_rng(seed)
     return bf16_bits(rng.standard_normal((N, K), dtype=np.float32) * np.float32(std))
+
+
+@dataclass
+class FusionInputs:
+    M: int
+    K: int
+    G: int
+    bits: int
+    widths: list
+    x: np.ndarray        # uint16 bf16 bits [M, K]
+    parts: list          # [(weights, scales)]: GPTQ words [K/8, N_p] or int8 [N_p, K]; fp16 bits [K/G, N_p]
+
+
+def gen_fusion(seed: int, M: int, K: int, widths, G: int = 128, bits: int = 4,
+               kind: str = "random") -> FusionInputs:
+    """Seeded projections that share one x, each drawn like gen_w4a16 / gen_w8a16."""
+    rng = np.random.default_rng(seed)
+    x = _x(rng, M, K, kind)
+    parts = []
+    for n in widths:
+        if bits == 4:
+            w = pack_gptq(rng.integers(0, 16, size=(K, n), dtype=np.uint8))
+            lo, hi = 0.002, 0.02
+        else:
+            w = rng.integers(-128, 128, size=(n, K), dtype=np.int8)
+            lo, hi = 2e-4, 2e-3
+        if kind == "intexact":
+            sc = fp16_bits(np.ones((K // G, n), dtype=np.float32))
+        else:
+            sc = fp16_bits(rng.uniform(lo, hi, size=(K // G, n)).astype(np.float32))
+        parts.append((w, sc))
+    return FusionInputs(M, K, G, bits, list(widths), x, parts)
+
+
+def gen_ct_w4a16(seed: int, N: int, K: int, G: int = 128):
+    """Seeded compressed-tensors W4A16 tensors: uniformly random int32 words
+    [N, K/8] (every nibble U{0..15}) and fp16 scales [N, K/G] ~ U[0.002, 0.02]."""
+    rng = np.random.default_rng(seed)
+    words = rng.integers(0, 2 ** 32, size=(N, K // 8), dtype=np.uint64).astype(np.uint32).view(np.int32)
+    sc = fp16_bits(rng.uniform(0.002, 0.02, size=(N, K // G)).astype(np.float32))
+    return words, sc
+
+
+# Projections fused at setup: K/V/Q of attention (K and V 4 x 256 wide, Q 24 x 256,
+# the head counts of the GPTQ card's "Model facts" with head_dim 256) and the MLP's
+# gate and up (two 17408-wide halves), at decode (M=1) and verify (M=5) sizes.
+FUSIONS = {
+    "kvq_m1":     dict(M=1, K=5120, widths=[1024, 1024, 6144], seed=701),
+    "kvq_m5":     dict(M=5, K=5120, widths=[1024, 1024, 6144], seed=702),
+    "gate_up_m1": dict(M=1, K=5120, widths=[17408, 17408], seed=703),
+    "gate_up_m5": dict(M=5, K=5120, widths=[17408, 17408], seed=704),
+}
 
 
 # Named workloads: single-stream decode (M=1), MTP verify chunks (M = 1 + drafts),

@@ -161,6 +161,54 @@ def test_rtn_quantize_validation(L):
     assert q(s=FAKE2 + 4096) == 7              # scales overlap codes
 
 
+def test_fuse_projections_validation(L):
+    P = ctypes.c_void_p
+
+    def f(bits=4, ws=(FAKE, FAKE + 65536), ss=(FAKE2, FAKE2 + 65536), widths=(256, 256), parts=None,
+          K=512, G=128, wf=FAKE3, sf=FAKE4):
+        n = (len(widths) if widths is not None else 2) if parts is None else parts
+        wa = (P * max(len(ws), 1))(*ws) if ws is not None else None
+        sa = (P * max(len(ss), 1))(*ss) if ss is not None else None
+        na = (ctypes.c_int64 * max(len(widths), 1))(*widths) if widths is not None else None
+        return L.svq_fuse_projections(bits, wa, sa, na, n, K, G, wf, sf, None)
+
+    assert f(ws=None) == 1
+    assert f(widths=None) == 1
+    assert f(wf=None) == 1
+    assert f(ws=(FAKE, None)) == 1
+    assert f(bits=2) == 10
+    assert f(parts=0) == 2
+    assert f(parts=17, ws=(FAKE,) * 17, ss=(FAKE2,) * 17, widths=(16,) * 17) == 2
+    assert f(widths=(256, 0)) == 2
+    assert f(K=0) == 2
+    assert f(widths=(1 << 24, 16)) == 2            # the fused width is out of range
+    assert f(G=16) == 3
+    assert f(K=96, G=32) == 4                       # K % 128
+    assert f(widths=(256, 24)) == 4                 # a width that is not a multiple of 16
+    assert f(ws=(FAKE + 2, FAKE + 65536)) == 6      # GPTQ words are read as 32-bit values
+    assert f(bits=8, ws=(FAKE + 4, FAKE + 65536)) == 6   # int8 codes are moved 16 bytes at a time
+    assert f(wf=FAKE3 + 4) == 6
+    assert f(ss=(FAKE2 + 1, FAKE2 + 65536)) == 6
+    assert f(wf=FAKE + 4096) == 7                   # output overlaps a part's weights
+    assert f(sf=FAKE2 + 65536 + 64) == 7            # scales output overlaps a part's scales
+    assert f(sf=FAKE3 + 1024) == 7                  # the two outputs overlap
+
+
+def test_ct_to_gptq_validation(L):
+    def c(wp=FAKE, ws=FAKE2, qw=FAKE3, s=FAKE4, N=100, K=512, G=128):
+        return L.svq_ct_to_gptq(wp, ws, qw, s, N, K, G, None)
+    assert c(wp=None) == 1
+    assert c(s=None) == 1
+    assert c(N=0) == 2
+    assert c(K=1 << 25) == 2
+    assert c(G=8) == 3
+    assert c(K=96, G=64) == 4
+    assert c(wp=FAKE + 2) == 6
+    assert c(s=FAKE4 + 1) == 6
+    assert c(qw=FAKE + 64) == 7
+    assert c(s=FAKE3 + 64) == 7
+
+
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     import spec_verify_amd as svq
     monkeypatch.setattr(svq, "_lib", None)

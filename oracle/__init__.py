@@ -318,6 +318,84 @@ def q4_unrepack(tiled: np.ndarray, N: int, K: int) -> np.ndarray:
     return out
 
 
+# ---- MXFP8 quantizer: plain and optimized round-to-nearest ---------------------
+
+def e4m3_nearest(a) -> np.ndarray:
+    """Non-negative fp32 magnitudes -> E4M3FN magnitude codes 0..0x7E: the
+    nearest finite E4M3 value, ties to the even code, everything at or above
+    448 saturating to 448 (the largest finite value)."""
+    vals = e4m3_table()[:0x7F]                       # codes 0..0x7E, ascending values
+    a = np.asarray(a, dtype=np.float64)
+    hi = np.clip(np.searchsorted(vals, a, side="left"), 1, 0x7E)
+    lo = hi - 1
+    dl, dh = a - vals[lo], vals[hi] - a
+    pick_hi = (dh < dl) | ((dh == dl) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo)
+    code = np.where(a >= vals[0x7E], 0x7E, code)
+    return code.astype(np.uint8)
+
+
+def mxfp8_quantize(w_bits: np.ndarray, optimized: bool = True, return_choice: bool = False):
+    """MXFP8 quantization of a dense bf16 weight [N, K], blocks of 32 along K.
+
+    MXFP8 card "Qwen3.8-27B-MXFP8-CT-AutoRound-mtp": plain RTN to E4M3 with one
+    E8M0 scale per 32 elements (opening summary), and the optimized RTN of the
+    section on the quantizer's behaviours: per block the baseline E8M0 scale
+    and the candidates twice and half as large are evaluated and the best one
+    is kept. Baseline (OCP MX conversion rule): amax = max |v|, X0 =
+    floor(log2 amax) - 8, b0 = clamp(X0 + 127, 0, 254); an all-zero block gets
+    b0 = 127. Candidates, in this order: b0, b0 + 1, b0 - 1 (those within
+    0..254). For a candidate b with X = b - 127, each code is E4M3_RNE(v / 2^X)
+    with the sign of v, saturating at 448, and its error is the squared
+    difference between v and the decoded value c * 2^X, summed over the 32
+    elements in ascending order in fp32. A later candidate replaces the kept
+    one only with a strictly smaller error. optimized=False keeps b0.
+    Returns (codes uint8 [N, K], scales uint8 [N, K/32]) and, with
+    return_choice, the index of the kept candidate per block (0, 1, 2).
+    """
+    w_bits = _c(w_bits, np.uint16)
+    N, K = w_bits.shape
+    if K % 32:
+        raise ValueError("K must be a multiple of 32")
+    W = ((w_bits.astype(np.uint32) << 16).view(np.float32)).reshape(N, K // 32, 32)
+    A = np.abs(W)
+    amax = A.max(axis=2)
+    _, ex = np.frexp(np.where(amax > 0, amax, np.float32(1)).astype(np.float64))
+    b0 = np.where(amax > 0, np.clip((ex - 1) - 8 + 127, 0, 254), 127).astype(np.int64)
+    table = e4m3_table()
+    sign = np.signbit(W)
+
+    def candidate(b):
+        X = (b - 127)[:, :, None]
+        scaled = np.ldexp(A, -X).astype(np.float32)               # exact power-of-two step
+        mag = e4m3_nearest(scaled)
+        d = np.ldexp(table[mag], X).astype(np.float32)            # decoded magnitude, exact
+        d = np.where(sign, -d, d).astype(np.float32)
+        diff = (W - d).astype(np.float32)
+        sq = (diff * diff).astype(np.float32)
+        err = np.zeros((N, K // 32), dtype=np.float32)
+        for i in range(32):
+            err = (err + sq[:, :, i]).astype(np.float32)
+        codes = (mag | (sign.astype(np.uint8) << np.uint8(7))).astype(np.uint8)
+        return codes, err
+
+    best_codes, best_err = candidate(b0)
+    best_b = b0.copy()
+    choice = np.zeros_like(b0)
+    if optimized:
+        for k, step in ((1, 1), (2, -1)):
+            b = b0 + step
+            ok = (b >= 0) & (b <= 254)
+            codes, err = candidate(np.clip(b, 0, 254))
+            take = ok & (err < best_err)
+            best_codes = np.where(take[:, :, None], codes, best_codes)
+            best_err = np.where(take, err, best_err)
+            best_b = np.where(take, b, best_b)
+            choice = np.where(take, k, choice)
+    out = (best_codes.reshape(N, K), best_b.astype(np.uint8))
+    return out + (choice,) if return_choice else out
+
+
 # ---- setup-time projection fusion and compressed-tensors ingest ----------------
 
 def fuse_incompatibility(parts, bits: int, group_size: int):

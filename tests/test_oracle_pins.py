@@ -584,3 +584,124 @@ def test_ct_ingest_gemm_matches_the_ct_definition():
     qw, s = oracle.ct_to_gptq(wp.view(np.int32), ws.view(np.uint16))
     y64, _ = oracle.w4a16(xb, qw, s, G)
     assert np.max(np.abs(y64 - ref)) <= 1e-12 * np.sqrt(np.mean(ref ** 2))
+
+
+# ---- MXFP8 quantizer (plain and optimized round-to-nearest) -------------------
+
+def test_e4m3_nearest_against_torch_and_the_generator_encoder():
+    torch = pytest.importorskip("torch")
+    u = np.arange(0x10000, dtype=np.uint32)
+    f = ((u << 16).view(np.float32))
+    f = f[np.isfinite(f)]
+    a = np.abs(f)
+    got = oracle.e4m3_nearest(a)
+    inr = a <= 448
+    ref = torch.from_numpy(a[inr]).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(got[inr], ref)
+    assert np.all(got[~inr] == 0x7E)
+    np.testing.assert_array_equal(got, synth.e4m3_encode_rne(a) & 0x7F)
+
+
+def test_mxfp8_plain_matches_the_generator_rtn():
+    W = (np.random.default_rng(50).standard_normal((8, 512)) * np.float32(0.05)).astype(np.float32)
+    W[0, :32] = 0
+    W[1, 32:64] *= 1e-30
+    wb = synth.bf16_bits(W)
+    c, s = oracle.mxfp8_quantize(wb, optimized=False)
+    c2, s2 = synth.mxfp8_quantize_rtn(oracle.bf16_bits_to_f64(wb).astype(np.float32))
+    np.testing.assert_array_equal(c, c2)
+    np.testing.assert_array_equal(s, s2)
+
+
+def test_mxfp8_optimized_rtn_handworked_cases():
+    n = 0
+    for _, name, opt, scale, kept, vals, codes in _rows("mxfp8_optrtn_handworked.txt"):
+        v = np.zeros(32, dtype=np.float32)
+        vv = [float(t) for t in vals.split(",")]
+        v[:len(vv)] = vv
+        wb = synth.bf16_bits(v).reshape(1, 32)
+        assert np.array_equal(oracle.bf16_bits_to_f64(wb).ravel(), v.astype(np.float64)), name
+        c, s, ch = oracle.mxfp8_quantize(wb, optimized=bool(int(opt)), return_choice=True)
+        want = np.zeros(32, dtype=np.uint8)
+        cc = [int(t, 16) for t in codes.split(",")]
+        want[:len(cc)] = cc
+        assert int(s[0, 0]) == int(scale) and int(ch[0, 0]) == int(kept), name
+        np.testing.assert_array_equal(c[0], want, err_msg=name)
+        n += 1
+    assert n == 8
+
+
+def _exact_block(vals, b):
+    """Exact rational E4M3 codes and squared error of one block at E8M0 code b:
+    every finite magnitude is scanned, ties go to the even code."""
+    mags = [Fraction(oracle.e4m3_to_f64(c)) for c in range(0x7F)]
+    scale = Fraction(2) ** (b - 127)
+    codes, err = [], Fraction(0)
+    for v in vals:
+        a = abs(v) / scale
+        best = None
+        for c, m in enumerate(mags):
+            d = abs(a - m)
+            if best is None or d < best[0] or (d == best[0] and c % 2 == 0):
+                best = (d, c)
+        c = best[1]
+        dec = mags[c] * scale * (-1 if v < 0 else 1)
+        codes.append(c | (0x80 if v < 0 else 0))
+        err += (v - dec) ** 2
+    return codes, err
+
+
+def test_mxfp8_optimized_rtn_exact_rational_bruteforce():
+    rng = np.random.default_rng(51)
+    W = (rng.standard_normal((2, 8 * 32)) * 0.03).astype(np.float32)
+    # force a few blocks to saturate at the baseline scale: amax / 2^X0 in (448, 512)
+    for blk in (1, 4, 6, 9, 13):
+        r, k = divmod(blk, 8)
+        seg = W[r, 32 * k:32 * k + 32]
+        X0 = math.floor(math.log2(float(np.abs(seg).max()))) - 8
+        seg[int(np.argmax(np.abs(seg)))] = np.float32(rng.uniform(452, 510) * 2.0 ** X0)
+    wb = synth.bf16_bits(W)
+    c, s, ch = oracle.mxfp8_quantize(wb, optimized=True, return_choice=True)
+    vals = oracle.bf16_bits_to_f64(wb)
+    chosen = 0
+    for r in range(2):
+        for k in range(8):
+            blk = [Fraction(float(t)) for t in vals[r, 32 * k:32 * k + 32]]
+            amax = max(abs(t) for t in blk)
+            b0 = min(max(math.floor(math.log2(amax)) - 8 + 127, 0), 254)
+            cands = [_exact_block(blk, b) for b in (b0, b0 + 1, b0 - 1)]
+            i = int(ch[r, k])
+            best = min(e for _, e in cands)
+            # the kept candidate is the exact minimum, up to fp32 rounding of the sums
+            assert cands[i][1] <= best * (1 + Fraction(1, 10 ** 6)), (r, k, i)
+            assert int(s[r, k]) == (b0, b0 + 1, b0 - 1)[i]
+            assert list(c[r, 32 * k:32 * k + 32]) == cands[i][0], (r, k)
+            chosen += i == 1
+    assert chosen >= 4
+
+
+def test_mxfp8_optimized_rtn_invariants():
+    rng = np.random.default_rng(52)
+    W = (rng.standard_normal((64, 1024)) * 0.02).astype(np.float32)
+    wb = synth.bf16_bits(W)
+    cp, sp = oracle.mxfp8_quantize(wb, optimized=False)
+    co, so, ch = oracle.mxfp8_quantize(wb, optimized=True, return_choice=True)
+    tab = oracle.e4m3_table()
+    Wf = oracle.bf16_bits_to_f64(wb).reshape(64, 32, 32)
+
+    def blk_err(c, s):
+        d = tab[c].reshape(64, 32, 32) * np.ldexp(1.0, s.astype(np.int64) - 127)[:, :, None]
+        return ((Wf - d) ** 2).sum(axis=2)
+    ep, eo = blk_err(cp, sp), blk_err(co, so)
+    assert np.all(eo <= ep * (1 + 1e-6))
+    # half the baseline scale saturates the block maximum, so it is never kept
+    assert not np.any(ch == 2)
+    # twice the scale is kept only where the baseline saturates an element
+    X0 = sp.astype(np.int64) - 127
+    sat = np.abs(Wf).max(axis=2) / np.ldexp(1.0, X0) > 448
+    assert np.all(sat[ch == 1]) and np.any(ch == 1)
+    np.testing.assert_array_equal(so, np.where(ch == 1, sp + 1, sp))
+    # a power-of-two factor moves only the scales
+    c8, s8 = oracle.mxfp8_quantize(synth.bf16_bits(W * np.float32(2.0 ** 5)), optimized=True)
+    np.testing.assert_array_equal(c8, co)
+    np.testing.assert_array_equal(s8.astype(np.int64), so.astype(np.int64) + 5)

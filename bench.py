@@ -12,7 +12,8 @@ time, GB/s, TFLOP/s and roofline fraction for every named workload (decode,
 M=3/5 verify chunks, M=128 batched verify, MXFP8 at M=1/5/128), and the CPU
 oracle's throughput on a bounded sample (``cpu_baseline``), the fused K/V/Q and
 gate/up projections against the same projections launched one by one
-(``fusion``), and the setup-time steps (``quantizer``, ``ct_ingest``).
+(``fusion``), and the setup-time steps (``quantizer``, ``ct_ingest``,
+``mxfp8_quantizer``).
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--quick] [--no-cpu]
     python bench.py --copy-probe    # a plain 1 GiB device copy, to calibrate HBM counters
@@ -342,6 +343,37 @@ def time_fusion(torch, svq, oracle, names):
     return rows_out
 
 
+def time_mxfp8_quantizer(torch, svq, oracle, N=17408, K=5120, reps=10):
+    """The MXFP8 quantizer (plain and optimized round-to-nearest) on one
+    MLP-sized projection, bf16 [N, K]: µs per call, GB/s over its bytes (bf16
+    read, codes and scales written) and the share of blocks that keep the
+    doubled scale; sampled rows are checked bit for bit against the oracle."""
+    wb = synth.gen_dense_bf16(962, N, K)
+    w = torch.from_numpy(wb.view(np.int16)).to("cuda:0")
+    res = {"N": N, "K": K}
+    rows = np.arange(0, N, 509)
+    for opt in (False, True):
+        c, sc = svq.mxfp8_quantize(w, opt)
+        torch.cuda.synchronize()
+        c_ref, s_ref = oracle.mxfp8_quantize(wb[rows], opt)
+        if not (np.array_equal(c.cpu().numpy()[rows], c_ref) and np.array_equal(sc.cpu().numpy()[rows], s_ref)):
+            raise SystemExit(f"MXFP8 quantizer parity failure (optimized={opt})")
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            svq.mxfp8_quantize(w, opt, codes=c, scales=sc)
+        b.record()
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) * 1e3 / reps
+        key = "opt" if opt else "plain"
+        res[f"us_{key}"] = round(us, 1)
+        res[f"GBps_{key}"] = round((N * K * 3 + N * K // 32) / (us * 1e-6) / 1e9, 1)
+        if opt:
+            plain = svq.mxfp8_quantize(w, False)[1]
+            res["doubled_scale_frac"] = round(float((sc != plain).float().mean().item()), 5)
+    return res
+
+
 def time_ct_ingest(torch, svq, oracle, N=17408, K=5120, G=128, reps=20):
     """The compressed-tensors ingest (a transpose of words and scales) on one
     MLP-sized projection: µs per call and GB/s over its bytes (read + write),
@@ -392,6 +424,8 @@ def main():
     ap.add_argument("--only", default="",
                     help="comma-separated workloads: time just these (per-workload table, no decode "
                          "step, no CPU leg) and print their rows as JSON; for profiling runs")
+    ap.add_argument("--setup-only", action="store_true",
+                    help="time only the setup-time steps (quantizers, ingest) and print them as JSON")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run 5 copies of a 1 GiB device buffer (known bytes for counter calibration)")
     args = ap.parse_args()
@@ -414,6 +448,11 @@ def main():
     props = torch.cuda.get_device_properties(0)
     log(f"device: {props.name} ({getattr(props, 'gcnArchName', '?')}), CUs {props.multi_processor_count}, "
         f"torch {torch.__version__}, hip {torch.version.hip}")
+    if args.setup_only:
+        print(json.dumps({"quantizer": time_quantizer(torch, svq, oracle),
+                          "ct_ingest": time_ct_ingest(torch, svq, oracle),
+                          "mxfp8_quantizer": time_mxfp8_quantizer(torch, svq, oracle)}), flush=True)
+        return
     if args.only:
         names = [n for n in args.only.split(",") if n]
         rows = workload_table(torch, svq, oracle, [n for n in names if n in synth.WORKLOADS])
@@ -467,11 +506,15 @@ def main():
         log(f"load-time RTN quantizer, bf16 [{quant['N']}, {quant['K']}]: int8 {quant['us_int8']:.1f} µs "
             f"({quant['GBps_int8']:.1f} GB/s), int4 {quant['us_int4']:.1f} µs ({quant['GBps_int4']:.1f} GB/s)")
 
-    fusion = ct = None
+    fusion = ct = mxq = None
     if not args.quick:
         fusion = time_fusion(torch, svq, oracle, list(synth.FUSIONS))
         ct = time_ct_ingest(torch, svq, oracle)
         log(f"compressed-tensors ingest [{ct['N']}, {ct['K']}]: {ct['us']:.1f} µs ({ct['GBps']:.1f} GB/s)")
+        mxq = time_mxfp8_quantizer(torch, svq, oracle)
+        log(f"MXFP8 quantizer [{mxq['N']}, {mxq['K']}]: plain {mxq['us_plain']:.1f} µs ({mxq['GBps_plain']:.1f} GB/s), "
+            f"optimized {mxq['us_opt']:.1f} µs ({mxq['GBps_opt']:.1f} GB/s), doubled scale in "
+            f"{100 * mxq['doubled_scale_frac']:.2f}% of blocks")
 
     cpu = None if args.no_cpu else cpu_baseline()
     if cpu:
@@ -502,6 +545,7 @@ def main():
         "quantizer": quant,
         "fusion": fusion,
         "ct_ingest": ct,
+        "mxfp8_quantizer": mxq,
     }
     print(json.dumps(line), flush=True)
 

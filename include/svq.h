@@ -211,6 +211,32 @@ int svq_mxfp8_gemm_with(int kernel, const void *x, const uint8_t *w, const uint8
 
 const char *svq_mxfp8_kernel_name(int kernel, int64_t M, int64_t N, int64_t K);
 
+/*
+ * MXFP8 quantization of a dense bf16 projection into the svq_mxfp8_gemm input,
+ * as a model is quantized (MXFP8 card "Qwen3.8-27B-MXFP8-CT-AutoRound-mtp":
+ * plain round-to-nearest, opening summary; the optimized round-to-nearest of
+ * its notes on the quantizer, which evaluates the baseline block scale with
+ * the scales twice and half as large and keeps the best). Per block of 32
+ * consecutive K-elements of row n:
+ *   baseline  X0 = floor(log2 amax) - 8, b0 = clamp(X0 + 127, 0, 254); an
+ *             all-zero block takes b0 = 127
+ *   candidate b: codes E4M3_RNE(|v| / 2^(b-127)) with the sign of v (-0 and
+ *             negatives that round to zero give 0x80), saturating at 448;
+ *             score = sum over the block, in ascending order, of fp32
+ *             (v - decoded)^2 with round-to-nearest subtract, multiply, add
+ *   optimized = 1: candidates b0, b0 + 1, b0 - 1 (those in 0..254); a later
+ *             one is kept only with a strictly smaller score. optimized = 0:
+ *             b0 (plain round-to-nearest).
+ *   w       bf16 [N][K] (row n = output column n), 16-byte aligned, finite
+ *   codes   E4M3FN [N][K], 16-byte aligned
+ *   scales  E8M0 [N][K/32]
+ * Requires K % 32 == 0 (svq_mxfp8_gemm further needs N >= 128, K % 128 == 0).
+ * Outputs must not overlap w or each other. optimized outside {0, 1} returns
+ * SVQ_ERR_UNSUPPORTED.
+ */
+int svq_mxfp8_quantize(const void *w, int32_t optimized, uint8_t *codes, uint8_t *scales, int64_t N,
+                       int64_t K, void *stream);
+
 /* ---- quantized vocabulary head (W8A16) and the load-time quantizer --------- */
 
 /*

@@ -379,6 +379,13 @@ def mxfp8_quantize(w_bits: np.ndarray, optimized: bool = True, return_choice: bo
         codes = (mag | (sign.astype(np.uint8) << np.uint8(7))).astype(np.uint8)
         return codes, err
 
+    # near the top of the bf16 range a decoded value or a squared difference can
+    # overflow fp32 to infinity; that is the defined fp32 result of these steps
+    with np.errstate(over="ignore", under="ignore"):
+        return _mxfp8_select(candidate, b0, optimized, N, K, return_choice)
+
+
+def _mxfp8_select(candidate, b0, optimized, N, K, return_choice):
     best_codes, best_err = candidate(b0)
     best_b = b0.copy()
     choice = np.zeros_like(b0)

@@ -22,7 +22,7 @@ __all__ = [
     "lib", "library_path", "q4_repack", "w4a16_gemm", "mxfp8_gemm", "w4a16_kernel_name",
     "mxfp8_kernel_name", "w4a16_workspace_bytes", "mxfp8_workspace_bytes", "Workspace",
     "EXPORTED_SYMBOLS", "rtn_quantize", "w8a16_gemm", "w8a16_workspace_bytes", "w8a16_kernel_name",
-    "fuse_projections", "fuse_or_keep", "ct_to_gptq", "MAX_FUSED_PARTS",
+    "fuse_projections", "fuse_or_keep", "ct_to_gptq", "MAX_FUSED_PARTS", "mxfp8_quantize",
 ]
 
 KERNEL_AUTO, KERNEL_DOT2, KERNEL_MFMA_SKINNY, KERNEL_MFMA_WIDE = 0, 1, 2, 3
@@ -36,7 +36,7 @@ EXPORTED_SYMBOLS = (
     "svq_w4a16_kernel_name", "svq_mxfp8_workspace_bytes", "svq_mxfp8_gemm",
     "svq_mxfp8_gemm_with", "svq_mxfp8_kernel_name", "svq_rtn_quantize",
     "svq_w8a16_workspace_bytes", "svq_w8a16_gemm", "svq_w8a16_kernel_name",
-    "svq_fuse_projections", "svq_ct_to_gptq",
+    "svq_fuse_projections", "svq_ct_to_gptq", "svq_mxfp8_quantize",
 )
 
 MAX_FUSED_PARTS = 16
@@ -99,6 +99,8 @@ def lib():
         L.svq_fuse_projections.restype = ctypes.c_int
         L.svq_fuse_projections.argtypes = [_i32, _p, _p, _p, _i32, _i64, _i32, _p, _p, _p]
         L.svq_ct_to_gptq.restype = ctypes.c_int
+        L.svq_mxfp8_quantize.restype = ctypes.c_int
+        L.svq_mxfp8_quantize.argtypes = [_p, _i32, _p, _p, _i64, _i64, _p]
         L.svq_ct_to_gptq.argtypes = [_p, _p, _p, _p, _i64, _i64, _i32, _p]
         _lib = L
         return L
@@ -253,6 +255,26 @@ def mxfp8_gemm(x, w, scales, out=None, kernel=KERNEL_AUTO, workspace=None):
                                      _dev_ptr(out, "out"), M, N, K, 32, ws_ptr, ws_bytes, stream),
            "svq_mxfp8_gemm")
     return out
+
+
+def mxfp8_quantize(w, optimized=True, codes=None, scales=None):
+    """MXFP8 quantization of bf16 w [N, K] (device): E4M3 codes [N, K] and E8M0
+    scales [N, K/32] (uint8), the mxfp8_gemm input. optimized=True keeps, per
+    32-element block, the best of the baseline, doubled and halved scale."""
+    torch = _torch()
+    N, K = w.shape
+    _check_elem(w, "w", 2)
+    if codes is None:
+        codes = torch.empty((N, K), dtype=torch.uint8, device=w.device)
+    if scales is None:
+        scales = torch.empty((N, K // 32), dtype=torch.uint8, device=w.device)
+    _check_elem(codes, "codes", 1)
+    _check_elem(scales, "scales", 1)
+    if codes.numel() != N * K or scales.numel() != N * (K // 32):
+        raise ValueError("codes or scales have the wrong size")
+    _check(lib().svq_mxfp8_quantize(_dev_ptr(w, "w"), 1 if optimized else 0, _dev_ptr(codes, "codes"),
+                                    _dev_ptr(scales, "scales"), N, K, _stream_ptr(w)), "svq_mxfp8_quantize")
+    return codes, scales
 
 
 # ---- quantized vocabulary head ----------------------------------------------------

@@ -418,6 +418,21 @@ int svq_rtn_quantize(const void *w, int32_t bits, int32_t G, void *codes, void *
     return SVQ_OK;
 }
 
+int svq_mxfp8_quantize(const void *w, int32_t optimized, uint8_t *codes, uint8_t *scales, int64_t N,
+                       int64_t K, void *stream) {
+    if (!w || !codes || !scales) return SVQ_ERR_NULL;
+    if (N <= 0 || K <= 0 || N > kMaxDim || K > kMaxDim || N * K > (int64_t(1) << 40)) return SVQ_ERR_DIM;
+    if (optimized != 0 && optimized != 1) return SVQ_ERR_UNSUPPORTED;
+    if (K % 32) return SVQ_ERR_DIVISIBILITY;
+    if (!aligned(w, 16) || !aligned(codes, 16)) return SVQ_ERR_ALIGN;
+    const size_t wb = (size_t)N * K * 2, cb = (size_t)N * K, sb = (size_t)N * (K / 32);
+    if (overlap(codes, cb, w, wb) || overlap(scales, sb, w, wb) || overlap(codes, cb, scales, sb))
+        return SVQ_ERR_OVERLAP;
+    if (launch_mxfp8_quantize(w, optimized, codes, scales, N, K, (hipStream_t)stream) != hipSuccess)
+        return SVQ_ERR_HIP;
+    return SVQ_OK;
+}
+
 size_t svq_w8a16_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t G) {
     if (check_w4a16_shape(M, N, K, G) != SVQ_OK || M > 16) return (size_t)-1;
     return plan_smallm(M, N, K, device_cus()).workspace_bytes;

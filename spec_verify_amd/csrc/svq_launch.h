@@ -101,6 +101,8 @@ hipError_t launch_mxfp8_skinny(const SmallPlan &plan, const void *x, const uint8
 hipError_t launch_w8a16_skinny(const SmallPlan &plan, const void *x, const int8_t *w,
                                const void *scales, void *out, int M, int64_t N, int64_t K, int G,
                                void *workspace, hipStream_t stream);
+hipError_t launch_mxfp8_quantize(const void *w, int optimized, uint8_t *codes, uint8_t *scales,
+                                 int64_t N, int64_t K, hipStream_t stream);
 hipError_t launch_rtn_quantize(const void *w, int bits, int G, void *codes, void *scales, int64_t N,
                                int64_t K, hipStream_t stream);
 

@@ -209,6 +209,21 @@ def test_ct_to_gptq_validation(L):
     assert c(s=FAKE3 + 64) == 7
 
 
+def test_mxfp8_quantize_validation(L):
+    def q(w=FAKE, opt=1, c=FAKE2, s=FAKE3, N=256, K=512):
+        return L.svq_mxfp8_quantize(w, opt, c, s, N, K, None)
+    assert q(w=None) == 1
+    assert q(c=None) == 1
+    assert q(N=0) == 2
+    assert q(K=1 << 25) == 2
+    assert q(opt=2) == 10
+    assert q(K=48) == 4
+    assert q(w=FAKE + 8) == 6
+    assert q(c=FAKE2 + 8) == 6
+    assert q(c=FAKE + 1024) == 7               # codes overlap w
+    assert q(s=FAKE2 + 4096) == 7              # scales overlap codes
+
+
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     import spec_verify_amd as svq
     monkeypatch.setattr(svq, "_lib", None)

@@ -197,8 +197,11 @@ __global__ __launch_bounds__(64 * WR * WC) void mxfp8_wide_kernel(
     constexpr int BM = 16 * MBW * WR;
     constexpr int BN = 16 * CT * WC;
     constexpr int XROW = 128 + 8;
-    constexpr int UPT = BM * 16 / NT;
-    constexpr int TPR = 16 / UPT;
+    // x stage: 16 lanes per row (16 chunks of 16 bytes = one step of a row),
+    // NT / 16 rows per pass, UPT passes
+    constexpr int RPP = NT / 16;
+    constexpr int UPT = BM / RPP;
+    static_assert(UPT * RPP == BM, "x stage split over the threads");
     constexpr int NV = MBW * CT;
     __shared__ __attribute__((aligned(16))) uint16_t xs[2][BM][XROW];
     __shared__ int s_sk[3];
@@ -211,7 +214,16 @@ __global__ __launch_bounds__(64 * WR * WC) void mxfp8_wide_kernel(
     const int wg = blockIdx.x;
     const int64_t u_begin = (int64_t)wg * units / grid;
     const int64_t u_end = (int64_t)(wg + 1) * units / grid;
-    const int srow = tid / TPR, sseg = tid % TPR;
+    const int srow = tid >> 4, schunk = tid & 15;
+
+    // Buffer views: a per-lane offset past the end reads zeros without touching
+    // memory, which turns rows >= M and the prefetch after a segment's last step
+    // into loads that need no branch (a conditional load would make the
+    // compiler wait for every load in flight before the next compute).
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, (uint32_t)((size_t)M * K * 2));
+    const __amdgpu_buffer_rsrc_t wrs = make_rsrc(w, (uint32_t)((size_t)N * K));
+    const __amdgpu_buffer_rsrc_t srs = make_rsrc(sc, (uint32_t)((size_t)N * (K >> 5)));
+    constexpr uint32_t kOob = 0x80000000u;
 
     for (int64_t u = u_begin; u < u_end;) {
         const int tile = (int)(u / KT);
@@ -220,19 +232,26 @@ __global__ __launch_bounds__(64 * WR * WC) void mxfp8_wide_kernel(
         const int rt = tile / col_tiles, cb = tile % col_tiles;
         const int row0 = rt * BM;
 
-        const uint8_t *wp[CT];
-        const uint8_t *spp[CT];
-        bool ctv[CT];
+        // lane (r, g) of column tile ct: column colg, K-rows 32g.. of each step
+        // (one 32-element scale block); the step's four block scales of the
+        // column are one aligned dword, byte g is this lane's
+        uint32_t wvo[CT], svo[CT];
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
             const int nbg = cb * (BN / 16) + wc * CT + ct;
-            ctv[ct] = nbg < NB16;
-            const int colg = (ctv[ct] ? nbg : NB16 - 1) * 16 + r;
-            wp[ct] = w + (size_t)colg * K + g * 32;
-            spp[ct] = sc + (size_t)colg * (K >> 5) + g;
+            const int colg = (nbg < NB16 ? nbg : NB16 - 1) * 16 + r;
+            wvo[ct] = (uint32_t)colg * (uint32_t)K + g * 32;
+            svo[ct] = (uint32_t)colg * (uint32_t)(K >> 5);
         }
-        const bool srv = row0 + srow < M;
-        const uint4 *xsrc = (const uint4 *)(x + (size_t)(srv ? row0 + srow : 0) * K) + sseg * UPT;
+        // rows past M read row M - 1 (their products are never stored)
+        uint32_t xvo[UPT];
+#pragma unroll
+        for (int v = 0; v < UPT; ++v) {
+            const int row = row0 + srow + RPP * v;
+            xvo[v] = (uint32_t)(row < M ? row : M - 1) * (uint32_t)K * 2u + schunk * 16;
+        }
+        // kOob for a step past the segment (operands stay below 2^31 bytes)
+        auto past = [&](int s) { return (uint32_t)(s1 - 1 - s) & kOob; };
 
         f32x4 acc[NV];
 #pragma unroll
@@ -242,19 +261,31 @@ __global__ __launch_bounds__(64 * WR * WC) void mxfp8_wide_kernel(
         uint4 wcur[CT][2], wnext[CT][2];
         uint32_t scur[CT], snext[CT];
 
-        auto load_x = [&](int s) {
+        // loads of K step s (s >= s1: out of range, zeros, no traffic)
+        // (the out-of-range bit is formed arithmetically: a select on the
+        // wave-uniform condition would become a branch around the loads)
+        // A step's loads are issued in one fixed order, x then weights and
+        // scales, fenced from the surrounding code: the s_waitcnt counts then
+        // agree on every path into the loop. The empty asm with a memory
+        // clobber keeps the optimizer from sinking the loads below the next
+        // compute phase (it emits no instruction and no wait).
+        auto load_step = [&](uint4(&W)[CT][2], uint32_t(&S)[CT], int s) {
+            const uint32_t o = past(s);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int v = 0; v < UPT; ++v) xreg[v] = srv ? xsrc[(size_t)s * 16 + v] : make_uint4(0, 0, 0, 0);
-        };
-        auto load_w = [&](uint4(&W)[CT][2], uint32_t(&S)[CT], int s) {
+            for (int v = 0; v < UPT; ++v) xreg[v] = bload16(xr, (xvo[v] + (uint32_t)s * 256u) | o, 0);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int ct = 0; ct < CT; ++ct) {
-                W[ct][0] = load_stream16(wp[ct] + (size_t)s * 128);
-                W[ct][1] = load_stream16(wp[ct] + (size_t)s * 128 + 16);
-                S[ct] = spp[ct][(size_t)s * 4];
+                const uint32_t vo = (wvo[ct] + (uint32_t)s * 128u) | o;
+                W[ct][0] = bload16(wrs, vo, 0);
+                W[ct][1] = bload16(wrs, vo + 16, 0);
+                S[ct] = bload4(srs, (svo[ct] + (uint32_t)s * 4u) | o, 0);
             }
+            __builtin_amdgcn_sched_barrier(0);
+            asm volatile("" ::: "memory");
         };
-        auto compute = [&](int buf) {
+        auto compute = [&](int buf, const uint4 (&W)[CT][2], const uint32_t (&S)[CT]) {
             const int rbase = wr * MBW * 16;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -263,34 +294,37 @@ __global__ __launch_bounds__(64 * WR * WC) void mxfp8_wide_kernel(
                 for (int rb = 0; rb < MBW; ++rb) A[rb] = *(const uint4 *)&xs[buf][rbase + rb * 16 + r][32 * g + 8 * j];
 #pragma unroll
                 for (int ct = 0; ct < CT; ++ct) {
-                    const float sf = e8m0_to_f32(scur[ct]);
-                    const uint4 &wv = wcur[ct][j >> 1];
+                    const float sf = e8m0_to_f32((S[ct] >> (8 * g)) & 0xFFu);
+                    const uint4 &wv = W[ct][j >> 1];
                     const uint4 B = (j & 1) ? cvt8_e4m3_bf16(wv.z, wv.w, sf) : cvt8_e4m3_bf16(wv.x, wv.y, sf);
 #pragma unroll
                     for (int rb = 0; rb < MBW; ++rb) acc[rb * CT + ct] = mfma16x16x32(A[rb], B, acc[rb * CT + ct]);
                 }
             }
         };
+        auto stage_x = [&](int buf) {
+#pragma unroll
+            for (int v = 0; v < UPT; ++v) *(uint4 *)&xs[buf][srow + RPP * v][schunk * 8] = xreg[v];
+        };
 
+        // Two register sets for the weights and scales, used alternately, so
+        // that the compute of a step never reads registers that the next
+        // step's loads are still filling (a copy between the sets would make
+        // every step wait for the next step's loads).
+        // Steps go in pairs; every half issues its prefetch (past the segment
+        // it reads zeros), and only the compute of a missing second step is
+        // skipped, so no load sits behind a branch.
         __syncthreads();
-        load_x(s0);
-        load_w(wcur, scur, s0);
-        for (int s = s0; s < s1; ++s) {
-            const int buf = (s - s0) & 1;
-#pragma unroll
-            for (int v = 0; v < UPT; ++v) *(uint4 *)&xs[buf][srow][(sseg * UPT + v) * 8] = xreg[v];
+        load_step(wcur, scur, s0);
+        for (int s = s0; s < s1; s += 2) {
+            stage_x(0);
             __syncthreads();
-            if (s + 1 < s1) {
-                load_x(s + 1);
-                load_w(wnext, snext, s + 1);
-            }
-            compute(buf);
-#pragma unroll
-            for (int ct = 0; ct < CT; ++ct) {
-                wcur[ct][0] = wnext[ct][0];
-                wcur[ct][1] = wnext[ct][1];
-                scur[ct] = snext[ct];
-            }
+            load_step(wnext, snext, s + 1);
+            compute(0, wcur, scur);
+            stage_x(1);
+            __syncthreads();
+            load_step(wcur, scur, s + 2);
+            if (s + 1 < s1) compute(1, wnext, snext);
         }
 
         const int rowb = row0 + wr * MBW * 16 + 4 * g;

@@ -46,6 +46,15 @@ static WidePlan make_plan(int64_t M, int64_t N, int64_t K, int num_cus, int bm, 
     const int64_t tiles = (int64_t)p.row_tiles * p.col_tiles;
     p.units = tiles * KT;
     p.grid = (int)std::min<int64_t>(std::max(num_cus, 1), p.units);
+    // With fewer tiles than CUs, a grid of tiles x floor(CUs / tiles) gives every
+    // workgroup one K range of one tile (the unit split below is then tile
+    // aligned): the contributors of a tile finish together, and no workgroup
+    // starts a second tile late, which would hold up that tile's reduction.
+    // Used when it keeps at least three quarters of the CUs busy.
+    if (tiles <= num_cus) {
+        const int64_t S = std::min<int64_t>(num_cus / tiles, KT);
+        if (tiles * S * 4 >= (int64_t)num_cus * 3) p.grid = (int)(tiles * S);
+    }
     int maxt = 1;
     bool shared = false;
     for (int w = 0; w < p.grid; ++w) {

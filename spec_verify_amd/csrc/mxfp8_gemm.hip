@@ -431,7 +431,9 @@ hipError_t launch_mxfp8_skinny(const SmallPlan &plan, const void *x, const uint8
 hipError_t launch_mxfp8_wide(const WidePlan &plan, const void *x, const uint8_t *w,
                              const uint8_t *scales, void *out, int64_t M, int64_t N, int64_t K,
                              void *workspace, hipStream_t stream) {
-    if (plan.bm == 128) return mx_wide_launch<4, 2, 2, 4>(plan, x, w, scales, out, M, N, K, workspace, stream);
+    // 128 x 128 tiles: four waves side by side (each all 128 rows x 32 columns),
+    // so every weight byte is loaded and converted by one wave only
+    if (plan.bm == 128) return mx_wide_launch<8, 1, 4, 2>(plan, x, w, scales, out, M, N, K, workspace, stream);
     return mx_wide_launch<4, 1, 4, 4>(plan, x, w, scales, out, M, N, K, workspace, stream);
 }
 

@@ -36,6 +36,9 @@
  *    quantization) cannot be expressed: there are no such parameters.
  *  - Row-major everywhere; bf16 and fp16 values are passed as their 16-bit
  *    patterns.
+ *  - GEMM operands stay below 2 GiB each (M*K*2, N*K, M*N*2 < 2^31 bytes;
+ *    the kernels use 32-bit buffer offsets); larger shapes return
+ *    SVQ_ERR_DIM.
  *  - Results are deterministic: repeated calls with equal inputs give equal
  *    bits (all reductions run in a fixed order).
  */

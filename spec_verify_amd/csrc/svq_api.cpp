@@ -109,10 +109,13 @@ bool overlap(const void *a, size_t na, const void *b, size_t nb) {
     return pa < pb + nb && pb < pa + na;
 }
 
+// The GEMM kernels address every operand through 32-bit buffer offsets, so
+// each one stays below 2^31 bytes: x (2MK), weights (at most NK, int8/fp8),
+// y (2MN).
 bool dims_ok(int64_t M, int64_t N, int64_t K) {
     return M > 0 && N > 0 && K > 0 && M <= kMaxDim && N <= kMaxDim && K <= kMaxDim &&
-           M * K <= (int64_t(1) << 40) && N * K <= (int64_t(1) << 40) &&
-           M * N <= (int64_t(1) << 40);
+           M * K < (int64_t(1) << 30) && N * K < (int64_t(1) << 31) &&
+           M * N < (int64_t(1) << 30);
 }
 
 int resolve_kernel(int kernel, int64_t M, bool mxfp8) {

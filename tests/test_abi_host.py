@@ -57,6 +57,7 @@ def test_w4a16_validation(L):
     assert _w4(L, M=0) == 2
     assert _w4(L, N=-16) == 2
     assert _w4(L, K=1 << 25) == 2
+    assert _w4(L, N=1 << 18, K=1 << 13) == 2     # 2^31 weight elements: past the 32-bit offsets
     assert _w4(L, G=16) == 3
     assert _w4(L, G=256) == 3
     assert _w4(L, N=250) == 4

@@ -72,7 +72,9 @@ typedef enum svq_status {
  * SVQ_KERNEL_AUTO is what svq_w4a16_gemm / svq_mxfp8_gemm use. */
 typedef enum svq_kernel {
     SVQ_KERNEL_AUTO = 0,
-    SVQ_KERNEL_DOT2 = 1,        /* VALU bf16 dot2 with row broadcast of x, M <= 8 */
+    SVQ_KERNEL_DOT2 = 1,        /* VALU bf16 dot2, M <= 8: 16-column blocks with row
+                                   broadcast of x; for M <= 2 and fewer 16-column
+                                   blocks than CUs, 4-column units with x in LDS */
     SVQ_KERNEL_MFMA_SKINNY = 2, /* one 16-row MFMA tile, waves split K, M <= 16 */
     SVQ_KERNEL_MFMA_WIDE = 3    /* LDS-staged x, 64/128-row MFMA tiles, split-K, any M */
 } svq_kernel;

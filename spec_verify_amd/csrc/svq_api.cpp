@@ -303,6 +303,8 @@ const char *svq_w4a16_kernel_name(int kernel, int64_t M, int64_t N, int64_t K, i
     if (check_w4a16_shape(M, N, K, G) != SVQ_OK) return nullptr;
     const int k = resolve_kernel(kernel, M, false);
     if (kernel_fits(k, M) != SVQ_OK) return nullptr;
+    if (k == SVQ_KERNEL_DOT2 && w4a16_dot2_is_narrow(w4a16_small_plan(k, M, N, K, device_cus()), (int)M, N, K, G))
+        return "w4a16_narrow_kernel";
     return w4a16_name(k);
 }
 

@@ -172,6 +172,23 @@ __device__ __forceinline__ uint4 word_to_bf16x8(uint32_t w) {
     return make_uint4(a, b, c, d);
 }
 
+// The same four pairs for VALU consumers (no trailing wait states). Written as
+// asm because v_and_or_b32 takes no literal operand: left to itself the
+// compiler builds each pair with three instructions.
+__device__ __forceinline__ uint4 word_to_pairs(uint32_t w) {
+    uint32_t a, b, c, d, t1, t2, t3;
+    asm("v_and_or_b32 %0, %7, %8, %9\n\t"
+        "v_lshrrev_b32 %4, 4, %7\n\t"
+        "v_lshrrev_b32 %5, 8, %7\n\t"
+        "v_lshrrev_b32 %6, 12, %7\n\t"
+        "v_and_or_b32 %1, %4, %8, %9\n\t"
+        "v_and_or_b32 %2, %5, %8, %9\n\t"
+        "v_and_or_b32 %3, %6, %8, %9"
+        : "=&v"(a), "=&v"(b), "=&v"(c), "=&v"(d), "=&v"(t1), "=&v"(t2), "=&v"(t3)
+        : "v"(w), "s"(kNibblePairMask), "v"(kMagic128Pair));
+    return make_uint4(a, b, c, d);
+}
+
 // E8M0 code -> fp32 scale 2^(b-127) (b = 0 gives the fp32 subnormal 2^-127).
 __device__ __forceinline__ float e8m0_to_f32(uint32_t b) {
     return bits_f32(b == 0 ? 0x00400000u : (b << 23));

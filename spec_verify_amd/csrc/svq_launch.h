@@ -81,6 +81,9 @@ inline int pick_waves(int64_t wgs, int cus, int res16, int res8) {
 // max_tiles: the most K tiles one workgroup may take (0: no limit).
 SmallPlan plan_smallm(int64_t M, int64_t N, int64_t K, int num_cus, int64_t max_tiles = 0);
 
+// True when launch_w4a16_dot2 runs the narrow-unit GEMV for this shape (too
+// few 16-column blocks to fill the chip, M <= 2) rather than the block kernel.
+bool w4a16_dot2_is_narrow(const SmallPlan &plan, int M, int64_t N, int64_t K, int G);
 hipError_t launch_w4a16_dot2(const SmallPlan &plan, const void *x, const int32_t *wt,
                              const void *scales, void *out, int M, int64_t N, int64_t K, int G,
                              void *workspace, hipStream_t stream);

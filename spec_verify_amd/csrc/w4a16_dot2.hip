@@ -120,8 +120,161 @@ __global__ __launch_bounds__(64 * WAVES) void w4a16_dot2_kernel(
     smallm_finish(v, M, N, nb, sp, splits, out, cnt, part, &s_flag);
 }
 
+// Narrow-unit GEMV for M = 1..2 where the matrix has fewer 16-column blocks
+// than the chip has CUs (a decode projection with N = 1024 has 64 blocks: the
+// kernel above would leave three quarters of the CUs idle, and splitting K
+// across workgroups costs a cross-workgroup handoff). The work unit is 4
+// output columns over all of K, so N/4 units spread over all the CUs with no
+// split of K. Measured on the MI355X, M = 1, K = 5120: N = 1024 takes 4.4 us
+// against 5.0 us for the block kernel; with N >= 16 x CUs the block kernel is
+// as fast or faster, so it keeps those shapes.
+//  * A workgroup owns `upw` consecutive units; `wpu` waves share each unit's
+//    128-row tiles, four tiles per load: lane l reads the 16 bytes of tile
+//    4g + l/16 that hold rows 32*((l/4)%4).. of the unit's column l%4 (four
+//    lanes read one contiguous 64-byte run), so one wave load covers four
+//    tiles of the unit and every byte is read once.
+//  * x (M rows, zero-padded to whole groups of four tiles) is staged in LDS
+//    once per workgroup with the sums of each 32-row run (for the -136*sum(x)
+//    bias); each lane then reads its 32 rows of x from LDS.
+//  * All of a wave's weight and scale loads are issued before x is staged, so
+//    the HBM stream starts at once; the x loads are issued before them, so the
+//    wait for x leaves the weight loads in flight.
+//  * Reduction: the 16 lanes of a column (4 tiles x 4 row runs) with row
+//    rotations and permlane swaps, the waves of a unit through LDS, in a fixed
+//    order.
+constexpr int kNarrowCols = 4;      // output columns per unit
+constexpr int kNarrowXChunks = 4;   // most 16-byte x chunks one thread stages
+
+template <int M, int CW, int LPW, int GSHIFT>
+__global__ __launch_bounds__(1024) void w4a16_narrow_kernel(
+    const uint16_t *__restrict__ x, const uint4 *__restrict__ wt, const uint16_t *__restrict__ sc,
+    uint16_t *__restrict__ out, int N, int K, int upw, int wpu) {
+    extern __shared__ __align__(16) unsigned char narrow_lds[];
+    constexpr uint32_t kOob = 0x80000000u;  // buffer offset past every operand: reads zero
+    constexpr int TPL = 16 / CW;  // tiles per wave load
+    const int KT = K >> 7;
+    const int TG = (KT + TPL - 1) / TPL;  // groups of TPL tiles
+    const int KTp = TG * TPL;
+    uint16_t *xs = (uint16_t *)narrow_lds;                    // [M][KTp * 128] bf16
+    float *xsum = (float *)(narrow_lds + (size_t)M * KTp * 256);  // [M][KTp * 4]
+    float *red = xsum + M * KTp * 4;                           // [waves][M][CW]
+
+    const int lane = threadIdx.x & 63;
+    const int wave = wave_id();
+    const int lb = xcd_contiguous(blockIdx.x, gridDim.x);
+    const int units = N / CW;
+    const int unit = lb * upw + wave / wpu;
+    const int sub = wave % wpu;
+    const bool live = unit < units;
+    const int nb = unit / TPL, c0 = (unit % TPL) * CW;
+    const int u = lane / (4 * CW), rg = (lane / CW) & 3, c = lane % CW;
+    const int n = nb * 16 + c0 + c;
+
+    // x chunks first (16 bytes each; past K or past the stage: zero, no traffic)
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, (uint32_t)(M * K * 2));
+    const int xchunks = M * KTp * 16;
+    uint4 xv[kNarrowXChunks];
+#pragma unroll
+    for (int i = 0; i < kNarrowXChunks; ++i) {
+        const int ch = threadIdx.x + i * blockDim.x;
+        const int m = ch / (KTp * 16), k0 = (ch - m * KTp * 16) * 8;
+        const uint32_t vo = (ch < xchunks && k0 < K) ? (uint32_t)((m * K + k0) * 2) : kOob;
+        xv[i] = bload16(xr, vo, 0);
+    }
+    // then every weight and scale load of this wave, in the order they are
+    // used (the scheduling barriers keep the issue order: waits are in order)
+    __builtin_amdgcn_sched_barrier(0);
+    const __amdgpu_buffer_rsrc_t wr = make_rsrc(wt, (uint32_t)((size_t)N * K / 2));
+    const __amdgpu_buffer_rsrc_t sr = make_rsrc(sc, (uint32_t)((size_t)(K >> GSHIFT) * N * 2));
+    uint4 w[LPW];
+    uint32_t s[LPW];
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+        const int t = (sub + i * wpu) * TPL + u;
+        const bool ok = live && t < KT;
+        const uint32_t wvo = ok ? (uint32_t)((nb * KT + t) * 1024 + rg * 256 + (c0 + c) * 16) : kOob;
+        const int g = (t * 128 + rg * 32) >> GSHIFT;
+        const uint32_t svo = ok ? (uint32_t)(((g * N + n) * 2) & ~3) : kOob;
+        w[i] = bload16(wr, wvo, 0);
+        s[i] = bload4(sr, svo, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // stage x and the sums of its 32-row runs (four consecutive chunks, which
+    // sit in four consecutive lanes)
+#pragma unroll
+    for (int i = 0; i < kNarrowXChunks; ++i) {
+        const int ch = threadIdx.x + i * blockDim.x;
+        const uint32_t wd[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
+        float v = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v += bits_f32(wd[j] << 16) + bits_f32(wd[j] & 0xFFFF0000u);
+        v += bits_f32(__builtin_amdgcn_mov_dpp(f32_bits(v), 0xB1, 0xF, 0xF, true));  // quad_perm [1,0,3,2]
+        v += bits_f32(__builtin_amdgcn_mov_dpp(f32_bits(v), 0x4E, 0xF, 0xF, true));  // quad_perm [2,3,0,1]
+        if (ch < xchunks) {
+            *(uint4 *)(xs + (size_t)ch * 8) = xv[i];
+            if ((ch & 3) == 0) xsum[ch >> 2] = v;
+        }
+    }
+    lds_barrier();
+
+    float acc[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) acc[m] = 0.f;
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+        const int tg = sub + i * wpu;
+        if (!live || tg >= TG) break;
+        const int t = tg * TPL + u;
+        const uint32_t wj[4] = {w[i].x, w[i].y, w[i].z, w[i].w};
+        const float sf = fp16_bits_to_f32((uint16_t)(s[i] >> ((n & 1) * 16)));
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            const u32x4 *xp = (const u32x4 *)(xs + (size_t)m * KTp * 128 + t * 128 + rg * 32);
+            const u32x4 xa = xp[0], xb = xp[1], xc = xp[2], xd = xp[3];
+            const uint32_t xq[16] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w,
+                                     xc.x, xc.y, xc.z, xc.w, xd.x, xd.y, xd.z, xd.w};
+            // two interleaved chains (pairs of even and odd word index)
+            float p0 = -136.f * xsum[m * KTp * 4 + t * 4 + rg], p1 = 0.f;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint4 pw = word_to_pairs(wj[j]);
+                const uint32_t pr[4] = {pw.x, pw.y, pw.z, pw.w};
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    if (j & 1) p1 = dot2_bf16(pr[q], xq[4 * j + q], p1);
+                    else p0 = dot2_bf16(pr[q], xq[4 * j + q], p0);
+                }
+            }
+            acc[m] = __builtin_fmaf(sf, p0 + p1, acc[m]);
+        }
+    }
+
+    // column sums: over the four row runs (rotations by 4 and 8 within a row),
+    // then over the four tiles (the 16-lane rows)
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        float v = acc[m];
+        if constexpr (CW == 4)
+            v += bits_f32(__builtin_amdgcn_mov_dpp(f32_bits(v), 0x124, 0xF, 0xF, true));  // row_ror:4
+        v += bits_f32(__builtin_amdgcn_mov_dpp(f32_bits(v), 0x128, 0xF, 0xF, true));  // row_ror:8
+        v = rows4_sum(v);
+        if (lane < CW) red[(wave * M + m) * CW + lane] = v;
+    }
+    lds_barrier();
+    const int tid = threadIdx.x;
+    if (tid < upw * M * CW) {
+        const int ul = tid / (M * CW), m = (tid / CW) % M, cc = tid % CW;
+        const int un = lb * upw + ul;
+        float v = 0.f;
+        for (int q = 0; q < wpu; ++q) v += red[((ul * wpu + q) * M + m) * CW + cc];
+        if (un < units) out[(size_t)m * N + un * CW + cc] = f32_to_bf16_rne(v);
+    }
+}
+
 namespace {
 constexpr int kDot2Depth = 4;
+constexpr int kNarrowPerCu = 1;  // workgroups per CU of the balanced plan
 
 template <int M, int WAVES, int GS>
 hipError_t dot2_launch_w(const SmallPlan &p, const void *x, const int32_t *wt, const void *sc, void *out,
@@ -145,9 +298,66 @@ hipError_t dot2_launch(const SmallPlan &p, const void *x, const int32_t *wt, con
     }
 }
 
+// Balanced plan: units of 4 columns, `upw` per workgroup (about `per_cu`
+// workgroups per CU), `wpu` waves per unit, each wave issuing at most `lpw`
+// four-tile loads, all of them up front.
+struct NarrowPlan {
+    int upw, wpu, lpw, waves, grid;
+    size_t lds;
+};
+
+bool plan_narrow(int M, int64_t N, int64_t K, int cus, int per_cu, NarrowPlan &p) {
+    if (M > 2 || cus <= 0) return false;
+    const int64_t units = N / kNarrowCols, KT = K / 128, TPL = 16 / kNarrowCols, TG = (KT + TPL - 1) / TPL;
+    if (N / 16 >= cus) return false;  // enough 16-column blocks: the block kernel
+    if (units < cus) return false;     // too few units to fill the chip: the split-K path
+    const int64_t target = (int64_t)cus * per_cu;
+    const int64_t upw = (units + target - 1) / target;
+    if (upw > 16) return false;
+    const int64_t wpu = std::min<int64_t>(16 / upw, TG);
+    const int64_t lpw = (TG + wpu - 1) / wpu;
+    if (lpw > 8) return false;
+    const int64_t waves = upw * wpu;
+    if ((int64_t)M * TG * TPL * 16 > (int64_t)kNarrowXChunks * waves * 64) return false;
+    p.upw = (int)upw;
+    p.wpu = (int)wpu;
+    p.lpw = (int)lpw;
+    p.waves = (int)waves;
+    p.grid = (int)((units + upw - 1) / upw);
+    p.lds = (size_t)M * TG * TPL * (256 + 16) + (size_t)waves * M * kNarrowCols * 4;
+    return p.lds <= 64 * 1024;
+}
+
+template <int M, int LPW, int GS>
+hipError_t narrow_launch_l(const NarrowPlan &p, const void *x, const int32_t *wt, const void *sc,
+                           void *out, int64_t N, int64_t K, hipStream_t stream) {
+    hipLaunchKernelGGL((w4a16_narrow_kernel<M, kNarrowCols, LPW, GS>), dim3((uint32_t)p.grid), dim3(64 * p.waves),
+                       p.lds, stream, (const uint16_t *)x, (const uint4 *)wt, (const uint16_t *)sc,
+                       (uint16_t *)out, (int)N, (int)K, p.upw, p.wpu);
+    return hipGetLastError();
+}
+
+template <int M, int GS>
+hipError_t narrow_launch(const NarrowPlan &p, const void *x, const int32_t *wt, const void *sc,
+                         void *out, int64_t N, int64_t K, hipStream_t stream) {
+    switch (p.lpw) {
+    case 1: return narrow_launch_l<M, 1, GS>(p, x, wt, sc, out, N, K, stream);
+    case 2: return narrow_launch_l<M, 2, GS>(p, x, wt, sc, out, N, K, stream);
+    case 3: return narrow_launch_l<M, 3, GS>(p, x, wt, sc, out, N, K, stream);
+    case 4: return narrow_launch_l<M, 4, GS>(p, x, wt, sc, out, N, K, stream);
+    case 5: return narrow_launch_l<M, 5, GS>(p, x, wt, sc, out, N, K, stream);
+    case 6: return narrow_launch_l<M, 6, GS>(p, x, wt, sc, out, N, K, stream);
+    default: return narrow_launch_l<M, 8, GS>(p, x, wt, sc, out, N, K, stream);
+    }
+}
+
 template <int GS>
 hipError_t dot2_by_m(const SmallPlan &p, int M, const void *x, const int32_t *wt, const void *sc,
                      void *out, int64_t N, int64_t K, void *ws, hipStream_t stream) {
+    NarrowPlan np;
+    if (p.splits == 1 && plan_narrow(M, N, K, p.cus, kNarrowPerCu, np))
+        return M == 1 ? narrow_launch<1, GS>(np, x, wt, sc, out, N, K, stream)
+                      : narrow_launch<2, GS>(np, x, wt, sc, out, N, K, stream);
     switch (M) {
     case 1: return dot2_launch<1, GS>(p, x, wt, sc, out, N, K, ws, stream);
     case 2: return dot2_launch<2, GS>(p, x, wt, sc, out, N, K, ws, stream);
@@ -161,6 +371,12 @@ hipError_t dot2_by_m(const SmallPlan &p, int M, const void *x, const int32_t *wt
     }
 }
 }  // namespace
+
+bool w4a16_dot2_is_narrow(const SmallPlan &plan, int M, int64_t N, int64_t K, int G) {
+    (void)G;
+    NarrowPlan np;
+    return plan.splits == 1 && plan_narrow(M, N, K, plan.cus, kNarrowPerCu, np);
+}
 
 hipError_t launch_w4a16_dot2(const SmallPlan &plan, const void *x, const int32_t *wt,
                              const void *scales, void *out, int M, int64_t N, int64_t K, int G,

@@ -104,6 +104,13 @@ W4_CASES = (
                                             (8, 640, 5376, 64), (5, 1280, 9216, 128), (1, 1280, 9216, 32))]
 )
 
+# dot2 shapes that run the narrow-unit GEMV on a 256-CU part (M <= 2, fewer 16-column
+# blocks than CUs, at least one 4-column unit per CU): ragged groups of four tiles
+# (K = 1280, 640), one to four units per workgroup, every group size, long K
+W4_NARROW = [(1, m, K, N, G) for (m, K, N, G) in (
+    (1, 1280, 1024, 128), (2, 1280, 1040, 32), (1, 5120, 4080, 64), (2, 640, 2064, 32),
+    (1, 17408, 1024, 128), (1, 5120, 1024, 32), (2, 5120, 3088, 64))]
+
 
 @pytest.mark.parametrize("kernel,M,K,N,G", W4_CASES, ids=_ids(W4_CASES))
 def test_w4a16_random(kernel, M, K, N, G):
@@ -112,6 +119,19 @@ def test_w4a16_random(kernel, M, K, N, G):
     out, _ = run_w4a16(inp, kernel)
     y64, y32 = oracle.w4a16(inp.x, inp.qweight, inp.scales, G)
     assert_gate(out, y64, y32, f"kernel {kernel} M{M} K{K} N{N} G{G}")
+
+
+@pytest.mark.parametrize("kernel,M,K,N,G", W4_NARROW, ids=_ids(W4_NARROW))
+def test_w4a16_narrow(kernel, M, K, N, G):
+    import spec_verify_amd as svq
+    _say("w4a16 narrow M K N G", M, K, N, G)
+    if torch.cuda.get_device_properties(0).multi_processor_count != 256:
+        pytest.skip("shapes chosen for a 256-CU part")
+    assert svq.w4a16_kernel_name(M, N, K, G, kernel=1) == "w4a16_narrow_kernel"
+    inp = synth.gen_w4a16(2000 + 7 * M + K + N + G, M, K, N, G)
+    out, _ = run_w4a16(inp, kernel)
+    y64, y32 = oracle.w4a16(inp.x, inp.qweight, inp.scales, G)
+    assert_gate(out, y64, y32, f"narrow M{M} K{K} N{N} G{G}")
 
 
 W4_EXACT = [
@@ -379,5 +399,6 @@ def test_output_canaries_and_error_path_leave_memory_untouched():
 def test_kernel_names_match_dispatch():
     import spec_verify_amd as svq
     assert svq.w4a16_kernel_name(1, 5120, 5120) == "w4a16_dot2_kernel"
+    assert svq.w4a16_kernel_name(1, 1024, 5120) == "w4a16_narrow_kernel"
     assert svq.w4a16_kernel_name(5, 17408, 5120) == "w4a16_skinny_kernel"
     assert svq.w4a16_kernel_name(128, 17408, 5120) == "w4a16_wide_kernel"

@@ -199,4 +199,38 @@ __device__ __forceinline__ void smallm_finish(float v, int M, int N, int nb, int
     if (t == 0) clear_counter(&cnt[nb]);
 }
 
+// The same for a workgroup that owns `nblk` consecutive column blocks
+// nb0 .. nb0 + nblk - 1 (one K range of each): thread t < nblk * 16 * M holds
+// the sum v of block t / (16M), row (t / 16) % M, column t % 16 of the block.
+// s_flags needs nblk ints of LDS.
+__device__ __forceinline__ void multiblock_finish(float v, int M, int N, int nb0, int nblk, int sp,
+                                                  int splits, uint16_t *__restrict__ out,
+                                                  uint32_t *__restrict__ cnt, float *__restrict__ part,
+                                                  int *s_flags) {
+    const int t = threadIdx.x;
+    const int per = 16 * M;
+    const bool owner = t < nblk * per;
+    const int b = t / per, tt = t - b * per, m = tt >> 4, c = tt & 15;
+    const int nb = nb0 + b;
+    if (splits == 1) {
+        if (owner) out[(size_t)m * N + nb * 16 + c] = f32_to_bf16_rne(v);
+        return;
+    }
+    float *slots = part + (size_t)nb * splits * per;
+    if (owner) __hip_atomic_store(slots + (size_t)sp * per + tt, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    wait_all_memory();
+    __syncthreads();
+    if (t < nblk) s_flags[t] = (arrive(&cnt[nb0 + t]) == (uint32_t)(splits - 1));
+    __syncthreads();
+    if (owner && s_flags[b]) {
+        float s2 = 0.f;
+        for (int k = 0; k < splits; ++k)
+            s2 += (k == sp) ? v
+                            : __hip_atomic_load(slots + (size_t)k * per + tt, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT);
+        out[(size_t)m * N + nb * 16 + c] = f32_to_bf16_rne(s2);
+    }
+    if (t < nblk && s_flags[t]) clear_counter(&cnt[nb0 + t]);
+}
+
 }  // namespace svq

@@ -29,15 +29,18 @@ namespace svq {
 
 // ---------------------------------------------------------------------------
 // Skinny kernel: M <= 16, one 16-row MFMA tile (MFMA rows >= M repeat row M-1
-// and their results are dropped). A workgroup owns one 16-column block and a
-// range of S K-tiles; its waves take the tiles round-robin. The workgroup's
-// x rows (M x 128*S bf16) are staged once in LDS, so the A operands come from
-// LDS and the vector-memory path carries only weights and scales, which each
-// wave prefetches 2*D tiles deep behind the staging loads. Memory-bound; the
+// and their results are dropped). A workgroup owns BPW consecutive 16-column
+// blocks and one range of S K-tiles of each; WAVES / BPW waves per block take
+// its tiles round-robin. The workgroup's x rows (M x 128*S bf16) are staged
+// once in LDS and shared by its blocks, so the A operands come from LDS and the
+// vector-memory path carries only weights and scales, which each wave
+// prefetches 2*D tiles deep behind the staging loads. Several blocks per
+// workgroup keep every workgroup resident at once where one x stage per block
+// would not fit the chip's LDS (the launcher picks BPW). Memory-bound; the
 // MFMA pipe is mostly idle, so the -136 * sum(x) term is also computed on it,
 // by an MFMA against a constant -136 operand.
 // ---------------------------------------------------------------------------
-template <int WAVES, int D, int GSHIFT>
+template <int WAVES, int BPW, int D, int GSHIFT>
 __global__ __launch_bounds__(64 * WAVES) void w4a16_skinny_kernel(
     const uint16_t *__restrict__ x, const uint4 *__restrict__ wt,
     const uint16_t *__restrict__ sc, uint16_t *__restrict__ out, uint32_t *__restrict__ cnt,
@@ -50,7 +53,13 @@ __global__ __launch_bounds__(64 * WAVES) void w4a16_skinny_kernel(
     const int wave = wave_id();
     const int r = lane & 15, g = lane >> 4;
     const int lb = xcd_contiguous(blockIdx.x, gridDim.x);
-    const int nb = lb / splits, sp = lb % splits;
+    const int sp = lb % splits;
+    static_assert(WAVES % BPW == 0, "whole waves per block");
+    constexpr int wpb = WAVES / BPW;                   // waves per block
+    const int nb0 = (lb / splits) * BPW;               // first block of the workgroup
+    const int nblk = min(BPW, (N >> 4) - nb0);         // blocks it owns (last one: fewer)
+    const int bw = wave / wpb, wsub = wave - bw * wpb;   // this wave's block and rank in it
+    const int nb = nb0 + min(bw, nblk - 1);            // clamped: a wave past the last block idles
     const int KT = K >> 7;
     const __amdgpu_buffer_rsrc_t wr = make_rsrc(wt + (size_t)nb * KT * 64, (uint32_t)KT * 1024);
     const __amdgpu_buffer_rsrc_t sr = make_rsrc(sc + nb * 16, (uint32_t)(((size_t)(K >> GSHIFT) * N - nb * 16) * 2));
@@ -61,14 +70,14 @@ __global__ __launch_bounds__(64 * WAVES) void w4a16_skinny_kernel(
     // this workgroup's K range: tiles [kbeg, kbeg + kcnt) of the column block
     const int kbeg = sp * S;
     const int kcnt = KT - kbeg < S ? KT - kbeg : S;
-    const int ntile = wave < kcnt ? (kcnt - 1 - wave) / WAVES + 1 : 0;
+    const int ntile = (bw < nblk && wsub < kcnt) ? (kcnt - 1 - wsub) / wpb + 1 : 0;
     const uint4 bneg = make_uint4(kBf16Neg136Pair, kBf16Neg136Pair, kBf16Neg136Pair, kBf16Neg136Pair);
 
     uint4 wA[D], wB[D];
     uint32_t sA[D][NG], sB[D][NG];
 #define SVQ_LOAD(W, SS, I0)                                                          \
     _Pragma("unroll") for (int d = 0; d < D; ++d) if ((I0) + d < ntile) {            \
-        const int kt = kbeg + wave + ((I0) + d) * WAVES;                             \
+        const int kt = kbeg + wsub + ((I0) + d) * wpb;                               \
         W[d] = bload16(wr, w_vo, kt * 1024);                                         \
         _Pragma("unroll") for (int q = 0; q < NG; ++q) SS[d][q] = bload4(sr, s_vo, (kt * NG + q) * N * 2); \
     }
@@ -113,7 +122,7 @@ __global__ __launch_bounds__(64 * WAVES) void w4a16_skinny_kernel(
         }                                                                            \
         _Pragma("unroll") for (int d = 0; d < D; ++d) {                              \
             if ((I0) + d < ntile) {                                                  \
-                const uint8_t *ap = abase + (wave + ((I0) + d) * WAVES) * 256;       \
+                const uint8_t *ap = abase + (wsub + ((I0) + d) * wpb) * 256;         \
                 _Pragma("unroll") for (int q = 0; q < NG; ++q) {                     \
                     f32x4 P = {0.f, 0.f, 0.f, 0.f};                                  \
                     _Pragma("unroll") for (int jj = 0; jj < SPG; ++jj) {             \
@@ -151,12 +160,13 @@ __global__ __launch_bounds__(64 * WAVES) void w4a16_skinny_kernel(
         if (row < M) red[(wave * M + row) * 16 + r] = acc[i];
     }
     __syncthreads();
-    __shared__ int s_flag;
+    __shared__ int s_flags[16];
     float v = 0.f;
-    if (threadIdx.x < 16 * M) {
-        for (int w = 0; w < WAVES; ++w) v += red[w * M * 16 + threadIdx.x];
+    if (threadIdx.x < nblk * 16 * M) {
+        const int b = threadIdx.x / (16 * M), t = threadIdx.x - b * 16 * M;
+        for (int w = 0; w < wpb; ++w) v += red[((b * wpb + w) * M) * 16 + t];
     }
-    smallm_finish(v, M, N, nb, sp, splits, out, cnt, part, &s_flag);
+    multiblock_finish(v, M, N, nb0, nblk, sp, splits, out, cnt, part, s_flags);
 }
 
 // ---------------------------------------------------------------------------
@@ -515,27 +525,74 @@ __global__ __launch_bounds__(64 * WR * WC) void w4a16_wide_kernel(
 namespace {
 constexpr int kSkinnyDepth = 2;
 
-template <int WAVES, int GS>
-hipError_t skinny_launch_w(const SmallPlan &p, const void *x, const int32_t *wt, const void *sc, void *out,
-                           int M, int64_t N, int64_t K, void *ws, hipStream_t stream) {
-    hipLaunchKernelGGL((w4a16_skinny_kernel<WAVES, kSkinnyDepth, GS>),
-                       dim3((uint32_t)(N / 16 * p.splits)), dim3(64 * WAVES),
+template <int WAVES, int BPW, int GS>
+hipError_t skinny_launch_b(const SmallPlan &p, const void *x, const int32_t *wt, const void *sc,
+                           void *out, int M, int64_t N, int64_t K, void *ws, hipStream_t stream) {
+    const int64_t groups = (N / 16 + BPW - 1) / BPW;
+    hipLaunchKernelGGL((w4a16_skinny_kernel<WAVES, BPW, kSkinnyDepth, GS>),
+                       dim3((uint32_t)(groups * p.splits)), dim3(64 * WAVES),
                        skinny_lds_bytes(M, p.S, WAVES), stream,
                        (const uint16_t *)x, (const uint4 *)wt, (const uint16_t *)sc, (uint16_t *)out,
                        ws_counters(ws), (float *)ws_partials(ws), M, (int)N, (int)K, p.splits, p.S);
     return hipGetLastError();
 }
 
+template <int WAVES, int GS>
+hipError_t skinny_launch_w(const SmallPlan &p, int bpw, const void *x, const int32_t *wt, const void *sc,
+                           void *out, int M, int64_t N, int64_t K, void *ws, hipStream_t stream) {
+    switch (bpw) {
+    case 1: return skinny_launch_b<WAVES, 1, GS>(p, x, wt, sc, out, M, N, K, ws, stream);
+    case 2: return skinny_launch_b<WAVES, 2, GS>(p, x, wt, sc, out, M, N, K, ws, stream);
+    default: return skinny_launch_b<WAVES, 4, GS>(p, x, wt, sc, out, M, N, K, ws, stream);
+    }
+}
+
+// Workgroup shape: WAVES waves and bpw column blocks per workgroup (WAVES/bpw
+// waves per block), chosen so that the whole grid is resident at once
+// (registers, waves and LDS per CU), with as many waves per block as
+// possible and then as few blocks per workgroup as possible. One x stage per workgroup is shared by its blocks, so more blocks
+// per workgroup means fewer stages in LDS. If nothing fits, 4 waves and one
+// block per workgroup.
+struct SkinnyShape {
+    int waves, bpw;
+};
+
+template <int GS>
+SkinnyShape skinny_shape(const SmallPlan &p, int M, int64_t N) {
+    // register-limited residency (the BPW = 2 and 4 instances use as many registers)
+    static const int r16 = resident_blocks(w4a16_skinny_kernel<16, 1, kSkinnyDepth, GS>, 1024);
+    static const int r8 = resident_blocks(w4a16_skinny_kernel<8, 1, kSkinnyDepth, GS>, 512);
+    static const int r4 = resident_blocks(w4a16_skinny_kernel<4, 1, kSkinnyDepth, GS>, 256);
+    const int64_t blocks = N / 16;
+    SkinnyShape best{4, 1};
+    int best_wpb = 0;
+    for (const int waves : {16, 8, 4}) {
+        const int r_occ = waves == 16 ? r16 : waves == 8 ? r8 : r4;
+        const int r = std::min(r_occ, (int)(kLdsPerCu / skinny_lds_bytes(M, p.S, waves)));
+        // bpw * 16 * M outputs are summed by one thread each: bpw * M <= 4 * waves
+        for (int bpw = 1; bpw <= 4 && bpw * M <= 4 * waves; bpw *= 2) {
+            if ((blocks + bpw - 1) / bpw * p.splits <= (int64_t)r * p.cus) {
+                // most waves per block; on a tie, fewer blocks per workgroup
+                // (measured: 640 workgroups of 8 waves beat 320 of 16 waves)
+                if (waves / bpw > best_wpb || (waves / bpw == best_wpb && bpw < best.bpw)) {
+                    best = SkinnyShape{waves, bpw};
+                    best_wpb = waves / bpw;
+                }
+                break;
+            }
+        }
+    }
+    return best;
+}
+
 template <int GS>
 hipError_t skinny_launch(const SmallPlan &p, const void *x, const int32_t *wt, const void *sc, void *out,
                          int M, int64_t N, int64_t K, void *ws, hipStream_t stream) {
-    static const int r16 = resident_blocks(w4a16_skinny_kernel<16, kSkinnyDepth, GS>, 1024);
-    static const int r8 = resident_blocks(w4a16_skinny_kernel<8, kSkinnyDepth, GS>, 512);
-    const int by_lds = (int)(kLdsPerCu / skinny_lds_bytes(M, p.S, 16));
-    switch (pick_waves(N / 16 * p.splits, p.cus, std::min(r16, by_lds), std::min(r8, by_lds))) {
-    case 16: return skinny_launch_w<16, GS>(p, x, wt, sc, out, M, N, K, ws, stream);
-    case 8: return skinny_launch_w<8, GS>(p, x, wt, sc, out, M, N, K, ws, stream);
-    default: return skinny_launch_w<4, GS>(p, x, wt, sc, out, M, N, K, ws, stream);
+    const SkinnyShape sh = skinny_shape<GS>(p, M, N);
+    switch (sh.waves) {
+    case 16: return skinny_launch_w<16, GS>(p, sh.bpw, x, wt, sc, out, M, N, K, ws, stream);
+    case 8: return skinny_launch_w<8, GS>(p, sh.bpw, x, wt, sc, out, M, N, K, ws, stream);
+    default: return skinny_launch_w<4, GS>(p, sh.bpw, x, wt, sc, out, M, N, K, ws, stream);
     }
 }
 

@@ -186,6 +186,28 @@ def test_w4a16_workloads(name):
     np.testing.assert_array_equal(tiled.cpu().numpy(), oracle.q4_repack(inp.qweight))
 
 
+# Skinny shapes whose workgroups own several column blocks on a 256-CU part (one x
+# stage of 59 KB per workgroup: two workgroups per CU): N = 5136 -> 2 blocks per
+# workgroup, N = 6416 -> 4; both leave a last workgroup with a single block, and both
+# split K = 17408 three ways (the split path reduces per block).
+@pytest.mark.parametrize("N", [5136, 6416])
+def test_w4a16_skinny_multiblock(N):
+    M, K = 5, 17408
+    _say("w4a16 skinny multi-block M K N", M, K, N)
+    if torch.cuda.get_device_properties(0).multi_processor_count != 256:
+        pytest.skip("shapes chosen for a 256-CU part")
+    inp = synth.gen_w4a16(3000 + N, M, K, N, 128)
+    out, _ = run_w4a16(inp, 2)
+    rows, cols = _sample(M, N, 1200, N)
+    cols[4:36] = np.arange(N - 32, N)        # the last workgroup's single block and its neighbour
+    y64, y32 = oracle.w4a16_points(inp.x, inp.qweight, inp.scales, 128, rows, cols)
+    sel = out[rows, cols]
+    ok, err, rms = oracle.gate(sel, y64)
+    assert ok, f"N={N}: err={err:.4g} rms={rms:.4g}"
+    assert oracle.gate(sel, y32.astype(np.float64))[0]
+    assert np.all(np.isfinite(oracle.bf16_bits_to_f64(out)))
+
+
 # ---- MXFP8 -------------------------------------------------------------------------
 
 MX_CASES = (

@@ -289,6 +289,10 @@ namespace {
 SmallPlan w4a16_small_plan(int k, int64_t M, int64_t N, int64_t K, int cus) {
     return plan_smallm(M, N, K, cus, k == SVQ_KERNEL_MFMA_SKINNY ? skinny_max_tiles(M) : 0);
 }
+// the MXFP8 skinny kernel stages x in LDS the same way
+SmallPlan mxfp8_small_plan(int k, int64_t M, int64_t N, int64_t K, int cus) {
+    return plan_smallm(M, N, K, cus, k == SVQ_KERNEL_MFMA_SKINNY ? skinny_max_tiles(M) : 0);
+}
 }  // namespace
 
 size_t svq_w4a16_workspace_bytes(int kernel, int64_t M, int64_t N, int64_t K, int32_t G) {
@@ -361,7 +365,7 @@ size_t svq_mxfp8_workspace_bytes(int kernel, int64_t M, int64_t N, int64_t K) {
     if (check_mxfp8_shape(M, N, K, 32) != SVQ_OK) return (size_t)-1;
     const int k = resolve_kernel(kernel, M, true);
     if (kernel_fits(k, M) != SVQ_OK) return (size_t)-1;
-    if (k != SVQ_KERNEL_MFMA_WIDE) return plan_smallm(M, N, K, device_cus()).workspace_bytes;
+    if (k != SVQ_KERNEL_MFMA_WIDE) return mxfp8_small_plan(k, M, N, K, device_cus()).workspace_bytes;
     return plan_mxfp8_wide(M, N, K, device_cus()).workspace_bytes;
 }
 
@@ -391,7 +395,7 @@ int svq_mxfp8_gemm_with(int kernel, const void *x, const uint8_t *w, const uint8
         need = wplan.workspace_bytes;
         if (need && (size_t)wplan.row_tiles * wplan.col_tiles * kSkCountersPerTile > kMaxCounters) return SVQ_ERR_UNSUPPORTED;
     } else {
-        splan = plan_smallm(M, N, K, cus);
+        splan = mxfp8_small_plan(k, M, N, K, cus);
         need = splan.workspace_bytes;
         if (splan.splits > 1 && N / 16 > (int64_t)kMaxCounters) return SVQ_ERR_UNSUPPORTED;
     }

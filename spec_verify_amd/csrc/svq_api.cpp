@@ -453,7 +453,7 @@ int svq_mxfp8_quantize(const void *w, int32_t optimized, uint8_t *codes, uint8_t
 
 size_t svq_w8a16_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t G) {
     if (check_w4a16_shape(M, N, K, G) != SVQ_OK || M > 16) return (size_t)-1;
-    return plan_smallm(M, N, K, device_cus()).workspace_bytes;
+    return plan_smallm(M, N, K, device_cus(), skinny_max_tiles(M)).workspace_bytes;
 }
 
 const char *svq_w8a16_kernel_name(int64_t M, int64_t N, int64_t K, int32_t G) {
@@ -470,7 +470,8 @@ int svq_w8a16_gemm(const void *x, const int8_t *w, const void *scales, void *out
     const size_t xb = (size_t)M * K * 2, wb = (size_t)N * K, sb = (size_t)(K / G) * N * 2, ob = (size_t)M * N * 2;
     st = check_gemm_buffers(x, xb, w, wb, scales, sb, out, ob, nullptr, 0, 0, 4);
     if (st != SVQ_OK) return st;
-    const SmallPlan plan = plan_smallm(M, N, K, device_cus());
+    // the kernel stages x of its K range in LDS: cap the range as for the W4A16 skinny kernel
+    const SmallPlan plan = plan_smallm(M, N, K, device_cus(), skinny_max_tiles(M));
     if (plan.splits > 1 && N / 16 > (int64_t)kMaxCounters) return SVQ_ERR_UNSUPPORTED;
     st = check_gemm_buffers(x, xb, w, wb, scales, sb, out, ob, workspace, workspace_bytes,
                             plan.workspace_bytes, 4);

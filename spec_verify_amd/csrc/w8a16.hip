@@ -46,13 +46,17 @@ __device__ __forceinline__ uint4 i8x8_to_bf16(uint32_t lo, uint32_t hi) {
 }
 
 // ---------------------------------------------------------------------------
-// W8A16 skinny MFMA kernel, M <= 16
+// W8A16 skinny MFMA kernel, M <= 16: one 16-column block and a range of S
+// K-tiles per workgroup, x of the range staged once in LDS (the vocabulary
+// head, M = 1, K = 5120, N = 248320: 243 -> 218 us against x loaded per tile),
+// waves take the tiles round-robin, 8 MFMAs per tile (4 bias, 4 weight).
 // ---------------------------------------------------------------------------
 template <int WAVES, int D, int GSHIFT>
 __global__ __launch_bounds__(64 * WAVES) void w8a16_skinny_kernel(
     const uint16_t *__restrict__ x, const int8_t *__restrict__ w,
     const uint16_t *__restrict__ sc, uint16_t *__restrict__ out, uint32_t *__restrict__ cnt,
     float *__restrict__ part, int M, int N, int K, int splits, int S) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     constexpr int NG = 128 >> GSHIFT;  // groups per 128-row tile
     constexpr int SPG = 4 / NG;        // MFMA steps per group
     constexpr bool kTrans = GSHIFT < 7;
@@ -63,13 +67,8 @@ __global__ __launch_bounds__(64 * WAVES) void w8a16_skinny_kernel(
     const int nb = lb / splits, sp = lb % splits;
     const int KT = K >> 7;
     const __amdgpu_buffer_rsrc_t wr = make_rsrc(w + (size_t)nb * 16 * K, (uint32_t)16 * K);
-    const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, (uint32_t)M * K * 2);
     const __amdgpu_buffer_rsrc_t sr = make_rsrc(sc + nb * 16, (uint32_t)(((size_t)(K >> GSHIFT) * N - nb * 16) * 2));
     const uint32_t w_vo = r * K + g * 32;
-    // A operand of MFMA step j: x row r (rows >= M read as zero), K-rows
-    // 32j + 8g.. for every group size below 128 (the weight words are
-    // transposed to match) or 32g + 8j.. for 128
-    const uint32_t x_vo = r * K * 2 + (kTrans ? 16 * g : 64 * g);
     constexpr int kXStep = kTrans ? 64 : 16;
     // the aligned dword holding this lane's fp16 scale; s_sh selects the half
     const uint32_t s_vo = (r & 14) * 2;
@@ -81,19 +80,48 @@ __global__ __launch_bounds__(64 * WAVES) void w8a16_skinny_kernel(
     const uint4 bneg = make_uint4(kBf16Neg128Pair, kBf16Neg128Pair, kBf16Neg128Pair, kBf16Neg128Pair);
 
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    uint4 vA[D][2], vB[D][2], aA[D][4], aB[D][4];
+    uint4 vA[D][2], vB[D][2];
     uint32_t sA[D][NG], sB[D][NG];
 
-#define SVQ_LOAD(V, A, SS, I0)                                                       \
+#define SVQ_LOAD(V, SS, I0)                                                          \
     _Pragma("unroll") for (int d = 0; d < D; ++d) if ((I0) + d < ntile) {            \
         const int kt = kbeg + wave + ((I0) + d) * WAVES;                             \
         V[d][0] = bload16(wr, w_vo, kt * 128);                                       \
         V[d][1] = bload16(wr, w_vo + 16, kt * 128);                                  \
-        _Pragma("unroll") for (int j = 0; j < 4; ++j) A[d][j] = bload16(xr, x_vo + kXStep * j, kt * 256); \
         _Pragma("unroll") for (int q = 0; q < NG; ++q) SS[d][q] = bload4(sr, s_vo, (kt * NG + q) * N * 2); \
     }
-#define SVQ_COMPUTE(V, A, SS, I0)                                                    \
+    // stage x[0..M)[128*kbeg, 128*(kbeg+kcnt)) in LDS by DMA (one 64-chunk
+    // segment of a row per instruction), rows padded by 16 bytes so that the
+    // 16-byte A reads of different rows fall in different banks; the weight
+    // prefetch is issued behind it and only the x loads are waited for
+    const int xs_stride = kcnt * 256 + 16;
+    {
+        const int row_chunks = kcnt * 16;
+        const int nseg = (row_chunks + 63) >> 6;
+        for (int i = wave; i < M * nseg; i += WAVES) {
+            const int m = i / nseg, c = ((i - m * nseg) << 6) + lane;
+            if (c < row_chunks)
+                dma16(x + (size_t)m * K + (size_t)kbeg * 128 + c * 8, smem + m * xs_stride + ((c - lane) << 4));
+        }
+    }
+    if (ntile > 0) SVQ_LOAD(vA, sA, 0)
+    if (ntile > D) SVQ_LOAD(vB, sB, D)
+    {
+        const int na = ntile < D ? ntile : D;
+        const int nb2 = ntile - D < 0 ? 0 : (ntile - D < D ? ntile - D : D);
+        wait_vmcnt_at_most<2 * D * (2 + NG)>((na + nb2) * (2 + NG));
+    }
+    // a bare barrier: __syncthreads() would also wait for the weight prefetch
+    __builtin_amdgcn_s_barrier();
+    // A operand of MFMA step j: x row min(r, M-1) (rows past M repeat the last
+    // row; their products are never stored), K-rows 32j + 8g.. for every group
+    // size below 128 (the weight words are transposed to match) or 32g + 8j..
+    const int arow = r < M ? r : M - 1;
+    const uint8_t *abase = smem + arow * xs_stride + (kTrans ? 16 * g : 64 * g);
+
+#define SVQ_COMPUTE(V, SS, I0)                                                       \
     _Pragma("unroll") for (int d = 0; d < D; ++d) if ((I0) + d < ntile) {            \
+        const uint8_t *ap = abase + (wave + ((I0) + d) * WAVES) * 256;               \
         uint32_t lo[4] = {V[d][0].x, V[d][0].z, V[d][1].x, V[d][1].z};               \
         uint32_t hi[4] = {V[d][0].y, V[d][0].w, V[d][1].y, V[d][1].w};               \
         if constexpr (kTrans) {                                                      \
@@ -104,8 +132,9 @@ __global__ __launch_bounds__(64 * WAVES) void w8a16_skinny_kernel(
             f32x4 P = {0.f, 0.f, 0.f, 0.f};                                          \
             _Pragma("unroll") for (int jj = 0; jj < SPG; ++jj) {                     \
                 const int j = q * SPG + jj;                                          \
-                P = mfma16x16x32(A[d][j], bneg, P);                                  \
-                P = mfma16x16x32(A[d][j], i8x8_to_bf16(lo[j], hi[j]), P);            \
+                const uint4 A = *(const uint4 *)(ap + j * kXStep);                   \
+                P = mfma16x16x32(A, bneg, P);                                        \
+                P = mfma16x16x32(A, i8x8_to_bf16(lo[j], hi[j]), P);                  \
             }                                                                        \
             const float sf = fp16_bits_to_f32((uint16_t)(SS[d][q] >> s_sh));         \
             _Pragma("unroll") for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(sf, P[i], acc[i]); \
@@ -113,29 +142,32 @@ __global__ __launch_bounds__(64 * WAVES) void w8a16_skinny_kernel(
     }
 
     if (ntile > 0) {
-        SVQ_LOAD(vA, aA, sA, 0)
         for (int i0 = 0;; i0 += 2 * D) {
-            SVQ_LOAD(vB, aB, sB, i0 + D)
-            SVQ_COMPUTE(vA, aA, sA, i0)
+            SVQ_COMPUTE(vA, sA, i0)
             if (i0 + D >= ntile) break;
-            SVQ_LOAD(vA, aA, sA, i0 + 2 * D)
-            SVQ_COMPUTE(vB, aB, sB, i0 + D)
+            SVQ_LOAD(vA, sA, i0 + 2 * D)
+            SVQ_COMPUTE(vB, sB, i0 + D)
             if (i0 + 2 * D >= ntile) break;
+            SVQ_LOAD(vB, sB, i0 + 3 * D)
         }
     }
 #undef SVQ_LOAD
 #undef SVQ_COMPUTE
 
-    // cross-wave sum of the valid rows through LDS, in wave order
-    __shared__ float red[WAVES][16][17];
+    // cross-wave sum of the valid rows through LDS, in wave order (the x
+    // stage is dead now)
+    __syncthreads();
+    float *red = (float *)smem;  // [WAVES][M][16]
 #pragma unroll
-    for (int i = 0; i < 4; ++i) red[wave][4 * g + i][r] = acc[i];
+    for (int i = 0; i < 4; ++i) {
+        const int row = 4 * g + i;
+        if (row < M) red[(wave * M + row) * 16 + r] = acc[i];
+    }
     __syncthreads();
     __shared__ int s_flag;
     float v = 0.f;
     if (threadIdx.x < 16 * M) {
-#pragma unroll
-        for (int wv = 0; wv < WAVES; ++wv) v += red[wv][threadIdx.x >> 4][threadIdx.x & 15];
+        for (int wv = 0; wv < WAVES; ++wv) v += red[wv * M * 16 + threadIdx.x];
     }
     smallm_finish(v, M, N, nb, sp, splits, out, cnt, part, &s_flag);
 }
@@ -215,7 +247,7 @@ template <int WAVES, int GS>
 hipError_t w8_skinny_launch_w(const SmallPlan &p, const void *x, const int8_t *w, const void *sc,
                               void *out, int M, int64_t N, int64_t K, void *ws, hipStream_t stream) {
     hipLaunchKernelGGL((w8a16_skinny_kernel<WAVES, kW8SkinnyDepth, GS>), dim3((uint32_t)(N / 16 * p.splits)),
-                       dim3(64 * WAVES), 0, stream, (const uint16_t *)x, w, (const uint16_t *)sc,
+                       dim3(64 * WAVES), skinny_lds_bytes(M, p.S, WAVES), stream, (const uint16_t *)x, w, (const uint16_t *)sc,
                        (uint16_t *)out, ws_counters(ws), (float *)ws_partials(ws), M, (int)N, (int)K,
                        p.splits, p.S);
     return hipGetLastError();
@@ -226,7 +258,8 @@ hipError_t w8_skinny_launch(const SmallPlan &p, const void *x, const int8_t *w, 
                             void *out, int M, int64_t N, int64_t K, void *ws, hipStream_t stream) {
     static const int r16 = resident_blocks(w8a16_skinny_kernel<16, kW8SkinnyDepth, GS>, 1024);
     static const int r8 = resident_blocks(w8a16_skinny_kernel<8, kW8SkinnyDepth, GS>, 512);
-    switch (pick_waves(N / 16 * p.splits, p.cus, r16, r8)) {
+    const int by_lds = (int)(kLdsPerCu / skinny_lds_bytes(M, p.S, 16));
+    switch (pick_waves(N / 16 * p.splits, p.cus, std::min(r16, by_lds), std::min(r8, by_lds))) {
     case 16: return w8_skinny_launch_w<16, GS>(p, x, w, sc, out, M, N, K, ws, stream);
     case 8: return w8_skinny_launch_w<8, GS>(p, x, w, sc, out, M, N, K, ws, stream);
     default: return w8_skinny_launch_w<4, GS>(p, x, w, sc, out, M, N, K, ws, stream);

@@ -56,6 +56,9 @@ def host_u16(t):
 CASES = [
     ("w4a16-dot2-split", "w4a16", 1, 5120, 256, 1),
     ("w4a16-skinny-split", "w4a16", 5, 17408, 512, 2),
+    # two column blocks per workgroup (x stages would not all fit one per block),
+    # a ragged last workgroup, K split three ways: counters cleared per block
+    ("w4a16-skinny-multiblock-split", "w4a16", 5, 17408, 5136, 2),
     ("w4a16-wide-streamk", "w4a16", 128, 2048, 1024, 3),
     ("mxfp8-dot2-split", "mxfp8", 2, 4096, 256, 1),
     ("mxfp8-wide-streamk", "mxfp8", 100, 2048, 512, 3),

@@ -134,6 +134,27 @@ def test_w4a16_narrow(kernel, M, K, N, G):
     assert_gate(out, y64, y32, f"narrow M{M} K{K} N{N} G{G}")
 
 
+# fp16 scales at the ends of their range, per (group, column): zero, the smallest
+# subnormal (2^-24), the smallest normal (2^-14), the largest finite value, negative
+# values and one; the kernels convert the scale to fp32 exactly, so the gate against
+# the fp64 and fp32 oracles holds as for ordinary scales
+EXTREME_SCALES = np.array([0x0000, 0x0001, 0x0400, 0x7BFF, 0xB800, 0x3C00, 0x8001, 0x03FF], dtype=np.uint16)
+
+
+@pytest.mark.parametrize("kernel,M,N", [(1, 1, 64), (1, 1, 1024), (1, 3, 64), (2, 5, 64), (3, 40, 64)],
+                         ids=["dot2-1", "narrow-1", "dot2-3", "skinny-5", "wide-40"])
+@pytest.mark.parametrize("G", [32, 128])
+def test_w4a16_extreme_scales(kernel, M, N, G):
+    _say("w4a16 extreme scales kernel", kernel, "M", M, "N", N, "G", G)
+    K = 512
+    inp = synth.gen_w4a16(4000 + 13 * M + G, M, K, N, G)
+    rng = np.random.default_rng(4100 + M + G)
+    inp.scales = EXTREME_SCALES[rng.integers(0, len(EXTREME_SCALES), size=inp.scales.shape)]
+    out, _ = run_w4a16(inp, kernel)
+    y64, y32 = oracle.w4a16(inp.x, inp.qweight, inp.scales, G)
+    assert_gate(out, y64, y32, f"extreme scales kernel {kernel} M{M} G{G}")
+
+
 W4_EXACT = [
     (1, 1, 1024, 32, 128), (1, 5, 1024, 32, 32), (1, 8, 640, 48, 64),
     (2, 1, 1024, 32, 128), (2, 7, 1024, 32, 32), (2, 16, 640, 48, 64),

@@ -174,66 +174,104 @@ __global__ __launch_bounds__(64 * WAVES) void w8a16_skinny_kernel(
 
 // ---------------------------------------------------------------------------
 // Load-time quantizer: dense bf16 W [N][K] -> codes + fp16 scales [K/G][N].
-// Thread (n, group): lanes of a wave take consecutive rows n, the waves of a
-// workgroup consecutive groups, so the scale and GPTQ-word stores of a wave
-// are contiguous. Per group, in fp32 with IEEE division:
+// A workgroup quantizes four groups of 64 consecutive rows: G/8 lanes per row,
+// each lane 8 consecutive weights (one 16-byte load; a row's group is one
+// contiguous run of 2G bytes, read by consecutive lanes). The group maximum is
+// reduced over the row's lanes with DPP and each lane quantizes its 8 weights.
+// int8 codes go straight to [N][K] (8 contiguous bytes per lane); GPTQ words
+// ([K/8][N]) and scales ([K/G][N]) are transposed through LDS, so that one
+// wave stores 64 consecutive columns at once. Per group, in fp32 with IEEE
+// division:
 //   amax = max |w|, s = fp16_rne(amax / qmax), q = clamp(rint(w / s), -qmax-1, qmax)
 // with s used as stored; a group whose stored scale is zero gets q = 0.
 // ---------------------------------------------------------------------------
+constexpr int kRtnGroupsPerWg = 4;  // groups one workgroup quantizes (loads issued together)
+
 template <int BITS, int GSHIFT>
-__global__ __launch_bounds__(256) void rtn_quantize_kernel(const uint16_t *__restrict__ w,
-                                                           void *__restrict__ codes,
-                                                           uint16_t *__restrict__ scales, int N,
-                                                           int K) {
+__global__ __launch_bounds__(8 << GSHIFT) void rtn_quantize_kernel(const uint16_t *__restrict__ w,
+                                                                 void *__restrict__ codes,
+                                                                 uint16_t *__restrict__ scales, int N,
+                                                                 int K) {
     constexpr int G = 1 << GSHIFT;
+    constexpr int L = G / 8;  // lanes per row (4, 8 or 16: within one 16-lane DPP row)
+    constexpr int GP = kRtnGroupsPerWg;
     constexpr float kQmax = (float)((1 << (BITS - 1)) - 1);
-    const int n = blockIdx.x * 64 + (threadIdx.x & 63);
-    const int grp = blockIdx.y * 4 + (threadIdx.x >> 6);
-    if (n >= N || grp >= (K >> GSHIFT)) return;
-    const uint4 *src = (const uint4 *)(w + (size_t)n * K + (size_t)grp * G);
-    uint4 v[G / 8];
+    __shared__ uint32_t words[BITS == 4 ? GP : 1][BITS == 4 ? L : 1][65];
+    __shared__ uint16_t sc_lds[GP][64];
+    const int t = threadIdx.x;
+    const int r = t / L, l = t % L;  // row within the workgroup, lane within the row
+    const int n0 = blockIdx.x * 64;
+    const int n = n0 + r;
+    const int ngroups = K >> GSHIFT;
+    const int g0 = blockIdx.y * GP;
+    uint4 v[GP];
 #pragma unroll
-    for (int i = 0; i < G / 8; ++i) v[i] = src[i];
-    auto elem = [&](int e) {  // bf16 -> fp32, exact
-        const uint4 &c = v[e >> 3];
-        const uint32_t word = ((e >> 1) & 3) == 0 ? c.x : ((e >> 1) & 3) == 1 ? c.y : ((e >> 1) & 3) == 2 ? c.z : c.w;
-        return bits_f32((e & 1) ? (word & 0xffff0000u) : (word << 16));
-    };
-    float amax = 0.f;
+    for (int gi = 0; gi < GP; ++gi) {
+        v[gi] = make_uint4(0u, 0u, 0u, 0u);
+        if (n < N && g0 + gi < ngroups) v[gi] = *(const uint4 *)(w + (size_t)n * K + (size_t)(g0 + gi) * G + 8 * l);
+    }
 #pragma unroll
-    for (int e = 0; e < G; ++e) amax = fmaxf(amax, fabsf(elem(e)));
-    const __half s16 = __float2half_rn(__fdiv_rn(amax, kQmax));
-    const float s = __half2float(s16);
-    scales[(size_t)grp * N + n] = __half_as_ushort(s16);
-    auto code = [&](int e) -> int {
-        if (!(s > 0.f)) return 0;
-        const float t = rintf(__fdiv_rn(elem(e), s));
-        return (int)fminf(fmaxf(t, -kQmax - 1.f), kQmax);
-    };
-    if constexpr (BITS == 8) {
-        uint4 *dst = (uint4 *)((int8_t *)codes + (size_t)n * K + (size_t)grp * G);
+    for (int gi = 0; gi < GP; ++gi) {
+        const int grp = g0 + gi;
+        const uint32_t wd[4] = {v[gi].x, v[gi].y, v[gi].z, v[gi].w};
+        float e[8];
 #pragma unroll
-        for (int i = 0; i < G / 16; ++i) {
-            uint32_t d[4];
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                uint32_t word = 0;
-#pragma unroll
-                for (int b = 0; b < 4; ++b) word |= ((uint32_t)code(16 * i + 4 * c + b) & 0xffu) << (8 * b);
-                d[c] = word;
-            }
-            dst[i] = make_uint4(d[0], d[1], d[2], d[3]);
+        for (int i = 0; i < 4; ++i) {  // bf16 -> fp32, exact
+            e[2 * i] = bits_f32(wd[i] << 16);
+            e[2 * i + 1] = bits_f32(wd[i] & 0xffff0000u);
         }
-    } else {
-        // GPTQ words [K/8][N]: nibble i of word k/8 is row k (least significant first)
-        int32_t *dst = (int32_t *)codes + (size_t)grp * (G / 8) * N + n;
+        float amax = 0.f;
 #pragma unroll
-        for (int j = 0; j < G / 8; ++j) {
+        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(e[i]));
+        // maximum over the row's L lanes: quads, then pairs of quads, then halves
+        amax = fmaxf(amax, bits_f32(__builtin_amdgcn_mov_dpp(f32_bits(amax), 0xB1, 0xF, 0xF, true)));  // quad_perm [1,0,3,2]
+        amax = fmaxf(amax, bits_f32(__builtin_amdgcn_mov_dpp(f32_bits(amax), 0x4E, 0xF, 0xF, true)));  // quad_perm [2,3,0,1]
+        if constexpr (L >= 8)
+            amax = fmaxf(amax, bits_f32(__builtin_amdgcn_mov_dpp(f32_bits(amax), 0x141, 0xF, 0xF, true)));  // row_half_mirror
+        if constexpr (L >= 16)
+            amax = fmaxf(amax, bits_f32(__builtin_amdgcn_mov_dpp(f32_bits(amax), 0x140, 0xF, 0xF, true)));  // row_mirror
+        const __half s16 = __float2half_rn(__fdiv_rn(amax, kQmax));
+        const float s = __half2float(s16);
+        if (l == 0) sc_lds[gi][r] = __half_as_ushort(s16);
+        int q[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            q[i] = 0;
+            if (s > 0.f) {
+                const float tq = rintf(__fdiv_rn(e[i], s));
+                q[i] = (int)fminf(fmaxf(tq, -kQmax - 1.f), kQmax);
+            }
+        }
+        if constexpr (BITS == 8) {
+            uint32_t lo = 0, hi = 0;
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                lo |= ((uint32_t)q[b] & 0xffu) << (8 * b);
+                hi |= ((uint32_t)q[4 + b] & 0xffu) << (8 * b);
+            }
+            if (n < N && grp < ngroups)
+                *(uint2 *)((int8_t *)codes + (size_t)n * K + (size_t)grp * G + 8 * l) = make_uint2(lo, hi);
+        } else {
+            // GPTQ word grp*L + l of column n: nibble b is row 8 * (grp*L + l) + b
             uint32_t word = 0;
 #pragma unroll
-            for (int b = 0; b < 8; ++b) word |= (uint32_t)(code(8 * j + b) + 8) << (4 * b);
-            dst[(size_t)j * N] = (int32_t)word;
+            for (int b = 0; b < 8; ++b) word |= (uint32_t)(q[b] + 8) << (4 * b);
+            words[gi][l][r] = word;
         }
+    }
+    __syncthreads();
+    if (t < 64 && n0 + t < N) {
+#pragma unroll
+        for (int gi = 0; gi < GP; ++gi)
+            if (g0 + gi < ngroups) scales[(size_t)(g0 + gi) * N + n0 + t] = sc_lds[gi][t];
+    }
+    if constexpr (BITS == 4) {
+        // thread t stores word row grp*L + t/64, column n0 + t%64 (blockDim = 64 * L)
+        const int kw = t >> 6, c = t & 63;
+#pragma unroll
+        for (int gi = 0; gi < GP; ++gi)
+            if (n0 + c < N && g0 + gi < ngroups)
+                ((int32_t *)codes)[((size_t)(g0 + gi) * L + kw) * N + n0 + c] = (int32_t)words[gi][kw][c];
     }
 }
 
@@ -271,8 +309,9 @@ hipError_t w8_skinny_launch(const SmallPlan &p, const void *x, const int8_t *w, 
 
 template <int BITS, int GS>
 hipError_t rtn_launch(const void *w, void *codes, void *scales, int64_t N, int64_t K, hipStream_t stream) {
-    const dim3 grid((uint32_t)((N + 63) / 64), (uint32_t)(((K >> GS) + 3) / 4));
-    hipLaunchKernelGGL((rtn_quantize_kernel<BITS, GS>), grid, dim3(256), 0, stream,
+    // one workgroup per (64 rows, kRtnGroupsPerWg groups): G/8 lanes per row
+    const dim3 grid((uint32_t)((N + 63) / 64), (uint32_t)(((K >> GS) + kRtnGroupsPerWg - 1) / kRtnGroupsPerWg));
+    hipLaunchKernelGGL((rtn_quantize_kernel<BITS, GS>), grid, dim3(8 << GS), 0, stream,
                        (const uint16_t *)w, codes, (uint16_t *)scales, (int)N, (int)K);
     return hipGetLastError();
 }

@@ -337,10 +337,11 @@ def test_w8a16_integer_exact(M, K, N, G):
 
 @pytest.mark.parametrize("bits", [8, 4])
 @pytest.mark.parametrize("G", [32, 64, 128])
-def test_rtn_quantize_bit_exact(bits, G):
+@pytest.mark.parametrize("N", [80, 77])
+def test_rtn_quantize_bit_exact(bits, G, N):
     import spec_verify_amd as svq
-    N, K = 80, 1024
-    _say("rtn bits G", bits, G)
+    K = 1024   # N = 80 and 77: the last 64-row workgroup holds 16 and 13 rows
+    _say("rtn bits G N", bits, G, N)
     wb = synth.gen_dense_bf16(700 + bits + G, N, K)
     wb[3, :G] = 0                                  # an all-zero group: scale 0, codes 0
     q, s = svq.rtn_quantize(dev(wb), bits, G)

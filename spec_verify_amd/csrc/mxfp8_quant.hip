@@ -14,7 +14,9 @@
 // between v and the decoded values, added in ascending element order in fp32.
 // A later candidate replaces the kept one only with a strictly smaller score.
 // The score is computed with explicit round-to-nearest subtract, multiply and
-// add (no contraction), so the choice depends on nothing but these steps.
+// add (no contraction), so the choice depends on nothing but these steps. The
+// kernel scores only the candidates that can win (the reasons are given where
+// the candidates are scored), which gives the same choice.
 //
 // One thread per block: 64 bytes of bf16 in, 32 code bytes and 1 scale byte
 // out. Consecutive threads take consecutive blocks of a row, so loads, code
@@ -102,11 +104,28 @@ __global__ __launch_bounds__(256) void mxfp8_quantize_kernel(const uint4 *__rest
     uint32_t best[8], cand[8];
     float best_err = mx_candidate(v, b0, best);
     int best_b = b0;
+    // Of the other two candidates only twice the scale can win, and only when
+    // the baseline saturates an element (amax / 2^X > 448), so only then is it
+    // scored; the choice is the same as scoring both in order:
+    //  * No element above 448 * 2^X: at twice the scale every element's nearest
+    //    representable value is one the baseline also has, so each element's
+    //    error is at least the baseline's, and the fp32 sum of element errors
+    //    in the same order (rounded addition is monotonic) is not smaller.
+    //  * Half the scale (b0 > 0, so amax / 2^X is in [256, 512)): the block
+    //    maximum saturates and its error grows by at least 768 * 4^X, while only
+    //    elements below the baseline's normal range (error < 2^(2X-10) each)
+    //    can gain; fp32 rounding of the sums is far below the difference, and
+    //    where 4^X is so small that it is not, those gains round to zero. So
+    //    half the scale is never strictly better and is not scored.
+    const bool sat = ldexpf(amax, 127 - b0) > 448.0f;
     if (optimized) {
+        // the candidates in the definition's order, skipping those that cannot
+        // win (the loop form keeps one copy of the scoring code)
 #pragma unroll 1
         for (int k = 0; k < 2; ++k) {
             const int bc = k == 0 ? b0 + 1 : b0 - 1;
-            if (bc < 0 || bc > 254) continue;
+            const bool can_win = k == 0 && sat;
+            if (bc < 0 || bc > 254 || !can_win) continue;
             const float e = mx_candidate(v, bc, cand);
             if (e < best_err) {
                 best_err = e;

@@ -19,12 +19,6 @@ constexpr uint32_t kNibblePairMask = 0x000F000Fu;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// 16-byte streaming load (non-temporal hint: weights are read exactly once).
-__device__ __forceinline__ uint4 load_stream16(const void *p) {
-    const u32x4 v = __builtin_nontemporal_load((const u32x4 *)p);
-    return make_uint4(v.x, v.y, v.z, v.w);
-}
-
 // Raw (unswizzled, byte-addressed) buffer resource over [base, base + bytes).
 // Loads past `bytes` return zero, which the kernels use for padding rows.
 // DWORD3 = 0x00020000: 32-bit data format, the gfx9-family value for raw loads.
@@ -37,15 +31,6 @@ __device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff
 }
 __device__ __forceinline__ uint32_t bload4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
     return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
-}
-// The 16- and 8-bit loads return their own width: widening the result at the
-// load would make the compiler wait for the load right there (it masks the
-// high bits), which serializes a prefetch.
-__device__ __forceinline__ uint16_t bload2(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-    return __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
-}
-__device__ __forceinline__ uint8_t bload1(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-    return __builtin_amdgcn_raw_buffer_load_b8(r, voff, soff, 0);
 }
 
 // The wave index as a wave-uniform (scalar) value.
@@ -64,13 +49,6 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 
 __device__ __forceinline__ float fp16_bits_to_f32(uint16_t h) {
     return (float)__builtin_bit_cast(_Float16, h);
-}
-
-// Two bf16 weights (128 + q_lo, 128 + q_hi) from nibble slots s and s+4 of a
-// repacked word (the repack puts rows 2s and 2s+1 of an 8-row run there).
-template <int S>
-__device__ __forceinline__ uint32_t nibble_pair_bf16(uint32_t w) {
-    return ((w >> (4 * S)) & kNibblePairMask) | kMagic128Pair;
 }
 
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {

@@ -274,7 +274,7 @@ __global__ __launch_bounds__(1024) void w4a16_narrow_kernel(
 
 namespace {
 constexpr int kDot2Depth = 4;
-constexpr int kNarrowPerCu = 1;  // workgroups per CU of the balanced plan
+constexpr int kNarrowPerCu = 1;  // workgroups per CU of the narrow-unit plan
 
 template <int M, int WAVES, int GS>
 hipError_t dot2_launch_w(const SmallPlan &p, const void *x, const int32_t *wt, const void *sc, void *out,
@@ -298,7 +298,7 @@ hipError_t dot2_launch(const SmallPlan &p, const void *x, const int32_t *wt, con
     }
 }
 
-// Balanced plan: units of 4 columns, `upw` per workgroup (about `per_cu`
+// Narrow-unit plan: units of 4 columns, `upw` per workgroup (about `per_cu`
 // workgroups per CU), `wpu` waves per unit, each wave issuing at most `lpw`
 // four-tile loads, all of them up front.
 struct NarrowPlan {

@@ -520,13 +520,7 @@ def main():
     if cpu:
         log(f"cpu oracle: {cpu['value']} GB/s on {cpu['cores']} threads ({cpu['sample']})")
 
-    traffic = None
-    tf_path = os.path.join(ROOT, "profiles", "traffic.json")
-    if os.path.exists(tf_path):
-        with open(tf_path) as f:
-            t = json.load(f).get(DOMINANT)
-        if t and t.get("kernel_source_sha") == _kernel_source_sha():
-            traffic = t.get("bytes_per_launch")
+    traffic = measured_traffic()
 
     line = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -564,6 +558,20 @@ def _kernel_source_sha():
         with open(os.path.join(csrc, n), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
+
+
+def measured_traffic(path=None):
+    """HBM bytes per launch of the dominant kernel from its recorded FETCH_SIZE /
+    WRITE_SIZE counters, or None when there is no record or the record was taken
+    on other sources than the ones built now."""
+    path = path or os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f).get(DOMINANT)
+    if not t or t.get("kernel_source_sha") != _kernel_source_sha():
+        return None
+    return t.get("bytes_per_launch")
 
 
 if __name__ == "__main__":

@@ -6,7 +6,7 @@ packed INT4 words with fp16 group scales, and MXFP8 (E4M3 element codes with an
 E8M0 scale per 32 K-elements). It contains none of the layer's arithmetic: no
 unpacking, no dequantisation, no dot products, no output rounding.
 
-Formats produced (readings of the pages):
+Formats produced (each the plainest reading of the cited page where it leaves a detail open):
 
 * W4A16, GPTQ layout -- GPTQ INT4 card "Qwen3.8-27B-GPTQ-Int4-sym-G128-MTP-BF16",
   section "Quantization contract": symmetric INT4, group size 128, desc_act off,

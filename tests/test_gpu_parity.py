@@ -427,6 +427,42 @@ def test_dot2_deterministic_and_counters_cleared():
     assert_gate(host_bits(a), y64, y32, "dot2 repeated")
 
 
+# shapes whose K range is split across workgroups, one per kernel family that
+# reduces partials through the workspace
+SPLIT_CASES = [
+    ("w4a16", 2, 5, 5120, 512),     # skinny: 32 column blocks
+    ("w4a16", 3, 128, 2560, 512),   # wide: 2 tiles over 20 K steps
+    ("mxfp8", 2, 5, 5120, 512),
+    ("mxfp8", 3, 128, 2560, 512),
+]
+
+
+@pytest.mark.parametrize("op,kernel,M,K,N", SPLIT_CASES)
+def test_split_k_deterministic_and_counters_cleared(op, kernel, M, K, N):
+    import spec_verify_amd as svq
+    if op == "w4a16":
+        inp = synth.gen_w4a16(70 + M, M, K, N)
+        x, s = dev(inp.x), dev(inp.scales)
+        tiled = svq.q4_repack(dev(inp.qweight))
+        nbytes = svq.w4a16_workspace_bytes(M, N, K, 128, kernel)
+        run = lambda ws: svq.w4a16_gemm(x, tiled, s, N, 128, kernel=kernel, workspace=ws)
+        y64, y32 = oracle.w4a16(inp.x, inp.qweight, inp.scales, 128)
+    else:
+        inp = synth.gen_mxfp8(70 + M, M, K, N)
+        x, w, s = dev(inp.x), dev(inp.w), dev(inp.scales)
+        nbytes = svq.mxfp8_workspace_bytes(M, N, K, kernel)
+        run = lambda ws: svq.mxfp8_gemm(x, w, s, kernel=kernel, workspace=ws)
+        y64, y32 = oracle.mxfp8(inp.x, inp.w, inp.scales)
+    assert nbytes > 256 * 1024                 # counters plus partials: K is split
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    outs = [run(ws) for _ in range(3)]
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        assert torch.equal(outs[0].view(torch.int16), o.view(torch.int16))
+    assert int(ws[: 256 * 1024].count_nonzero()) == 0   # arrival counters back at zero
+    assert_gate(host_bits(outs[0]), y64, y32, f"{op} kernel {kernel} split K")
+
+
 def test_output_canaries_and_error_path_leave_memory_untouched():
     import spec_verify_amd as svq
     M, K, N = 5, 1024, 64

@@ -705,3 +705,80 @@ def test_mxfp8_optimized_rtn_invariants():
     c8, s8 = oracle.mxfp8_quantize(synth.bf16_bits(W * np.float32(2.0 ** 5)), optimized=True)
     np.testing.assert_array_equal(c8, co)
     np.testing.assert_array_equal(s8.astype(np.int64), so.astype(np.int64) + 5)
+
+
+# ---- point evaluators: the sampled-output forms the full-size checks rely on ----
+
+def _points(M, N, n, seed):
+    """Random (row, col) pairs plus the four corners and repeated points."""
+    rng = np.random.default_rng(seed)
+    rows = rng.integers(0, M, n)
+    cols = rng.integers(0, N, n)
+    rows = np.concatenate([[0, M - 1, 0, M - 1], rows, rows[:3]])
+    cols = np.concatenate([[0, 0, N - 1, N - 1], cols, cols[:3]])
+    return rows, cols
+
+
+@pytest.mark.parametrize("G", [32, 64, 128])
+def test_w4a16_points_are_the_full_result(G):
+    M, K, N = 5, 512, 48
+    inp = synth.gen_w4a16(61 + G, M, K, N, G)
+    y64, y32 = oracle.w4a16(inp.x, inp.qweight, inp.scales, G)
+    rows, cols = _points(M, N, 40, G)
+    p64, p32 = oracle.w4a16_points(inp.x, inp.qweight, inp.scales, G, rows, cols)
+    np.testing.assert_array_equal(p64.view(np.uint64), y64[rows, cols].view(np.uint64))
+    np.testing.assert_array_equal(p32.view(np.uint32), y32[rows, cols].view(np.uint32))
+
+
+def test_w4a16_points_integer_exact_against_int64_matmul():
+    M, K, N, G = 3, 384, 32, 64
+    inp = synth.gen_w4a16(67, M, K, N, G, kind="intexact", keep_q=True)
+    exact = oracle.bf16_bits_to_f64(inp.x).astype(np.int64) @ (inp.q.astype(np.int64) - 8)
+    rows, cols = _points(M, N, 30, 5)
+    p64, p32 = oracle.w4a16_points(inp.x, inp.qweight, inp.scales, G, rows, cols)
+    np.testing.assert_array_equal(p64, exact[rows, cols].astype(np.float64))
+    np.testing.assert_array_equal(p32.astype(np.float64), exact[rows, cols].astype(np.float64))
+
+
+def test_mxfp8_points_are_the_full_result():
+    M, K, N = 4, 512, 144
+    inp = synth.gen_mxfp8(71, M, K, N)
+    y64, y32 = oracle.mxfp8(inp.x, inp.w, inp.scales)
+    rows, cols = _points(M, N, 40, 7)
+    p64, p32 = oracle.mxfp8_points(inp.x, inp.w, inp.scales, rows, cols)
+    np.testing.assert_array_equal(p64.view(np.uint64), y64[rows, cols].view(np.uint64))
+    np.testing.assert_array_equal(p32.view(np.uint32), y32[rows, cols].view(np.uint32))
+    # integer-valued inputs: the points equal an int64 matmul of the decoded codes
+    ie = synth.gen_mxfp8(72, M, K, N, kind="intexact")
+    exact = oracle.bf16_bits_to_f64(ie.x).astype(np.int64) @ oracle.e4m3_table()[ie.w].astype(np.int64).T
+    q64, q32 = oracle.mxfp8_points(ie.x, ie.w, ie.scales, rows, cols)
+    np.testing.assert_array_equal(q64, exact[rows, cols].astype(np.float64))
+    np.testing.assert_array_equal(q32.astype(np.float64), exact[rows, cols].astype(np.float64))
+
+
+@pytest.mark.parametrize("G", [32, 64, 128])
+def test_w8a16_points_are_the_full_result(G):
+    M, K, N = 3, 512, 48
+    inp = synth.gen_w8a16(81 + G, M, K, N, G)
+    y64, y32 = oracle.w8a16(inp.x, inp.w, inp.scales, G)
+    rows, cols = _points(M, N, 40, 8 + G)
+    p64, p32 = oracle.w8a16_points(inp.x, inp.w, inp.scales, G, rows, cols)
+    np.testing.assert_array_equal(p64.view(np.uint64), y64[rows, cols].view(np.uint64))
+    np.testing.assert_array_equal(p32.view(np.uint32), y32[rows, cols].view(np.uint32))
+    ie = synth.gen_w8a16(82 + G, M, K, N, G, kind="intexact")
+    exact = oracle.bf16_bits_to_f64(ie.x).astype(np.int64) @ ie.w.astype(np.int64).T
+    q64, _ = oracle.w8a16_points(ie.x, ie.w, ie.scales, G, rows, cols)
+    np.testing.assert_array_equal(q64, exact[rows, cols].astype(np.float64))
+
+
+def test_points_reject_out_of_range_indices():
+    inp = synth.gen_w4a16(91, 2, 256, 32, 128)
+    mx = synth.gen_mxfp8(92, 2, 256, 32)
+    w8 = synth.gen_w8a16(93, 2, 256, 32, 128)
+    for rows, cols in (([2], [0]), ([0], [32]), ([-1], [0]), ([0], [-1])):
+        with pytest.raises(ValueError):
+            oracle.w4a16_points(inp.x, inp.qweight, inp.scales, 128, rows, cols)
+        with pytest.raises(ValueError):
+            oracle.mxfp8_points(mx.x, mx.w, mx.scales, rows, cols)
+        with pytest.raises(ValueError):
+            oracle.w8a16_points(w8.x, w8.w, w8.scales, 128, rows, cols)

@@ -7,15 +7,26 @@ than 1 GiB so every launch streams them from HBM, not from the 256 MB Infinity
 Cache. `value` is the step's algorithmic bytes (packed weights + scales + x + y,
 each once) per second.
 
+Timing protocol: every figure is the median of 5 trials; a trial replays a HIP
+graph of launches that rotate over the weight copies (at least 200 launches, or
+exactly `--steps` decode steps for the headline) after untimed warm-up, timed
+with HIP events on the replay stream. Parity against the oracle is checked on
+the first and last weight copies of every workload before and after timing.
+
 Also reported (stderr table and the JSON line's "workloads" list): per-kernel
 time, GB/s, TFLOP/s and roofline fraction for every named workload (decode,
-M=3/5 verify chunks, M=128 batched verify, MXFP8 at M=1/5/128), and the CPU
-oracle's throughput on a bounded sample (``cpu_baseline``), the fused K/V/Q and
-gate/up projections against the same projections launched one by one
-(``fusion``), and the setup-time steps (``quantizer``, ``ct_ingest``,
-``mxfp8_quantizer``).
+M=3/5 verify chunks, M=128 batched verify, MXFP8 at M=1/5/128, the vocabulary
+heads, G=32/64 variants), each beside a read-only stream probe of the same bytes
+in the kernel's own launch shape and in the best of a fixed sweep of shapes
+("probe"), a stream probe of >1 GiB ("chip_stream"), the run record (versions,
+device, host CPU, input SHA-256 digests), the CPU oracle on every workload
+(``cpu_oracle``, bounded column samples scaled to the full width) and on whole
+decode steps (``cpu_baseline``), the fused K/V/Q and gate/up projections against
+the same projections launched one by one (``fusion``), and the setup-time steps
+(``quantizer``, ``ct_ingest``, ``mxfp8_quantizer``).
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--quick] [--no-cpu]
+    python bench.py --only decode_n6144,mxfp8_m128   # a few workloads, for profiling runs
     python bench.py --copy-probe    # a plain 1 GiB device copy, to calibrate HBM counters
 """
 from __future__ import annotations
@@ -23,6 +34,8 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import platform
+import statistics
 import sys
 import time
 
@@ -37,26 +50,52 @@ import synth  # noqa: E402
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, vendor figure
 POOL_BYTES = 1.2 * (1 << 30)
+TRIALS = 5                      # every figure is the median of this many trials
+MIN_LAUNCHES = 200              # launches per trial (or one per weight copy, if more)
 METRIC = "W4A16 GEMM µs, weight-stream GB/s and % HBM peak at M=1/5/128; TFLOP/s"
 DECODE = ["decode_n5120", "decode_n6144", "decode_n1024"]
 DOMINANT = "decode_n6144"
+TABLE = ["decode_n5120", "decode_n6144", "decode_n1024", "verify3_up", "verify3_down", "verify5_up",
+         "verify5_down", "batch128_up", "batch128_down", "mxfp8_m1", "mxfp8_m5", "mxfp8_m128",
+         "vocab_w8_m1", "vocab_w4_m1", "decode_n6144_g32", "decode_n6144_g64", "verify5_up_g32",
+         "verify5_up_g64", "batch128_up_g32", "batch128_up_g64"]
+OPS = {"w4a16": 1, "mxfp8": 2, "w8a16": 3}
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def group(w):
+    return 32 if w["op"] == "mxfp8" else w.get("G", 128)
+
+
 def weight_bytes(w):
-    K, N = w["K"], w["N"]
+    K, N, G = w["K"], w["N"], group(w)
     if w["op"] == "w4a16":
-        return K * N // 2 + (K // 128) * N * 2
+        return K * N // 2 + (K // G) * N * 2
     if w["op"] == "w8a16":
-        return K * N + (K // 128) * N * 2
+        return K * N + (K // G) * N * 2
     return K * N + (K // 32) * N
 
 
 def algo_bytes(w):
     return weight_bytes(w) + 2 * w["M"] * w["K"] + 2 * w["M"] * w["N"]
+
+
+def flops(w):
+    return 2.0 * w["M"] * w["N"] * w["K"]
+
+
+def med(v):
+    return statistics.median(v)
+
+
+def _dev(torch, a):
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).to("cuda:0")
 
 
 class Problem:
@@ -68,34 +107,26 @@ class Problem:
         self.torch, self.svq = torch, svq
         inp = synth.gen_workload(name)
         self.inp = inp
-        dev = torch.device("cuda:0")
-
-        def d(a):
-            a = np.ascontiguousarray(a)
-            if a.dtype == np.uint16:
-                a = a.view(np.int16)
-            return torch.from_numpy(a).to(dev)
-
-        self.x = d(inp.x)
-        M, K, N = self.w["M"], self.w["K"], self.w["N"]
-        self.out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        self.digest = inp.digest()
+        M, K, N, G = self.w["M"], self.w["K"], self.w["N"], group(self.w)
+        self.G = G
+        self.x = _dev(torch, inp.x)
+        self.out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda:0")
         ncopy = max(2, int(pool_bytes // max(weight_bytes(self.w), 1)))
-        if self.w["op"] == "w4a16":
-            base_w = svq.q4_repack(d(inp.qweight))
-            base_s = d(inp.scales)
-            self.kernel = svq.w4a16_kernel_name(M, N, K)
-            nb = svq.w4a16_workspace_bytes(M, N, K)
-        elif self.w["op"] == "w8a16":
-            base_w = torch.from_numpy(np.ascontiguousarray(inp.w)).to(dev)
-            base_s = d(inp.scales)
-            self.kernel = svq.w8a16_kernel_name(M, N, K)
-            nb = svq.w8a16_workspace_bytes(M, N, K)
+        op = self.w["op"]
+        if op == "w4a16":
+            base_w = svq.q4_repack(_dev(torch, inp.qweight))
+            base_s = _dev(torch, inp.scales)
+        elif op == "w8a16":
+            base_w = torch.from_numpy(np.ascontiguousarray(inp.w)).to("cuda:0")
+            base_s = _dev(torch, inp.scales)
         else:
-            base_w = d(inp.w)
-            base_s = d(inp.scales)
-            self.kernel = svq.mxfp8_kernel_name(M, N, K)
-            nb = svq.mxfp8_workspace_bytes(M, N, K)
-        self.ws = torch.zeros(max(nb, 256), dtype=torch.uint8, device=dev) if nb else None
+            base_w = _dev(torch, inp.w)
+            base_s = _dev(torch, inp.scales)
+        self.kernel = svq.kernel_name(OPS[op], M, N, K, G)
+        self.geometry = svq.launch_geometry(OPS[op], M, N, K, G)
+        nb = svq.workspace_bytes(OPS[op], M, N, K, G)
+        self.ws = torch.zeros(max(nb, 256), dtype=torch.uint8, device="cuda:0") if nb else None
         self.ws_w = [base_w] + [base_w.clone() for _ in range(ncopy - 1)]
         self.ws_s = [base_s] + [base_s.clone() for _ in range(ncopy - 1)]
         self.i = 0
@@ -105,10 +136,10 @@ class Problem:
         self.i = (self.i + 1) % len(self.ws_w)
         w = self.w
         if w["op"] == "w4a16":
-            self.svq.w4a16_gemm(self.x, self.ws_w[i], self.ws_s[i], w["N"], 128, out=self.out,
+            self.svq.w4a16_gemm(self.x, self.ws_w[i], self.ws_s[i], w["N"], self.G, out=self.out,
                                 workspace=self.ws)
         elif w["op"] == "w8a16":
-            self.svq.w8a16_gemm(self.x, self.ws_w[i], self.ws_s[i], 128, out=self.out, workspace=self.ws)
+            self.svq.w8a16_gemm(self.x, self.ws_w[i], self.ws_s[i], self.G, out=self.out, workspace=self.ws)
         else:
             self.svq.mxfp8_gemm(self.x, self.ws_w[i], self.ws_s[i], out=self.out, workspace=self.ws)
 
@@ -124,9 +155,9 @@ class Problem:
             torch.cuda.synchronize()
             bits = self.out.view(torch.int16).cpu().numpy().view(np.uint16)[rows, cols]
             if w["op"] == "w4a16":
-                y64, _ = oracle.w4a16_points(inp.x, inp.qweight, inp.scales, 128, rows, cols)
+                y64, _ = oracle.w4a16_points(inp.x, inp.qweight, inp.scales, self.G, rows, cols)
             elif w["op"] == "w8a16":
-                y64, _ = oracle.w8a16_points(inp.x, inp.w, inp.scales, 128, rows, cols)
+                y64, _ = oracle.w8a16_points(inp.x, inp.w, inp.scales, self.G, rows, cols)
             else:
                 y64, _ = oracle.mxfp8_points(inp.x, inp.w, inp.scales, rows, cols)
             ok, err, rms = oracle.gate(bits, y64)
@@ -167,16 +198,181 @@ def time_graph(torch, g, reps):
     return a.elapsed_time(b) * 1e-3 / reps
 
 
-def time_kernel(torch, prob, launches=100, reps=5):
-    """Mean µs per launch of one kernel: a graph of `launches` launches that
-    rotate over the weight pool, replayed `reps` times."""
-    g = graph_of(torch, lambda i: prob.launch(i % len(prob.ws_w)), launches)
-    t = time_graph(torch, g, reps)
+def time_trials(torch, fn, n, trials=TRIALS):
+    """µs per call of fn(i), i = 0..n-1 captured in one graph: one value per trial
+    (each trial one replay of the n calls, after one untimed replay)."""
+    g = graph_of(torch, fn, n)
+    out = [time_graph(torch, g, 1) / n * 1e6 for _ in range(trials)]
     del g
-    return t / launches * 1e6
+    return out
 
 
-def cpu_baseline(budget_s=12.0):
+def time_kernel(torch, prob, launches=None):
+    """µs per launch of one kernel, one value per trial: graphs of at least
+    MIN_LAUNCHES launches (one per weight copy if there are more) rotating over
+    the weight pool."""
+    n = launches or max(MIN_LAUNCHES, len(prob.ws_w))
+    return time_trials(torch, lambda i: prob.launch(i % len(prob.ws_w)), n)
+
+
+def summary(trials):
+    return {"median": round(med(trials), 3), "min": round(min(trials), 3), "max": round(max(trials), 3),
+            "trials": [round(t, 3) for t in trials]}
+
+
+# ---- streaming probe --------------------------------------------------------------------
+
+class ProbePool:
+    """Copies of `nbytes` (rounded up to 16) in one device buffer totalling more than
+    1 GiB, read in turn by the stream probe, so that each launch reads from HBM."""
+
+    def __init__(self, torch, nbytes, pool_bytes=POOL_BYTES):
+        self.torch = torch
+        self.nbytes = (nbytes + 15) // 16 * 16
+        self.n = max(2, int(pool_bytes // self.nbytes))
+        self.buf = torch.randint(-2 ** 31, 2 ** 31 - 1, (self.n * self.nbytes // 4,), dtype=torch.int32,
+                                 device="cuda:0")
+        self.sink = torch.zeros(1 << 20, dtype=torch.int32, device="cuda:0")
+
+    def time(self, svq, grid, threads):
+        view = lambda i: self.buf[(i % self.n) * self.nbytes // 4:]
+        fn = lambda i: svq.stream_probe(view(i), self.nbytes, grid, threads, self.sink)
+        return time_trials(self.torch, fn, max(MIN_LAUNCHES, self.n))
+
+    def release(self):
+        self.buf = self.sink = None
+
+
+def probe_shapes(cus, nbytes):
+    """A fixed sweep of launch shapes for the best-of probe: one to eight workgroups
+    per CU of 256..1024 threads, and many small workgroups of ~5 KiB each."""
+    shapes = [(cus, 1024), (2 * cus, 512), (4 * cus, 256), (8 * cus, 256), (2 * cus, 1024)]
+    small = max(cus, min(1 << 20, nbytes // 5120))
+    shapes.append((small, 256))
+    return shapes
+
+
+def probe_workload(torch, svq, prob, cus):
+    """Stream-probe µs for the workload's algorithmic bytes: in the GEMM's own launch
+    shape, and the best of the fixed sweep."""
+    pool = ProbePool(torch, algo_bytes(prob.w))
+    grid, threads, _ = prob.geometry
+    same = pool.time(svq, grid, threads)
+    best, best_shape = None, None
+    for g, t in probe_shapes(cus, pool.nbytes):
+        v = med(pool.time(svq, g, t))
+        if best is None or v < best:
+            best, best_shape = v, (g, t)
+    pool.release()
+    return {"same_shape": [grid, threads], "same_us": round(med(same), 3), "best_us": round(best, 3),
+            "best_shape": list(best_shape)}
+
+
+def chip_stream(torch, svq, cus):
+    """The chip's streaming ceiling: the probe over 1 GiB in the sweep's shapes."""
+    nbytes = 1 << 30
+    buf = torch.randint(-2 ** 31, 2 ** 31 - 1, (nbytes // 4,), dtype=torch.int32, device="cuda:0")
+    sink = torch.zeros(1 << 20, dtype=torch.int32, device="cuda:0")
+    res = []
+    for g, t in probe_shapes(cus, nbytes) + [(16 * cus, 256), (4 * cus, 1024)]:
+        us = med(time_trials(torch, lambda i: svq.stream_probe(buf, nbytes, g, t, sink), 20))
+        res.append({"shape": [g, t], "us": round(us, 1), "GBps": round(nbytes / (us * 1e-6) / 1e9, 1)})
+    best = max(res, key=lambda r: r["GBps"])
+    del buf, sink
+    return {"bytes": nbytes, "best_GBps": best["GBps"], "best_shape": best["shape"],
+            "hbm_frac": round(best["GBps"] / HBM_PEAK_GBS, 4), "shapes": res}
+
+
+# ---- run record -----------------------------------------------------------------------------
+
+def _read(path):
+    try:
+        with open(path) as f:
+            return f.read().strip()
+    except OSError:
+        return None
+
+
+def host_cpu():
+    model = None
+    txt = _read("/proc/cpuinfo") or ""
+    for line in txt.splitlines():
+        if line.startswith("model name"):
+            model = line.split(":", 1)[1].strip()
+            break
+    smt = _read("/sys/devices/system/cpu/smt/active")
+    threads = len(os.sched_getaffinity(0))
+    # SMT siblings among the usable CPUs: count distinct physical cores
+    cores = set()
+    for c in os.sched_getaffinity(0):
+        sib = _read(f"/sys/devices/system/cpu/cpu{c}/topology/core_id")
+        pkg = _read(f"/sys/devices/system/cpu/cpu{c}/topology/physical_package_id")
+        if sib is not None:
+            cores.add((pkg, sib))
+    return {"model": model, "usable_threads": threads, "physical_cores_of_usable": len(cores) or None,
+            "smt_active": None if smt is None else smt == "1", "machine": platform.machine()}
+
+
+def run_record(torch):
+    props = torch.cuda.get_device_properties(0)
+    rec = {"device": props.name, "gfx_arch": getattr(props, "gcnArchName", None),
+           "compute_units": props.multi_processor_count, "torch": torch.__version__,
+           "hip": torch.version.hip, "rocm": _read("/opt/rocm/.info/version"),
+           "python": platform.python_version(), "host_cpu": host_cpu()}
+    clk = getattr(props, "clock_rate", None)
+    if clk:
+        rec["max_shader_clock_mhz"] = round(clk / 1000.0, 1)
+    return rec
+
+
+# ---- CPU oracle --------------------------------------------------------------------------
+
+def _column_slice(inp, op, nc):
+    if op == "w4a16":
+        return (inp.x, np.ascontiguousarray(inp.qweight[:, :nc]), np.ascontiguousarray(inp.scales[:, :nc]))
+    if op == "w8a16":
+        return (inp.x, np.ascontiguousarray(inp.w[:nc]), np.ascontiguousarray(inp.scales[:, :nc]))
+    return (inp.x, np.ascontiguousarray(inp.w[:nc]), np.ascontiguousarray(inp.scales[:nc]))
+
+
+def cpu_oracle_rows(oracle, names, gpu_us, budget_s=0.25):
+    """The plain oracle (fp64 sums and the fp32-sequential sum, OpenMP over output
+    columns) on each workload: timed on the first `columns` output columns (sized
+    for about budget_s per run), one warm-up then 3 runs, median, scaled to the full
+    width; rates over the workload's algorithmic bytes and flops."""
+    rows = []
+    for name in names:
+        w = synth.WORKLOADS[name]
+        inp = INPUTS.get(name) or synth.gen_workload(name)
+        op, G = w["op"], group(w)
+        fn = {"w4a16": lambda a: oracle.w4a16(*a, G), "w8a16": lambda a: oracle.w8a16(*a, G),
+              "mxfp8": lambda a: oracle.mxfp8(*a)}[op]
+        nc = min(w["N"], 64)
+        a = _column_slice(inp, op, nc)
+        t0 = time.perf_counter()
+        fn(a)
+        per_col = (time.perf_counter() - t0) / nc
+        nc = int(min(w["N"], max(16, budget_s / max(per_col, 1e-9))) // 16 * 16) or 16
+        a = _column_slice(inp, op, nc)
+        fn(a)
+        ts = []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            fn(a)
+            ts.append(time.perf_counter() - t0)
+        us = med(ts) * w["N"] / nc * 1e6
+        r = {"workload": name, "columns": nc, "us": round(us, 1),
+             "GBps": round(algo_bytes(w) / (us * 1e-6) / 1e9, 3),
+             "GFLOPs": round(flops(w) / (us * 1e-6) / 1e9, 3)}
+        if name in gpu_us:
+            r["gpu_speedup"] = round(us / gpu_us[name], 1)
+        rows.append(r)
+        log(f"cpu oracle {name:17s} {nc:6d} cols  {us:12.1f} µs  {r['GBps']:8.3f} GB/s  {r['GFLOPs']:8.3f} GFLOP/s"
+            + (f"  GPU x{r['gpu_speedup']}" if "gpu_speedup" in r else ""))
+    return rows
+
+
+def cpu_baseline(budget_s=10.0):
     """The oracle as it stands, timed on this host on a bounded sample of the decode step."""
     import oracle
     probs = [synth.gen_workload(n) for n in DECODE]
@@ -190,38 +386,65 @@ def cpu_baseline(budget_s=12.0):
             oracle.w4a16(p.x, p.qweight, p.scales)
         steps += 1
     dt = time.perf_counter() - t0
+    cpu = host_cpu()
     return {"value": round(bytes_step * steps / dt / 1e9, 4), "unit": "GB/s", "cores": oracle.num_threads(),
             "kind": "oracle",
-            "sample": f"{steps} full decode steps (3 GEMVs, M=1, K=5120, N=5120/6144/1024) in {dt:.1f} s; "
-                      "fp64 sums plus the fp32-sequential sum, OpenMP over output columns",
+            "sample": f"{steps} full decode steps (3 GEMVs, M=1, K=5120, N=5120/6144/1024) in {dt:.1f} s",
+            "sums": "both the fp64 sum and the fp32-sequential sum of every output (the oracle as it stands)",
+            "threads": oracle.num_threads(), "cpu_model": cpu["model"], "smt_active": cpu["smt_active"],
+            "physical_cores_of_usable": cpu["physical_cores_of_usable"],
             "ms_per_step": round(dt / steps * 1e3, 3)}
 
 
-def workload_table(torch, svq, oracle, names):
-    """µs per launch (graph of 100 rotating launches, parity checked before and
-    after) and the derived rates of each named workload."""
-    log(f"{'workload':15s} {'kernel':22s} {'µs':>8s} {'GB/s':>8s} {'%HBM':>6s} "
-        f"{'TFLOP/s':>8s} {'%MFMA':>6s}")
+INPUTS = {}   # generated inputs by workload name, reused by the CPU oracle leg
+
+
+def workload_table(torch, svq, oracle, names, cus, probe=True):
+    """µs per launch (median of 5 trials of graphs of >= 200 rotating launches, parity
+    checked before and after), derived rates, and the stream probe of the same bytes."""
+    log(f"{'workload':17s} {'kernel':22s} {'µs':>8s} {'GB/s':>8s} {'%HBM':>6s} {'probe':>7s} {'%probe':>7s} "
+        f"{'best':>7s} {'%best':>6s} {'TFLOP/s':>8s} {'%MFMA':>6s}")
     detail = []
     for n in names:
         p = Problem(torch, svq, n, POOL_BYTES)
         p.check(oracle)
-        us = time_kernel(torch, p, launches=100, reps=3)
+        tr = time_kernel(torch, p)
         p.check(oracle)
+        us = med(tr)
         w = p.w
         gbs = algo_bytes(w) / (us * 1e-6) / 1e9
-        tfl = 2.0 * w["M"] * w["N"] * w["K"] / (us * 1e-6) / 1e12
-        detail.append({"workload": n, "op": w["op"], "M": w["M"], "K": w["K"], "N": w["N"], "kernel": p.kernel,
-                       "us": round(us, 3),
-                       "GBps": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
-                       "weight_GBps": round(weight_bytes(w) / (us * 1e-6) / 1e9, 1),
-                       "TFLOPs": round(tfl, 2), "mfma_frac": round(tfl / MFMA_BF16_PEAK_TFLOPS, 4)})
-        log(f"{n:15s} {p.kernel:22s} {us:8.2f} {gbs:8.1f} {100 * gbs / HBM_PEAK_GBS:6.1f} "
-            f"{tfl:8.2f} {100 * tfl / MFMA_BF16_PEAK_TFLOPS:6.2f}")
+        tfl = flops(w) / (us * 1e-6) / 1e12
+        row = {"workload": n, "op": w["op"], "M": w["M"], "K": w["K"], "N": w["N"], "G": group(w),
+               "kernel": p.kernel, "launch_shape": list(p.geometry), "us": round(us, 3), "us_trials": summary(tr),
+               "GBps": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+               "weight_GBps": round(weight_bytes(w) / (us * 1e-6) / 1e9, 1),
+               "TFLOPs": round(tfl, 2), "mfma_frac": round(tfl / MFMA_BF16_PEAK_TFLOPS, 4),
+               "bytes": algo_bytes(w), "input_sha256": p.digest, "weight_copies": len(p.ws_w)}
+        INPUTS[n] = p.inp
         p.release()
         del p
         torch.cuda.empty_cache()
+        if probe:
+            pr = probe_workload(torch, svq, _ProbeView(w), cus)
+            pr["frac_same"] = round(pr["same_us"] / us, 4)
+            pr["frac_best"] = round(pr["best_us"] / us, 4)
+            row["probe"] = pr
+        detail.append(row)
+        pr = row.get("probe", {})
+        log(f"{n:17s} {row['kernel']:22s} {us:8.2f} {gbs:8.1f} {100 * gbs / HBM_PEAK_GBS:6.1f} "
+            f"{pr.get('same_us', 0):7.2f} {100 * pr.get('frac_same', 0):7.1f} {pr.get('best_us', 0):7.2f} "
+            f"{100 * pr.get('frac_best', 0):6.1f} {tfl:8.2f} {100 * tfl / MFMA_BF16_PEAK_TFLOPS:6.2f}")
+        torch.cuda.empty_cache()
     return detail
+
+
+class _ProbeView:
+    """The parts of a workload the probe needs: its bytes and the GEMM's launch shape."""
+
+    def __init__(self, w):
+        import spec_verify_amd as svq
+        self.w = w
+        self.geometry = svq.launch_geometry(OPS[w["op"]], w["M"], w["N"], w["K"], group(w))
 
 
 def time_quantizer(torch, svq, oracle, N=24832, K=5120, G=128, reps=20):
@@ -420,7 +643,8 @@ def main():
     ap.add_argument("--steps", type=int, default=300)
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--quick", action="store_true", help="decode step only, no per-workload table")
-    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle legs")
+    ap.add_argument("--no-probe", action="store_true", help="skip the stream probes")
     ap.add_argument("--only", default="",
                     help="comma-separated workloads: time just these (per-workload table, no decode "
                          "step, no CPU leg) and print their rows as JSON; for profiling runs")
@@ -445,9 +669,10 @@ def main():
         from spec_verify_amd import build
         build.build()
     svq.lib()
-    props = torch.cuda.get_device_properties(0)
-    log(f"device: {props.name} ({getattr(props, 'gcnArchName', '?')}), CUs {props.multi_processor_count}, "
-        f"torch {torch.__version__}, hip {torch.version.hip}")
+    record = run_record(torch)
+    cus = record["compute_units"]
+    log(f"device: {record['device']} ({record['gfx_arch']}), CUs {cus}, torch {record['torch']}, "
+        f"hip {record['hip']}, rocm {record['rocm']}; host {record['host_cpu']}")
     if args.setup_only:
         print(json.dumps({"quantizer": time_quantizer(torch, svq, oracle),
                           "ct_ingest": time_ct_ingest(torch, svq, oracle),
@@ -455,7 +680,8 @@ def main():
         return
     if args.only:
         names = [n for n in args.only.split(",") if n]
-        rows = workload_table(torch, svq, oracle, [n for n in names if n in synth.WORKLOADS])
+        rows = workload_table(torch, svq, oracle, [n for n in names if n in synth.WORKLOADS], cus,
+                              probe=not args.no_probe)
         fus = time_fusion(torch, svq, oracle, [n for n in names if n in synth.FUSIONS])
         print(json.dumps({"workloads": rows, "fusion": fus}), flush=True)
         return
@@ -467,7 +693,7 @@ def main():
     bytes_step = sum(algo_bytes(p.w) for p in probs)
     dom = probs[DECODE.index(DOMINANT)]
     # one graph = `chunk` decode steps (3 launches each, weights rotating over the
-    # pool); it is replayed until `steps` steps have run, after `warmup` steps
+    # pool); a trial replays it until exactly `steps` steps have run
     chunk = next(c for c in range(min(args.steps, 100), 0, -1) if args.steps % c == 0)
     reps = args.steps // chunk
 
@@ -478,27 +704,32 @@ def main():
     for _ in range(max(1, -(-args.warmup // chunk))):
         g.replay()
     torch.cuda.synchronize()
-    sec = time_graph(torch, g, reps)
-    steps_run = chunk * reps
-    ms_step = sec / chunk * 1e3
+    step_trials = [time_graph(torch, g, reps) / chunk * 1e3 for _ in range(TRIALS)]   # ms per step
+    ms_step = med(step_trials)
     del g
-    dom_us = time_kernel(torch, dom, launches=100, reps=5)
+    dom_trials = time_kernel(torch, dom)
+    dom_us = med(dom_trials)
     value = bytes_step / (ms_step * 1e-3) / 1e9
     dom_gbs = algo_bytes(dom.w) / (dom_us * 1e-6) / 1e9
     dom.check(oracle)
-    log(f"decode step: {ms_step * 1e3:.2f} µs/step, {value:.1f} GB/s; {DOMINANT} ({dom.kernel}) "
-        f"{dom_us:.2f} µs/launch = {dom_gbs:.1f} GB/s ({100 * dom_gbs / HBM_PEAK_GBS:.1f}% of HBM peak)")
+    log(f"decode step: {ms_step * 1e3:.2f} µs/step (trials {[round(t * 1e3, 2) for t in step_trials]}), "
+        f"{value:.1f} GB/s; {DOMINANT} ({dom.kernel}) {dom_us:.2f} µs/launch = {dom_gbs:.1f} GB/s "
+        f"({100 * dom_gbs / HBM_PEAK_GBS:.1f}% of HBM peak)")
+    digests = {p.name: p.digest for p in probs}
     for p in probs:
         p.release()
     torch.cuda.empty_cache()
+    dom_probe = None if args.no_probe else probe_workload(torch, svq, _ProbeView(dom.w), cus)
 
     # ---- per-workload table ------------------------------------------------------
     detail = []
+    chip = None
     if not args.quick:
-        detail = workload_table(torch, svq, oracle, [
-            "decode_n5120", "decode_n6144", "decode_n1024", "verify3_up", "verify3_down", "verify5_up",
-            "verify5_down", "batch128_up", "batch128_down", "mxfp8_m1", "mxfp8_m5", "mxfp8_m128",
-            "vocab_w8_m1", "vocab_w4_m1"])
+        if not args.no_probe:
+            chip = chip_stream(torch, svq, cus)
+            log(f"chip stream probe, 1 GiB: best {chip['best_GBps']} GB/s ({100 * chip['hbm_frac']:.1f}% of "
+                f"8 TB/s) in {chip['best_shape']}")
+        detail = workload_table(torch, svq, oracle, TABLE, cus, probe=not args.no_probe)
 
     quant = None
     if not args.quick:
@@ -516,26 +747,42 @@ def main():
             f"optimized {mxq['us_opt']:.1f} µs ({mxq['GBps_opt']:.1f} GB/s), doubled scale in "
             f"{100 * mxq['doubled_scale_frac']:.2f}% of blocks")
 
-    cpu = None if args.no_cpu else cpu_baseline()
-    if cpu:
+    cpu = cpu_rows = None
+    if not args.no_cpu:
+        cpu = cpu_baseline()
         log(f"cpu oracle: {cpu['value']} GB/s on {cpu['cores']} threads ({cpu['sample']})")
+        gpu_us = {r["workload"]: r["us"] for r in detail}
+        gpu_us.setdefault(DOMINANT, dom_us)
+        cpu_rows = cpu_oracle_rows(oracle, [r["workload"] for r in detail] or DECODE, gpu_us)
 
     traffic = measured_traffic()
-
+    trace = measured_trace()
+    roofline = {"bound": "hbm", "achieved": round(dom_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "kernel": dom.kernel, "workload": DOMINANT, "us_per_launch": round(dom_us, 3),
+                "us_trials": summary(dom_trials), "bytes_per_launch": algo_bytes(dom.w),
+                "timing": "HIP events around graph replays of rotating launches, median of 5 trials"}
+    if trace:
+        roofline["trace"] = {**trace, "frac_median": round(algo_bytes(dom.w) / (trace["median_us"] * 1e-6) / 1e9
+                                                           / HBM_PEAK_GBS, 4)}
+    if dom_probe:
+        roofline["probe"] = {**dom_probe, "frac_same": round(dom_probe["same_us"] / dom_us, 4),
+                             "frac_best": round(dom_probe["best_us"] / dom_us, 4)}
     line = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms_step, 6), "steps_timed": steps_run, "higher_is_better": True, "scaling": "weak",
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 6), "steps_timed": args.steps,
+        "step_trials_ms": [round(t, 6) for t in step_trials], "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "single-stream decode step: three W4A16 g128 GEMVs, M=1, K=5120, "
                                "N=5120/6144/1024, weights rotated over >1 GiB of copies",
                    "M": 1, "K": 5120, "N": [5120, 6144, 1024], "group_size": 128,
-                   "bytes_per_step": bytes_step},
-        "roofline": {"bound": "hbm", "achieved": round(dom_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": dom.kernel, "workload": DOMINANT, "us_per_launch": round(dom_us, 3),
-                     "bytes_per_launch": algo_bytes(dom.w)},
+                   "bytes_per_step": bytes_step, "input_sha256": digests},
+        "roofline": roofline,
         "cpu_baseline": cpu,
+        "run_record": record,
+        "chip_stream": chip,
         "workloads": detail,
+        "cpu_oracle": cpu_rows,
         "quantizer": quant,
         "fusion": fusion,
         "ct_ingest": ct,
@@ -558,6 +805,20 @@ def _kernel_source_sha():
         with open(os.path.join(csrc, n), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
+
+
+def measured_trace(path=None):
+    """The dominant kernel's rocprofv3 kernel-trace durations (median, mean, count)
+    from profiles/trace.json, or None when there is no record or it was taken on
+    other sources than the ones built now."""
+    path = path or os.path.join(ROOT, "profiles", "trace.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f).get(DOMINANT)
+    if not t or t.get("kernel_source_sha") != _kernel_source_sha():
+        return None
+    return {k: t[k] for k in ("median_us", "mean_us", "dispatches", "command") if k in t}
 
 
 def measured_traffic(path=None):

@@ -79,6 +79,14 @@ typedef enum svq_kernel {
     SVQ_KERNEL_MFMA_WIDE = 3    /* LDS-staged x, 64/128-row MFMA tiles, split-K, any M */
 } svq_kernel;
 
+/* Operations, for the format-generic queries svq_workspace_bytes and
+ * svq_kernel_name. */
+typedef enum svq_op {
+    SVQ_OP_W4A16 = 1,  /* svq_w4a16_gemm */
+    SVQ_OP_MXFP8 = 2,  /* svq_mxfp8_gemm (group_size must be 32) */
+    SVQ_OP_W8A16 = 3   /* svq_w8a16_gemm */
+} svq_op;
+
 int svq_abi_version(void);
 
 /* Static text for a status code; never NULL. */
@@ -149,7 +157,8 @@ int svq_fuse_projections(int32_t bits, const void *const *weights, const void *c
  *   qweight       int32 [K/8][N], 4-byte aligned (the svq_q4_repack input)
  *   scales        fp16 [K/G][N], 2-byte aligned
  *   group_size    G in {32, 64, 128}; K % G == 0 (any N >= 1)
- * Outputs must not overlap the inputs or each other.
+ * Outputs must not overlap the inputs or each other. Words and scales are
+ * transposed in one launch.
  */
 int svq_ct_to_gptq(const int32_t *weight_packed, const void *weight_scale, int32_t *qweight,
                    void *scales, int64_t N, int64_t K, int32_t group_size, void *stream);
@@ -161,7 +170,12 @@ size_t svq_w4a16_workspace_bytes(int kernel, int64_t M, int64_t N, int64_t K,
                                  int32_t group_size);
 
 /*
- * y = x . ((q - 8) * s)^T
+ * y = x . ((q - 8) * s)^T, the W4A16 linear layer: symmetric INT4 with zero
+ * point 8, one fp16 scale per group of G K-rows, no group reordering (GPTQ
+ * INT4 card "Qwen3.8-27B-GPTQ-Int4-sym-G128-MTP-BF16", section "Quantization
+ * contract": INT4, symmetric, group 128, desc_act off, packed int32; Eole
+ * recipe, section "Compressed-tensors INT4 layout": groups of 32, 64 or 128).
+ * Products are accumulated in fp32 and y is rounded to bf16 (nearest even).
  *   x             bf16 [M][K], 16-byte aligned
  *   qweight_tiled output of svq_q4_repack, 16-byte aligned
  *   scales        fp16 [K/G][N], 4-byte aligned (read as aligned 32-bit words)
@@ -194,7 +208,13 @@ const char *svq_w4a16_kernel_name(int kernel, int64_t M, int64_t N, int64_t K,
 size_t svq_mxfp8_workspace_bytes(int kernel, int64_t M, int64_t N, int64_t K);
 
 /*
- * y = x . (e4m3(w) * 2^(e8m0(s) - 127))^T
+ * y = x . (e4m3(w) * 2^(e8m0(s) - 127))^T, the MXFP8 linear layer: OCP E4M3FN
+ * elements with one E8M0 power-of-two scale per 32 consecutive K-elements
+ * (MXFP8 card "Qwen3.8-27B-MXFP8-CT-AutoRound-mtp", opening summary and
+ * section "8. License and attribution"); the kernel constraints N >= 128 and
+ * K % 32 == 0 of its section "2. Precision plan" are checked and reported as
+ * SVQ_ERR_MXFP8_SHAPE (its section "7. Known issues and caveats" records a
+ * crash at N = 96). fp32 accumulation, bf16 (nearest even) output.
  *   x       bf16 [M][K], 16-byte aligned
  *   w       E4M3FN codes [N][K] (row n holds the K elements of output column n),
  *           16-byte aligned
@@ -269,7 +289,11 @@ size_t svq_w8a16_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group_
 
 /*
  * y = x . (q * s)^T for the int8 codes of svq_rtn_quantize, M <= 16
- * (SVQ_ERR_UNSUPPORTED above).
+ * (SVQ_ERR_UNSUPPORTED above): the quantized vocabulary head (Eole recipe,
+ * section "Optional vocabulary-head quantization"; the AWQ card
+ * "Qwen3.8-27B-AWQ-INT4-MTP-LowLatency" measures the decode-latency gain of
+ * a quantized head in its head-precision section). fp32 accumulation, bf16
+ * (nearest even) output.
  *   x       bf16 [M][K], 16-byte aligned
  *   w       int8 codes [N][K], 16-byte aligned
  *   scales  fp16 [K/G][N], 4-byte aligned (read as aligned 32-bit words)
@@ -283,6 +307,55 @@ int svq_w8a16_gemm(const void *x, const int8_t *w, const void *scales, void *out
 
 /* Name of the kernel svq_w8a16_gemm would launch (static text), or NULL. */
 const char *svq_w8a16_kernel_name(int64_t M, int64_t N, int64_t K, int32_t group_size);
+
+/* ---- format-generic queries ---------------------------------------------------- */
+
+/* Workspace bytes the GEMM of `op` (an svq_op) needs with its automatic kernel
+ * choice: svq_w4a16_workspace_bytes(SVQ_KERNEL_AUTO, ...),
+ * svq_mxfp8_workspace_bytes(SVQ_KERNEL_AUTO, ...) (group_size must be 32) or
+ * svq_w8a16_workspace_bytes(...). (size_t)-1 for an unknown op or invalid
+ * arguments. */
+size_t svq_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int32_t group_size);
+
+/* Name of the kernel the GEMM of `op` would launch for this shape (static
+ * text), or NULL for an unknown op or invalid arguments. */
+const char *svq_kernel_name(int op, int64_t M, int64_t N, int64_t K, int32_t group_size);
+
+/* ---- measurement ---------------------------------------------------------------- */
+
+/*
+ * Launch shape of a GEMM call: the grid (workgroups), workgroup size (threads)
+ * and dynamic LDS bytes the call would launch with, for op (an svq_op) and
+ * kernel (an svq_kernel; SVQ_KERNEL_AUTO only for SVQ_OP_W8A16). Nothing is
+ * launched. Returns the status the call would return for valid buffers.
+ */
+int svq_launch_geometry(int op, int kernel, int64_t M, int64_t N, int64_t K, int32_t group_size,
+                        uint64_t *grid, uint32_t *threads, size_t *lds_bytes);
+
+/*
+ * Streaming probe: reads `bytes` (a non-zero multiple of 16) from src (16-byte
+ * aligned) in `grid` workgroups of `threads` threads (a multiple of 64, at most
+ * 1024), each workgroup one contiguous share, and does nothing with them. It
+ * measures the bandwidth a plain read of that many bytes reaches in that
+ * launch shape: the ceiling of a GEMM's weight stream. sink (grid words, 4-byte
+ * aligned) may be written with data-dependent values; nothing else is.
+ */
+int svq_stream_probe(const void *src, size_t bytes, uint32_t grid, uint32_t threads, uint32_t *sink,
+                     void *stream);
+
+/* ---- test hook ----------------------------------------------------------------- */
+
+/*
+ * Wait budgets of the cross-workgroup reduction in the wide (M > 16) kernels,
+ * in ticks of the 100 MHz s_memrealtime clock (defaults: 2000 for the wait on
+ * the other contributors' partials, 1000 for the last arriver's wait on the
+ * other reducers). A workgroup that runs out of budget stops waiting and the
+ * last arriver reduces what is still missing, so results never depend on the
+ * budget; 0 makes every member give up at once. Negative values restore the
+ * defaults. Process-wide; applies to launches made after the call. For tests
+ * of that fallback path.
+ */
+void svq_debug_streamk_wait_ticks(int64_t arrive_ticks, int64_t range_ticks);
 
 #ifdef __cplusplus
 }

@@ -23,6 +23,8 @@ __all__ = [
     "mxfp8_kernel_name", "w4a16_workspace_bytes", "mxfp8_workspace_bytes", "Workspace",
     "EXPORTED_SYMBOLS", "rtn_quantize", "w8a16_gemm", "w8a16_workspace_bytes", "w8a16_kernel_name",
     "fuse_projections", "fuse_or_keep", "ct_to_gptq", "MAX_FUSED_PARTS", "mxfp8_quantize",
+    "OP_W4A16", "OP_MXFP8", "OP_W8A16", "workspace_bytes", "kernel_name", "debug_streamk_wait_ticks",
+    "launch_geometry", "stream_probe",
 ]
 
 KERNEL_AUTO, KERNEL_DOT2, KERNEL_MFMA_SKINNY, KERNEL_MFMA_WIDE = 0, 1, 2, 3
@@ -36,8 +38,11 @@ EXPORTED_SYMBOLS = (
     "svq_w4a16_kernel_name", "svq_mxfp8_workspace_bytes", "svq_mxfp8_gemm",
     "svq_mxfp8_gemm_with", "svq_mxfp8_kernel_name", "svq_rtn_quantize",
     "svq_w8a16_workspace_bytes", "svq_w8a16_gemm", "svq_w8a16_kernel_name",
-    "svq_fuse_projections", "svq_ct_to_gptq", "svq_mxfp8_quantize",
+    "svq_fuse_projections", "svq_ct_to_gptq", "svq_mxfp8_quantize", "svq_workspace_bytes",
+    "svq_kernel_name", "svq_debug_streamk_wait_ticks", "svq_launch_geometry", "svq_stream_probe",
 )
+
+OP_W4A16, OP_MXFP8, OP_W8A16 = 1, 2, 3
 
 MAX_FUSED_PARTS = 16
 
@@ -102,6 +107,18 @@ def lib():
         L.svq_mxfp8_quantize.restype = ctypes.c_int
         L.svq_mxfp8_quantize.argtypes = [_p, _i32, _p, _p, _i64, _i64, _p]
         L.svq_ct_to_gptq.argtypes = [_p, _p, _p, _p, _i64, _i64, _i32, _p]
+        L.svq_workspace_bytes.restype = _sz
+        L.svq_workspace_bytes.argtypes = [ctypes.c_int, _i64, _i64, _i64, _i32]
+        L.svq_kernel_name.restype = ctypes.c_char_p
+        L.svq_kernel_name.argtypes = [ctypes.c_int, _i64, _i64, _i64, _i32]
+        L.svq_launch_geometry.restype = ctypes.c_int
+        L.svq_launch_geometry.argtypes = [ctypes.c_int, ctypes.c_int, _i64, _i64, _i64, _i32,
+                                          ctypes.POINTER(ctypes.c_uint64), ctypes.POINTER(ctypes.c_uint32),
+                                          ctypes.POINTER(_sz)]
+        L.svq_stream_probe.restype = ctypes.c_int
+        L.svq_stream_probe.argtypes = [_p, _sz, ctypes.c_uint32, ctypes.c_uint32, _p, _p]
+        L.svq_debug_streamk_wait_ticks.restype = None
+        L.svq_debug_streamk_wait_ticks.argtypes = [_i64, _i64]
         _lib = L
         return L
 
@@ -191,6 +208,44 @@ def w4a16_kernel_name(M, N, K, group_size=128, kernel=KERNEL_AUTO):
 def mxfp8_kernel_name(M, N, K, kernel=KERNEL_AUTO):
     r = lib().svq_mxfp8_kernel_name(kernel, M, N, K)
     return r.decode() if r else None
+
+
+def workspace_bytes(op, M, N, K, group_size=128) -> int:
+    """Workspace bytes of the GEMM of `op` (OP_W4A16, OP_MXFP8 with group_size 32,
+    OP_W8A16) with its automatic kernel choice."""
+    v = lib().svq_workspace_bytes(op, M, N, K, group_size)
+    if v == ctypes.c_size_t(-1).value:
+        raise SvqError(10, "svq_workspace_bytes")
+    return v
+
+
+def kernel_name(op, M, N, K, group_size=128):
+    """Name of the kernel the GEMM of `op` would launch, or None."""
+    r = lib().svq_kernel_name(op, M, N, K, group_size)
+    return r.decode() if r else None
+
+
+def launch_geometry(op, M, N, K, group_size=128, kernel=KERNEL_AUTO):
+    """(grid, threads, dynamic LDS bytes) the GEMM call would launch with."""
+    g, t, l = ctypes.c_uint64(), ctypes.c_uint32(), _sz()
+    _check(lib().svq_launch_geometry(op, kernel, M, N, K, group_size, ctypes.byref(g), ctypes.byref(t),
+                                     ctypes.byref(l)), "svq_launch_geometry")
+    return g.value, t.value, l.value
+
+
+def stream_probe(src, nbytes, grid, threads, sink):
+    """Read-only stream of the first nbytes of the device tensor src in (grid,
+    threads); sink is a device tensor of at least grid 32-bit words."""
+    if nbytes > src.numel() * src.element_size() or sink.numel() * sink.element_size() < 4 * grid:
+        raise ValueError("src or sink too small")
+    _check(lib().svq_stream_probe(_dev_ptr(src, "src"), nbytes, grid, threads, _dev_ptr(sink, "sink"),
+                                  _stream_ptr(src)), "svq_stream_probe")
+
+
+def debug_streamk_wait_ticks(arrive_ticks=-1, range_ticks=-1):
+    """Test hook: wait budgets of the wide kernels' cross-workgroup reduction
+    (negative restores the defaults)."""
+    lib().svq_debug_streamk_wait_ticks(int(arrive_ticks), int(range_ticks))
 
 
 def q4_repack(qweight, out=None):

@@ -226,7 +226,7 @@ __global__ __launch_bounds__(64 * WR * WC) void mxfp8_wide_kernel(
     const uint16_t *__restrict__ x, const uint8_t *__restrict__ w,
     const uint8_t *__restrict__ sc, uint16_t *__restrict__ out, uint32_t *__restrict__ cnt,
     f32x4 *__restrict__ part, int M, int N, int K, int col_tiles, int64_t units, int grid,
-    int maxt) {
+    int maxt, SkWait skw) {
     constexpr int NT = 64 * WR * WC;
     constexpr int BM = 16 * MBW * WR;
     constexpr int BN = 16 * CT * WC;
@@ -378,7 +378,7 @@ __global__ __launch_bounds__(64 * WR * WC) void mxfp8_wide_kernel(
 #pragma unroll
             for (int v = 0; v < NV; ++v) store_v(v, acc[v]);
         } else {
-            sk_reduce<NV, NT>(acc, tile, KT, units, grid, maxt, cnt, part, s_sk, store_v);
+            sk_reduce<NV, NT>(acc, tile, KT, units, grid, maxt, cnt, part, s_sk, skw, store_v);
         }
         u += s1 - s0;
     }
@@ -397,10 +397,9 @@ constexpr int kMxSkinnyDepth = 2;
 template <int M, int WAVES>
 hipError_t mx_dot2_launch_w(const SmallPlan &p, const void *x, const uint8_t *w, const uint8_t *sc,
                             void *out, int64_t N, int64_t K, void *ws, hipStream_t stream) {
-    hipLaunchKernelGGL((mxfp8_dot2_kernel<M, WAVES, kMxDot2Depth>), dim3((uint32_t)(N / 16 * p.splits)),
+    return launch_gemm(mxfp8_dot2_kernel<M, WAVES, kMxDot2Depth>, dim3((uint32_t)(N / 16 * p.splits)),
                        dim3(64 * WAVES), 0, stream, (const uint32_t *)x, w, sc, (uint16_t *)out,
                        ws_counters(ws), (float *)ws_partials(ws), (int)N, (int)K, p.splits, p.S);
-    return hipGetLastError();
 }
 
 template <int M>
@@ -418,11 +417,10 @@ hipError_t mx_dot2_launch(const SmallPlan &p, const void *x, const uint8_t *w, c
 template <int WAVES>
 hipError_t mx_skinny_launch_w(const SmallPlan &p, const void *x, const uint8_t *w, const uint8_t *sc,
                               void *out, int M, int64_t N, int64_t K, void *ws, hipStream_t stream) {
-    hipLaunchKernelGGL((mxfp8_skinny_kernel<WAVES, kMxSkinnyDepth>), dim3((uint32_t)(N / 16 * p.splits)),
+    return launch_gemm(mxfp8_skinny_kernel<WAVES, kMxSkinnyDepth>, dim3((uint32_t)(N / 16 * p.splits)),
                        dim3(64 * WAVES), skinny_lds_bytes(M, p.S, WAVES), stream, (const uint16_t *)x, w, sc,
                        (uint16_t *)out, ws_counters(ws), (float *)ws_partials(ws), M, (int)N,
                        (int)K, p.splits, p.S);
-    return hipGetLastError();
 }
 
 template <int MBW, int WR, int WC, int CT>
@@ -430,10 +428,9 @@ hipError_t mx_wide_launch(const WidePlan &p, const void *x, const uint8_t *w, co
                           void *out, int64_t M, int64_t N, int64_t K, void *ws, hipStream_t stream) {
     uint32_t *cnt = ws_counters(ws);
     f32x4 *part = (f32x4 *)ws_partials(ws);
-    hipLaunchKernelGGL((mxfp8_wide_kernel<MBW, WR, WC, CT>), dim3((uint32_t)p.grid),
+    return launch_gemm(mxfp8_wide_kernel<MBW, WR, WC, CT>, dim3((uint32_t)p.grid),
                        dim3(64 * WR * WC), 0, stream, (const uint16_t *)x, w, sc, (uint16_t *)out,
-                       cnt, part, (int)M, (int)N, (int)K, p.col_tiles, p.units, p.grid, p.maxt);
-    return hipGetLastError();
+                       cnt, part, (int)M, (int)N, (int)K, p.col_tiles, p.units, p.grid, p.maxt, SkWait{p.wait_arrive, p.wait_range});
 }
 }  // namespace
 

@@ -119,13 +119,13 @@ hipError_t launch_fuse_pack(int bits, const void *const *w, const void *const *s
 // [N][K/G]; the GPTQ layout is their transpose, with each word unchanged (Eole
 // recipe, section "Compressed-tensors INT4 layout"). A 64 x 64 tile transpose
 // through LDS: reads run along a source row, writes along a destination row,
-// and the padded LDS rows keep both phases free of bank conflicts.
+// and the padded LDS rows keep both phases free of bank conflicts. Words and
+// scales go in one launch: the first `word_tiles` workgroups transpose word
+// tiles, the rest scale tiles (a wave-uniform choice per workgroup).
 template <typename T>
-__global__ __launch_bounds__(256) void transpose_kernel(const T *__restrict__ src,
-                                                        T *__restrict__ dst, int64_t rows,
-                                                        int64_t cols) {
-    __shared__ uint32_t tile[64][65];
-    const int64_t r0 = (int64_t)blockIdx.x * 64, c0 = (int64_t)blockIdx.y * 64;
+__device__ __forceinline__ void transpose_tile(const T *__restrict__ src, T *__restrict__ dst,
+                                               int64_t rows, int64_t cols, int64_t r0, int64_t c0,
+                                               uint32_t (*tile)[65]) {
     const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
     for (int i = ty; i < 64; i += 4) {
         const int64_t r = r0 + i, c = c0 + tx;
@@ -138,15 +138,29 @@ __global__ __launch_bounds__(256) void transpose_kernel(const T *__restrict__ sr
     }
 }
 
+__global__ __launch_bounds__(256) void ct_transpose_kernel(const uint32_t *__restrict__ wp,
+                                                           uint32_t *__restrict__ qw,
+                                                           const uint16_t *__restrict__ ws,
+                                                           uint16_t *__restrict__ s, int64_t N,
+                                                           int64_t K8, int64_t KG, int64_t word_tiles) {
+    __shared__ uint32_t tile[64][65];
+    const int64_t tn = (N + 63) / 64;
+    int64_t b = blockIdx.x;
+    if (b < word_tiles) {
+        transpose_tile<uint32_t>(wp, qw, N, K8, (b % tn) * 64, (b / tn) * 64, tile);
+    } else {
+        b -= word_tiles;
+        transpose_tile<uint16_t>(ws, s, N, KG, (b % tn) * 64, (b / tn) * 64, tile);
+    }
+}
+
 hipError_t launch_ct_to_gptq(const int32_t *wp, const void *ws, int32_t *qw, void *s, int64_t N,
                              int64_t K, int G, hipStream_t stream) {
-    const int64_t K8 = K / 8, KG = K / G;
-    hipLaunchKernelGGL(transpose_kernel<uint32_t>, dim3((uint32_t)((N + 63) / 64), (uint32_t)((K8 + 63) / 64)),
-                       dim3(256), 0, stream, (const uint32_t *)wp, (uint32_t *)qw, N, K8);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(transpose_kernel<uint16_t>, dim3((uint32_t)((N + 63) / 64), (uint32_t)((KG + 63) / 64)),
-                       dim3(256), 0, stream, (const uint16_t *)ws, (uint16_t *)s, N, KG);
+    const int64_t K8 = K / 8, KG = K / G, tn = (N + 63) / 64;
+    const int64_t word_tiles = tn * ((K8 + 63) / 64), scale_tiles = tn * ((KG + 63) / 64);
+    hipLaunchKernelGGL(ct_transpose_kernel, dim3((uint32_t)(word_tiles + scale_tiles)), dim3(256), 0,
+                       stream, (const uint32_t *)wp, (uint32_t *)qw, (const uint16_t *)ws,
+                       (uint16_t *)s, N, K8, KG, word_tiles);
     return hipGetLastError();
 }
 

@@ -7,6 +7,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <climits>
 #include <cstdint>
 
 #include "svq_launch.h"
@@ -20,8 +21,21 @@ constexpr int kWideThreads = 256;              // threads per wide-kernel workgr
 constexpr int kWideAccPerThread = 16;          // f32x4 accumulators per thread
 
 std::atomic<int> g_num_cus[kMaxDevices];
+// stream-K wait budgets of the wide kernels (changed only by the test hook)
+std::atomic<uint32_t> g_wait_arrive{kSkArriveWaitDefault};
+std::atomic<uint32_t> g_wait_range{kSkRangeWaitDefault};
 
 }  // namespace
+
+LaunchShape *&capture_slot() {
+    static thread_local LaunchShape *slot = nullptr;
+    return slot;
+}
+
+void streamk_wait_ticks(uint32_t &arrive, uint32_t &range) {
+    arrive = g_wait_arrive.load(std::memory_order_relaxed);
+    range = g_wait_range.load(std::memory_order_relaxed);
+}
 
 // Compute units of the current device (cached per device).
 int device_cus() {
@@ -63,6 +77,7 @@ static WidePlan make_plan(int64_t M, int64_t N, int64_t K, int num_cus, int bm, 
         if (b % KT != 0 || e % KT != 0) shared = true;
     }
     p.maxt = maxt;
+    streamk_wait_ticks(p.wait_arrive, p.wait_range);
     if (shared) p.workspace_bytes = kCounterBytes + (size_t)p.grid * p.maxt * slot_bytes;
     return p;
 }
@@ -416,6 +431,81 @@ int svq_mxfp8_gemm(const void *x, const uint8_t *w, const uint8_t *scales, void 
                    void *stream) {
     return svq_mxfp8_gemm_with(SVQ_KERNEL_AUTO, x, w, scales, out, M, N, K, G, workspace,
                                workspace_bytes, stream);
+}
+
+size_t svq_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int32_t G) {
+    switch (op) {
+    case SVQ_OP_W4A16: return svq_w4a16_workspace_bytes(SVQ_KERNEL_AUTO, M, N, K, G);
+    case SVQ_OP_MXFP8: return G == 32 ? svq_mxfp8_workspace_bytes(SVQ_KERNEL_AUTO, M, N, K) : (size_t)-1;
+    case SVQ_OP_W8A16: return svq_w8a16_workspace_bytes(M, N, K, G);
+    default: return (size_t)-1;
+    }
+}
+
+const char *svq_kernel_name(int op, int64_t M, int64_t N, int64_t K, int32_t G) {
+    switch (op) {
+    case SVQ_OP_W4A16: return svq_w4a16_kernel_name(SVQ_KERNEL_AUTO, M, N, K, G);
+    case SVQ_OP_MXFP8: return G == 32 ? svq_mxfp8_kernel_name(SVQ_KERNEL_AUTO, M, N, K) : nullptr;
+    case SVQ_OP_W8A16: return svq_w8a16_kernel_name(M, N, K, G);
+    default: return nullptr;
+    }
+}
+
+int svq_launch_geometry(int op, int kernel, int64_t M, int64_t N, int64_t K, int32_t G,
+                        uint64_t *grid, uint32_t *threads, size_t *lds_bytes) {
+    if (!grid || !threads || !lds_bytes) return SVQ_ERR_NULL;
+    // the entry point validates and plans as for a real call; its launcher
+    // records the shape in this thread's capture slot instead of launching.
+    // The operand addresses are aligned, disjoint and never dereferenced.
+    const uintptr_t base = uintptr_t(1) << 44;
+    const void *x = (const void *)(1 * base), *w = (const void *)(2 * base), *s = (const void *)(3 * base);
+    void *out = (void *)(4 * base), *ws = (void *)(5 * base);
+    const size_t ws_bytes = size_t(1) << 40;
+    LaunchShape shape{};
+    capture_slot() = &shape;
+    int st;
+    switch (op) {
+    case SVQ_OP_W4A16:
+        st = svq_w4a16_gemm_with(kernel, x, (const int32_t *)w, s, out, M, N, K, G, ws, ws_bytes, nullptr);
+        break;
+    case SVQ_OP_MXFP8:
+        st = svq_mxfp8_gemm_with(kernel, x, (const uint8_t *)w, (const uint8_t *)s, out, M, N, K, G, ws,
+                                 ws_bytes, nullptr);
+        break;
+    case SVQ_OP_W8A16:
+        st = kernel == SVQ_KERNEL_AUTO
+                 ? svq_w8a16_gemm(x, (const int8_t *)w, s, out, M, N, K, G, ws, ws_bytes, nullptr)
+                 : SVQ_ERR_UNSUPPORTED;
+        break;
+    default: st = SVQ_ERR_UNSUPPORTED;
+    }
+    capture_slot() = nullptr;
+    if (st != SVQ_OK) return st;
+    if (shape.launches != 1) return SVQ_ERR_UNSUPPORTED;
+    *grid = shape.grid;
+    *threads = shape.threads;
+    *lds_bytes = shape.lds;
+    return SVQ_OK;
+}
+
+int svq_stream_probe(const void *src, size_t bytes, uint32_t grid, uint32_t threads, uint32_t *sink,
+                     void *stream) {
+    if (!src || !sink) return SVQ_ERR_NULL;
+    if (bytes == 0 || bytes % 16 || grid == 0 || grid > (1u << 24) || threads == 0 || threads > 1024 ||
+        threads % 64)
+        return SVQ_ERR_DIM;
+    if (!aligned(src, 16) || !aligned(sink, 4)) return SVQ_ERR_ALIGN;
+    if (overlap(sink, (size_t)grid * 4, src, bytes)) return SVQ_ERR_OVERLAP;
+    return launch_stream_probe(src, bytes, grid, threads, sink, (hipStream_t)stream) == hipSuccess ? SVQ_OK
+                                                                                                   : SVQ_ERR_HIP;
+}
+
+void svq_debug_streamk_wait_ticks(int64_t arrive_ticks, int64_t range_ticks) {
+    const auto clamp = [](int64_t v, uint32_t dflt) {
+        return v < 0 ? dflt : (uint32_t)std::min<int64_t>(v, INT32_MAX);
+    };
+    g_wait_arrive.store(clamp(arrive_ticks, kSkArriveWaitDefault), std::memory_order_relaxed);
+    g_wait_range.store(clamp(range_ticks, kSkRangeWaitDefault), std::memory_order_relaxed);
 }
 
 // ---- quantized vocabulary head -------------------------------------------------

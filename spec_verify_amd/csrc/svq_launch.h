@@ -10,6 +10,35 @@
 
 namespace svq {
 
+// Launch shape of a GEMM launch (grid and workgroup size, dynamic LDS). A
+// launch query sets the calling thread's capture slot: the GEMM launchers then
+// record their shape there instead of launching.
+struct LaunchShape {
+    uint64_t grid;
+    uint32_t threads;
+    size_t lds;
+    int launches;
+};
+LaunchShape *&capture_slot();  // this thread's slot (null: launch normally)
+
+template <typename F, typename... Args>
+hipError_t launch_gemm(F kernel, dim3 grid, dim3 block, size_t lds, hipStream_t stream, Args... args) {
+    if (LaunchShape *c = capture_slot()) {
+        c->grid = (uint64_t)grid.x * grid.y * grid.z;
+        c->threads = block.x * block.y * block.z;
+        c->lds = lds;
+        ++c->launches;
+        return hipSuccess;
+    }
+    hipLaunchKernelGGL(kernel, grid, block, lds, stream, args...);
+    return hipGetLastError();
+}
+
+// Read-only stream of `bytes` (a multiple of 16) in `grid` workgroups of
+// `threads` threads; sink holds `grid` words.
+hipError_t launch_stream_probe(const void *src, size_t bytes, uint32_t grid, uint32_t threads, uint32_t *sink,
+                               hipStream_t stream);
+
 hipError_t launch_q4_repack(const int32_t *src, int32_t *dst, int64_t N, int64_t K,
                             hipStream_t stream);
 
@@ -28,12 +57,19 @@ hipError_t launch_ct_to_gptq(const int32_t *wp, const void *ws, int32_t *qw, voi
 // `grid` persistent workgroups; a workgroup touches at most `maxt` tiles.
 struct WidePlan {
     int bm, bn;
+    uint32_t wait_arrive, wait_range;  // stream-K wait budgets (s_memrealtime ticks)
     int row_tiles, col_tiles;
     int64_t units;
     int grid;
     int maxt;
     size_t workspace_bytes;  // arrival counters + fp32 partials (0 if no tile is shared)
 };
+
+// Stream-K wait budgets of the wide kernels: defaults 2000 ticks (20 us) for
+// the arrivals and 1000 (10 us) for the ranges; a test hook can change them.
+constexpr uint32_t kSkArriveWaitDefault = 2000;
+constexpr uint32_t kSkRangeWaitDefault = 1000;
+void streamk_wait_ticks(uint32_t &arrive, uint32_t &range);
 
 WidePlan plan_w4a16_wide(int64_t M, int64_t N, int64_t K, int num_cus);
 WidePlan plan_mxfp8_wide(int64_t M, int64_t N, int64_t K, int num_cus);

@@ -55,13 +55,19 @@ __device__ __forceinline__ int sk_first_tile(int w, int64_t units, int grid, int
 // missing, so the tile is complete whether or not the members were resident
 // at the same time; a range reduced twice is written twice with the same
 // values. The last contributor to depart clears the three counters.
-constexpr uint64_t kSkArriveWaitTicks = 2000;  // s_memrealtime runs at 100 MHz: 20 us
-constexpr uint64_t kSkRangeWaitTicks = 1000;   // 10 us
+// The two wait budgets are kernel arguments (SkWait, in ticks of the 100 MHz
+// s_memrealtime clock); a budget of 0 makes every member give up at once, so
+// the owner reduces every range itself.
+struct SkWait {
+    uint32_t arrive_ticks, range_ticks;
+};
 constexpr int kSkMaxRanges = 32;               // one bit each
 
 // Spin (thread 0) until (*p & mask) == mask, or at least `want` for mask 0,
-// for at most `ticks`; returns whether it happened.
+// for at most `ticks`; returns whether it happened. A budget of 0 gives up at
+// once without looking.
 __device__ __forceinline__ bool sk_wait(uint32_t *p, uint32_t want, uint32_t mask, uint64_t ticks) {
+    if (ticks == 0) return false;
     const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
     for (;;) {
         const uint32_t v = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -74,7 +80,7 @@ __device__ __forceinline__ bool sk_wait(uint32_t *p, uint32_t want, uint32_t mas
 template <int NV, int NT, typename StoreV>
 __device__ __forceinline__ void sk_reduce(const f32x4 (&acc)[NV], int tile, int KT, int64_t units,
                                           int grid, int maxt, uint32_t *cnt, f32x4 *part,
-                                          int *s_sk, StoreV store_v) {
+                                          int *s_sk, SkWait wt, StoreV store_v) {
     const int tid = threadIdx.x;
     const int wg = blockIdx.x;
     uint32_t *c = cnt + kSkCountersPerTile * tile;
@@ -135,7 +141,7 @@ __device__ __forceinline__ void sk_reduce(const f32x4 (&acc)[NV], int tile, int 
 
     bool mine_ready = owner;
     if (!owner && me < nf) {
-        if (tid == 0) s_sk[1] = sk_wait(&c[0], nc, 0u, kSkArriveWaitTicks) ? 1 : 0;
+        if (tid == 0) s_sk[1] = sk_wait(&c[0], nc, 0u, wt.arrive_ticks) ? 1 : 0;
         __syncthreads();
         mine_ready = __builtin_amdgcn_readfirstlane(s_sk[1]) != 0;
     }
@@ -148,7 +154,7 @@ __device__ __forceinline__ void sk_reduce(const f32x4 (&acc)[NV], int tile, int 
         // the other members' ranges: wait a bounded time for their bits, then
         // reduce whatever is still missing
         if (tid == 0) {
-            sk_wait(&c[1], 0u, all, kSkRangeWaitTicks);
+            sk_wait(&c[1], 0u, all, wt.range_ticks);
             s_sk[2] = (int)__hip_atomic_load(&c[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         __syncthreads();

@@ -279,11 +279,10 @@ constexpr int kNarrowPerCu = 1;  // workgroups per CU of the narrow-unit plan
 template <int M, int WAVES, int GS>
 hipError_t dot2_launch_w(const SmallPlan &p, const void *x, const int32_t *wt, const void *sc, void *out,
                          int64_t N, int64_t K, void *ws, hipStream_t stream) {
-    hipLaunchKernelGGL((w4a16_dot2_kernel<M, WAVES, kDot2Depth, GS>),
+    return launch_gemm(w4a16_dot2_kernel<M, WAVES, kDot2Depth, GS>,
                        dim3((uint32_t)(N / 16 * p.splits)), dim3(64 * WAVES), 0, stream,
                        (const uint32_t *)x, (const uint4 *)wt, (const uint16_t *)sc, (uint16_t *)out,
                        ws_counters(ws), (float *)ws_partials(ws), (int)N, (int)K, p.splits, p.S);
-    return hipGetLastError();
 }
 
 template <int M, int GS>
@@ -331,10 +330,9 @@ bool plan_narrow(int M, int64_t N, int64_t K, int cus, int per_cu, NarrowPlan &p
 template <int M, int LPW, int GS>
 hipError_t narrow_launch_l(const NarrowPlan &p, const void *x, const int32_t *wt, const void *sc,
                            void *out, int64_t N, int64_t K, hipStream_t stream) {
-    hipLaunchKernelGGL((w4a16_narrow_kernel<M, kNarrowCols, LPW, GS>), dim3((uint32_t)p.grid), dim3(64 * p.waves),
+    return launch_gemm(w4a16_narrow_kernel<M, kNarrowCols, LPW, GS>, dim3((uint32_t)p.grid), dim3(64 * p.waves),
                        p.lds, stream, (const uint16_t *)x, (const uint4 *)wt, (const uint16_t *)sc,
                        (uint16_t *)out, (int)N, (int)K, p.upw, p.wpu);
-    return hipGetLastError();
 }
 
 template <int M, int GS>

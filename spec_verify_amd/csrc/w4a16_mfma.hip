@@ -273,7 +273,7 @@ __global__ __launch_bounds__(64 * WR * WC) void w4a16_wide_kernel(
     const uint16_t *__restrict__ x, const uint4 *__restrict__ wt,
     const uint16_t *__restrict__ sc, uint16_t *__restrict__ out, uint32_t *__restrict__ cnt,
     f32x4 *__restrict__ part, int M, int N, int K, int col_tiles, int64_t units, int grid,
-    int maxt) {
+    int maxt, SkWait skw) {
     using C = WideCfg<MBW, WR, WC, CT, GSHIFT>;
     constexpr int BM = C::BM, BN = C::BN, NG = C::NG, SPG = C::SPG, NV = C::NV;
     __shared__ __attribute__((aligned(16))) uint8_t ring[3 * C::SLOT];
@@ -513,7 +513,7 @@ __global__ __launch_bounds__(64 * WR * WC) void w4a16_wide_kernel(
 #pragma unroll
             for (int v = 0; v < NV; ++v) store_v(v, acc[v]);
         } else {
-            sk_reduce<NV, C::NT>(acc, tile, KT, units, grid, maxt, cnt, part, s_sk, store_v);
+            sk_reduce<NV, C::NT>(acc, tile, KT, units, grid, maxt, cnt, part, s_sk, skw, store_v);
         }
         u += n;
     }
@@ -529,12 +529,11 @@ template <int WAVES, int BPW, int GS>
 hipError_t skinny_launch_b(const SmallPlan &p, const void *x, const int32_t *wt, const void *sc,
                            void *out, int M, int64_t N, int64_t K, void *ws, hipStream_t stream) {
     const int64_t groups = (N / 16 + BPW - 1) / BPW;
-    hipLaunchKernelGGL((w4a16_skinny_kernel<WAVES, BPW, kSkinnyDepth, GS>),
+    return launch_gemm(w4a16_skinny_kernel<WAVES, BPW, kSkinnyDepth, GS>,
                        dim3((uint32_t)(groups * p.splits)), dim3(64 * WAVES),
                        skinny_lds_bytes(M, p.S, WAVES), stream,
                        (const uint16_t *)x, (const uint4 *)wt, (const uint16_t *)sc, (uint16_t *)out,
                        ws_counters(ws), (float *)ws_partials(ws), M, (int)N, (int)K, p.splits, p.S);
-    return hipGetLastError();
 }
 
 template <int WAVES, int GS>
@@ -601,11 +600,10 @@ hipError_t wide_launch(const WidePlan &p, const void *x, const int32_t *wt, cons
                        void *out, int64_t M, int64_t N, int64_t K, void *ws, hipStream_t stream) {
     uint32_t *cnt = ws_counters(ws);
     f32x4 *part = (f32x4 *)ws_partials(ws);
-    hipLaunchKernelGGL((w4a16_wide_kernel<MBW, WR, WC, CT, GS>), dim3((uint32_t)p.grid),
+    return launch_gemm(w4a16_wide_kernel<MBW, WR, WC, CT, GS>, dim3((uint32_t)p.grid),
                        dim3(64 * WR * WC), 0, stream, (const uint16_t *)x, (const uint4 *)wt,
                        (const uint16_t *)sc, (uint16_t *)out, cnt, part, (int)M, (int)N, (int)K,
-                       p.col_tiles, p.units, p.grid, p.maxt);
-    return hipGetLastError();
+                       p.col_tiles, p.units, p.grid, p.maxt, SkWait{p.wait_arrive, p.wait_range});
 }
 
 template <int GS>

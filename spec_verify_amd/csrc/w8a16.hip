@@ -287,11 +287,10 @@ constexpr int kW8SkinnyDepth = 4;
 template <int WAVES, int GS>
 hipError_t w8_skinny_launch_w(const SmallPlan &p, const void *x, const int8_t *w, const void *sc,
                               void *out, int M, int64_t N, int64_t K, void *ws, hipStream_t stream) {
-    hipLaunchKernelGGL((w8a16_skinny_kernel<WAVES, kW8SkinnyDepth, GS>), dim3((uint32_t)(N / 16 * p.splits)),
+    return launch_gemm(w8a16_skinny_kernel<WAVES, kW8SkinnyDepth, GS>, dim3((uint32_t)(N / 16 * p.splits)),
                        dim3(64 * WAVES), skinny_lds_bytes(M, p.S, WAVES), stream, (const uint16_t *)x, w, (const uint16_t *)sc,
                        (uint16_t *)out, ws_counters(ws), (float *)ws_partials(ws), M, (int)N, (int)K,
                        p.splits, p.S);
-    return hipGetLastError();
 }
 
 template <int GS>

@@ -315,13 +315,21 @@ WORKLOADS = {
     # quantized vocabulary head: N = 248320 (about 248k entries, a multiple of 256)
     "vocab_w8_m1":   dict(op="w8a16", M=1,   K=5120,  N=248320, seed=601),
     "vocab_w4_m1":   dict(op="w4a16", M=1,   K=5120,  N=248320, seed=602),
+    # the smaller group sizes the compressed-tensors layout allows (32 and 64)
+    "decode_n6144_g32":  dict(op="w4a16", M=1,   K=5120, N=6144,  seed=211, G=32),
+    "decode_n6144_g64":  dict(op="w4a16", M=1,   K=5120, N=6144,  seed=212, G=64),
+    "verify5_up_g32":    dict(op="w4a16", M=5,   K=5120, N=17408, seed=311, G=32),
+    "verify5_up_g64":    dict(op="w4a16", M=5,   K=5120, N=17408, seed=312, G=64),
+    "batch128_up_g32":   dict(op="w4a16", M=128, K=5120, N=17408, seed=411, G=32),
+    "batch128_up_g64":   dict(op="w4a16", M=128, K=5120, N=17408, seed=412, G=64),
 }
 
 
 def gen_workload(name: str, kind: str = "random"):
     w = WORKLOADS[name]
+    G = w.get("G", 128)
     if w["op"] == "w4a16":
-        return gen_w4a16(w["seed"], w["M"], w["K"], w["N"], 128, kind)
+        return gen_w4a16(w["seed"], w["M"], w["K"], w["N"], G, kind)
     if w["op"] == "w8a16":
-        return gen_w8a16(w["seed"], w["M"], w["K"], w["N"], 128, kind)
+        return gen_w8a16(w["seed"], w["M"], w["K"], w["N"], G, kind)
     return gen_mxfp8(w["seed"], w["M"], w["K"], w["N"], kind)

@@ -231,3 +231,46 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(svq, "library_path", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="libsvq.so not found"):
         svq.lib()
+
+
+def test_format_generic_queries_match_the_per_format_ones(L):
+    bad = ctypes.c_size_t(-1).value
+    for M in (1, 3, 5, 16, 17, 128):
+        for (N, K) in ((5120, 5120), (17408, 5120), (5120, 17408), (256, 1280)):
+            assert L.svq_kernel_name(1, M, N, K, 128) == L.svq_w4a16_kernel_name(0, M, N, K, 128)
+            assert L.svq_workspace_bytes(1, M, N, K, 64) == L.svq_w4a16_workspace_bytes(0, M, N, K, 64)
+            assert L.svq_kernel_name(2, M, N, K, 32) == L.svq_mxfp8_kernel_name(0, M, N, K)
+            assert L.svq_workspace_bytes(2, M, N, K, 32) == L.svq_mxfp8_workspace_bytes(0, M, N, K)
+            if M <= 16:
+                assert L.svq_kernel_name(3, M, N, K, 128) == L.svq_w8a16_kernel_name(M, N, K, 128)
+                assert L.svq_workspace_bytes(3, M, N, K, 128) == L.svq_w8a16_workspace_bytes(M, N, K, 128)
+    assert L.svq_kernel_name(2, 1, 5120, 5120, 128) is None      # MXFP8 groups are 32
+    assert L.svq_workspace_bytes(2, 1, 5120, 5120, 128) == bad
+    assert L.svq_kernel_name(0, 1, 5120, 5120, 128) is None      # unknown op
+    assert L.svq_workspace_bytes(4, 1, 5120, 5120, 128) == bad
+    assert L.svq_kernel_name(3, 17, 5120, 5120, 128) is None     # W8A16 takes M <= 16
+
+
+def test_streamk_wait_hook_is_callable_without_a_gpu(L):
+    L.svq_debug_streamk_wait_ticks(0, 0)
+    L.svq_debug_streamk_wait_ticks(-1, -1)
+
+
+def test_launch_geometry_and_stream_probe_validation(L):
+    g, t, l = ctypes.c_uint64(), ctypes.c_uint32(), ctypes.c_size_t()
+    ref = (ctypes.byref(g), ctypes.byref(t), ctypes.byref(l))
+    assert L.svq_launch_geometry(1, 0, 1, 5120, 5121, 128, *ref) == 4     # N % 16
+    assert L.svq_launch_geometry(1, 0, 0, 5120, 5120, 128, *ref) == 2
+    assert L.svq_launch_geometry(2, 0, 1, 96, 5120, 32, *ref) == 5        # MXFP8 N >= 128
+    assert L.svq_launch_geometry(1, 1, 9, 5120, 5120, 128, *ref) == 10    # dot2 takes M <= 8
+    assert L.svq_launch_geometry(9, 0, 1, 5120, 5120, 128, *ref) == 10    # unknown op
+    assert L.svq_launch_geometry(1, 0, 1, 5120, 5120, 128, None, ref[1], ref[2]) == 1
+    assert L.svq_stream_probe(None, 1 << 20, 256, 256, FAKE2, None) == 1
+    assert L.svq_stream_probe(FAKE, 1 << 20, 256, 256, None, None) == 1
+    assert L.svq_stream_probe(FAKE, 0, 256, 256, FAKE2, None) == 2
+    assert L.svq_stream_probe(FAKE, 1000, 256, 256, FAKE2, None) == 2     # not a multiple of 16
+    assert L.svq_stream_probe(FAKE, 1 << 20, 0, 256, FAKE2, None) == 2
+    assert L.svq_stream_probe(FAKE, 1 << 20, 256, 96, FAKE2, None) == 2   # threads % 64
+    assert L.svq_stream_probe(FAKE, 1 << 20, 256, 2048, FAKE2, None) == 2
+    assert L.svq_stream_probe(FAKE + 8, 1 << 20, 256, 256, FAKE2, None) == 6
+    assert L.svq_stream_probe(FAKE, 1 << 20, 256, 256, FAKE + 64, None) == 7   # sink inside src

@@ -5,7 +5,8 @@ Tolerance (random inputs): max |fp32(out) - y_ref| <= 2e-2 * RMS(y_ref) against
 both the fp64-summed oracle and the fp32-sequential oracle. Integer-valued inputs
 have one exact answer: outputs must equal bf16_RNE(exact) bit for bit. Repack is
 bit-exact. Small shapes are compared element by element; the full-size
-workloads (in the launch configuration the benchmark times) on sampled outputs.
+workloads (in the launch configuration the benchmark times) over every output,
+except the vocabulary heads (N = 248320), which are checked on sampled outputs.
 """
 import os
 import sys
@@ -191,18 +192,10 @@ def test_w4a16_workloads(name):
     _say("w4a16 workload", name, w)
     inp = synth.gen_workload(name)
     out, tiled = run_w4a16(inp)
-    if inp.M * inp.N * inp.K <= 5 * 17408 * 5120:
-        y64, y32 = oracle.w4a16(inp.x, inp.qweight, inp.scales)
-        assert_gate(out, y64, y32, name)
-    else:
-        rows, cols = _sample(inp.M, inp.N, 1500, w["seed"])
-        y64, y32 = oracle.w4a16_points(inp.x, inp.qweight, inp.scales, 128, rows, cols)
-        sel = out[rows, cols]
-        # the gate's RMS is that of the whole output; the sample estimates it
-        ok, err, rms = oracle.gate(sel, y64)
-        assert ok, f"{name}: err={err:.4g} rms={rms:.4g}"
-        assert oracle.gate(sel, y32.astype(np.float64))[0]
-        assert np.all(np.isfinite(oracle.bf16_bits_to_f64(out)))
+    # every output against the full oracle (fp64 and fp32-sequential sums); at
+    # M = 128 that is 2.2 M outputs per projection, a few seconds on the host
+    y64, y32 = oracle.w4a16(inp.x, inp.qweight, inp.scales)
+    assert_gate(out, y64, y32, name)
     # the repacked weights of the full-size run are the oracle's, bit for bit
     np.testing.assert_array_equal(tiled.cpu().numpy(), oracle.q4_repack(inp.qweight))
 
@@ -297,14 +290,9 @@ def test_mxfp8_workloads(name):
     _say("mxfp8 workload", name, w)
     inp = synth.gen_workload(name)
     out = run_mxfp8(inp)
-    if inp.M <= 5:
-        y64, y32 = oracle.mxfp8(inp.x, inp.w, inp.scales)
-        assert_gate(out, y64, y32, name)
-    else:
-        rows, cols = _sample(inp.M, inp.N, 1500, w["seed"])
-        y64, y32 = oracle.mxfp8_points(inp.x, inp.w, inp.scales, rows, cols)
-        ok, err, rms = oracle.gate(out[rows, cols], y64)
-        assert ok, f"{name}: err={err:.4g} rms={rms:.4g}"
+    # every output, against both the fp64 and the fp32-sequential oracle
+    y64, y32 = oracle.mxfp8(inp.x, inp.w, inp.scales)
+    assert_gate(out, y64, y32, name)
 
 
 # ---- quantized vocabulary head: W8A16 and the load-time RTN quantizer --------------

@@ -203,6 +203,29 @@ int svq_w4a16_gemm_with(int kernel, const void *x, const int32_t *qweight_tiled,
 const char *svq_w4a16_kernel_name(int kernel, int64_t M, int64_t N, int64_t K,
                                   int32_t group_size);
 
+/* Size of the device scratch array svq_w4a16_gemm_noalloc uses on each device:
+ * the 256 KiB counter region plus 32 MiB of fp32 partials. */
+#define SVQ_NOALLOC_SCRATCH_BYTES ((size_t)(32u << 20) + (size_t)(256u << 10))
+
+/*
+ * svq_w4a16_gemm without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation. Same arguments, results and errors as
+ * svq_w4a16_gemm with the automatic kernel choice (identical bits: the same
+ * kernels run); the cross-workgroup reductions use a file-scope device array
+ * of SVQ_NOALLOC_SCRATCH_BYTES that each device holds until the process ends.
+ * It allocates nothing (no hipMalloc, hipFree or allocating library call).
+ * Shapes whose workspace (svq_w4a16_workspace_bytes) exceeds the array return
+ * SVQ_ERR_WORKSPACE before anything is enqueued. The first call on a device
+ * looks the array up and enqueues one small fill kernel on `stream` that
+ * clears its counter region. All calls on one device share the array and each
+ * call leaves it as the last call wrote it: calls that overlap in time on one
+ * device race and must be ordered by the caller (one stream, or events).
+ */
+int svq_w4a16_gemm_noalloc(const void *x, const int32_t *qweight_tiled, const void *scales,
+                           void *out, int64_t M, int64_t N, int64_t K, int32_t group_size,
+                           void *stream);
+
 /* ---- MXFP8 ------------------------------------------------------------------ */
 
 size_t svq_mxfp8_workspace_bytes(int kernel, int64_t M, int64_t N, int64_t K);

@@ -40,6 +40,7 @@ EXPORTED_SYMBOLS = (
     "svq_w8a16_workspace_bytes", "svq_w8a16_gemm", "svq_w8a16_kernel_name",
     "svq_fuse_projections", "svq_ct_to_gptq", "svq_mxfp8_quantize", "svq_workspace_bytes",
     "svq_kernel_name", "svq_debug_streamk_wait_ticks", "svq_launch_geometry", "svq_stream_probe",
+    "svq_w4a16_gemm_noalloc",
 )
 
 OP_W4A16, OP_MXFP8, OP_W8A16 = 1, 2, 3
@@ -117,6 +118,8 @@ def lib():
                                           ctypes.POINTER(_sz)]
         L.svq_stream_probe.restype = ctypes.c_int
         L.svq_stream_probe.argtypes = [_p, _sz, ctypes.c_uint32, ctypes.c_uint32, _p, _p]
+        L.svq_w4a16_gemm_noalloc.restype = ctypes.c_int
+        L.svq_w4a16_gemm_noalloc.argtypes = [_p, _p, _p, _p, _i64, _i64, _i64, _i32, _p]
         L.svq_debug_streamk_wait_ticks.restype = None
         L.svq_debug_streamk_wait_ticks.argtypes = [_i64, _i64]
         _lib = L

@@ -20,7 +20,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libsvq.so")
 ROOT = os.path.dirname(PKG)
 
-SOURCES = ["q4_repack.hip", "w4a16_dot2.hip", "w4a16_mfma.hip", "mxfp8_gemm.hip", "w8a16.hip", "mxfp8_quant.hip", "svq_probe.hip", "svq_api.cpp"]
+SOURCES = ["q4_repack.hip", "w4a16_dot2.hip", "w4a16_mfma.hip", "mxfp8_gemm.hip", "w8a16.hip", "mxfp8_quant.hip", "svq_probe.hip", "svq_noalloc.hip", "svq_api.cpp"]
 ARCH = os.environ.get("SVQ_OFFLOAD_ARCH", "gfx950")
 
 

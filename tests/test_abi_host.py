@@ -274,3 +274,12 @@ def test_launch_geometry_and_stream_probe_validation(L):
     assert L.svq_stream_probe(FAKE, 1 << 20, 256, 2048, FAKE2, None) == 2
     assert L.svq_stream_probe(FAKE + 8, 1 << 20, 256, 256, FAKE2, None) == 6
     assert L.svq_stream_probe(FAKE, 1 << 20, 256, 256, FAKE + 64, None) == 7   # sink inside src
+
+
+def test_noalloc_entry_point_validation_without_a_gpu(L):
+    # shape errors are those of svq_w4a16_gemm; a workspace beyond the scratch
+    # array (2 x 160 tiles over 256 workgroups: 64 MiB of partials) is refused
+    assert L.svq_w4a16_gemm_noalloc(FAKE, FAKE2, FAKE3, FAKE4, 1, 5121 - 1 + 8, 5120, 128, None) == 4
+    assert L.svq_w4a16_gemm_noalloc(FAKE, FAKE2, FAKE3, FAKE4, 0, 5120, 5120, 128, None) == 2
+    assert L.svq_w4a16_gemm_noalloc(FAKE, FAKE2, FAKE3, FAKE4, 1, 5120, 5120, 16, None) == 3
+    assert L.svq_w4a16_gemm_noalloc(FAKE, FAKE2, FAKE3, FAKE4, 256, 40960, 5120, 128, None) == 8

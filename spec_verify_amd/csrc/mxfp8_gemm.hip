@@ -18,6 +18,7 @@
 // 128-bit loads). The three kernels mirror the W4A16 ones: a VALU dot2 kernel
 // with a row broadcast of x for M <= 8, a one-MFMA-tile kernel for M <= 16, and
 // the persistent stream-K MFMA kernel with LDS-staged x for larger M.
+#include "svq_dma.h"
 #include "svq_launch.h"
 #include "svq_streamk.h"
 #include "dot2_asm.h"
@@ -219,169 +220,249 @@ __global__ __launch_bounds__(64 * WAVES) void mxfp8_skinny_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// wide stream-K MFMA kernel, any M
+// wide MFMA kernel, M > 16 (any M). Output tiles of BM x 128 (BM = 32, 64 or
+// 128 by M); with fewer tiles than CUs each tile's K range is split evenly over
+// floor(CUs / tiles) workgroups, otherwise the (tile, K step) units are split
+// evenly over one workgroup per CU (stream-K). A tile computed whole by one
+// workgroup is written as bf16 directly; a shared tile's fp32 partials are
+// written with plain stores to the workspace and summed, in contributor order,
+// by a second launch (mxfp8_wide_reduce): the launch boundary orders the
+// partials' stores before their loads, so no workgroup waits for another, and
+// no coherent (cache-bypassing) memory traffic is needed. Measured on the
+// MI355X at M = 128, K = N = 5120 (40 tiles x 6 K ranges): 27.2 us with the
+// partials reduced inside the kernel through coherent stores, arrival counters
+// and bounded waits (about 14 us of it after the K loop), 20.8 us with the
+// second launch.
+//
+// Workgroup: 8 waves as 2 row halves x 4 column quarters; a wave owns MBW
+// 16-row blocks x 2 16-column tiles (16x16x32 bf16 MFMA). Every K step of 128
+// is staged in one slot of a three-slot LDS ring by LDS-DMA (buffer loads that
+// write LDS directly; rows past M and columns past N read as zero): x (BM rows,
+// 16-byte chunks XOR-swizzled by row so that the A reads are bank-conflict
+// free), the E4M3 codes of the tile's 128 columns and their E8M0 scales. The
+// ring runs two steps ahead of the MFMAs; one barrier per step frees the slot
+// the next DMAs go to. Lane (r, g) of a column tile converts the 32 codes of
+// its column at K 32g.. (one E8M0 block) with the block scale applied in the
+// conversion, and MFMA step j takes bytes 8j.. of them against x at the same K.
 // ---------------------------------------------------------------------------
-template <int MBW, int WR, int WC, int CT>
-__global__ __launch_bounds__(64 * WR * WC) void mxfp8_wide_kernel(
-    const uint16_t *__restrict__ x, const uint8_t *__restrict__ w,
-    const uint8_t *__restrict__ sc, uint16_t *__restrict__ out, uint32_t *__restrict__ cnt,
-    f32x4 *__restrict__ part, int M, int N, int K, int col_tiles, int64_t units, int grid,
-    int maxt, SkWait skw) {
-    constexpr int NT = 64 * WR * WC;
-    constexpr int BM = 16 * MBW * WR;
-    constexpr int BN = 16 * CT * WC;
-    constexpr int XROW = 128 + 8;
-    // x stage: 16 lanes per row (16 chunks of 16 bytes = one step of a row),
-    // NT / 16 rows per pass, UPT passes
-    constexpr int RPP = NT / 16;
-    constexpr int UPT = BM / RPP;
-    static_assert(UPT * RPP == BM, "x stage split over the threads");
-    constexpr int NV = MBW * CT;
-    __shared__ __attribute__((aligned(16))) uint16_t xs[2][BM][XROW];
-    __shared__ int s_sk[3];
+template <int MBW>
+struct MxWideCfg {
+    static constexpr int WR = 2, WC = 4, WAVES = WR * WC, NT = 64 * WAVES, CT = 2;
+    static constexpr int BM = 16 * MBW * WR;
+    static constexpr int BN = 16 * CT * WC;       // 128 columns
+    static constexpr int NV = MBW * CT;           // f32x4 accumulators per lane
+    static constexpr int XB = BM * 256;           // x: BM rows x 128 K, bf16
+    static constexpr int WB = BN * 128;           // E4M3 codes: BN columns x 128 K
+    static constexpr int SB = BN * 4;             // E8M0: BN columns x 4 blocks
+    static constexpr int OFF_W = XB, OFF_S = XB + WB, SLOT = XB + WB + SB;
+    static constexpr int XI = XB / 1024 / WAVES;  // x DMAs (1 KiB each) per wave per step
+    static constexpr int WI = WB / 1024 / WAVES;  // code DMAs per wave per step
+    static constexpr int SI = SB / 256;           // scale DMAs per step (waves 0 .. SI-1)
+    static constexpr int MAXPS = XI + WI + 1;     // most DMAs one wave issues per step
+    static_assert(XI >= 1 && XI * 1024 * WAVES == XB, "x stage split over the waves");
+    static_assert(WI * 1024 * WAVES == WB && SI <= WAVES, "code and scale stages split over the waves");
+    static_assert(SLOT % 16 == 0 && 3 * SLOT <= 160 * 1024, "three slots fit the LDS");
+};
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wr = wave / WC, wc = wave % WC;
+// Partial tile of workgroup wg for its `slot`-th tile: NV f32x4 per thread,
+// thread-major ([v][thread]), so that both launches move 16 contiguous bytes
+// per lane.
+template <int NV, int NT>
+__device__ __forceinline__ f32x4 *mx_partial(f32x4 *part, int wg, int maxt, int slot) {
+    return part + ((size_t)wg * maxt + slot) * NV * NT;
+}
+
+template <int MBW>
+__global__ __launch_bounds__(512) void mxfp8_wide_kernel(
+    const uint16_t *__restrict__ x, const uint8_t *__restrict__ w,
+    const uint8_t *__restrict__ sc, uint16_t *__restrict__ out, f32x4 *__restrict__ part,
+    int M, int N, int K, int col_tiles, int64_t units, int grid, int maxt) {
+    using C = MxWideCfg<MBW>;
+    constexpr int BM = C::BM, BN = C::BN, NV = C::NV, CT = C::CT;
+    __shared__ __attribute__((aligned(16))) uint8_t ring[3 * C::SLOT];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = wave_id();
+    const int wr = wave / C::WC, wc = wave % C::WC;
     const int r = lane & 15, g = lane >> 4;
     const int KT = K >> 7;
     const int NB16 = N >> 4;
     const int wg = blockIdx.x;
     const int64_t u_begin = (int64_t)wg * units / grid;
     const int64_t u_end = (int64_t)(wg + 1) * units / grid;
-    const int srow = tid >> 4, schunk = tid & 15;
+    const uint32_t ring_lds = lds_addr(ring);
+    // buffer views: reads past the end return zero (rows >= M, columns >= N)
+    const BufDesc xr = buf_desc(x, (uint32_t)((size_t)M * K * 2));
+    const BufDesc wrs = buf_desc(w, (uint32_t)((size_t)N * K));
+    const BufDesc srs = buf_desc(sc, (uint32_t)((size_t)N * (K >> 5)));
 
-    // Buffer views: a per-lane offset past the end reads zeros without touching
-    // memory, which turns rows >= M and the prefetch after a segment's last step
-    // into loads that need no branch (a conditional load would make the
-    // compiler wait for every load in flight before the next compute).
-    const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, (uint32_t)((size_t)M * K * 2));
-    const __amdgpu_buffer_rsrc_t wrs = make_rsrc(w, (uint32_t)((size_t)N * K));
-    const __amdgpu_buffer_rsrc_t srs = make_rsrc(sc, (uint32_t)((size_t)N * (K >> 5)));
-    constexpr uint32_t kOob = 0x80000000u;
+    // per-lane LDS offsets within a slot
+    uint32_t offA[4];  // A of MFMA step j: row r of the wave's first row block, K 32g + 8j..
+#pragma unroll
+    for (int j = 0; j < 4; ++j) offA[j] = wr * MBW * 4096 + r * 256 + (((4 * g + j) ^ r) << 4);
+    uint32_t offB[CT], offS[CT];  // codes of column (wc*CT + ct)*16 + r at K 32g.., its scale dword
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+        const int cb16 = wc * CT + ct;
+        offB[ct] = C::OFF_W + (cb16 * 2 + (g >> 1)) * 1024 + ((g & 1) * 32 + r) * 16;
+        offS[ct] = C::OFF_S + (cb16 * 16 + r) * 4;
+    }
+    const int per_step = C::XI + C::WI + (wave < C::SI ? 1 : 0);  // this wave's DMAs per stage
 
-    for (int64_t u = u_begin; u < u_end;) {
-        const int tile = (int)(u / KT);
-        const int s0 = (int)(u % KT);
-        const int s1 = (int)((u_end - u) < (int64_t)(KT - s0) ? s0 + (u_end - u) : KT);
-        const int rt = tile / col_tiles, cb = tile % col_tiles;
-        const int row0 = rt * BM;
-
-        // lane (r, g) of column tile ct: column colg, K-rows 32g.. of each step
-        // (one 32-element scale block); the step's four block scales of the
-        // column are one aligned dword, byte g is this lane's
-        uint32_t wvo[CT], svo[CT];
+    struct Seg {
+        int tile, s0, n, rt, cb;
+    };
+    auto seg_at = [&](int64_t u) {
+        Seg sg;
+        sg.tile = (int)(u / KT);
+        sg.s0 = (int)(u % KT);
+        sg.n = (int)((u_end - u) < (int64_t)(KT - sg.s0) ? (u_end - u) : (KT - sg.s0));
+        sg.rt = sg.tile / col_tiles;
+        sg.cb = sg.tile % col_tiles;
+        return sg;
+    };
+    // DMA of K step kt of segment sg into slot st: x (1 KiB = 4 rows per
+    // instruction), codes (16 columns x 64 K per instruction), scales (64
+    // columns x 4 blocks per instruction)
+    auto issue = [&](const Seg &sg, int st, int kt) {
+        const uint32_t base = ring_lds + st * C::SLOT;
+#pragma unroll
+        for (int v = 0; v < C::XI; ++v) {
+            const int q = wave * C::XI + v;
+            const int rl = 4 * q + (lane >> 4);
+            const uint32_t vx = (uint32_t)(sg.rt * BM + rl) * (uint32_t)K * 2u + (uint32_t)(((lane & 15) ^ (rl & 15)) * 16);
+            dma_b128(xr, base + q * 1024, vx, (uint32_t)kt * 256u);
+        }
+#pragma unroll
+        for (int v = 0; v < C::WI; ++v) {
+            const int t = wave * C::WI + v;  // column block t/2, K half t%2
+            const uint32_t col = (uint32_t)(sg.cb * BN + (t >> 1) * 16 + (lane & 15));
+            dma_b128(wrs, base + C::OFF_W + t * 1024, col * (uint32_t)K + (uint32_t)(64 * (t & 1) + 16 * (lane >> 4)),
+                     (uint32_t)kt * 128u);
+        }
+        if (wave < C::SI) {
+            const uint32_t col = (uint32_t)(sg.cb * BN + wave * 64 + lane);
+            dma_b32(srs, base + C::OFF_S + wave * 256, col * (uint32_t)(K >> 5), (uint32_t)kt * 4u);
+        }
+    };
+    auto compute = [&](int st, f32x4 (&acc)[NV]) {
+        const lds_u8 *b = lds_opaque(ring_lds + st * C::SLOT);
+        uint4 wv[CT][2];
+        float sf[CT];
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
-            const int nbg = cb * (BN / 16) + wc * CT + ct;
-            const int colg = (nbg < NB16 ? nbg : NB16 - 1) * 16 + r;
-            wvo[ct] = (uint32_t)colg * (uint32_t)K + g * 32;
-            svo[ct] = (uint32_t)colg * (uint32_t)(K >> 5);
+            wv[ct][0] = lds_ld16(b + offB[ct]);
+            wv[ct][1] = lds_ld16(b + offB[ct] + 256);
+            sf[ct] = e8m0_to_f32((lds_ld<uint32_t>(b + offS[ct]) >> (8 * g)) & 0xFFu);
         }
-        // rows past M read row M - 1 (their products are never stored)
-        uint32_t xvo[UPT];
 #pragma unroll
-        for (int v = 0; v < UPT; ++v) {
-            const int row = row0 + srow + RPP * v;
-            xvo[v] = (uint32_t)(row < M ? row : M - 1) * (uint32_t)K * 2u + schunk * 16;
+        for (int j = 0; j < 4; ++j) {
+            uint4 A[MBW];
+#pragma unroll
+            for (int rb = 0; rb < MBW; ++rb) A[rb] = lds_ld16(b + offA[j] + rb * 4096);
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) {
+                const uint4 &q = wv[ct][j >> 1];
+                const uint4 B = (j & 1) ? cvt8_e4m3_bf16(q.z, q.w, sf[ct]) : cvt8_e4m3_bf16(q.x, q.y, sf[ct]);
+#pragma unroll
+                for (int rb = 0; rb < MBW; ++rb) acc[rb * CT + ct] = mfma16x16x32(A[rb], B, acc[rb * CT + ct]);
+            }
         }
-        // kOob for a step past the segment (operands stay below 2^31 bytes)
-        auto past = [&](int s) { return (uint32_t)(s1 - 1 - s) & kOob; };
+    };
 
+    // Segments (runs of K steps of one tile) one after another; each runs the
+    // ring from its start: two stages issued, then per step a wait for this
+    // wave's stage, a barrier, the DMA of the stage two steps ahead and the
+    // step's MFMAs. (With fewer tiles than CUs every workgroup has one segment.)
+    for (int64_t u = u_begin; u < u_end;) {
+        const Seg sg = seg_at(u);
+        const int n = sg.n;
         f32x4 acc[NV];
 #pragma unroll
         for (int v = 0; v < NV; ++v) acc[v] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-        uint4 xreg[UPT];
-        uint4 wcur[CT][2], wnext[CT][2];
-        uint32_t scur[CT], snext[CT];
-
-        // loads of K step s (s >= s1: out of range, zeros, no traffic)
-        // (the out-of-range bit is formed arithmetically: a select on the
-        // wave-uniform condition would become a branch around the loads)
-        // A step's loads are issued in one fixed order, x then weights and
-        // scales, fenced from the surrounding code: the s_waitcnt counts then
-        // agree on every path into the loop. The empty asm with a memory
-        // clobber keeps the optimizer from sinking the loads below the next
-        // compute phase (it emits no instruction and no wait).
-        auto load_step = [&](uint4(&W)[CT][2], uint32_t(&S)[CT], int s) {
-            const uint32_t o = past(s);
-            __builtin_amdgcn_sched_barrier(0);
+        lds_barrier();  // the previous segment is done with every slot
+        issue(sg, 0, sg.s0);
+        if (n > 1) issue(sg, 1, sg.s0 + 1);
+        for (int i = 0; i < n; ++i) {
+            // this wave's stage of step i has landed (only step i+1's may be outstanding)
+            if (i + 1 < n) wait_vmcnt_at_most<C::MAXPS>(per_step);
+            else wait_vmcnt<0>();
+            lds_barrier();  // every wave's stage of step i is in; every wave is done with step i-1
+            if (i + 2 < n) issue(sg, (i + 2) % 3, sg.s0 + i + 2);
+            compute(i % 3, acc);
+        }
+        if (sg.s0 == 0 && n == KT) {
+            // the whole tile: bf16 straight to y
+            const int rowb = sg.rt * BM + wr * MBW * 16 + 4 * g;
 #pragma unroll
-            for (int v = 0; v < UPT; ++v) xreg[v] = bload16(xr, (xvo[v] + (uint32_t)s * 256u) | o, 0);
-            __builtin_amdgcn_sched_barrier(0);
+            for (int v = 0; v < NV; ++v) {
+                const int rb = v / CT, ct = v % CT;
+                const int nbg = sg.cb * (BN / 16) + wc * CT + ct;
+                if (nbg >= NB16) continue;
+                const int colg = nbg * 16 + r;
 #pragma unroll
-            for (int ct = 0; ct < CT; ++ct) {
-                const uint32_t vo = (wvo[ct] + (uint32_t)s * 128u) | o;
-                W[ct][0] = bload16(wrs, vo, 0);
-                W[ct][1] = bload16(wrs, vo + 16, 0);
-                S[ct] = bload4(srs, (svo[ct] + (uint32_t)s * 4u) | o, 0);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            asm volatile("" ::: "memory");
-        };
-        auto compute = [&](int buf, const uint4 (&W)[CT][2], const uint32_t (&S)[CT]) {
-            const int rbase = wr * MBW * 16;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                uint4 A[MBW];
-#pragma unroll
-                for (int rb = 0; rb < MBW; ++rb) A[rb] = *(const uint4 *)&xs[buf][rbase + rb * 16 + r][32 * g + 8 * j];
-#pragma unroll
-                for (int ct = 0; ct < CT; ++ct) {
-                    const float sf = e8m0_to_f32((S[ct] >> (8 * g)) & 0xFFu);
-                    const uint4 &wv = W[ct][j >> 1];
-                    const uint4 B = (j & 1) ? cvt8_e4m3_bf16(wv.z, wv.w, sf) : cvt8_e4m3_bf16(wv.x, wv.y, sf);
-#pragma unroll
-                    for (int rb = 0; rb < MBW; ++rb) acc[rb * CT + ct] = mfma16x16x32(A[rb], B, acc[rb * CT + ct]);
+                for (int i = 0; i < 4; ++i) {
+                    const int row = rowb + rb * 16 + i;
+                    if (row < M) out[(size_t)row * N + colg] = f32_to_bf16_rne(acc[v][i]);
                 }
             }
-        };
-        auto stage_x = [&](int buf) {
-#pragma unroll
-            for (int v = 0; v < UPT; ++v) *(uint4 *)&xs[buf][srow + RPP * v][schunk * 8] = xreg[v];
-        };
-
-        // Two register sets for the weights and scales, used alternately, so
-        // that the compute of a step never reads registers that the next
-        // step's loads are still filling (a copy between the sets would make
-        // every step wait for the next step's loads).
-        // Steps go in pairs; every half issues its prefetch (past the segment
-        // it reads zeros), and only the compute of a missing second step is
-        // skipped, so no load sits behind a branch.
-        __syncthreads();
-        load_step(wcur, scur, s0);
-        for (int s = s0; s < s1; s += 2) {
-            stage_x(0);
-            __syncthreads();
-            load_step(wnext, snext, s + 1);
-            compute(0, wcur, scur);
-            stage_x(1);
-            __syncthreads();
-            load_step(wcur, scur, s + 2);
-            if (s + 1 < s1) compute(1, wnext, snext);
-        }
-
-        const int rowb = row0 + wr * MBW * 16 + 4 * g;
-        // accumulator v = (row block v / CT, column tile v % CT) of this thread
-        auto store_v = [&](int v, const f32x4 &val) {
-            const int rb = v / CT, ct = v % CT;
-            const int nbg = cb * (BN / 16) + wc * CT + ct;
-            if (nbg >= NB16) return;
-            const int colg = nbg * 16 + r;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = rowb + rb * 16 + i;
-                if (row < M) out[(size_t)row * N + colg] = f32_to_bf16_rne(val[i]);
-            }
-        };
-        if (s0 == 0 && s1 == KT) {
-#pragma unroll
-            for (int v = 0; v < NV; ++v) store_v(v, acc[v]);
         } else {
-            sk_reduce<NV, NT>(acc, tile, KT, units, grid, maxt, cnt, part, s_sk, skw, store_v);
+            // a K range of a shared tile: the fp32 partial, summed by mxfp8_wide_reduce
+            f32x4 *mp = mx_partial<NV, C::NT>(part, wg, maxt, sg.tile - sk_first_tile(wg, units, grid, KT));
+#pragma unroll
+            for (int v = 0; v < NV; ++v) mp[v * C::NT + threadIdx.x] = acc[v];
         }
-        u += s1 - s0;
+        u += n;
     }
+}
+
+// Sum of a shared tile's partials: workgroup (tile, v) adds accumulator v of
+// every contributor of the tile (the workgroups whose unit ranges cover it),
+// in workgroup order, and writes the bf16 outputs that accumulator v of each
+// thread of the wide kernel holds. Tiles computed whole by one workgroup were
+// written by the wide kernel and are skipped.
+template <int MBW>
+__global__ __launch_bounds__(512) void mxfp8_wide_reduce(const f32x4 *__restrict__ part,
+                                                         uint16_t *__restrict__ out, int M, int N, int K,
+                                                         int col_tiles, int64_t units, int grid, int maxt) {
+    using C = MxWideCfg<MBW>;
+    constexpr int BM = C::BM, BN = C::BN, NV = C::NV, CT = C::CT, NT = C::NT;
+    const int tile = blockIdx.x / NV, v = blockIdx.x % NV;
+    const int KT = K >> 7;
+    const int64_t t0 = (int64_t)tile * KT;
+    const int fw = sk_owner(t0, units, grid), lw = sk_owner(t0 + KT - 1, units, grid);
+    if (fw == lw) return;  // one workgroup computed the whole tile
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wr = wave / C::WC, wc = wave % C::WC, r = lane & 15, g = lane >> 4;
+    // The contributors' ranges are consecutive: every one after the first
+    // starts inside this tile (its partial is in its slot 0); only the first
+    // may have begun in an earlier tile.
+    const int slot_fw = tile - sk_first_tile(fw, units, grid, KT);
+    const size_t stride = (size_t)maxt * NV * NT;  // f32x4 per workgroup
+    const f32x4 *p0 = part + (size_t)v * NT + tid;
+    f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+    for (int w0 = fw; w0 <= lw; w0 += 8) {
+        // eight loads in flight, none behind a branch (past the last
+        // contributor the index is clamped and the value not added)
+        f32x4 a[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int w = w0 + k < lw ? w0 + k : lw;
+            a[k] = p0[(size_t)w * stride + (w == fw ? (size_t)slot_fw * NV * NT : 0)];
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            if (w0 + k <= lw) sum += a[k];
+    }
+    const int rt = tile / col_tiles, cb = tile % col_tiles;
+    const int rb = v / CT, ct = v % CT;
+    const int nbg = cb * (BN / 16) + wc * CT + ct;
+    if (nbg >= (N >> 4)) return;
+    const int colg = nbg * 16 + r;
+    const int rowb = rt * BM + wr * MBW * 16 + rb * 16 + 4 * g;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        if (rowb + i < M) out[(size_t)(rowb + i) * N + colg] = f32_to_bf16_rne(sum[i]);
 }
 
 // ---------------------------------------------------------------------------
@@ -423,14 +504,19 @@ hipError_t mx_skinny_launch_w(const SmallPlan &p, const void *x, const uint8_t *
                        (int)K, p.splits, p.S);
 }
 
-template <int MBW, int WR, int WC, int CT>
+template <int MBW>
 hipError_t mx_wide_launch(const WidePlan &p, const void *x, const uint8_t *w, const uint8_t *sc,
                           void *out, int64_t M, int64_t N, int64_t K, void *ws, hipStream_t stream) {
-    uint32_t *cnt = ws_counters(ws);
+    using C = MxWideCfg<MBW>;
     f32x4 *part = (f32x4 *)ws_partials(ws);
-    return launch_gemm(mxfp8_wide_kernel<MBW, WR, WC, CT>, dim3((uint32_t)p.grid),
-                       dim3(64 * WR * WC), 0, stream, (const uint16_t *)x, w, sc, (uint16_t *)out,
-                       cnt, part, (int)M, (int)N, (int)K, p.col_tiles, p.units, p.grid, p.maxt, SkWait{p.wait_arrive, p.wait_range});
+    hipError_t e = launch_gemm(mxfp8_wide_kernel<MBW>, dim3((uint32_t)p.grid), dim3(C::NT), 0, stream,
+                               (const uint16_t *)x, w, sc, (uint16_t *)out, part, (int)M, (int)N, (int)K,
+                               p.col_tiles, p.units, p.grid, p.maxt);
+    if (e != hipSuccess || !p.workspace_bytes) return e;
+    // shared tiles: the partials' sum, one workgroup per (tile, accumulator)
+    return launch_gemm(mxfp8_wide_reduce<MBW>, dim3((uint32_t)((int64_t)p.row_tiles * p.col_tiles * C::NV)),
+                       dim3(C::NT), 0, stream, (const f32x4 *)part, (uint16_t *)out, (int)M, (int)N, (int)K,
+                       p.col_tiles, p.units, p.grid, p.maxt);
 }
 }  // namespace
 
@@ -466,10 +552,12 @@ hipError_t launch_mxfp8_skinny(const SmallPlan &plan, const void *x, const uint8
 hipError_t launch_mxfp8_wide(const WidePlan &plan, const void *x, const uint8_t *w,
                              const uint8_t *scales, void *out, int64_t M, int64_t N, int64_t K,
                              void *workspace, hipStream_t stream) {
-    // 128 x 128 tiles: four waves side by side (each all 128 rows x 32 columns),
-    // so every weight byte is loaded and converted by one wave only
-    if (plan.bm == 128) return mx_wide_launch<8, 1, 4, 2>(plan, x, w, scales, out, M, N, K, workspace, stream);
-    return mx_wide_launch<4, 1, 4, 4>(plan, x, w, scales, out, M, N, K, workspace, stream);
+    // row tiles of 32, 64 or 128 (MBW = 1, 2, 4 row blocks per wave), 128 columns
+    switch (plan.bm) {
+    case 32: return mx_wide_launch<1>(plan, x, w, scales, out, M, N, K, workspace, stream);
+    case 64: return mx_wide_launch<2>(plan, x, w, scales, out, M, N, K, workspace, stream);
+    default: return mx_wide_launch<4>(plan, x, w, scales, out, M, N, K, workspace, stream);
+    }
 }
 
 }  // namespace svq

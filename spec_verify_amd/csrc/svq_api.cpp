@@ -17,8 +17,6 @@ namespace {
 
 constexpr int64_t kMaxDim = int64_t(1) << 24;  // per dimension
 constexpr int kMaxDevices = 64;
-constexpr int kWideThreads = 256;              // threads per wide-kernel workgroup
-constexpr int kWideAccPerThread = 16;          // f32x4 accumulators per thread
 
 std::atomic<int> g_num_cus[kMaxDevices];
 // stream-K wait budgets of the wide kernels (changed only by the test hook)
@@ -107,8 +105,9 @@ WidePlan plan_w4a16_wide(int64_t M, int64_t N, int64_t K, int num_cus) {
     return make_plan(M, N, K, num_cus, 128, 256, (size_t)128 * 256 * 4);
 }
 WidePlan plan_mxfp8_wide(int64_t M, int64_t N, int64_t K, int num_cus) {
-    const int bm = M > 64 ? 128 : 64, bn = M > 64 ? 128 : 256;
-    return make_plan(M, N, K, num_cus, bm, bn, (size_t)kWideAccPerThread * kWideThreads * 16);
+    // row tiles of 32, 64 or 128 by M, 128 columns; a partial is one fp32 tile
+    const int bm = M <= 32 ? 32 : (M <= 64 ? 64 : 128);
+    return make_plan(M, N, K, num_cus, bm, 128, (size_t)bm * 128 * 4);
 }
 
 }  // namespace svq
@@ -409,6 +408,11 @@ int svq_mxfp8_gemm_with(int kernel, const void *x, const uint8_t *w, const uint8
         wplan = plan_mxfp8_wide(M, N, K, cus);
         need = wplan.workspace_bytes;
         if (need && (size_t)wplan.row_tiles * wplan.col_tiles * kSkCountersPerTile > kMaxCounters) return SVQ_ERR_UNSUPPORTED;
+        // x rows padded to whole row tiles and columns padded to whole column
+        // tiles are addressed with 32-bit buffer offsets
+        if ((uint64_t)wplan.row_tiles * wplan.bm * K * 2 >= (1ull << 32) ||
+            (uint64_t)wplan.col_tiles * wplan.bn * K >= (1ull << 32))
+            return SVQ_ERR_UNSUPPORTED;
     } else {
         splan = mxfp8_small_plan(k, M, N, K, cus);
         need = splan.workspace_bytes;
@@ -481,7 +485,7 @@ int svq_launch_geometry(int op, int kernel, int64_t M, int64_t N, int64_t K, int
     }
     capture_slot() = nullptr;
     if (st != SVQ_OK) return st;
-    if (shape.launches != 1) return SVQ_ERR_UNSUPPORTED;
+    if (shape.launches < 1) return SVQ_ERR_UNSUPPORTED;
     *grid = shape.grid;
     *threads = shape.threads;
     *lds_bytes = shape.lds;

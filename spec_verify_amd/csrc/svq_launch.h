@@ -10,9 +10,10 @@
 
 namespace svq {
 
-// Launch shape of a GEMM launch (grid and workgroup size, dynamic LDS). A
-// launch query sets the calling thread's capture slot: the GEMM launchers then
-// record their shape there instead of launching.
+// Launch shape of a GEMM call (grid and workgroup size, dynamic LDS of its
+// first, main launch; the number of launches). A launch query sets the calling
+// thread's capture slot: the GEMM launchers then record their shape there
+// instead of launching.
 struct LaunchShape {
     uint64_t grid;
     uint32_t threads;
@@ -24,10 +25,11 @@ LaunchShape *&capture_slot();  // this thread's slot (null: launch normally)
 template <typename F, typename... Args>
 hipError_t launch_gemm(F kernel, dim3 grid, dim3 block, size_t lds, hipStream_t stream, Args... args) {
     if (LaunchShape *c = capture_slot()) {
-        c->grid = (uint64_t)grid.x * grid.y * grid.z;
-        c->threads = block.x * block.y * block.z;
-        c->lds = lds;
-        ++c->launches;
+        if (c->launches++ == 0) {  // the first launch is the call's main kernel
+            c->grid = (uint64_t)grid.x * grid.y * grid.z;
+            c->threads = block.x * block.y * block.z;
+            c->lds = lds;
+        }
         return hipSuccess;
     }
     hipLaunchKernelGGL(kernel, grid, block, lds, stream, args...);

@@ -184,11 +184,11 @@ def test_w8a16_smallest_k(K, M, G):
 
 # ---- the give-up path of the wide kernels' cross-workgroup reduction ------------------
 
-# Shapes whose output tiles are shared by several workgroups: 2 tiles over 20 K
-# steps (10 contributors each), and one tile over 40 K steps (40 contributors:
-# more than the 32 reduction ranges a tile is split into).
-GIVEUP = [("w4a16", 128, 2560, 272, 128), ("w4a16", 64, 5120, 256, 32), ("w4a16", 100, 5120, 256, 128),
-          ("mxfp8", 128, 2560, 272, 32), ("mxfp8", 64, 5120, 256, 32)]
+# W4A16 shapes whose output tiles are shared by several workgroups: 2 tiles over
+# 20 K steps (10 contributors each), and one tile over 40 K steps (40
+# contributors: more than the 32 reduction ranges a tile is split into). (The
+# MXFP8 wide kernel sums shared tiles in a second launch instead; see below.)
+GIVEUP = [("w4a16", 128, 2560, 272, 128), ("w4a16", 64, 5120, 256, 32), ("w4a16", 100, 5120, 256, 128)]
 
 
 @pytest.mark.parametrize("op,M,K,N,G", GIVEUP, ids=["-".join(map(str, c)) for c in GIVEUP])
@@ -218,6 +218,28 @@ def test_wide_reduction_give_up_path(op, M, K, N, G):
     again = p.run(3, workspace=ws)               # defaults restored: same bits
     torch.cuda.synchronize()
     assert torch.equal(again.view(torch.int16), normal.view(torch.int16))
+
+
+# MXFP8 wide shapes whose tiles are shared: the partials are summed by a second
+# launch in contributor order. 128 x 2560 x 272: 3 column tiles over 20 K steps;
+# 64 x 5120 x 256: 2 tiles over 40 K steps, 40 contributors each (the sum runs in
+# groups of 8); 200 x 1280 x 640: 2 row tiles x 5 column tiles.
+MX_SHARED = [(128, 2560, 272), (64, 5120, 256), (200, 1280, 640), (17, 5120, 128)]
+
+
+@pytest.mark.parametrize("M,K,N", MX_SHARED, ids=["-".join(map(str, c)) for c in MX_SHARED])
+def test_mxfp8_wide_shared_tiles_second_launch(M, K, N):
+    _say("mxfp8 wide shared M K N", M, K, N)
+    p = MX(5650 + M + K + N, M, K, N)
+    nbytes = p.ws_bytes(3)
+    assert nbytes > COUNTER_BYTES                # tiles are shared: partials exist
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    outs = [p.run(3, workspace=ws) for _ in range(3)]
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16))
+    assert int(ws[:COUNTER_BYTES].count_nonzero()) == 0
+    assert_gate(host_bits(outs[0]), *p.ref(), f"mxfp8 wide shared M{M} K{K} N{N}")
 
 
 # ---- guard bytes around the workspace and the output ---------------------------------

@@ -366,20 +366,6 @@ int svq_launch_geometry(int op, int kernel, int64_t M, int64_t N, int64_t K, int
 int svq_stream_probe(const void *src, size_t bytes, uint32_t grid, uint32_t threads, uint32_t *sink,
                      void *stream);
 
-/* ---- test hook ----------------------------------------------------------------- */
-
-/*
- * Wait budgets of the cross-workgroup reduction in the wide (M > 16) kernels,
- * in ticks of the 100 MHz s_memrealtime clock (defaults: 2000 for the wait on
- * the other contributors' partials, 1000 for the last arriver's wait on the
- * other reducers). A workgroup that runs out of budget stops waiting and the
- * last arriver reduces what is still missing, so results never depend on the
- * budget; 0 makes every member give up at once. Negative values restore the
- * defaults. Process-wide; applies to launches made after the call. For tests
- * of that fallback path.
- */
-void svq_debug_streamk_wait_ticks(int64_t arrive_ticks, int64_t range_ticks);
-
 #ifdef __cplusplus
 }
 #endif

@@ -23,7 +23,7 @@ __all__ = [
     "mxfp8_kernel_name", "w4a16_workspace_bytes", "mxfp8_workspace_bytes", "Workspace",
     "EXPORTED_SYMBOLS", "rtn_quantize", "w8a16_gemm", "w8a16_workspace_bytes", "w8a16_kernel_name",
     "fuse_projections", "fuse_or_keep", "ct_to_gptq", "MAX_FUSED_PARTS", "mxfp8_quantize",
-    "OP_W4A16", "OP_MXFP8", "OP_W8A16", "workspace_bytes", "kernel_name", "debug_streamk_wait_ticks",
+    "OP_W4A16", "OP_MXFP8", "OP_W8A16", "workspace_bytes", "kernel_name",
     "launch_geometry", "stream_probe",
 ]
 
@@ -39,7 +39,7 @@ EXPORTED_SYMBOLS = (
     "svq_mxfp8_gemm_with", "svq_mxfp8_kernel_name", "svq_rtn_quantize",
     "svq_w8a16_workspace_bytes", "svq_w8a16_gemm", "svq_w8a16_kernel_name",
     "svq_fuse_projections", "svq_ct_to_gptq", "svq_mxfp8_quantize", "svq_workspace_bytes",
-    "svq_kernel_name", "svq_debug_streamk_wait_ticks", "svq_launch_geometry", "svq_stream_probe",
+    "svq_kernel_name", "svq_launch_geometry", "svq_stream_probe",
     "svq_w4a16_gemm_noalloc",
 )
 
@@ -120,8 +120,6 @@ def lib():
         L.svq_stream_probe.argtypes = [_p, _sz, ctypes.c_uint32, ctypes.c_uint32, _p, _p]
         L.svq_w4a16_gemm_noalloc.restype = ctypes.c_int
         L.svq_w4a16_gemm_noalloc.argtypes = [_p, _p, _p, _p, _i64, _i64, _i64, _i32, _p]
-        L.svq_debug_streamk_wait_ticks.restype = None
-        L.svq_debug_streamk_wait_ticks.argtypes = [_i64, _i64]
         _lib = L
         return L
 
@@ -243,12 +241,6 @@ def stream_probe(src, nbytes, grid, threads, sink):
         raise ValueError("src or sink too small")
     _check(lib().svq_stream_probe(_dev_ptr(src, "src"), nbytes, grid, threads, _dev_ptr(sink, "sink"),
                                   _stream_ptr(src)), "svq_stream_probe")
-
-
-def debug_streamk_wait_ticks(arrive_ticks=-1, range_ticks=-1):
-    """Test hook: wait budgets of the wide kernels' cross-workgroup reduction
-    (negative restores the defaults)."""
-    lib().svq_debug_streamk_wait_ticks(int(arrive_ticks), int(range_ticks))
 
 
 def q4_repack(qweight, out=None):

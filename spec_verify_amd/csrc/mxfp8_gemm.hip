@@ -226,7 +226,7 @@ __global__ __launch_bounds__(64 * WAVES) void mxfp8_skinny_kernel(
 // evenly over one workgroup per CU (stream-K). A tile computed whole by one
 // workgroup is written as bf16 directly; a shared tile's fp32 partials are
 // written with plain stores to the workspace and summed, in contributor order,
-// by a second launch (mxfp8_wide_reduce): the launch boundary orders the
+// by a second launch (wide_sum_kernel): the launch boundary orders the
 // partials' stores before their loads, so no workgroup waits for another, and
 // no coherent (cache-bypassing) memory traffic is needed. Measured on the
 // MI355X at M = 128, K = N = 5120 (40 tiles x 6 K ranges): 27.2 us with the
@@ -263,14 +263,6 @@ struct MxWideCfg {
     static_assert(WI * 1024 * WAVES == WB && SI <= WAVES, "code and scale stages split over the waves");
     static_assert(SLOT % 16 == 0 && 3 * SLOT <= 160 * 1024, "three slots fit the LDS");
 };
-
-// Partial tile of workgroup wg for its `slot`-th tile: NV f32x4 per thread,
-// thread-major ([v][thread]), so that both launches move 16 contiguous bytes
-// per lane.
-template <int NV, int NT>
-__device__ __forceinline__ f32x4 *mx_partial(f32x4 *part, int wg, int maxt, int slot) {
-    return part + ((size_t)wg * maxt + slot) * NV * NT;
-}
 
 template <int MBW>
 __global__ __launch_bounds__(512) void mxfp8_wide_kernel(
@@ -407,62 +399,13 @@ __global__ __launch_bounds__(512) void mxfp8_wide_kernel(
                 }
             }
         } else {
-            // a K range of a shared tile: the fp32 partial, summed by mxfp8_wide_reduce
-            f32x4 *mp = mx_partial<NV, C::NT>(part, wg, maxt, sg.tile - sk_first_tile(wg, units, grid, KT));
+            // a K range of a shared tile: the fp32 partial, summed by wide_sum_kernel
+            f32x4 *mp = wide_partial<NV, C::NT>(part, wg, maxt, sg.tile - sk_first_tile(wg, units, grid, KT));
 #pragma unroll
             for (int v = 0; v < NV; ++v) mp[v * C::NT + threadIdx.x] = acc[v];
         }
         u += n;
     }
-}
-
-// Sum of a shared tile's partials: workgroup (tile, v) adds accumulator v of
-// every contributor of the tile (the workgroups whose unit ranges cover it),
-// in workgroup order, and writes the bf16 outputs that accumulator v of each
-// thread of the wide kernel holds. Tiles computed whole by one workgroup were
-// written by the wide kernel and are skipped.
-template <int MBW>
-__global__ __launch_bounds__(512) void mxfp8_wide_reduce(const f32x4 *__restrict__ part,
-                                                         uint16_t *__restrict__ out, int M, int N, int K,
-                                                         int col_tiles, int64_t units, int grid, int maxt) {
-    using C = MxWideCfg<MBW>;
-    constexpr int BM = C::BM, BN = C::BN, NV = C::NV, CT = C::CT, NT = C::NT;
-    const int tile = blockIdx.x / NV, v = blockIdx.x % NV;
-    const int KT = K >> 7;
-    const int64_t t0 = (int64_t)tile * KT;
-    const int fw = sk_owner(t0, units, grid), lw = sk_owner(t0 + KT - 1, units, grid);
-    if (fw == lw) return;  // one workgroup computed the whole tile
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wr = wave / C::WC, wc = wave % C::WC, r = lane & 15, g = lane >> 4;
-    // The contributors' ranges are consecutive: every one after the first
-    // starts inside this tile (its partial is in its slot 0); only the first
-    // may have begun in an earlier tile.
-    const int slot_fw = tile - sk_first_tile(fw, units, grid, KT);
-    const size_t stride = (size_t)maxt * NV * NT;  // f32x4 per workgroup
-    const f32x4 *p0 = part + (size_t)v * NT + tid;
-    f32x4 sum = {0.f, 0.f, 0.f, 0.f};
-    for (int w0 = fw; w0 <= lw; w0 += 8) {
-        // eight loads in flight, none behind a branch (past the last
-        // contributor the index is clamped and the value not added)
-        f32x4 a[8];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const int w = w0 + k < lw ? w0 + k : lw;
-            a[k] = p0[(size_t)w * stride + (w == fw ? (size_t)slot_fw * NV * NT : 0)];
-        }
-#pragma unroll
-        for (int k = 0; k < 8; ++k)
-            if (w0 + k <= lw) sum += a[k];
-    }
-    const int rt = tile / col_tiles, cb = tile % col_tiles;
-    const int rb = v / CT, ct = v % CT;
-    const int nbg = cb * (BN / 16) + wc * CT + ct;
-    if (nbg >= (N >> 4)) return;
-    const int colg = nbg * 16 + r;
-    const int rowb = rt * BM + wr * MBW * 16 + rb * 16 + 4 * g;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-        if (rowb + i < M) out[(size_t)(rowb + i) * N + colg] = f32_to_bf16_rne(sum[i]);
 }
 
 // ---------------------------------------------------------------------------
@@ -514,9 +457,10 @@ hipError_t mx_wide_launch(const WidePlan &p, const void *x, const uint8_t *w, co
                                p.col_tiles, p.units, p.grid, p.maxt);
     if (e != hipSuccess || !p.workspace_bytes) return e;
     // shared tiles: the partials' sum, one workgroup per (tile, accumulator)
-    return launch_gemm(mxfp8_wide_reduce<MBW>, dim3((uint32_t)((int64_t)p.row_tiles * p.col_tiles * C::NV)),
-                       dim3(C::NT), 0, stream, (const f32x4 *)part, (uint16_t *)out, (int)M, (int)N, (int)K,
-                       p.col_tiles, p.units, p.grid, p.maxt);
+    return launch_gemm(wide_sum_kernel<MBW, C::WR, C::WC, C::CT, C::BM, C::BN>,
+                       dim3((uint32_t)((int64_t)p.row_tiles * p.col_tiles * C::NV)), dim3(C::NT), 0, stream,
+                       (const f32x4 *)part, (uint16_t *)out, (int)M, (int)N, (int)K, p.col_tiles, p.units,
+                       p.grid, p.maxt);
 }
 }  // namespace
 

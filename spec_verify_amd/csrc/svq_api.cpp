@@ -19,20 +19,12 @@ constexpr int64_t kMaxDim = int64_t(1) << 24;  // per dimension
 constexpr int kMaxDevices = 64;
 
 std::atomic<int> g_num_cus[kMaxDevices];
-// stream-K wait budgets of the wide kernels (changed only by the test hook)
-std::atomic<uint32_t> g_wait_arrive{kSkArriveWaitDefault};
-std::atomic<uint32_t> g_wait_range{kSkRangeWaitDefault};
 
 }  // namespace
 
 LaunchShape *&capture_slot() {
     static thread_local LaunchShape *slot = nullptr;
     return slot;
-}
-
-void streamk_wait_ticks(uint32_t &arrive, uint32_t &range) {
-    arrive = g_wait_arrive.load(std::memory_order_relaxed);
-    range = g_wait_range.load(std::memory_order_relaxed);
 }
 
 // Compute units of the current device (cached per device).
@@ -75,7 +67,6 @@ static WidePlan make_plan(int64_t M, int64_t N, int64_t K, int num_cus, int bm, 
         if (b % KT != 0 || e % KT != 0) shared = true;
     }
     p.maxt = maxt;
-    streamk_wait_ticks(p.wait_arrive, p.wait_range);
     if (shared) p.workspace_bytes = kCounterBytes + (size_t)p.grid * p.maxt * slot_bytes;
     return p;
 }
@@ -345,7 +336,6 @@ int svq_w4a16_gemm_with(int kernel, const void *x, const int32_t *wt, const void
     if (k == SVQ_KERNEL_MFMA_WIDE) {
         wplan = plan_w4a16_wide(M, N, K, cus);
         need = wplan.workspace_bytes;
-        if (need && (size_t)wplan.row_tiles * wplan.col_tiles * kSkCountersPerTile > kMaxCounters) return SVQ_ERR_UNSUPPORTED;
         // the kernel addresses x (padded to whole row tiles), the weights and
         // the scales with 32-bit buffer offsets
         if ((uint64_t)wplan.row_tiles * wplan.bm * K * 2 >= (1ull << 32) || (uint64_t)N * K / 2 >= (1ull << 32))
@@ -407,7 +397,6 @@ int svq_mxfp8_gemm_with(int kernel, const void *x, const uint8_t *w, const uint8
     if (k == SVQ_KERNEL_MFMA_WIDE) {
         wplan = plan_mxfp8_wide(M, N, K, cus);
         need = wplan.workspace_bytes;
-        if (need && (size_t)wplan.row_tiles * wplan.col_tiles * kSkCountersPerTile > kMaxCounters) return SVQ_ERR_UNSUPPORTED;
         // x rows padded to whole row tiles and columns padded to whole column
         // tiles are addressed with 32-bit buffer offsets
         if ((uint64_t)wplan.row_tiles * wplan.bm * K * 2 >= (1ull << 32) ||
@@ -504,13 +493,6 @@ int svq_stream_probe(const void *src, size_t bytes, uint32_t grid, uint32_t thre
                                                                                                    : SVQ_ERR_HIP;
 }
 
-void svq_debug_streamk_wait_ticks(int64_t arrive_ticks, int64_t range_ticks) {
-    const auto clamp = [](int64_t v, uint32_t dflt) {
-        return v < 0 ? dflt : (uint32_t)std::min<int64_t>(v, INT32_MAX);
-    };
-    g_wait_arrive.store(clamp(arrive_ticks, kSkArriveWaitDefault), std::memory_order_relaxed);
-    g_wait_range.store(clamp(range_ticks, kSkRangeWaitDefault), std::memory_order_relaxed);
-}
 
 // ---- quantized vocabulary head -------------------------------------------------
 

@@ -59,19 +59,12 @@ hipError_t launch_ct_to_gptq(const int32_t *wp, const void *ws, int32_t *qw, voi
 // `grid` persistent workgroups; a workgroup touches at most `maxt` tiles.
 struct WidePlan {
     int bm, bn;
-    uint32_t wait_arrive, wait_range;  // stream-K wait budgets (s_memrealtime ticks)
     int row_tiles, col_tiles;
     int64_t units;
     int grid;
     int maxt;
-    size_t workspace_bytes;  // arrival counters + fp32 partials (0 if no tile is shared)
+    size_t workspace_bytes;  // counter region + fp32 partials (0 if no tile is shared)
 };
-
-// Stream-K wait budgets of the wide kernels: defaults 2000 ticks (20 us) for
-// the arrivals and 1000 (10 us) for the ranges; a test hook can change them.
-constexpr uint32_t kSkArriveWaitDefault = 2000;
-constexpr uint32_t kSkRangeWaitDefault = 1000;
-void streamk_wait_ticks(uint32_t &arrive, uint32_t &range);
 
 WidePlan plan_w4a16_wide(int64_t M, int64_t N, int64_t K, int num_cus);
 WidePlan plan_mxfp8_wide(int64_t M, int64_t N, int64_t K, int num_cus);
@@ -154,8 +147,6 @@ hipError_t launch_rtn_quantize(const void *w, int bits, int G, void *codes, void
 // callers reuse one workspace.
 constexpr size_t kCounterBytes = 256 * 1024;
 constexpr size_t kMaxCounters = kCounterBytes / 4;
-// counters a stream-K tile shared by several workgroups uses (wide kernels)
-constexpr size_t kSkCountersPerTile = 3;
 inline uint32_t *ws_counters(void *ws) { return (uint32_t *)ws; }
 inline void *ws_partials(void *ws) { return ws ? (void *)((char *)ws + kCounterBytes) : nullptr; }
 hipError_t launch_mxfp8_wide(const WidePlan &plan, const void *x, const uint8_t *w,

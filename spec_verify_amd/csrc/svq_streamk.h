@@ -1,22 +1,22 @@
 // Cross-workgroup reductions shared by the kernels that split work.
 //
-// Handoff without fences: an agent-scope release/acquire fence on gfx950 writes
-// back / invalidates the XCD-local L2 caches and costs tens of microseconds per
-// workgroup when hundreds of workgroups do it, so partials travel with
-// coherent ("sc1") stores and loads that bypass the non-coherent L2 state
-// instead. A contributor stores its partial coherently, waits until its stores
-// have completed (s_waitcnt), and only then bumps the arrival counter with an
-// agent-scope atomic; the workgroup that observes the final count reads the
-// other partials with coherent loads. Partials are added in a fixed order, so
-// results are deterministic, and the last arriver clears the counter.
+// Small-M kernels (a few K splits of a column block): handoff without fences.
+// An agent-scope release/acquire fence on gfx950 writes back / invalidates the
+// XCD-local L2 caches and costs tens of microseconds per workgroup when
+// hundreds of workgroups do it, so partials travel with agent-coherent atomic
+// stores and loads instead. A contributor stores its partial, waits until its
+// stores have completed (s_waitcnt), and only then bumps the arrival counter
+// with an agent-scope atomic; the workgroup that observes the final count reads
+// the other partials. Partials are added in a fixed order, so results are
+// deterministic, and the last arriver clears the counter.
+//
+// Wide kernels (M > 16): a second launch sums the partials (below).
 #pragma once
 
 #include "svq_device.h"
 #include "svq_launch.h"
 
 namespace svq {
-
-constexpr int kCoherent = 16;  // cache-policy bits of a buffer access: sc1
 
 // Wait until every outstanding memory access of this wave has completed.
 __device__ __forceinline__ void wait_all_memory() { __builtin_amdgcn_s_waitcnt(0); }
@@ -40,134 +40,67 @@ __device__ __forceinline__ int sk_first_tile(int w, int64_t units, int grid, int
     return (int)(((int64_t)w * units / grid) / KT);
 }
 
-// Finish of a tile shared by several workgroups. Counters of tile t (at
-// cnt[3t..3t+2]): arrivals, a bit mask of reduced chunk ranges, departures.
+// ---- split-K of the wide MFMA kernels: partials summed by a second launch ----
 //
-// Every contributor stores its partial tile (NV f32x4 per thread, NT threads;
-// slots laid out [workgroup][slot][NV][NT]) and arrives. The tile is reduced
-// per accumulator index v (all contributors added in workgroup order, so the
-// result does not depend on which workgroup reduces it). The contributors for
-// which this tile is the last piece of work (the "finishing group", known
-// from the schedule) split the NV indices into ranges, one each: a member
-// waits, for a bounded time, until every partial is in, reduces its range and
-// sets its bit. The last arriver reduces its own range if it has one, waits
-// (bounded) for the other bits, and reduces every range whose bit is still
-// missing, so the tile is complete whether or not the members were resident
-// at the same time; a range reduced twice is written twice with the same
-// values. The last contributor to depart clears the three counters.
-// The two wait budgets are kernel arguments (SkWait, in ticks of the 100 MHz
-// s_memrealtime clock); a budget of 0 makes every member give up at once, so
-// the owner reduces every range itself.
-struct SkWait {
-    uint32_t arrive_ticks, range_ticks;
-};
-constexpr int kSkMaxRanges = 32;               // one bit each
-
-// Spin (thread 0) until (*p & mask) == mask, or at least `want` for mask 0,
-// for at most `ticks`; returns whether it happened. A budget of 0 gives up at
-// once without looking.
-__device__ __forceinline__ bool sk_wait(uint32_t *p, uint32_t want, uint32_t mask, uint64_t ticks) {
-    if (ticks == 0) return false;
-    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-    for (;;) {
-        const uint32_t v = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (mask ? (v & mask) == mask : v >= want) return true;
-        if (__builtin_amdgcn_s_memrealtime() - t0 > ticks) return false;
-        __builtin_amdgcn_s_sleep(2);
-    }
+// A wide kernel's workgroup holds NV f32x4 accumulators per thread (NT threads)
+// for each output tile it works on: accumulator v of thread (wave, lane) holds
+// rows 16*(wr*MBW + v/CT) + 4*(lane/16) + i (i = 0..3) and column
+// 16*(wc*CT + v%CT) + lane%16 of the tile, where wave = wr*WC + wc. A tile that
+// one workgroup computes over all of K is written as bf16 by the wide kernel;
+// for a tile whose K steps are split over several workgroups, each writes its
+// fp32 partial with plain stores into its slot of the workspace
+// ([workgroup][slot][v][thread], slot = the tile's index among the workgroup's
+// tiles), and wide_sum_kernel, launched next on the same stream, adds the
+// partials in contributor (workgroup) order and writes bf16. The launch
+// boundary orders every partial's stores before its loads: nothing is
+// exchanged between workgroups of one launch, no coherent memory traffic or
+// arrival counter is needed, and no workgroup waits for another.
+template <int NV, int NT>
+__device__ __forceinline__ f32x4 *wide_partial(f32x4 *part, int wg, int maxt, int slot) {
+    return part + ((size_t)wg * maxt + slot) * NV * NT;
 }
 
-template <int NV, int NT, typename StoreV>
-__device__ __forceinline__ void sk_reduce(const f32x4 (&acc)[NV], int tile, int KT, int64_t units,
-                                          int grid, int maxt, uint32_t *cnt, f32x4 *part,
-                                          int *s_sk, SkWait wt, StoreV store_v) {
-    const int tid = threadIdx.x;
-    const int wg = blockIdx.x;
-    uint32_t *c = cnt + kSkCountersPerTile * tile;
-    const uint32_t slot_bytes = (uint32_t)NV * NT * 16;
-    const int slot = tile - sk_first_tile(wg, units, grid, KT);
-    const __amdgpu_buffer_rsrc_t mine = make_rsrc(part + (size_t)(wg * maxt + slot) * NV * NT, slot_bytes);
+// Workgroup (tile, v) of grid row_tiles * col_tiles * NV: accumulator v of
+// every thread, summed over the tile's contributors. The contributors' unit
+// ranges are consecutive and every one after the first starts inside the tile
+// (its partial is in its slot 0); only the first may have begun in an earlier
+// tile. Eight loads are kept in flight, none behind a branch.
+template <int MBW, int WR, int WC, int CT, int BM, int BN>
+__global__ __launch_bounds__(64 * WR * WC) void wide_sum_kernel(const f32x4 *__restrict__ part,
+                                                                uint16_t *__restrict__ out, int M, int N,
+                                                                int K, int col_tiles, int64_t units, int grid,
+                                                                int maxt) {
+    constexpr int NV = MBW * CT, NT = 64 * WR * WC;
+    const int tile = blockIdx.x / NV, v = blockIdx.x % NV;
+    const int KT = K >> 7;
+    const int64_t t0 = (int64_t)tile * KT;
+    const int fw = sk_owner(t0, units, grid), lw = sk_owner(t0 + KT - 1, units, grid);
+    if (fw == lw) return;  // one workgroup computed the whole tile
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wr = wave / WC, wc = wave % WC, r = lane & 15, g = lane >> 4;
+    const int slot_fw = tile - sk_first_tile(fw, units, grid, KT);
+    const size_t stride = (size_t)maxt * NV * NT;  // f32x4 per workgroup
+    const f32x4 *p0 = part + (size_t)v * NT + tid;
+    f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+    for (int w0 = fw; w0 <= lw; w0 += 8) {
+        f32x4 a[8];
 #pragma unroll
-    for (int v = 0; v < NV; ++v)
-        __builtin_amdgcn_raw_buffer_store_b128(acc[v], mine, (uint32_t)(v * NT + tid) * 16, 0, kCoherent);
-    const int64_t tend = (int64_t)tile * KT + KT;  // one past the tile's last unit
-    const int fw = __builtin_amdgcn_readfirstlane(sk_owner((int64_t)tile * KT, units, grid));
-    const int lw = __builtin_amdgcn_readfirstlane(sk_owner(tend - 1, units, grid));
-    const uint32_t nc = (uint32_t)(lw - fw + 1);
-    // finishing group: fw..lw-1 (their ranges end inside the tile) and lw if
-    // its range ends with the tile
-    const int nf0 = lw - fw + ((int64_t)(lw + 1) * units / grid <= tend ? 1 : 0);
-    const int nf = nf0 < kSkMaxRanges ? nf0 : kSkMaxRanges;
-    const int me = wg - fw;  // my range, if me < nf (the ranges cover all NV indices)
-    const uint32_t all = nf == 32 ? 0xffffffffu : ((1u << nf) - 1u);
-    wait_all_memory();
-    __syncthreads();
-    if (tid == 0) s_sk[0] = (int)arrive(&c[0]);
-    __syncthreads();
-    const bool owner = (uint32_t)__builtin_amdgcn_readfirstlane(s_sk[0]) == nc - 1;
-
-    auto view = [&](int w) {
-        const int wslot = __builtin_amdgcn_readfirstlane(tile - sk_first_tile(w, units, grid, KT));
-        return make_rsrc(part + (size_t)(w * maxt + wslot) * NV * NT, slot_bytes);
-    };
-    // reduce accumulator indices [v0, v1), two at a time with eight
-    // contributors' loads each in flight (every load is a round trip to the
-    // device-coherent level)
-    auto reduce = [&](int v0, int v1) {
-        for (int v = v0; v < v1; v += 2) {
-            const bool two = v + 1 < v1;
-            f32x4 sa = f32x4{0.f, 0.f, 0.f, 0.f}, sb = sa;
-            for (int w0 = fw; w0 <= lw; w0 += 8) {
-                f32x4 a[8], b[8];
-#pragma unroll
-                for (int k = 0; k < 8; ++k) {
-                    if (w0 + k > lw) continue;
-                    const __amdgpu_buffer_rsrc_t rs = view(w0 + k);
-                    a[k] = __builtin_amdgcn_raw_buffer_load_b128(rs, (uint32_t)(v * NT + tid) * 16, 0, kCoherent);
-                    if (two) b[k] = __builtin_amdgcn_raw_buffer_load_b128(rs, (uint32_t)((v + 1) * NT + tid) * 16, 0, kCoherent);
-                }
-#pragma unroll
-                for (int k = 0; k < 8; ++k) {
-                    if (w0 + k > lw) continue;
-                    sa += a[k];
-                    if (two) sb += b[k];
-                }
-            }
-            store_v(v, sa);
-            if (two) store_v(v + 1, sb);
+        for (int k = 0; k < 8; ++k) {
+            const int w = w0 + k < lw ? w0 + k : lw;
+            a[k] = p0[(size_t)w * stride + (w == fw ? (size_t)slot_fw * NV * NT : 0)];
         }
-    };
-    auto range_lo = [&](int e) { return e * NV / nf; };
-
-    bool mine_ready = owner;
-    if (!owner && me < nf) {
-        if (tid == 0) s_sk[1] = sk_wait(&c[0], nc, 0u, wt.arrive_ticks) ? 1 : 0;
-        __syncthreads();
-        mine_ready = __builtin_amdgcn_readfirstlane(s_sk[1]) != 0;
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            if (w0 + k <= lw) sum += a[k];
     }
-    if (mine_ready && me < nf) {
-        reduce(range_lo(me), range_lo(me + 1));
-        __syncthreads();
-        if (tid == 0) __hip_atomic_fetch_or(&c[1], 1u << me, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    if (owner) {
-        // the other members' ranges: wait a bounded time for their bits, then
-        // reduce whatever is still missing
-        if (tid == 0) {
-            sk_wait(&c[1], 0u, all, wt.range_ticks);
-            s_sk[2] = (int)__hip_atomic_load(&c[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-        __syncthreads();
-        const uint32_t done = (uint32_t)__builtin_amdgcn_readfirstlane(s_sk[2]);
-        for (int e = 0; e < nf; ++e)
-            if (!((done >> e) & 1u)) reduce(range_lo(e), range_lo(e + 1));
-    }
-    __syncthreads();
-    if (tid == 0 && arrive(&c[2]) == nc - 1) {
-        clear_counter(&c[0]);
-        clear_counter(&c[1]);
-        clear_counter(&c[2]);
-    }
+    const int rt = tile / col_tiles, cb = tile % col_tiles;
+    const int nbg = cb * (BN / 16) + wc * CT + v % CT;
+    if (nbg >= (N >> 4)) return;
+    const int colg = nbg * 16 + r;
+    const int rowb = rt * BM + (wr * MBW + v / CT) * 16 + 4 * g;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        if (rowb + i < M) out[(size_t)(rowb + i) * N + colg] = f32_to_bf16_rne(sum[i]);
 }
 
 

@@ -171,11 +171,15 @@ __global__ __launch_bounds__(64 * WAVES) void w4a16_skinny_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Wide kernel: any M (built for M = 128). Persistent stream-K: one workgroup
-// per compute unit, each taking an equal contiguous share of the (output tile,
-// 128-row K step) units. A tile computed by several workgroups is reduced by
-// the ones that finish it together (sk_reduce): fp32 partials added in
-// workgroup order, so the result is deterministic.
+// Wide kernel: any M (built for M = 128). Stream-K: the (output tile, 128-row
+// K step) units are split evenly over the workgroups (tile-aligned K ranges when
+// there are fewer tiles than CUs). A tile computed whole by one workgroup is
+// written as bf16; a shared tile's fp32 partials are plain-stored and summed in
+// workgroup order by a second launch (wide_sum_kernel), so the result is
+// deterministic and no workgroup waits for another. Measured on the MI355X at
+// M = 128 (K = 5120, N = 17408 / K = 17408, N = 5120): 45.0 / 46.0 us with the
+// partials reduced inside the kernel through coherent stores, arrival counters
+// and bounded waits, 41.5 / 39.6 us with the second launch.
 //
 // Workgroup: WR x WC waves (two per SIMD, so one wave's MFMAs cover the other's
 // VALU work), output tile BM x BN; a wave owns MBW 16-row blocks x CT 16-column
@@ -187,9 +191,10 @@ __global__ __launch_bounds__(64 * WAVES) void w4a16_skinny_kernel(
 // bank-conflict free), the BN/16 weight tiles, the fp16 scales, and
 // -136 * (group sums of x). Stages are filled by LDS-DMA (buffer loads that
 // write LDS directly; rows past M and columns past N read as zero), two steps
-// ahead; the group sums of step i+1 are computed during step i. Each slot is
-// its own LDS object, so the compiler can tell a DMA into one slot from reads
-// of another and does not wait for in-flight DMAs before every LDS read.
+// ahead; the group sums of step i+1 are computed during step i. The DMAs are
+// issued from inline asm and waited for explicitly (s_waitcnt vmcnt), because
+// the compiler cannot tell a DMA into one slot from reads of another and would
+// wait for every DMA in flight before each LDS read.
 //
 // MFMA step j of a K step covers rows 32j..32j+31; lane (r, g) supplies
 // K-rows 32j+8g.. of x row r and of column r, and its weight word is word g of
@@ -225,13 +230,11 @@ struct WideCfg {
 template <int MBW, int WR, int WC, int CT, int GSHIFT>
 __global__ __launch_bounds__(64 * WR * WC) void w4a16_wide_kernel(
     const uint16_t *__restrict__ x, const uint4 *__restrict__ wt,
-    const uint16_t *__restrict__ sc, uint16_t *__restrict__ out, uint32_t *__restrict__ cnt,
-    f32x4 *__restrict__ part, int M, int N, int K, int col_tiles, int64_t units, int grid,
-    int maxt, SkWait skw) {
+    const uint16_t *__restrict__ sc, uint16_t *__restrict__ out, f32x4 *__restrict__ part, int M,
+    int N, int K, int col_tiles, int64_t units, int grid, int maxt) {
     using C = WideCfg<MBW, WR, WC, CT, GSHIFT>;
     constexpr int BM = C::BM, BN = C::BN, NG = C::NG, SPG = C::SPG, NV = C::NV;
     __shared__ __attribute__((aligned(16))) uint8_t ring[3 * C::SLOT];
-    __shared__ int s_sk[3];
 
     const int lane = threadIdx.x & 63;
     const int wave = wave_id();
@@ -467,7 +470,10 @@ __global__ __launch_bounds__(64 * WR * WC) void w4a16_wide_kernel(
 #pragma unroll
             for (int v = 0; v < NV; ++v) store_v(v, acc[v]);
         } else {
-            sk_reduce<NV, C::NT>(acc, tile, KT, units, grid, maxt, cnt, part, s_sk, skw, store_v);
+            // a K range of a shared tile: the fp32 partial, summed by wide_sum_kernel
+            f32x4 *mp = wide_partial<NV, C::NT>(part, wg, maxt, tile - sk_first_tile(wg, units, grid, KT));
+#pragma unroll
+            for (int v = 0; v < NV; ++v) mp[v * C::NT + threadIdx.x] = acc[v];
         }
         u += n;
     }
@@ -552,12 +558,18 @@ hipError_t skinny_launch(const SmallPlan &p, const void *x, const int32_t *wt, c
 template <int MBW, int WR, int WC, int CT, int GS>
 hipError_t wide_launch(const WidePlan &p, const void *x, const int32_t *wt, const void *sc,
                        void *out, int64_t M, int64_t N, int64_t K, void *ws, hipStream_t stream) {
-    uint32_t *cnt = ws_counters(ws);
+    using C = WideCfg<MBW, WR, WC, CT, GS>;
     f32x4 *part = (f32x4 *)ws_partials(ws);
-    return launch_gemm(w4a16_wide_kernel<MBW, WR, WC, CT, GS>, dim3((uint32_t)p.grid),
-                       dim3(64 * WR * WC), 0, stream, (const uint16_t *)x, (const uint4 *)wt,
-                       (const uint16_t *)sc, (uint16_t *)out, cnt, part, (int)M, (int)N, (int)K,
-                       p.col_tiles, p.units, p.grid, p.maxt, SkWait{p.wait_arrive, p.wait_range});
+    hipError_t e = launch_gemm(w4a16_wide_kernel<MBW, WR, WC, CT, GS>, dim3((uint32_t)p.grid),
+                               dim3(C::NT), 0, stream, (const uint16_t *)x, (const uint4 *)wt,
+                               (const uint16_t *)sc, (uint16_t *)out, part, (int)M, (int)N, (int)K,
+                               p.col_tiles, p.units, p.grid, p.maxt);
+    if (e != hipSuccess || !p.workspace_bytes) return e;
+    // shared tiles: the partials' sum, one workgroup per (tile, accumulator)
+    return launch_gemm(wide_sum_kernel<MBW, WR, WC, CT, C::BM, C::BN>,
+                       dim3((uint32_t)((int64_t)p.row_tiles * p.col_tiles * C::NV)), dim3(C::NT), 0, stream,
+                       (const f32x4 *)part, (uint16_t *)out, (int)M, (int)N, (int)K, p.col_tiles, p.units,
+                       p.grid, p.maxt);
 }
 
 template <int GS>

@@ -251,11 +251,6 @@ def test_format_generic_queries_match_the_per_format_ones(L):
     assert L.svq_kernel_name(3, 17, 5120, 5120, 128) is None     # W8A16 takes M <= 16
 
 
-def test_streamk_wait_hook_is_callable_without_a_gpu(L):
-    L.svq_debug_streamk_wait_ticks(0, 0)
-    L.svq_debug_streamk_wait_ticks(-1, -1)
-
-
 def test_launch_geometry_and_stream_probe_validation(L):
     g, t, l = ctypes.c_uint64(), ctypes.c_uint32(), ctypes.c_size_t()
     ref = (ctypes.byref(g), ctypes.byref(t), ctypes.byref(l))

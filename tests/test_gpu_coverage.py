@@ -182,42 +182,28 @@ def test_w8a16_smallest_k(K, M, G):
     assert_gate(host_bits(out), *oracle.w8a16(inp.x, inp.w, inp.scales, G), f"w8a16 M{M} K{K} G{G}")
 
 
-# ---- the give-up path of the wide kernels' cross-workgroup reduction ------------------
+# ---- shared tiles of the wide kernels: partials summed by a second launch ------------
 
-# W4A16 shapes whose output tiles are shared by several workgroups: 2 tiles over
-# 20 K steps (10 contributors each), and one tile over 40 K steps (40
-# contributors: more than the 32 reduction ranges a tile is split into). (The
-# MXFP8 wide kernel sums shared tiles in a second launch instead; see below.)
-GIVEUP = [("w4a16", 128, 2560, 272, 128), ("w4a16", 64, 5120, 256, 32), ("w4a16", 100, 5120, 256, 128)]
+# W4A16 wide shapes (128 x 256 tiles) whose tiles are shared: 2 tiles over 20 K
+# steps; one tile over 40 K steps (40 contributors, summed in groups of 8) at
+# G = 32 and with a ragged last row tile; two row tiles with stream-K ranges that
+# cross tiles (more tiles than CUs: each workgroup holds partials of two tiles).
+W4_SHARED = [(128, 2560, 272, 128), (64, 5120, 256, 32), (100, 5120, 256, 128), (256, 640, 40960, 64)]
 
 
-@pytest.mark.parametrize("op,M,K,N,G", GIVEUP, ids=["-".join(map(str, c)) for c in GIVEUP])
-def test_wide_reduction_give_up_path(op, M, K, N, G):
-    """With both wait budgets at 0 every member of a shared tile gives up at once
-    and the last arriver reduces every range itself. The kernels still exit
-    normally, the output is bit-identical to the normal run, the arrival
-    counters are back at zero and the oracle gate holds."""
-    import spec_verify_amd as svq
-    _say("give-up", op, "M K N G", M, K, N, G)
-    p = W4(5500 + M + K, M, K, N, G) if op == "w4a16" else MX(5600 + M + K, M, K, N)
+@pytest.mark.parametrize("M,K,N,G", W4_SHARED, ids=["-".join(map(str, c)) for c in W4_SHARED])
+def test_w4a16_wide_shared_tiles_second_launch(M, K, N, G):
+    _say("w4a16 wide shared M K N G", M, K, N, G)
+    p = W4(5550 + M + K + N + G, M, K, N, G)
     nbytes = p.ws_bytes(3)
     assert nbytes > COUNTER_BYTES                # tiles are shared: partials exist
     ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
-    normal = p.run(3, workspace=ws)
+    outs = [p.run(3, workspace=ws) for _ in range(3)]
     torch.cuda.synchronize()
-    try:
-        svq.debug_streamk_wait_ticks(0, 0)
-        fallback = [p.run(3, workspace=ws) for _ in range(2)]
-        torch.cuda.synchronize()
-    finally:
-        svq.debug_streamk_wait_ticks(-1, -1)
-    for o in fallback:
-        assert torch.equal(o.view(torch.int16), normal.view(torch.int16))
+    for o in outs[1:]:
+        assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16))
     assert int(ws[:COUNTER_BYTES].count_nonzero()) == 0
-    assert_gate(host_bits(fallback[-1]), *p.ref(), f"give-up {op} M{M} K{K} N{N}")
-    again = p.run(3, workspace=ws)               # defaults restored: same bits
-    torch.cuda.synchronize()
-    assert torch.equal(again.view(torch.int16), normal.view(torch.int16))
+    assert_gate(host_bits(outs[0]), *p.ref(), f"w4a16 wide shared M{M} K{K} N{N}")
 
 
 # MXFP8 wide shapes whose tiles are shared: the partials are summed by a second

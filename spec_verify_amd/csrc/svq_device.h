@@ -167,6 +167,29 @@ __device__ __forceinline__ uint4 word_to_pairs(uint32_t w) {
     return make_uint4(a, b, c, d);
 }
 
+// The same four pairs as word_to_bf16x8, but holding (q - 8) * s: each weight
+// is q * s + m8s in fp32 (m8s = -8 s; one rounding), then rounded to bf16
+// (nearest even). The nibble masks are asm so that the byte conversions read
+// them in place (left to itself the compiler extracts every nibble first).
+__device__ __forceinline__ uint4 word_to_bf16x8_scaled(uint32_t w, float s, float m8s) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    uint32_t lo, hi;  // nibbles 0, 2, 4, 6 and 1, 3, 5, 7 of w, one per byte
+    asm("v_and_b32 %0, %2, %3\n\t"
+        "v_lshrrev_b32 %1, 4, %2\n\t"
+        "v_and_b32 %1, %1, %3"
+        : "=&v"(lo), "=&v"(hi)
+        : "v"(w), "s"(0x0F0F0F0Fu));
+    auto f = [&](uint32_t v, int byte) { return __builtin_fmaf((float)((v >> (8 * byte)) & 0xFFu), s, m8s); };
+    auto pk = [](float a, float b) {
+        const f32x2 v = {a, b};
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+    };
+    // pair i: nibble i (low half), nibble i + 4 (high half)
+    return make_uint4(pk(f(lo, 0), f(lo, 2)), pk(f(hi, 0), f(hi, 2)), pk(f(lo, 1), f(lo, 3)),
+                      pk(f(hi, 1), f(hi, 3)));
+}
+
 // E8M0 code -> fp32 scale 2^(b-127) (b = 0 gives the fp32 subnormal 2^-127).
 __device__ __forceinline__ float e8m0_to_f32(uint32_t b) {
     return bits_f32(b == 0 ? 0x00400000u : (b << 23));

@@ -188,10 +188,22 @@ __global__ __launch_bounds__(64 * WAVES) void w4a16_skinny_kernel(
 //
 // Pipeline: a ring of three LDS stages, each one K step: x (BM rows x 128,
 // 16-byte chunks XOR-swizzled by row so that the MFMA A reads are
-// bank-conflict free), the BN/16 weight tiles, the fp16 scales, and
+// bank-conflict free), the BN/16 weight tiles, the fp16 scales, and (G = 128)
 // -136 * (group sums of x). Stages are filled by LDS-DMA (buffer loads that
 // write LDS directly; rows past M and columns past N read as zero), two steps
-// ahead; the group sums of step i+1 are computed during step i. The DMAs are
+// ahead.
+//
+// Two ways to apply the scales, by group size. G = 128: the weight operand is
+// the exact bf16 of 128 + q, each group's MFMA chain starts from -136 * (sum of
+// x over the group), computed for step i+1 during step i from the staged x,
+// and the chain's result is scaled by one fp32 FMA per output: about one FMA
+// per MFMA. G = 32 and 64: that costs 2 or 4 FMAs per MFMA (one per output per
+// group), which the dequantization then has to fit beside; instead the weight
+// operand itself is (q - 8) * s, formed in fp32 (q * s - 8 s, one rounding) and
+// rounded to bf16, so the MFMAs accumulate straight across groups, with no
+// group sums and no FMAs (23 VALU ops per weight word, shared by the MBW row
+// blocks). The bf16 rounding of each dequantized weight (relative 2^-9, random
+// in sign) stays far inside the accuracy gate. The DMAs are
 // issued from inline asm and waited for explicitly (s_waitcnt vmcnt), because
 // the compiler cannot tell a DMA into one slot from reads of another and would
 // wait for every DMA in flight before each LDS read.
@@ -210,19 +222,21 @@ struct WideCfg {
     static constexpr int NG = 128 >> GSHIFT;
     static constexpr int SPG = 4 / NG;
     static constexpr int NV = MBW * CT;          // f32x4 accumulators per lane
-    // one LDS stage (slot): x, weight tiles, fp16 scales [NG][BN], -136 *
-    // group sums of x [NG][BM]
+    static constexpr bool PS = GSHIFT < 7;       // scales applied in the dequantization
+    // one LDS stage (slot): x, weight tiles, fp16 scales [NG][BN], and for
+    // G = 128 -136 * group sums of x [BM]
     static constexpr int XB = BM * 256;
     static constexpr int WB = (BN / 16) * 1024;
     static constexpr int SB = NG * BN * 2;
     static constexpr int OFF_W = XB, OFF_S = XB + WB, OFF_N = XB + WB + SB;
-    static constexpr int SLOT = OFF_N + NG * BM * 4;
+    static constexpr int SLOT = OFF_N + (PS ? 0 : BM * 4);
     static constexpr int XI = BM / 4 / WAVES;    // x DMAs per wave per stage (1 KiB = 4 rows each)
     static constexpr int WI = BN / 16 / WAVES;   // weight DMAs per wave per stage (one tile each)
     static constexpr int SI = NG * BN / 128;     // scale DMAs per stage (128 fp16 each), waves 0..SI-1
+    static constexpr int MAXPS = XI + WI + 1;    // most DMAs one wave issues per stage
     static_assert(XI * 4 * WAVES == BM && WI * 16 * WAVES == BN, "stage split over the waves");
     static_assert(SI <= WAVES, "one scale DMA per wave at most");
-    static_assert(BM == 16 * WAVES, "each wave sums x over 16 rows");
+    static_assert(PS || BM == 16 * WAVES, "each wave sums x over 16 rows");
     static_assert(SLOT % 16 == 0 && SLOT < 65536, "slot offsets fit a ds immediate");
     static_assert(MBW % 2 == 0, "row blocks go in pairs");
 };
@@ -258,7 +272,10 @@ __global__ __launch_bounds__(64 * WR * WC) void w4a16_wide_kernel(
     const uint32_t offW = C::OFF_W + wc * CT * 1024 + (r << 4) + (g << 2);  // word g of lane 16j+r
     const uint32_t offS = C::OFF_S + (wc * CT * 16 + r) * 2;
     const uint32_t offN = C::OFF_N + 16 * g;
-    const int srow = 16 * wave + (lane >> 2), q4 = lane & 3;  // group-sum rows of this wave
+    // this wave's DMAs per stage: x, a scale row, weights
+    const int per_step = C::XI + (wave < C::SI ? 1 : 0) + C::WI;
+    // group sums (G = 128): rows and K quarters of this wave, and their LDS offsets
+    const int srow = 16 * wave + (lane >> 2), q4 = lane & 3;
     uint32_t offX[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) offX[c] = srow * 256 + (((4 * q4 + c) ^ (srow & 15)) << 4);
@@ -281,7 +298,7 @@ __global__ __launch_bounds__(64 * WR * WC) void w4a16_wide_kernel(
         return g;
     };
     // DMA of K step kt of segment g into slot st: x, then scales, then
-    // weights (the order the waits below rely on)
+    // weights (the order the G = 128 waits below rely on)
     auto issue = [&](const Seg &sg, int st, int kt) {
         const uint32_t base = ring_lds + st * C::SLOT;
 #pragma unroll
@@ -308,8 +325,9 @@ __global__ __launch_bounds__(64 * WR * WC) void w4a16_wide_kernel(
         const Seg sg = seg_at(u);
         const int tile = sg.tile, s0 = sg.s0, n = sg.n, rt = sg.rt, cb = sg.cb;
         const int s1 = s0 + n;
-        // -136 * (sum of x over each group) for rows 16*wave.. of slot st
+        // G = 128: -136 * (sum of x over the group) for rows 16*wave.. of slot st
         auto sums = [&](int st) {
+            static_assert(C::PS || NG == 1, "the sums cover one group per step");
             const lds_u8 *b = lds_opaque(ring_lds + st * C::SLOT);
             float t = 0.f;
 #pragma unroll
@@ -320,21 +338,13 @@ __global__ __launch_bounds__(64 * WR * WC) void w4a16_wide_kernel(
                 t = dot2_bf16(v.z, kBf16OnePair, t);
                 t = dot2_bf16(v.w, kBf16OnePair, t);
             }
+            // the four K quarters of a row sit in adjacent lanes: quad DPP sums
+            t += bits_f32(__builtin_amdgcn_mov_dpp(f32_bits(t), 0xB1, 0xF, 0xF, true));  // quad_perm [1,0,3,2]
+            t += bits_f32(__builtin_amdgcn_mov_dpp(f32_bits(t), 0x4E, 0xF, 0xF, true));  // quad_perm [2,3,0,1]
             __attribute__((address_space(3))) float *xn =
                 (__attribute__((address_space(3))) float *)(b + offNw);
-            // the four K quarters of a row sit in adjacent lanes: quad DPP sums
-            if constexpr (NG == 4) {
-                xn[q4 * BM] = -136.f * t;
-            } else if constexpr (NG == 2) {
-                t += bits_f32(__builtin_amdgcn_mov_dpp(f32_bits(t), 0xB1, 0xF, 0xF, true));  // quad_perm [1,0,3,2]
-                if ((q4 & 1) == 0) xn[(q4 >> 1) * BM] = -136.f * t;
-            } else {
-                t += bits_f32(__builtin_amdgcn_mov_dpp(f32_bits(t), 0xB1, 0xF, 0xF, true));  // quad_perm [1,0,3,2]
-                t += bits_f32(__builtin_amdgcn_mov_dpp(f32_bits(t), 0x4E, 0xF, 0xF, true));  // quad_perm [2,3,0,1]
-                if (q4 == 0) xn[0] = -136.f * t;
-            }
+            if (q4 == 0) xn[0] = -136.f * t;
         };
-
         f32x4 acc[NV];
 #pragma unroll
         for (int v = 0; v < NV; ++v) acc[v] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -353,7 +363,15 @@ __global__ __launch_bounds__(64 * WR * WC) void w4a16_wide_kernel(
 #pragma unroll
                 for (int q = 0; q < NG; ++q) sfa[q][ct] = fp16_bits_to_f32(lds_ld<uint16_t>(b + offS + (q * BN + ct * 16) * 2));
 #pragma unroll
-                for (int j = 0; j < 4; ++j) B[j][ct] = word_to_bf16x8(lds_ld<uint32_t>(b + offW + ct * 1024 + j * 256));
+                for (int j = 0; j < 4; ++j) {
+                    const uint32_t w = lds_ld<uint32_t>(b + offW + ct * 1024 + j * 256);
+                    if constexpr (C::PS) {
+                        const float s = sfa[j / SPG][ct];
+                        B[j][ct] = word_to_bf16x8_scaled(w, s, -8.f * s);
+                    } else {
+                        B[j][ct] = word_to_bf16x8(w);
+                    }
+                }
             }
         };
         auto compute = [&](int st, auto H) {
@@ -367,6 +385,32 @@ __global__ __launch_bounds__(64 * WR * WC) void w4a16_wide_kernel(
                 if ((i0 + NP <= half * NI / 2) || (i0 >= (half + 1) * NI / 2)) continue;
                 const int pa = (i0 < half * NI / 2 ? half * NI / 2 - i0 : 0);
                 const int pe = (i0 + NP > (half + 1) * NI / 2 ? (half + 1) * NI / 2 - i0 : NP);
+                if constexpr (C::PS) {
+                    // scaled weights: the MFMAs accumulate into acc directly
+                    uint4 A[2][2][SPG];
+                    auto load_a = [&](int p, uint4 (&Ap)[2][SPG]) {
+#pragma unroll
+                        for (int h = 0; h < 2; ++h)
+#pragma unroll
+                            for (int jj = 0; jj < SPG; ++jj)
+                                Ap[h][jj] = lds_ld16(b + offA[q * SPG + jj] + (wr * MBW + 2 * p + h) * 4096);
+                    };
+                    load_a(pa, A[pa & 1]);
+#pragma unroll
+                    for (int p = 0; p < NP; ++p) {
+                        if (p < pa || p >= pe) continue;
+                        if (p + 1 < pe) load_a(p + 1, A[(p + 1) & 1]);
+#pragma unroll
+                        for (int jj = 0; jj < SPG; ++jj)
+#pragma unroll
+                            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                                for (int ct = 0; ct < CT; ++ct)
+                                    acc[(2 * p + h) * CT + ct] = mfma16x16x32(A[p & 1][h][jj], B[q * SPG + jj][ct],
+                                                                              acc[(2 * p + h) * CT + ct]);
+                    }
+                    continue;
+                }
                 const float (&sf)[CT] = sfa[q];
                 // Row blocks go in pairs (2*CT independent MFMA chains); the
                 // next pair's A operands are read while this pair's MFMAs run,
@@ -421,22 +465,31 @@ __global__ __launch_bounds__(64 * WR * WC) void w4a16_wide_kernel(
             issue(sg, slot0, s0);
             if (n > 1) issue(sg, slot1, s0 + 1);
         }
-        // stage 0 has landed (at most stage 1's DMAs are outstanding)
-        if (n > 1) wait_vmcnt_at_most<C::XI + 1 + C::WI>(C::XI + (wave < C::SI ? 1 : 0) + C::WI);
-        else wait_vmcnt<0>();
-        lds_barrier();
-        sums(slot0);
+        if constexpr (!C::PS) {
+            // stage 0 has landed (at most stage 1's DMAs are outstanding)
+            if (n > 1) wait_vmcnt_at_most<C::MAXPS>(per_step);
+            else wait_vmcnt<0>();
+            lds_barrier();
+            sums(slot0);
+        }
         int st = slot0;
         for (int i = 0; i < n; ++i, st = (st == 2 ? 0 : st + 1)) {
-            // this wave's DMAs: all but the weights of step i+1 have landed
-            if (i + 1 < n) wait_vmcnt<C::WI>();
-            else wait_vmcnt<0>();
-            lds_barrier();  // every wave's slot st and x of slot st+1 are in; slot st+2 is free
+            if constexpr (C::PS) {
+                // this wave's stage of step i has landed (only step i+1's may be outstanding)
+                if (i + 1 < n) wait_vmcnt_at_most<C::MAXPS>(per_step);
+                else wait_vmcnt<0>();
+            } else {
+                // all but the weights of step i+1 have landed: its x is summed below
+                if (i + 1 < n) wait_vmcnt<C::WI>();
+                else wait_vmcnt<0>();
+            }
+            lds_barrier();  // every wave's slot st (and x of slot st+1) is in; slot st+2 is free
             const int st1 = st == 2 ? 0 : st + 1, st2 = st1 == 2 ? 0 : st1 + 1;
             prep(st);
             compute(st, std::integral_constant<int, 0>{});
             if (i + 2 < n) issue(sg, st2, s0 + i + 2);
-            if (i + 1 < n) sums(st1);
+            if constexpr (!C::PS)
+                if (i + 1 < n) sums(st1);
             if (i + 1 == n && u + n < u_end) {
                 // the next segment's first two stages go into the two slots
                 // this step does not use

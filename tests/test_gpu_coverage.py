@@ -235,25 +235,26 @@ PATTERN = 0xA5
 
 # one launch per kernel family that reduces through the workspace
 GUARDED = [
-    ("w4a16", 1, 1, 5120, 512),     # dot2 with K split across workgroups
-    ("w4a16", 2, 5, 5120, 512),     # skinny, split K
-    ("w4a16", 3, 128, 2560, 272),   # wide, shared tiles
-    ("mxfp8", 1, 1, 5120, 512),
-    ("mxfp8", 2, 5, 5120, 512),
-    ("mxfp8", 3, 128, 2560, 272),
-    ("w8a16", 0, 3, 5120, 512),
+    ("w4a16", 1, 1, 5120, 512, 128),     # dot2 with K split across workgroups
+    ("w4a16", 2, 5, 5120, 512, 128),     # skinny, split K
+    ("w4a16", 3, 128, 2560, 272, 128),   # wide, shared tiles
+    ("w4a16", 3, 128, 2560, 272, 32),    # wide, shared tiles, scales in the dequantization
+    ("mxfp8", 1, 1, 5120, 512, 32),
+    ("mxfp8", 2, 5, 5120, 512, 32),
+    ("mxfp8", 3, 128, 2560, 272, 32),
+    ("w8a16", 0, 3, 5120, 512, 128),
 ]
 
 
-@pytest.mark.parametrize("op,kernel,M,K,N", GUARDED, ids=["-".join(map(str, c)) for c in GUARDED])
-def test_workspace_and_output_guards(op, kernel, M, K, N):
+@pytest.mark.parametrize("op,kernel,M,K,N,G", GUARDED, ids=["-".join(map(str, c)) for c in GUARDED])
+def test_workspace_and_output_guards(op, kernel, M, K, N, G):
     """The kernels write only inside [workspace, workspace + bytes) and inside
     the output: guard bytes before and after both are untouched after three
     launches, the counters are back at zero and the result passes the gate."""
     import spec_verify_amd as svq
-    _say("guards", op, kernel, "M K N", M, K, N)
+    _say("guards", op, kernel, "M K N G", M, K, N, G)
     if op == "w4a16":
-        p = W4(5700 + M, M, K, N, 128)
+        p = W4(5700 + M + G, M, K, N, G)
         nbytes = p.ws_bytes(kernel)
         run = lambda out, ws: p.run(kernel, out=out, workspace=ws)
         ref = p.ref
@@ -263,11 +264,11 @@ def test_workspace_and_output_guards(op, kernel, M, K, N):
         run = lambda out, ws: p.run(kernel, out=out, workspace=ws)
         ref = p.ref
     else:
-        inp = synth.gen_w8a16(5900 + M, M, K, N, 128)
+        inp = synth.gen_w8a16(5900 + M, M, K, N, G)
         x, w, s = dev(inp.x), dev(inp.w), dev(inp.scales)
         nbytes = svq.w8a16_workspace_bytes(M, N, K)
-        run = lambda out, ws: svq.w8a16_gemm(x, w, s, 128, out=out, workspace=ws)
-        ref = lambda: oracle.w8a16(inp.x, inp.w, inp.scales, 128)
+        run = lambda out, ws: svq.w8a16_gemm(x, w, s, G, out=out, workspace=ws)
+        ref = lambda: oracle.w8a16(inp.x, inp.w, inp.scales, G)
     assert nbytes > COUNTER_BYTES                # this launch splits work across workgroups
     wbuf = torch.full((nbytes + 2 * GUARD,), PATTERN, dtype=torch.uint8, device="cuda")
     wbuf[GUARD:GUARD + nbytes].zero_()

@@ -60,49 +60,88 @@ __device__ __forceinline__ f32x4 *wide_partial(f32x4 *part, int wg, int maxt, in
     return part + ((size_t)wg * maxt + slot) * NV * NT;
 }
 
-// Workgroup (tile, v) of grid row_tiles * col_tiles * NV: accumulator v of
-// every thread, summed over the tile's contributors. The contributors' unit
-// ranges are consecutive and every one after the first starts inside the tile
-// (its partial is in its slot 0); only the first may have begun in an earlier
-// tile. Eight loads are kept in flight, none behind a branch.
+// Workgroup (tile, pair) of grid row_tiles * col_tiles * NV / 2: accumulators
+// 2*pair and 2*pair + 1 of every thread, summed over the tile's contributors.
+// The contributors' unit ranges are consecutive and every one after the first
+// starts inside the tile (its partial is in its slot 0); only the first may
+// have begun in an earlier tile. Two to four contributors (the usual split)
+// take one pass with exactly their loads in flight; more go eight at a time,
+// with the loads past the last one clamped to it (no load behind a branch).
+template <int NV, int NT>
+struct WideSum {
+    const f32x4 *p;  // part + thread
+    size_t stride;   // f32x4 per workgroup
+    int fw, slot_fw, v0;
+    __device__ __forceinline__ const f32x4 *at(int w, int j) const {
+        return p + (size_t)w * stride + (w == fw ? (size_t)slot_fw * NV * NT : 0) + (size_t)(v0 + j) * NT;
+    }
+    // contributors fw + k for k < C (C known), added in order into s
+    template <int C>
+    __device__ __forceinline__ void add(int w0, f32x4 (&s)[2]) const {
+        f32x4 a[C][2];
+#pragma unroll
+        for (int k = 0; k < C; ++k)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) a[k][j] = *at(w0 + k, j);
+#pragma unroll
+        for (int k = 0; k < C; ++k)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) s[j] += a[k][j];
+    }
+};
+
 template <int MBW, int WR, int WC, int CT, int BM, int BN>
 __global__ __launch_bounds__(64 * WR * WC) void wide_sum_kernel(const f32x4 *__restrict__ part,
                                                                 uint16_t *__restrict__ out, int M, int N,
                                                                 int K, int col_tiles, int64_t units, int grid,
                                                                 int maxt) {
     constexpr int NV = MBW * CT, NT = 64 * WR * WC;
-    const int tile = blockIdx.x / NV, v = blockIdx.x % NV;
+    static_assert(NV % 2 == 0, "accumulators go in pairs");
+    const int tile = blockIdx.x / (NV / 2), v0 = 2 * (blockIdx.x % (NV / 2));
     const int KT = K >> 7;
     const int64_t t0 = (int64_t)tile * KT;
     const int fw = sk_owner(t0, units, grid), lw = sk_owner(t0 + KT - 1, units, grid);
     if (fw == lw) return;  // one workgroup computed the whole tile
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wr = wave / WC, wc = wave % WC, r = lane & 15, g = lane >> 4;
-    const int slot_fw = tile - sk_first_tile(fw, units, grid, KT);
-    const size_t stride = (size_t)maxt * NV * NT;  // f32x4 per workgroup
-    const f32x4 *p0 = part + (size_t)v * NT + tid;
-    f32x4 sum = {0.f, 0.f, 0.f, 0.f};
-    for (int w0 = fw; w0 <= lw; w0 += 8) {
-        f32x4 a[8];
+    const WideSum<NV, NT> ws{part + tid, (size_t)maxt * NV * NT, fw, tile - sk_first_tile(fw, units, grid, KT), v0};
+    f32x4 sum[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    const int nc = lw - fw + 1;
+    if (nc == 2) {
+        ws.template add<2>(fw, sum);
+    } else if (nc == 3) {
+        ws.template add<3>(fw, sum);
+    } else if (nc == 4) {
+        ws.template add<4>(fw, sum);
+    } else {
+        for (int w0 = fw; w0 <= lw; w0 += 8) {
+            f32x4 a[8][2];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const int w = w0 + k < lw ? w0 + k : lw;
-            a[k] = p0[(size_t)w * stride + (w == fw ? (size_t)slot_fw * NV * NT : 0)];
+            for (int k = 0; k < 8; ++k) {
+                const int w = w0 + k < lw ? w0 + k : lw;
+#pragma unroll
+                for (int j = 0; j < 2; ++j) a[k][j] = *ws.at(w, j);
+            }
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+                if (w0 + k <= lw)
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) sum[j] += a[k][j];
         }
-#pragma unroll
-        for (int k = 0; k < 8; ++k)
-            if (w0 + k <= lw) sum += a[k];
     }
     const int rt = tile / col_tiles, cb = tile % col_tiles;
-    const int nbg = cb * (BN / 16) + wc * CT + v % CT;
-    if (nbg >= (N >> 4)) return;
-    const int colg = nbg * 16 + r;
-    const int rowb = rt * BM + (wr * MBW + v / CT) * 16 + 4 * g;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-        if (rowb + i < M) out[(size_t)(rowb + i) * N + colg] = f32_to_bf16_rne(sum[i]);
+    for (int j = 0; j < 2; ++j) {
+        const int v = v0 + j;
+        const int nbg = cb * (BN / 16) + wc * CT + v % CT;
+        if (nbg >= (N >> 4)) continue;
+        const int colg = nbg * 16 + r;
+        const int rowb = rt * BM + (wr * MBW + v / CT) * 16 + 4 * g;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (rowb + i < M) out[(size_t)(rowb + i) * N + colg] = f32_to_bf16_rne(sum[j][i]);
+    }
 }
-
 
 // Split-K finish of the small-M kernels. Workgroup (nb, sp) of `splits` holds,
 // in threads t < 16*M, the partial sum v of output (m = t/16, column 16*nb +

@@ -618,9 +618,9 @@ hipError_t wide_launch(const WidePlan &p, const void *x, const int32_t *wt, cons
                                (const uint16_t *)sc, (uint16_t *)out, part, (int)M, (int)N, (int)K,
                                p.col_tiles, p.units, p.grid, p.maxt);
     if (e != hipSuccess || !p.workspace_bytes) return e;
-    // shared tiles: the partials' sum, one workgroup per (tile, accumulator)
+    // shared tiles: the partials' sum, one workgroup per (tile, accumulator pair)
     return launch_gemm(wide_sum_kernel<MBW, WR, WC, CT, C::BM, C::BN>,
-                       dim3((uint32_t)((int64_t)p.row_tiles * p.col_tiles * C::NV)), dim3(C::NT), 0, stream,
+                       dim3((uint32_t)((int64_t)p.row_tiles * p.col_tiles * C::NV / 2)), dim3(C::NT), 0, stream,
                        (const f32x4 *)part, (uint16_t *)out, (int)M, (int)N, (int)K, p.col_tiles, p.units,
                        p.grid, p.maxt);
 }

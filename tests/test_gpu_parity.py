@@ -284,6 +284,41 @@ def test_mxfp8_hardware_decode_all_codes(kernel, scale_code):
     assert np.all((out[0][zero] & 0x7FFF) == 0)
 
 
+TINY_CASES = [(1, 1, 144), (1, 4, 144), (2, 5, 144), (2, 16, 144), (3, 128, 272)]
+
+
+@pytest.mark.parametrize("kernel,M,N", TINY_CASES, ids=_ids(TINY_CASES))
+@pytest.mark.parametrize("codes", [(0,), (1,), (2,), (0, 1, 2, 3, 120, 127)], ids=["b0", "b1", "b2", "mixed"])
+def test_mxfp8_tiny_scales_random(kernel, M, N, codes):
+    """E8M0 codes b <= 2 put E4M3 * 2^(b-127) (a multiple of 2^(b-136)) below
+    2^-126, where the bf16 operand the kernels build has subnormal spacing
+    2^-133: such an element moves by up to 2^-134 (code 0x05 at b = 0, 5 * 2^-136,
+    becomes 2^-133); at b >= 3 every element is exact. Random x, every finite
+    E4M3 code, scales drawn from `codes` per block: the result passes the gate,
+    and every output lies within the bound that follows from that operand
+    rounding, fp32 accumulation and the bf16 output rounding."""
+    _say("mxfp8 tiny scales kernel", kernel, "M N", M, N, "codes", codes)
+    K = 1280
+    rng = np.random.default_rng(4100 + 7 * kernel + M + len(codes) + codes[0])
+    x = synth.bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
+    w = rng.integers(0, 256, size=(N, K), dtype=np.uint8)
+    w[(w & 0x7F) == 0x7F] = 0x3F                  # NaN codes are not inputs
+    sc = rng.choice(np.array(codes, dtype=np.uint8), size=(N, K // 32))
+    inp = synth.MXFP8Inputs(M, K, N, x, w, sc)
+    out = run_mxfp8(inp, kernel)
+    y64, y32 = oracle.mxfp8(inp.x, inp.w, inp.scales)
+    assert_gate(out, y64, y32, f"mxfp8 tiny scales {codes} kernel {kernel} M{M}")
+    xs = np.abs(oracle.bf16_bits_to_f64(x))                              # [M, K]
+    table = oracle.e4m3_table()
+    wv = table[w] * np.vectorize(oracle.e8m0_to_f64)(np.repeat(sc, 32, axis=1))  # [N, K] exact
+    tiny = np.repeat(sc <= 2, 32, axis=1)
+    e_op = 2.0 ** -134 * (xs @ tiny.T.astype(np.float64))                # operand rounding
+    e_acc = K * 2.0 ** -24 / (1 - K * 2.0 ** -24) * (xs @ np.abs(wv).T) + K * 2.0 ** -150
+    bound = e_op + e_acc + (np.abs(y64) + e_op + e_acc) * 2.0 ** -8 + 2.0 ** -134
+    err = np.abs(oracle.bf16_bits_to_f64(out) - y64)
+    assert np.all(err <= bound), f"worst excess {np.max(err - bound):.3g} at {np.unravel_index(np.argmax(err - bound), err.shape)}"
+
+
 @pytest.mark.parametrize("name", ["mxfp8_m1", "mxfp8_m5", "mxfp8_m128"])
 def test_mxfp8_workloads(name):
     w = synth.WORKLOADS[name]

@@ -283,6 +283,33 @@ def chip_stream(torch, svq, cus):
             "hbm_frac": round(best["GBps"] / HBM_PEAK_GBS, 4), "shapes": res}
 
 
+# ---- matrix-core probe ------------------------------------------------------------------
+
+def mfma_floor(torch, svq, w, geometry):
+    """MFMA-issue floor of a batched workload: the matrix-core probe in the GEMM's own
+    launch shape, with the workload's MFMA count (rows padded to the 16 of one MFMA)
+    spread evenly over its waves."""
+    grid, threads, _ = geometry
+    total = -(-w["M"] // 16) * (w["N"] // 16) * (w["K"] // 32)
+    waves = grid * (threads // 64)
+    per_wave = -(-total // waves)
+    per_wave = -(-per_wave // 8) * 8
+    sink = torch.zeros(max(grid, 1), dtype=torch.float32, device="cuda:0")
+    us = med(time_trials(torch, lambda i: svq.mfma_probe(grid, threads, per_wave, sink), MIN_LAUNCHES))
+    tfl = per_wave * waves * 16 * 16 * 32 * 2 / (us * 1e-6) / 1e12
+    return {"shape": [grid, threads], "mfma_per_wave": per_wave, "us": round(us, 3), "TFLOPs": round(tfl, 1)}
+
+
+def chip_mfma(torch, svq, cus):
+    """The chip's sustained bf16 MFMA rate: the probe with two 8-wave workgroups per CU."""
+    grid, threads, per_wave = 2 * cus, 512, 4096
+    sink = torch.zeros(grid, dtype=torch.float32, device="cuda:0")
+    us = med(time_trials(torch, lambda i: svq.mfma_probe(grid, threads, per_wave, sink), 50))
+    tfl = grid * 8 * per_wave * 16 * 16 * 32 * 2 / (us * 1e-6) / 1e12
+    return {"shape": [grid, threads], "mfma_per_wave": per_wave, "us": round(us, 2), "TFLOPs": round(tfl, 1),
+            "mfma_frac": round(tfl / MFMA_BF16_PEAK_TFLOPS, 4)}
+
+
 # ---- run record -----------------------------------------------------------------------------
 
 def _read(path):
@@ -425,15 +452,22 @@ def workload_table(torch, svq, oracle, names, cus, probe=True):
         del p
         torch.cuda.empty_cache()
         if probe:
-            pr = probe_workload(torch, svq, _ProbeView(w), cus)
+            view = _ProbeView(w)
+            pr = probe_workload(torch, svq, view, cus)
             pr["frac_same"] = round(pr["same_us"] / us, 4)
             pr["frac_best"] = round(pr["best_us"] / us, 4)
             row["probe"] = pr
+            if w["M"] > 16:
+                mf = mfma_floor(torch, svq, w, view.geometry)
+                mf["frac"] = round(mf["us"] / us, 4)
+                row["mfma_probe"] = mf
         detail.append(row)
         pr = row.get("probe", {})
+        mf = row.get("mfma_probe")
         log(f"{n:17s} {row['kernel']:22s} {us:8.2f} {gbs:8.1f} {100 * gbs / HBM_PEAK_GBS:6.1f} "
             f"{pr.get('same_us', 0):7.2f} {100 * pr.get('frac_same', 0):7.1f} {pr.get('best_us', 0):7.2f} "
-            f"{100 * pr.get('frac_best', 0):6.1f} {tfl:8.2f} {100 * tfl / MFMA_BF16_PEAK_TFLOPS:6.2f}")
+            f"{100 * pr.get('frac_best', 0):6.1f} {tfl:8.2f} {100 * tfl / MFMA_BF16_PEAK_TFLOPS:6.2f}"
+            + (f"   MFMA probe {mf['us']:.2f} µs ({100 * mf['frac']:.1f}%)" if mf else ""))
         torch.cuda.empty_cache()
     return detail
 
@@ -729,6 +763,9 @@ def main():
             chip = chip_stream(torch, svq, cus)
             log(f"chip stream probe, 1 GiB: best {chip['best_GBps']} GB/s ({100 * chip['hbm_frac']:.1f}% of "
                 f"8 TB/s) in {chip['best_shape']}")
+            chip["mfma"] = chip_mfma(torch, svq, cus)
+            log(f"chip MFMA probe, bf16 16x16x32: {chip['mfma']['TFLOPs']} TFLOP/s "
+                f"({100 * chip['mfma']['mfma_frac']:.1f}% of 2.5 PFLOP/s) in {chip['mfma']['shape']}")
         detail = workload_table(torch, svq, oracle, TABLE, cus, probe=not args.no_probe)
 
     quant = None

@@ -366,6 +366,18 @@ int svq_launch_geometry(int op, int kernel, int64_t M, int64_t N, int64_t K, int
 int svq_stream_probe(const void *src, size_t bytes, uint32_t grid, uint32_t threads, uint32_t *sink,
                      void *stream);
 
+/*
+ * Matrix-core probe: every wave of `grid` workgroups of `threads` threads (a
+ * multiple of 64, at most 1024) issues `per_wave` bf16 16x16x32 MFMAs (a
+ * non-zero multiple of 8, at most 2^24) as eight independent chains on
+ * register operands, with no memory traffic: the floor that MFMA issue sets
+ * for a kernel doing that many MFMAs per wave in that launch shape (the
+ * compute-bound batched-verify case of the autobench page "Qwen3.8-27B · vLLM ·
+ * FP8 + MTP"). sink (grid floats, 4-byte aligned) may be written with
+ * data-dependent values; nothing else is.
+ */
+int svq_mfma_probe(uint32_t grid, uint32_t threads, uint32_t per_wave, float *sink, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

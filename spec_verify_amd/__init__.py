@@ -39,7 +39,7 @@ EXPORTED_SYMBOLS = (
     "svq_mxfp8_gemm_with", "svq_mxfp8_kernel_name", "svq_rtn_quantize",
     "svq_w8a16_workspace_bytes", "svq_w8a16_gemm", "svq_w8a16_kernel_name",
     "svq_fuse_projections", "svq_ct_to_gptq", "svq_mxfp8_quantize", "svq_workspace_bytes",
-    "svq_kernel_name", "svq_launch_geometry", "svq_stream_probe",
+    "svq_kernel_name", "svq_launch_geometry", "svq_stream_probe", "svq_mfma_probe",
     "svq_w4a16_gemm_noalloc",
 )
 
@@ -118,6 +118,8 @@ def lib():
                                           ctypes.POINTER(_sz)]
         L.svq_stream_probe.restype = ctypes.c_int
         L.svq_stream_probe.argtypes = [_p, _sz, ctypes.c_uint32, ctypes.c_uint32, _p, _p]
+        L.svq_mfma_probe.restype = ctypes.c_int
+        L.svq_mfma_probe.argtypes = [ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32, _p, _p]
         L.svq_w4a16_gemm_noalloc.restype = ctypes.c_int
         L.svq_w4a16_gemm_noalloc.argtypes = [_p, _p, _p, _p, _i64, _i64, _i64, _i32, _p]
         _lib = L
@@ -241,6 +243,15 @@ def stream_probe(src, nbytes, grid, threads, sink):
         raise ValueError("src or sink too small")
     _check(lib().svq_stream_probe(_dev_ptr(src, "src"), nbytes, grid, threads, _dev_ptr(sink, "sink"),
                                   _stream_ptr(src)), "svq_stream_probe")
+
+
+def mfma_probe(grid, threads, per_wave, sink):
+    """per_wave bf16 16x16x32 MFMAs per wave of (grid, threads), no memory
+    traffic; sink is a device tensor of at least grid floats."""
+    if sink.numel() * sink.element_size() < 4 * grid:
+        raise ValueError("sink too small")
+    _check(lib().svq_mfma_probe(grid, threads, per_wave, _dev_ptr(sink, "sink"), _stream_ptr(sink)),
+           "svq_mfma_probe")
 
 
 def q4_repack(qweight, out=None):

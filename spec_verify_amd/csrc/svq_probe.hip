@@ -1,3 +1,5 @@
+// Probes: ceilings for the GEMM kernels, measured on this chip.
+//
 // Streaming probe: a read-only kernel that moves a buffer's bytes from HBM to
 // the compute units and does nothing else. It measures the bandwidth a plain
 // read of a given number of bytes reaches on this chip in a given launch shape,
@@ -30,6 +32,39 @@ __global__ __launch_bounds__(1024) void stream_probe_kernel(const uint4 *__restr
         for (int u = 0; u < U; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
     }
     if (acc == 0x5EED5EEDu) sink[b] = acc;
+}
+
+// Matrix-core probe: every wave of `grid` workgroups of `threads` threads runs
+// `per_wave` v_mfma_f32_16x16x32_bf16 (a multiple of 8) as eight independent
+// accumulator chains on register operands, with no memory traffic. Its time is
+// the floor that MFMA issue alone sets for a kernel doing the same number of
+// MFMAs per wave in the same launch shape (batched verify: "FP8 decode is the
+// more compute-bound path", autobench "Qwen3.8-27B · vLLM · FP8 + MTP"). The
+// operands are small bf16 values, so the sums stay finite; their total decides
+// a store to sink[b] that never happens but keeps every MFMA live.
+__global__ __launch_bounds__(1024) void mfma_probe_kernel(uint32_t per_wave, float *__restrict__ sink) {
+    const uint32_t lane = threadIdx.x & 63;
+    // bf16 pairs of 2^-4 * (1 + lane/128) and 2^-4: exact, small
+    const uint32_t ha = 0x3D80u + (lane & 15u), hb = 0x3D80u;
+    uint4 a = make_uint4(ha | (ha << 16), ha | (ha << 16), ha | (ha << 16), ha | (ha << 16));
+    const uint4 b = make_uint4(hb | (hb << 16), hb | (hb << 16), hb | (hb << 16), hb | (hb << 16));
+    asm volatile("" : "+v"(a.x), "+v"(a.y), "+v"(a.z), "+v"(a.w));
+    f32x4 acc[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (uint32_t i = 0; i < per_wave; i += 8) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[j] = mfma16x16x32(a, b, acc[j]);
+    }
+    float t = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) t += acc[j][0] + acc[j][1] + acc[j][2] + acc[j][3];
+    if (t == -1.0f) sink[blockIdx.x] = t;
+}
+
+hipError_t launch_mfma_probe(uint32_t grid, uint32_t threads, uint32_t per_wave, float *sink, hipStream_t stream) {
+    hipLaunchKernelGGL(mfma_probe_kernel, dim3(grid), dim3(threads), 0, stream, per_wave, sink);
+    return hipGetLastError();
 }
 
 hipError_t launch_stream_probe(const void *src, size_t bytes, uint32_t grid, uint32_t threads, uint32_t *sink,

@@ -682,6 +682,9 @@ def main():
     ap.add_argument("--only", default="",
                     help="comma-separated workloads: time just these (per-workload table, no decode "
                          "step, no CPU leg) and print their rows as JSON; for profiling runs")
+    ap.add_argument("--launches", type=int, default=0,
+                    help="with --only: just launch each workload's GEMM this many times (rotating "
+                         "weight copies, parity checked once), untimed; for counter runs")
     ap.add_argument("--setup-only", action="store_true",
                     help="time only the setup-time steps (quantizers, ingest) and print them as JSON")
     ap.add_argument("--copy-probe", action="store_true",
@@ -711,6 +714,18 @@ def main():
         print(json.dumps({"quantizer": time_quantizer(torch, svq, oracle),
                           "ct_ingest": time_ct_ingest(torch, svq, oracle),
                           "mxfp8_quantizer": time_mxfp8_quantizer(torch, svq, oracle)}), flush=True)
+        return
+    if args.only and args.launches > 0:
+        for n in [n for n in args.only.split(",") if n in synth.WORKLOADS]:
+            p = Problem(torch, svq, n, POOL_BYTES)
+            p.check(oracle)
+            for _ in range(args.launches):
+                p.launch()
+            torch.cuda.synchronize()
+            log(f"{n}: {args.launches} launches of {p.kernel} {list(p.geometry)}")
+            p.release()
+            del p
+            torch.cuda.empty_cache()
         return
     if args.only:
         names = [n for n in args.only.split(",") if n]

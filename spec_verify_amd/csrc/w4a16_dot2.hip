@@ -78,16 +78,14 @@ __global__ __launch_bounds__(64 * WAVES) void w4a16_dot2_kernel(
         S[d] = bload4(sr, s_vo, kt * NG * N * 2);                                    \
     }
 #define SVQ_COMPUTE(W, X, S, I0)                                                     \
-    _Pragma("unroll") for (int d = 0; d < D; ++d) {                                  \
+    _Pragma("unroll") for (int d = 0; d < D; ++d) if ((I0) + d < ntile) {            \
         float p[M];                                                                  \
         _Pragma("unroll") for (int m = 0; m < M; ++m)                                \
             p[m] = -136.f * row16_sum(dot2_bf16(X[d][m], kBf16OnePair, 0.f));        \
         const uint32_t wj[4] = {W[d].x, W[d].y, W[d].z, W[d].w};                     \
         w4a16_tile_dots<M>(p, X[d], wj, kNibblePairMask, kMagic128Pair);             \
-        if ((I0) + d < ntile) {                                                      \
-            const float sf = fp16_bits_to_f32((uint16_t)(S[d] >> s_sh));                       \
-            _Pragma("unroll") for (int m = 0; m < M; ++m) acc[m] = __builtin_fmaf(sf, p[m], acc[m]); \
-        }                                                                            \
+        const float sf = fp16_bits_to_f32((uint16_t)(S[d] >> s_sh));                 \
+        _Pragma("unroll") for (int m = 0; m < M; ++m) acc[m] = __builtin_fmaf(sf, p[m], acc[m]); \
     }
 
     if (ntile > 0) {

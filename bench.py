@@ -685,6 +685,10 @@ def main():
     ap.add_argument("--launches", type=int, default=0,
                     help="with --only: just launch each workload's GEMM this many times (rotating "
                          "weight copies, parity checked once), untimed; for counter runs")
+    ap.add_argument("--record-profile", nargs="+", metavar="DIR",
+                    help="write profiles/trace.json and profiles/traffic.json for the dominant kernel from "
+                         "the rocprofv3 result databases under these directories, then exit")
+    ap.add_argument("--record-command", default="", help="the profiled command, kept with the trace record")
     ap.add_argument("--setup-only", action="store_true",
                     help="time only the setup-time steps (quantizers, ingest) and print them as JSON")
     ap.add_argument("--copy-probe", action="store_true",
@@ -696,6 +700,10 @@ def main():
         sys.exit(2)
     if args.copy_probe:
         copy_probe()
+        return
+
+    if args.record_profile:
+        record_profile(args.record_profile, args.record_command)
         return
 
     import torch
@@ -885,6 +893,74 @@ def measured_traffic(path=None):
     if not t or t.get("kernel_source_sha") != _kernel_source_sha():
         return None
     return t.get("bytes_per_launch")
+
+
+def _rocpd_rows(dirs):
+    """(database, kernel dispatches, per-dispatch counter sums) of every rocprofv3
+    result database under dirs."""
+    import glob
+    import sqlite3
+    for d in dirs:
+        for path in sorted(glob.glob(os.path.join(d, "**", "*.db"), recursive=True)):
+            db = sqlite3.connect(path)
+            names = {r[0] for r in db.execute("select name from sqlite_master where type in ('table','view')")}
+            if "kernels" not in names:
+                continue
+            disp = {r[0]: (r[1], r[2], r[3] - r[4]) for r in db.execute(
+                "select dispatch_id, name, grid_x * grid_y * grid_z, end, start from kernels")}
+            pmc = {}
+            if "pmc_events" in names:
+                for did, cn, cv in db.execute("select dispatch_id, counter_name, counter_value from pmc_events"):
+                    pmc.setdefault(did, {}).setdefault(cn, 0.0)
+                    pmc[did][cn] += cv
+            yield path, disp, pmc
+
+
+def record_profile(dirs, command):
+    """Write profiles/trace.json and profiles/traffic.json for the dominant kernel
+    from rocprofv3 result databases: durations from kernel-trace runs (databases
+    without counters), FETCH_SIZE / WRITE_SIZE per dispatch from counter runs,
+    scaled by what the same counters read for the copy probe's 1 GiB copies."""
+    import spec_verify_amd as svq
+    w = synth.WORKLOADS[DOMINANT]
+    grid, threads, _ = svq.launch_geometry(OPS[w["op"]], w["M"], w["N"], w["K"], group(w))
+    kname = svq.kernel_name(OPS[w["op"]], w["M"], w["N"], w["K"], group(w))
+    items = grid * threads
+    durs, fetch, write, cfetch, cwrite = [], [], [], [], []
+    copy_kib = (1 << 30) / 1024
+    for _, disp, pmc in _rocpd_rows(dirs):
+        for did, (name, n, dur) in disp.items():
+            mine = kname in name and n == items
+            if did in pmc:
+                c = pmc[did]
+                if mine:
+                    fetch += [c["FETCH_SIZE"]] if "FETCH_SIZE" in c else []
+                    write += [c["WRITE_SIZE"]] if "WRITE_SIZE" in c else []
+                elif "copyBuffer" in name:
+                    cfetch += [c["FETCH_SIZE"]] if "FETCH_SIZE" in c else []
+                    cwrite += [c["WRITE_SIZE"]] if "WRITE_SIZE" in c else []
+            elif mine:
+                durs.append(dur / 1e3)
+    sha = _kernel_source_sha()
+    out = []
+    if durs:
+        rec = {"kernel": kname, "kernel_source_sha": sha, "median_us": round(med(durs), 3),
+               "mean_us": round(sum(durs) / len(durs), 3), "dispatches": len(durs), "command": command}
+        with open(os.path.join(ROOT, "profiles", "trace.json"), "w") as f:
+            json.dump({DOMINANT: rec}, f, indent=2)
+            f.write("\n")
+        out.append(f"trace: {rec}")
+    if fetch and write and cfetch and cwrite:
+        ff, wf = copy_kib / med(cfetch), copy_kib / med(cwrite)
+        fk, wk = sum(fetch) / len(fetch), sum(write) / len(write)
+        rec = {"kernel": kname, "kernel_source_sha": sha, "fetch_kib_per_dispatch": round(fk, 1),
+               "write_kib_per_dispatch": round(wk, 1), "fetch_factor": round(ff, 3), "write_factor": round(wf, 3),
+               "dispatches": len(fetch), "bytes_per_launch": int(round((fk * ff + wk * wf) * 1024))}
+        with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as f:
+            json.dump({DOMINANT: rec}, f, indent=2)
+            f.write("\n")
+        out.append(f"traffic: {rec}")
+    log("\n".join(out) if out else "no matching dispatches")
 
 
 if __name__ == "__main__":

@@ -318,6 +318,48 @@ def q4_unrepack(tiled: np.ndarray, N: int, K: int) -> np.ndarray:
     return out
 
 
+# ---- MXFP8 tile layout ---------------------------------------------------------
+
+def _mxfp8_tile_index(N: int, K: int):
+    """For every byte offset o of the tiled buffer, the (column, K-element) of
+    the [N][K] code matrix it holds."""
+    if N % 16 or K % 128 or N <= 0 or K <= 0:
+        raise ValueError("the MXFP8 tile layout needs N % 16 == 0 and K % 128 == 0")
+    KT = K // 128
+    o = np.arange(N * K, dtype=np.int64)
+    tile, rem = o // 2048, o % 2048
+    half, lane, byte = rem // 1024, (rem % 1024) // 16, rem % 16
+    nb, kt = tile // KT, tile % KT
+    col = 16 * nb + lane % 16
+    k = 128 * kt + 32 * (lane // 16) + 16 * half + byte
+    return col, k
+
+
+def mxfp8_tile(w: np.ndarray) -> np.ndarray:
+    """E4M3 codes [N, K] -> the device tile layout (flat uint8, N*K bytes).
+
+    A layout of this library (the pages only say that weights are repacked
+    once at setup: Eole recipe, section "Pack inference projections"): tiles of
+    16 columns x 128 K-elements (2 KiB), column-block-major with the K-tiles of
+    a column block consecutive; byte 1024*h + 16*l + b of a tile holds column
+    16*nb + l%16, K-element 128*kt + 32*(l/16) + 16*h + b."""
+    w = np.ascontiguousarray(w, dtype=np.uint8)
+    N, K = w.shape
+    col, k = _mxfp8_tile_index(N, K)
+    return w[col, k]
+
+
+def mxfp8_untile(tiled: np.ndarray, N: int, K: int) -> np.ndarray:
+    """Inverse of mxfp8_tile: the flat tiled buffer back to codes [N, K]."""
+    tiled = np.ascontiguousarray(tiled, dtype=np.uint8).reshape(-1)
+    if tiled.size != N * K:
+        raise ValueError("size mismatch")
+    col, k = _mxfp8_tile_index(N, K)
+    out = np.empty((N, K), dtype=np.uint8)
+    out[col, k] = tiled
+    return out
+
+
 # ---- MXFP8 quantizer: plain and optimized round-to-nearest ---------------------
 
 def e4m3_nearest(a) -> np.ndarray:

@@ -335,6 +335,60 @@ def test_repack_bijection_and_tile_contents(N, K):
         assert (word >> (4 * slot_of_e[e])) & 15 == q[kk, nn]
 
 
+# ---- P17: the MXFP8 tile layout ------------------------------------------------
+
+def test_mxfp8_tile_handworked_offsets():
+    """Offsets worked by hand from the layout's definition (N = 32, K = 256): a
+    matrix whose code encodes its column, and one whose code encodes K, show
+    which element each listed offset holds."""
+    N, K = 32, 256
+    by_col = np.repeat(np.arange(N, dtype=np.uint8)[:, None], K, axis=1)
+    by_k = np.repeat(np.arange(K, dtype=np.uint8)[None, :], N, axis=0)
+    tc, tk = oracle.mxfp8_tile(by_col), oracle.mxfp8_tile(by_k)
+    cnt = 0
+    for off, col, k in _rows("mxfp8_tile_bytes.txt"):
+        assert (int(tc[int(off)]), int(tk[int(off)])) == (int(col), int(k)), off
+        cnt += 1
+    assert cnt == 10
+
+
+@pytest.mark.parametrize("N,K", [(16, 128), (48, 384), (160, 1280)])
+def test_mxfp8_tile_bijection_and_lane_runs(N, K):
+    """Every code lands exactly once; untile inverts tile; and read the way a
+    kernel lane reads it (two 16-byte loads, one from each 1 KiB half of a
+    tile), lane l of tile (nb, kt) gets the 32 consecutive K-elements of column
+    16*nb + l%16 that start at 128*kt + 32*(l/16), in order."""
+    rng = np.random.default_rng(N * 7 + K)
+    w = rng.integers(0, 256, size=(N, K), dtype=np.uint8)
+    t = oracle.mxfp8_tile(w)
+    assert t.size == N * K
+    np.testing.assert_array_equal(oracle.mxfp8_untile(t, N, K), w)
+    # bijection: the (column, K) labels carried through the layout (column and
+    # K split into bytes) come out as a permutation of all N*K pairs
+    cols = np.repeat(np.arange(N)[:, None], K, axis=1)
+    ks = np.repeat(np.arange(K)[None, :], N, axis=0)
+    planes = [oracle.mxfp8_tile(((a >> sh) & 255).astype(np.uint8)).astype(np.int64)
+              for a in (cols, ks) for sh in (0, 8)]
+    col_of = planes[0] | (planes[1] << 8)
+    k_of = planes[2] | (planes[3] << 8)
+    assert len(np.unique(col_of * K + k_of)) == N * K
+    KT = K // 128
+    for _ in range(50):
+        nb, kt, lane = int(rng.integers(N // 16)), int(rng.integers(KT)), int(rng.integers(64))
+        base = (nb * KT + kt) * 2048
+        run = np.concatenate([t[base + 16 * lane: base + 16 * lane + 16],
+                              t[base + 1024 + 16 * lane: base + 1024 + 16 * lane + 16]])
+        c, k0 = 16 * nb + lane % 16, 128 * kt + 32 * (lane // 16)
+        np.testing.assert_array_equal(run, w[c, k0:k0 + 32])
+        assert np.all(col_of[base + 16 * lane: base + 16 * lane + 16] == c)
+
+
+def test_mxfp8_tile_rejects_bad_shapes():
+    for N, K in ((8, 128), (16, 64), (16, 200)):
+        with pytest.raises(ValueError):
+            oracle.mxfp8_tile(np.zeros((N, K), dtype=np.uint8))
+
+
 def test_gate_accepts_rounding_and_rejects_a_wrong_weight():
     inp = synth.gen_w4a16(51, 1, 5120, 64, 128, keep_q=True)
     y64, _ = oracle.w4a16(inp.x, inp.qweight, inp.scales)

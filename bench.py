@@ -121,7 +121,7 @@ class Problem:
             base_w = torch.from_numpy(np.ascontiguousarray(inp.w)).to("cuda:0")
             base_s = _dev(torch, inp.scales)
         else:
-            base_w = _dev(torch, inp.w)
+            base_w = svq.mxfp8_repack(_dev(torch, inp.w))
             base_s = _dev(torch, inp.scales)
         self.kernel = svq.kernel_name(OPS[op], M, N, K, G)
         self.geometry = svq.launch_geometry(OPS[op], M, N, K, G)

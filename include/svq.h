@@ -228,6 +228,23 @@ int svq_w4a16_gemm_noalloc(const void *x, const int32_t *qweight_tiled, const vo
 
 /* ---- MXFP8 ------------------------------------------------------------------ */
 
+/*
+ * One-time repack of E4M3 codes into the device tile layout read by the MXFP8
+ * GEMM kernels (a byte permutation; reads and writes N*K bytes once; the
+ * pages repack weights once at setup, Eole recipe "Qwen3.8-27B and native MTP
+ * speculative decoding", section "Pack inference projections").
+ *   w        E4M3FN codes [N][K] (row n holds the K elements of output column
+ *            n), 16-byte aligned
+ *   w_tiled  N*K bytes, 16-byte aligned, must not overlap w. Layout: tiles of
+ *            16 columns x 128 K-elements (2 KiB), column-block-major with the
+ *            K-tiles of a block consecutive (tile (nb, kt) at byte
+ *            2048*(nb*K/128 + kt)); byte 1024*h + 16*l + b of a tile holds
+ *            column 16*nb + l%16, K-element 128*kt + 32*(l/16) + 16*h + b.
+ * Requires N % 16 == 0, K % 128 == 0. The E8M0 scales keep their [N][K/32]
+ * layout.
+ */
+int svq_mxfp8_repack(const uint8_t *w, uint8_t *w_tiled, int64_t N, int64_t K, void *stream);
+
 size_t svq_mxfp8_workspace_bytes(int kernel, int64_t M, int64_t N, int64_t K);
 
 /*
@@ -239,7 +256,7 @@ size_t svq_mxfp8_workspace_bytes(int kernel, int64_t M, int64_t N, int64_t K);
  * SVQ_ERR_MXFP8_SHAPE (its section "7. Known issues and caveats" records a
  * crash at N = 96). fp32 accumulation, bf16 (nearest even) output.
  *   x       bf16 [M][K], 16-byte aligned
- *   w       E4M3FN codes [N][K] (row n holds the K elements of output column n),
+ *   w       E4M3FN codes in the svq_mxfp8_repack tile layout (N*K bytes),
  *           16-byte aligned
  *   scales  E8M0 codes [N][K/32], one per 32 consecutive K-elements of a row,
  *           4-byte aligned (read as aligned 32-bit words)

@@ -39,7 +39,7 @@ EXPORTED_SYMBOLS = (
     "svq_mxfp8_gemm_with", "svq_mxfp8_kernel_name", "svq_rtn_quantize",
     "svq_w8a16_workspace_bytes", "svq_w8a16_gemm", "svq_w8a16_kernel_name",
     "svq_fuse_projections", "svq_ct_to_gptq", "svq_mxfp8_quantize", "svq_workspace_bytes",
-    "svq_kernel_name", "svq_launch_geometry", "svq_stream_probe", "svq_mfma_probe",
+    "svq_kernel_name", "svq_launch_geometry", "svq_stream_probe", "svq_mfma_probe", "svq_mxfp8_repack",
     "svq_w4a16_gemm_noalloc",
 )
 
@@ -118,6 +118,8 @@ def lib():
                                           ctypes.POINTER(_sz)]
         L.svq_stream_probe.restype = ctypes.c_int
         L.svq_stream_probe.argtypes = [_p, _sz, ctypes.c_uint32, ctypes.c_uint32, _p, _p]
+        L.svq_mxfp8_repack.restype = ctypes.c_int
+        L.svq_mxfp8_repack.argtypes = [_p, _p, _i64, _i64, _p]
         L.svq_mfma_probe.restype = ctypes.c_int
         L.svq_mfma_probe.argtypes = [ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32, _p, _p]
         L.svq_w4a16_gemm_noalloc.restype = ctypes.c_int
@@ -293,11 +295,34 @@ def w4a16_gemm(x, qweight_tiled, scales, N, group_size=128, out=None, kernel=KER
     return out
 
 
-def mxfp8_gemm(x, w, scales, out=None, kernel=KERNEL_AUTO, workspace=None):
-    """bf16 x [M, K] . (E4M3 w [N, K] * 2^(E8M0 scales [N, K/32] - 127))^T -> bf16 [M, N]."""
+def mxfp8_repack(w, out=None):
+    """E4M3 codes [N, K] (device uint8) -> the tile layout the GEMM reads (flat
+    uint8, N*K bytes)."""
+    torch = _torch()
+    N, K = w.shape
+    _check_elem(w, "w", 1)
+    if out is None:
+        out = torch.empty(N * K, dtype=torch.uint8, device=w.device)
+    _check_elem(out, "out", 1)
+    if out.numel() < N * K:
+        raise ValueError("out too small")
+    _check(lib().svq_mxfp8_repack(_dev_ptr(w, "w"), _dev_ptr(out, "out"), N, K, _stream_ptr(w)),
+           "svq_mxfp8_repack")
+    return out
+
+
+def mxfp8_gemm(x, w_tiled, scales, out=None, kernel=KERNEL_AUTO, workspace=None):
+    """bf16 x [M, K] . (E4M3 w [N, K] * 2^(E8M0 scales [N, K/32] - 127))^T -> bf16 [M, N].
+
+    w_tiled is the flat output of mxfp8_repack; N comes from scales [N, K/32]."""
     torch = _torch()
     M, K = x.shape
-    N = w.shape[0]
+    N = scales.shape[0]
+    if w_tiled.dim() != 1:
+        raise ValueError("w_tiled must be the flat output of mxfp8_repack")
+    if w_tiled.numel() != N * K or tuple(scales.shape) != (N, K // 32):
+        raise ValueError("w_tiled must hold N*K codes and scales must be [N, K/32]")
+    w = w_tiled
     _check_elem(x, "x", 2)
     _check_elem(w, "w", 1)
     _check_elem(scales, "scales", 1)

@@ -13,9 +13,16 @@
 // scale is applied before the products, so MFMA/dot2 accumulate straight into
 // the fp32 result.
 //
-// Lane mapping for a 16-column x 128-row (of K) tile: lane l owns column l%16
-// and the 32 consecutive K-rows 32*(l/16).. (one 32-element scale block, two
-// 128-bit loads). The three kernels mirror the W4A16 ones: a VALU dot2 kernel
+// Weights are read from the device tile layout written once at setup by
+// mxfp8_tile_kernel: tiles of 16 columns x 128 K-elements (2 KiB), column-block-
+// major with the K-tiles of a block consecutive, byte 1024*h + 16*l + b of a
+// tile holding column 16*nb + l%16, K-element 128*kt + 32*(l/16) + 16*h + b. So
+// lane l of a wave owns column l%16 and the 32 consecutive K-rows 32*(l/16)..
+// (one 32-element scale block) and reads them with two 128-bit loads, each of
+// which is a contiguous 1 KiB for the wave (the untouched [N][K] rows put each
+// lane's bytes K apart: a plain stream in that pattern measured 7.42 us against
+// 6.41 us for the same 26 MB in tiles, at N = K = 5120 in the M = 1 launch shape).
+// The three kernels mirror the W4A16 ones: a VALU dot2 kernel
 // with a row broadcast of x for M <= 8, a one-MFMA-tile kernel for M <= 16, and
 // the persistent stream-K MFMA kernel with LDS-staged x for larger M.
 #include "svq_dma.h"
@@ -44,11 +51,11 @@ __global__ __launch_bounds__(64 * WAVES) void mxfp8_dot2_kernel(
     const int lb = xcd_contiguous(blockIdx.x, gridDim.x);
     const int nb = lb / splits, sp = lb % splits;
     const int KT = K >> 7;
-    // this block's 16 weight rows ([N][K] layout) and their scale rows
+    // this block's tiles (2 KiB per K-tile, consecutive) and its 16 scale rows
     const __amdgpu_buffer_rsrc_t wr = make_rsrc(w + (size_t)nb * 16 * K, (uint32_t)16 * K);
     const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, (uint32_t)M * K * 2);
     const __amdgpu_buffer_rsrc_t sr = make_rsrc(sc + (size_t)nb * 16 * (K >> 5), (uint32_t)16 * (K >> 5));
-    const uint32_t w_vo = r * K + rg * 32;
+    const uint32_t w_vo = lane * 16;
     const uint32_t x_vo = lane * 4;
     // the dword holding the tile's four block scales; s_sh selects this lane's
     const uint32_t s_vo = r * (K >> 5);
@@ -67,8 +74,8 @@ __global__ __launch_bounds__(64 * WAVES) void mxfp8_dot2_kernel(
 #define SVQ_LOAD(V, X, S, I0)                                                        \
     _Pragma("unroll") for (int d = 0; d < D; ++d) if ((I0) + d < ntile) {            \
         const int kt = kbeg + wave + ((I0) + d) * WAVES;                                    \
-        V[d][0] = bload16(wr, w_vo, kt * 128);                                       \
-        V[d][1] = bload16(wr, w_vo + 16, kt * 128);                                  \
+        V[d][0] = bload16(wr, w_vo, kt * 2048);                                      \
+        V[d][1] = bload16(wr, w_vo + 1024, kt * 2048);                               \
         _Pragma("unroll") for (int m = 0; m < M; ++m) X[d][m] = bload4(xr, x_vo, m * K * 2 + kt * 256); \
         S[d] = bload4(sr, s_vo, kt * 4);                                             \
     }
@@ -131,7 +138,7 @@ __global__ __launch_bounds__(64 * WAVES) void mxfp8_skinny_kernel(
     const int KT = K >> 7;
     const __amdgpu_buffer_rsrc_t wr = make_rsrc(w + (size_t)nb * 16 * K, (uint32_t)16 * K);
     const __amdgpu_buffer_rsrc_t sr = make_rsrc(sc + (size_t)nb * 16 * (K >> 5), (uint32_t)16 * (K >> 5));
-    const uint32_t w_vo = r * K + g * 32;
+    const uint32_t w_vo = lane * 16;
     // the dword holding the tile's four block scales; s_sh selects this lane's
     const uint32_t s_vo = r * (K >> 5);
     const int s_sh = g * 8;
@@ -147,8 +154,8 @@ __global__ __launch_bounds__(64 * WAVES) void mxfp8_skinny_kernel(
 #define SVQ_LOAD(V, S, I0)                                                           \
     _Pragma("unroll") for (int d = 0; d < D; ++d) if ((I0) + d < ntile) {            \
         const int kt = kbeg + wave + ((I0) + d) * WAVES;                             \
-        V[d][0] = bload16(wr, w_vo, kt * 128);                                       \
-        V[d][1] = bload16(wr, w_vo + 16, kt * 128);                                  \
+        V[d][0] = bload16(wr, w_vo, kt * 2048);                                      \
+        V[d][1] = bload16(wr, w_vo + 1024, kt * 2048);                               \
         S[d] = bload4(sr, s_vo, kt * 4);                                             \
     }
     // stage x[0..M)[128*kbeg, 128*(kbeg+kcnt)) in LDS by DMA (one 64-chunk
@@ -239,7 +246,8 @@ __global__ __launch_bounds__(64 * WAVES) void mxfp8_skinny_kernel(
 // is staged in one slot of a three-slot LDS ring by LDS-DMA (buffer loads that
 // write LDS directly; rows past M and columns past N read as zero): x (BM rows,
 // 16-byte chunks XOR-swizzled by row so that the A reads are bank-conflict
-// free), the E4M3 codes of the tile's 128 columns and their E8M0 scales. The
+// free), the E4M3 codes of the tile's 128 columns (eight 2 KiB weight tiles)
+// and their E8M0 scales. The
 // ring runs two steps ahead of the MFMAs; one barrier per step frees the slot
 // the next DMAs go to. Lane (r, g) of a column tile converts the 32 codes of
 // its column at K 32g.. (one E8M0 block) with the block scale applied in the
@@ -292,11 +300,13 @@ __global__ __launch_bounds__(512) void mxfp8_wide_kernel(
     uint32_t offA[4];  // A of MFMA step j: row r of the wave's first row block, K 32g + 8j..
 #pragma unroll
     for (int j = 0; j < 4; ++j) offA[j] = wr * MBW * 4096 + r * 256 + (((4 * g + j) ^ r) << 4);
-    uint32_t offB[CT], offS[CT];  // codes of column (wc*CT + ct)*16 + r at K 32g.., its scale dword
+    // codes of column (wc*CT + ct)*16 + r at K 32g.. (the two halves of a
+    // staged tile, lane 16g + r of each), and its scale dword
+    uint32_t offB[CT], offS[CT];
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) {
         const int cb16 = wc * CT + ct;
-        offB[ct] = C::OFF_W + (cb16 * 2 + (g >> 1)) * 1024 + ((g & 1) * 32 + r) * 16;
+        offB[ct] = C::OFF_W + cb16 * 2048 + (16 * g + r) * 16;
         offS[ct] = C::OFF_S + (cb16 * 16 + r) * 4;
     }
     const int per_step = C::XI + C::WI + (wave < C::SI ? 1 : 0);  // this wave's DMAs per stage
@@ -314,7 +324,7 @@ __global__ __launch_bounds__(512) void mxfp8_wide_kernel(
         return sg;
     };
     // DMA of K step kt of segment sg into slot st: x (1 KiB = 4 rows per
-    // instruction), codes (16 columns x 64 K per instruction), scales (64
+    // instruction), codes (one 1 KiB half-tile per instruction), scales (64
     // columns x 4 blocks per instruction)
     auto issue = [&](const Seg &sg, int st, int kt) {
         const uint32_t base = ring_lds + st * C::SLOT;
@@ -327,10 +337,10 @@ __global__ __launch_bounds__(512) void mxfp8_wide_kernel(
         }
 #pragma unroll
         for (int v = 0; v < C::WI; ++v) {
-            const int t = wave * C::WI + v;  // column block t/2, K half t%2
-            const uint32_t col = (uint32_t)(sg.cb * BN + (t >> 1) * 16 + (lane & 15));
-            dma_b128(wrs, base + C::OFF_W + t * 1024, col * (uint32_t)K + (uint32_t)(64 * (t & 1) + 16 * (lane >> 4)),
-                     (uint32_t)kt * 128u);
+            const int t = wave * C::WI + v;  // column block t/2 of the tile, half t%2
+            const uint32_t blk = (uint32_t)(sg.cb * (BN / 16) + (t >> 1));  // blocks past N read as zero
+            dma_b128(wrs, base + C::OFF_W + t * 1024, (blk * (uint32_t)KT * 2048u) + (uint32_t)((t & 1) * 1024 + lane * 16),
+                     (uint32_t)kt * 2048u);
         }
         if (wave < C::SI) {
             const uint32_t col = (uint32_t)(sg.cb * BN + wave * 64 + lane);
@@ -344,7 +354,7 @@ __global__ __launch_bounds__(512) void mxfp8_wide_kernel(
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
             wv[ct][0] = lds_ld16(b + offB[ct]);
-            wv[ct][1] = lds_ld16(b + offB[ct] + 256);
+            wv[ct][1] = lds_ld16(b + offB[ct] + 1024);
             sf[ct] = e8m0_to_f32((lds_ld<uint32_t>(b + offS[ct]) >> (8 * g)) & 0xFFu);
         }
 #pragma unroll
@@ -463,6 +473,26 @@ hipError_t mx_wide_launch(const WidePlan &p, const void *x, const uint8_t *w, co
                        p.grid, p.maxt);
 }
 }  // namespace
+
+// Setup: [N][K] codes -> the tile layout above. Thread t moves the 16 bytes at
+// K-elements 16*(t % (K/16)).. of column t / (K/16): reads run along the rows.
+__global__ __launch_bounds__(256) void mxfp8_tile_kernel(const uint4 *__restrict__ src, uint4 *__restrict__ dst,
+                                                         int64_t N, int64_t K) {
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t k16 = K >> 4;
+    if (t >= N * k16) return;
+    const int64_t col = t / k16, c = t - col * k16;    // 16-byte chunk c of the row
+    const int64_t kt = c >> 3, q = (c & 7) >> 1, h = c & 1;
+    const int64_t lane = 16 * q + (col & 15);
+    dst[(((col >> 4) * (K >> 7) + kt) * 2048 + h * 1024 + lane * 16) >> 4] = src[t];
+}
+
+hipError_t launch_mxfp8_tile(const uint8_t *src, uint8_t *dst, int64_t N, int64_t K, hipStream_t stream) {
+    const int64_t chunks = N * K / 16;
+    hipLaunchKernelGGL(mxfp8_tile_kernel, dim3((uint32_t)((chunks + 255) / 256)), dim3(256), 0, stream,
+                       (const uint4 *)src, (uint4 *)dst, N, K);
+    return hipGetLastError();
+}
 
 hipError_t launch_mxfp8_dot2(const SmallPlan &plan, const void *x, const uint8_t *w,
                              const uint8_t *scales, void *out, int M, int64_t N, int64_t K,

@@ -230,6 +230,17 @@ int svq_q4_repack(const int32_t *src, int32_t *dst, int64_t N, int64_t K, void *
     return SVQ_OK;
 }
 
+int svq_mxfp8_repack(const uint8_t *src, uint8_t *dst, int64_t N, int64_t K, void *stream) {
+    if (!src || !dst) return SVQ_ERR_NULL;
+    if (N <= 0 || K <= 0 || N > kMaxDim || K > kMaxDim || N * K > (int64_t(1) << 40)) return SVQ_ERR_DIM;
+    if (N % 16 || K % 128) return SVQ_ERR_DIVISIBILITY;
+    if (!aligned(src, 16) || !aligned(dst, 16)) return SVQ_ERR_ALIGN;
+    const size_t bytes = (size_t)N * (size_t)K;
+    if (overlap(src, bytes, dst, bytes)) return SVQ_ERR_OVERLAP;
+    if (launch_mxfp8_tile(src, dst, N, K, (hipStream_t)stream) != hipSuccess) return SVQ_ERR_HIP;
+    return SVQ_OK;
+}
+
 static_assert(SVQ_MAX_FUSED_PARTS == kMaxFuseParts, "fusion table size");
 
 int svq_fuse_projections(int32_t bits, const void *const *weights, const void *const *scales,

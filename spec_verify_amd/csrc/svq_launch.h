@@ -46,6 +46,7 @@ hipError_t launch_mfma_probe(uint32_t grid, uint32_t threads, uint32_t per_wave,
 
 hipError_t launch_q4_repack(const int32_t *src, int32_t *dst, int64_t N, int64_t K,
                             hipStream_t stream);
+hipError_t launch_mxfp8_tile(const uint8_t *src, uint8_t *dst, int64_t N, int64_t K, hipStream_t stream);
 
 // Setup-time projection fusion (bits 4: GPTQ words -> fused tiles; bits 8: int8
 // codes [N_p][K] -> [sum N_p][K]) and fp16 scale concatenation, one launch.

@@ -98,6 +98,12 @@ def test_repack_validation(L):
     assert L.svq_q4_repack(FAKE, FAKE + 4096, 256, 512, None) == 7
     assert L.svq_q4_repacked_bytes(5120, 17408) == 5120 * 17408 // 2
     assert L.svq_q4_repacked_bytes(0, 5) == 0
+    assert L.svq_mxfp8_repack(None, FAKE2, 256, 512, None) == 1
+    assert L.svq_mxfp8_repack(FAKE, FAKE2, 0, 512, None) == 2
+    assert L.svq_mxfp8_repack(FAKE, FAKE2, 24, 512, None) == 4
+    assert L.svq_mxfp8_repack(FAKE, FAKE2, 256, 192, None) == 4
+    assert L.svq_mxfp8_repack(FAKE + 4, FAKE2, 256, 512, None) == 6
+    assert L.svq_mxfp8_repack(FAKE, FAKE + 4096, 256, 512, None) == 7
 
 
 def test_kernel_selection_names(L):

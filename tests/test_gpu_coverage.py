@@ -84,7 +84,8 @@ class MX:
     def __init__(self, seed, M, K, N):
         self.inp = synth.gen_mxfp8(seed, M, K, N)
         self.M, self.K, self.N = M, K, N
-        self.x, self.w, self.s = dev(self.inp.x), dev(self.inp.w), dev(self.inp.scales)
+        import spec_verify_amd as svq
+        self.x, self.w, self.s = dev(self.inp.x), svq.mxfp8_repack(dev(self.inp.w)), dev(self.inp.scales)
 
     def ref(self):
         return oracle.mxfp8(self.inp.x, self.inp.w, self.inp.scales)

@@ -76,7 +76,7 @@ def _setup(op, M, K, N, kernel):
         ref = lambda: oracle.w4a16(inp.x, inp.qweight, inp.scales)
     elif op == "mxfp8":
         inp = synth.gen_mxfp8(1300 + M, M, K, N)
-        x, w, s = dev(inp.x), dev(inp.w), dev(inp.scales)
+        x, w, s = dev(inp.x), svq.mxfp8_repack(dev(inp.w)), dev(inp.scales)
         nbytes = svq.mxfp8_workspace_bytes(M, N, K, kernel)
         call = lambda o, ws: svq.mxfp8_gemm(x, w, s, out=o, kernel=kernel, workspace=ws)
         ref = lambda: oracle.mxfp8(inp.x, inp.w, inp.scales)

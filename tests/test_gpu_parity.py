@@ -61,7 +61,7 @@ def run_w4a16(inp, kernel=0, out=None):
 
 def run_mxfp8(inp, kernel=0):
     import spec_verify_amd as svq
-    o = svq.mxfp8_gemm(dev(inp.x), dev(inp.w), dev(inp.scales), kernel=kernel)
+    o = svq.mxfp8_gemm(dev(inp.x), svq.mxfp8_repack(dev(inp.w)), dev(inp.scales), kernel=kernel)
     torch.cuda.synchronize()
     return host_bits(o)
 
@@ -84,6 +84,16 @@ def test_repack_bit_exact(N, K):
     np.testing.assert_array_equal(got, ref)
     if N * K <= 1 << 20:
         np.testing.assert_array_equal(oracle.q4_unrepack(got, N, K), inp.qweight)
+
+
+@pytest.mark.parametrize("N,K", [(16, 128), (48, 384), (256, 640), (5120, 5120), (1024, 17408)])
+def test_mxfp8_repack_bit_exact(N, K):
+    _say("mxfp8 repack", N, K)
+    rng = np.random.default_rng(17 + N + K)
+    w = rng.integers(0, 256, size=(N, K), dtype=np.uint8)
+    import spec_verify_amd as svq
+    got = svq.mxfp8_repack(torch.from_numpy(w).cuda()).cpu().numpy()
+    np.testing.assert_array_equal(got, oracle.mxfp8_tile(w))
 
 
 # ---- W4A16 small shapes, every kernel -------------------------------------------
@@ -472,7 +482,7 @@ def test_split_k_deterministic_and_counters_cleared(op, kernel, M, K, N):
         y64, y32 = oracle.w4a16(inp.x, inp.qweight, inp.scales, 128)
     else:
         inp = synth.gen_mxfp8(70 + M, M, K, N)
-        x, w, s = dev(inp.x), dev(inp.w), dev(inp.scales)
+        x, w, s = dev(inp.x), svq.mxfp8_repack(dev(inp.w)), dev(inp.scales)
         nbytes = svq.mxfp8_workspace_bytes(M, N, K, kernel)
         run = lambda ws: svq.mxfp8_gemm(x, w, s, kernel=kernel, workspace=ws)
         y64, y32 = oracle.mxfp8(inp.x, inp.w, inp.scales)

@@ -119,7 +119,7 @@ def test_mxfp8_quantize_then_gemm():
     w = torch.from_numpy(wb.view(np.int16)).cuda()
     c, s = svq.mxfp8_quantize(w, True)
     x = synth.gen_w4a16(972, M, K, 16).x
-    out = svq.mxfp8_gemm(torch.from_numpy(x.view(np.int16)).cuda(), c, s)
+    out = svq.mxfp8_gemm(torch.from_numpy(x.view(np.int16)).cuda(), svq.mxfp8_repack(c), s)
     torch.cuda.synchronize()
     c_ref, s_ref = oracle.mxfp8_quantize(wb, True)
     y64, y32 = oracle.mxfp8(x, c_ref, s_ref)

@@ -73,8 +73,8 @@ __global__ __launch_bounds__(64 * WAVES) void w4a16_dot2_kernel(
 #define SVQ_LOAD(W, X, S, I0)                                                        \
     _Pragma("unroll") for (int d = 0; d < D; ++d) if ((I0) + d < ntile) {            \
         const int kt = kbeg + wave + ((I0) + d) * WAVES;                                    \
-        W[d] = bload16(wr, w_vo, kt * 1024);                                         \
         _Pragma("unroll") for (int m = 0; m < M; ++m) X[d][m] = bload4(xr, x_vo, m * K * 2 + kt * 256); \
+        W[d] = bload16(wr, w_vo, kt * 1024);                                         \
         S[d] = bload4(sr, s_vo, kt * NG * N * 2);                                    \
     }
 #define SVQ_COMPUTE(W, X, S, I0)                                                     \

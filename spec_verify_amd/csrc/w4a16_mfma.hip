@@ -41,11 +41,11 @@ namespace svq {
 // MFMA pipe is mostly idle, so the -136 * sum(x) term is also computed on it,
 // by an MFMA against a constant -136 operand.
 // ---------------------------------------------------------------------------
-template <int WAVES, int BPW, int D, int GSHIFT>
+template <int WAVES, int WPB, int D, int GSHIFT>
 __global__ __launch_bounds__(64 * WAVES) void w4a16_skinny_kernel(
     const uint16_t *__restrict__ x, const uint4 *__restrict__ wt,
     const uint16_t *__restrict__ sc, uint16_t *__restrict__ out, uint32_t *__restrict__ cnt,
-    float *__restrict__ part, int M, int N, int K, int splits, int S) {
+    float *__restrict__ part, int M, int N, int K, int splits, int S, int groups) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     constexpr int NG = 128 >> GSHIFT;
     constexpr int SPG = 4 / NG;
@@ -55,10 +55,13 @@ __global__ __launch_bounds__(64 * WAVES) void w4a16_skinny_kernel(
     const int r = lane & 15, g = lane >> 4;
     const int lb = xcd_contiguous(blockIdx.x, gridDim.x);
     const int sp = lb % splits;
-    static_assert(WAVES % BPW == 0, "whole waves per block");
-    constexpr int wpb = WAVES / BPW;                   // waves per block
-    const int nb0 = (lb / splits) * BPW;               // first block of the workgroup
-    const int nblk = min(BPW, (N >> 4) - nb0);         // blocks it owns (last one: fewer)
+    // the column blocks are dealt evenly to `groups` workgroups per K range
+    // (floor or ceil of blocks / groups each, at most WAVES / WPB); WPB waves
+    // per block, waves past the workgroup's last block idle
+    constexpr int wpb = WPB;
+    const uint32_t grp = (uint32_t)(lb / splits), nblocks = (uint32_t)(N >> 4);
+    const int nb0 = (int)(grp * nblocks / (uint32_t)groups);                   // first block of the workgroup
+    const int nblk = (int)((grp + 1) * nblocks / (uint32_t)groups) - nb0;      // blocks it owns
     const int bw = wave / wpb, wsub = wave - bw * wpb;   // this wave's block and rank in it
     const int nb = nb0 + min(bw, nblk - 1);            // clamped: a wave past the last block idles
     const int KT = K >> 7;
@@ -538,46 +541,39 @@ __global__ __launch_bounds__(64 * WR * WC) void w4a16_wide_kernel(
 namespace {
 constexpr int kSkinnyDepth = 2;
 
-template <int WAVES, int BPW, int GS>
-hipError_t skinny_launch_b(const SmallPlan &p, const void *x, const int32_t *wt, const void *sc,
-                           void *out, int M, int64_t N, int64_t K, void *ws, hipStream_t stream) {
-    const int64_t groups = (N / 16 + BPW - 1) / BPW;
-    return launch_gemm(w4a16_skinny_kernel<WAVES, BPW, kSkinnyDepth, GS>,
-                       dim3((uint32_t)(groups * p.splits)), dim3(64 * WAVES),
-                       skinny_lds_bytes(M, p.S, WAVES), stream,
-                       (const uint16_t *)x, (const uint4 *)wt, (const uint16_t *)sc, (uint16_t *)out,
-                       ws_counters(ws), (float *)ws_partials(ws), M, (int)N, (int)K, p.splits, p.S);
-}
-
-template <int WAVES, int GS>
-hipError_t skinny_launch_w(const SmallPlan &p, int bpw, const void *x, const int32_t *wt, const void *sc,
-                           void *out, int M, int64_t N, int64_t K, void *ws, hipStream_t stream) {
-    switch (bpw) {
-    case 1: return skinny_launch_b<WAVES, 1, GS>(p, x, wt, sc, out, M, N, K, ws, stream);
-    case 2: return skinny_launch_b<WAVES, 2, GS>(p, x, wt, sc, out, M, N, K, ws, stream);
-    default: return skinny_launch_b<WAVES, 4, GS>(p, x, wt, sc, out, M, N, K, ws, stream);
-    }
-}
-
-// Workgroup shape: WAVES waves and bpw column blocks per workgroup (WAVES/bpw
-// waves per block), chosen so that the whole grid is resident at once
-// (registers, waves and LDS per CU), with as many waves per block as
-// possible and then as few blocks per workgroup as possible. One x stage per workgroup is shared by its blocks, so more blocks
-// per workgroup means fewer stages in LDS. If nothing fits, 4 waves and one
-// block per workgroup.
+// Workgroup shape: WAVES waves, WPB of them per column block, and `groups`
+// workgroups per K range over which the column blocks are dealt evenly (each
+// takes floor or ceil of blocks / groups). One x stage per workgroup is shared
+// by its blocks. First choice: 16 waves and one workgroup per CU and K range,
+// so that every CU streams the same number of blocks give or take one (with
+// 1088 blocks, 4 or 5 per CU, against 4 or 6 when 544 two-block workgroups land
+// 2 or 3 to a CU) and stages x once (measured: verify M = 5 up 14.9 -> 13.1 us,
+// M = 3 up 13.8 -> 12.7 us, M = 3 down 14.8 -> 14.0 us). When that does not
+// fit (more than 8 blocks per workgroup, or more outputs than threads), the
+// most waves per block, then the fewest blocks per workgroup, at 16, 8 or 4
+// waves and 1, 2 or 4 blocks, with the whole grid resident at once
+// (registers, waves and LDS per CU).
 struct SkinnyShape {
-    int waves, bpw;
+    int waves, wpb, groups;
 };
 
 template <int GS>
 SkinnyShape skinny_shape(const SmallPlan &p, int M, int64_t N) {
-    // register-limited residency (the BPW = 2 and 4 instances use as many registers)
-    static const int r16 = resident_blocks(w4a16_skinny_kernel<16, 1, kSkinnyDepth, GS>, 1024);
-    static const int r8 = resident_blocks(w4a16_skinny_kernel<8, 1, kSkinnyDepth, GS>, 512);
-    static const int r4 = resident_blocks(w4a16_skinny_kernel<4, 1, kSkinnyDepth, GS>, 256);
+    static const int r16 = resident_blocks(w4a16_skinny_kernel<16, 4, kSkinnyDepth, GS>, 1024);
+    static const int r8 = resident_blocks(w4a16_skinny_kernel<8, 4, kSkinnyDepth, GS>, 512);
+    static const int r4 = resident_blocks(w4a16_skinny_kernel<4, 4, kSkinnyDepth, GS>, 256);
     const int64_t blocks = N / 16;
-    SkinnyShape best{4, 1};
-    int best_wpb = 0;
+    {
+        const int r = std::min(r16, (int)(kLdsPerCu / skinny_lds_bytes(M, p.S, 16)));
+        const int64_t groups = std::min<int64_t>(blocks, (int64_t)p.cus / p.splits);
+        const int64_t maxblk = groups > 0 ? (blocks + groups - 1) / groups : 0;
+        if (r >= 1 && groups >= 1 && maxblk <= 8 && maxblk * M <= 64) {
+            const int wpb = (int)(16 / maxblk);
+            return SkinnyShape{16, wpb >= 16 ? 16 : wpb >= 8 ? 8 : wpb, (int)groups};
+        }
+    }
+    SkinnyShape best{4, 4, (int)blocks};
+    int best_wpb = 0, best_bpw = 1;
     for (const int waves : {16, 8, 4}) {
         const int r_occ = waves == 16 ? r16 : waves == 8 ? r8 : r4;
         const int r = std::min(r_occ, (int)(kLdsPerCu / skinny_lds_bytes(M, p.S, waves)));
@@ -586,9 +582,10 @@ SkinnyShape skinny_shape(const SmallPlan &p, int M, int64_t N) {
             if ((blocks + bpw - 1) / bpw * p.splits <= (int64_t)r * p.cus) {
                 // most waves per block; on a tie, fewer blocks per workgroup
                 // (measured: 640 workgroups of 8 waves beat 320 of 16 waves)
-                if (waves / bpw > best_wpb || (waves / bpw == best_wpb && bpw < best.bpw)) {
-                    best = SkinnyShape{waves, bpw};
+                if (waves / bpw > best_wpb || (waves / bpw == best_wpb && bpw < best_bpw)) {
+                    best = SkinnyShape{waves, waves / bpw, (int)((blocks + bpw - 1) / bpw)};
                     best_wpb = waves / bpw;
+                    best_bpw = bpw;
                 }
                 break;
             }
@@ -597,15 +594,45 @@ SkinnyShape skinny_shape(const SmallPlan &p, int M, int64_t N) {
     return best;
 }
 
+template <int WAVES, int WPB, int GS>
+hipError_t skinny_launch_g(const SmallPlan &p, int groups, const void *x, const int32_t *wt, const void *sc,
+                           void *out, int M, int64_t N, int64_t K, void *ws, hipStream_t stream) {
+    return launch_gemm(w4a16_skinny_kernel<WAVES, WPB, kSkinnyDepth, GS>,
+                       dim3((uint32_t)((int64_t)groups * p.splits)), dim3(64 * WAVES),
+                       skinny_lds_bytes(M, p.S, WAVES), stream,
+                       (const uint16_t *)x, (const uint4 *)wt, (const uint16_t *)sc, (uint16_t *)out,
+                       ws_counters(ws), (float *)ws_partials(ws), M, (int)N, (int)K, p.splits, p.S, groups);
+}
+
 template <int GS>
 hipError_t skinny_launch(const SmallPlan &p, const void *x, const int32_t *wt, const void *sc, void *out,
                          int M, int64_t N, int64_t K, void *ws, hipStream_t stream) {
     const SkinnyShape sh = skinny_shape<GS>(p, M, N);
-    switch (sh.waves) {
-    case 16: return skinny_launch_w<16, GS>(p, sh.bpw, x, wt, sc, out, M, N, K, ws, stream);
-    case 8: return skinny_launch_w<8, GS>(p, sh.bpw, x, wt, sc, out, M, N, K, ws, stream);
-    default: return skinny_launch_w<4, GS>(p, sh.bpw, x, wt, sc, out, M, N, K, ws, stream);
+    const int g = sh.groups;
+#define SVQ_SKINNY(W, P) return skinny_launch_g<W, P, GS>(p, g, x, wt, sc, out, M, N, K, ws, stream)
+    if (sh.waves == 16) {
+        switch (sh.wpb) {
+        case 16: SVQ_SKINNY(16, 16);
+        case 8: SVQ_SKINNY(16, 8);
+        case 5: SVQ_SKINNY(16, 5);
+        case 4: SVQ_SKINNY(16, 4);
+        case 3: SVQ_SKINNY(16, 3);
+        default: SVQ_SKINNY(16, 2);
+        }
     }
+    if (sh.waves == 8) {
+        switch (sh.wpb) {
+        case 8: SVQ_SKINNY(8, 8);
+        case 4: SVQ_SKINNY(8, 4);
+        default: SVQ_SKINNY(8, 2);
+        }
+    }
+    switch (sh.wpb) {
+    case 4: SVQ_SKINNY(4, 4);
+    case 2: SVQ_SKINNY(4, 2);
+    default: SVQ_SKINNY(4, 1);
+    }
+#undef SVQ_SKINNY
 }
 
 template <int MBW, int WR, int WC, int CT, int GS>

@@ -954,7 +954,7 @@ def record_profile(dirs, command):
         ff, wf = copy_kib / med(cfetch), copy_kib / med(cwrite)
         fk, wk = sum(fetch) / len(fetch), sum(write) / len(write)
         rec = {"kernel": kname, "kernel_source_sha": sha, "fetch_kib_per_dispatch": round(fk, 1),
-               "write_kib_per_dispatch": round(wk, 1), "fetch_factor": round(ff, 3), "write_factor": round(wf, 3),
+               "write_kib_per_dispatch": round(wk, 1), "fetch_factor": round(ff, 5), "write_factor": round(wf, 5),
                "dispatches": len(fetch), "bytes_per_launch": int(round((fk * ff + wk * wf) * 1024))}
         with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as f:
             json.dump({DOMINANT: rec}, f, indent=2)

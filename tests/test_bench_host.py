@@ -40,10 +40,12 @@ def test_committed_traffic_record_is_consistent():
     with open(os.path.join(ROOT, "profiles", "traffic.json")) as f:
         t = json.load(f)[bench.DOMINANT]
     assert t["kernel"] == "w4a16_dot2_kernel"
-    # bytes = (FETCH_SIZE x fetch factor + WRITE_SIZE x write factor) KiB, the
-    # KiB figures rounded to 0.1 in the record
+    # bytes = (FETCH_SIZE x fetch factor + WRITE_SIZE x write factor) KiB, from
+    # the unrounded figures: the record rounds the KiB to 0.1 and the factors to
+    # 0.001 (or finer)
     est = (t["fetch_kib_per_dispatch"] * t["fetch_factor"] + t["write_kib_per_dispatch"] * t["write_factor"]) * 1024
-    slack = 0.05 * (t["fetch_factor"] + t["write_factor"]) * 1024
+    slack = (0.05 * (t["fetch_factor"] + t["write_factor"])
+             + 0.0005 * (t["fetch_kib_per_dispatch"] + t["write_kib_per_dispatch"])) * 1024
     assert abs(t["bytes_per_launch"] - est) <= slack
     # measured traffic of a streaming kernel cannot be below its algorithmic bytes
     N, K, G = 6144, 5120, 128

@@ -349,7 +349,26 @@ def run_record(torch):
     clk = getattr(props, "clock_rate", None)
     if clk:
         rec["max_shader_clock_mhz"] = round(clk / 1000.0, 1)
+    clocks = gpu_clocks()
+    if clocks:
+        rec["clocks"] = clocks
     return rec
+
+
+def gpu_clocks():
+    """Current clock levels of the first GPU as rocm-smi reports them (sclk, mclk,
+    fclk, ...), or None where rocm-smi is missing or says nothing parseable."""
+    import subprocess
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=20)
+        d = json.loads(r.stdout[r.stdout.index("{"):]) if "{" in r.stdout else {}
+    except Exception:
+        return None
+    for card in sorted(d):
+        vals = {k: v for k, v in d[card].items() if isinstance(v, str) and "clock" in k.lower()}
+        if vals:
+            return vals
+    return None
 
 
 # ---- CPU oracle --------------------------------------------------------------------------

@@ -356,19 +356,27 @@ def run_record(torch):
 
 
 def gpu_clocks():
-    """Current clock levels of the first GPU as rocm-smi reports them (sclk, mclk,
-    fclk, ...), or None where rocm-smi is missing or says nothing parseable."""
+    """The first GPU's supported shader and memory clock levels in MHz, as
+    rocm-smi lists them (the highest shader level is the peak figures' clock),
+    or None where rocm-smi is missing or prints nothing parseable."""
+    import re
     import subprocess
     try:
-        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=20)
-        d = json.loads(r.stdout[r.stdout.index("{"):]) if "{" in r.stdout else {}
+        txt = subprocess.run(["rocm-smi", "--showclkfrq"], capture_output=True, text=True, timeout=20).stdout
     except Exception:
         return None
-    for card in sorted(d):
-        vals = {k: v for k, v in d[card].items() if isinstance(v, str) and "clock" in k.lower()}
-        if vals:
-            return vals
-    return None
+    out, cur = {}, None
+    for line in txt.splitlines():
+        if "GPU[0]" not in line:
+            continue
+        m = re.search(r"Supported (\w+) frequencies", line)
+        if m:
+            cur = m.group(1)
+            continue
+        m = re.search(r":\s*\d+:\s*(\d+)\s*Mhz", line)
+        if m and cur:
+            out.setdefault(cur + "_levels_mhz", []).append(int(m.group(1)))
+    return out or None
 
 
 # ---- CPU oracle --------------------------------------------------------------------------

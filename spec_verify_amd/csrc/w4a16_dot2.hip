@@ -311,7 +311,16 @@ bool plan_narrow(int M, int64_t N, int64_t K, int cus, int per_cu, NarrowPlan &p
     const int64_t target = (int64_t)cus * per_cu;
     const int64_t upw = (units + target - 1) / target;
     if (upw > 16) return false;
-    const int64_t wpu = std::min<int64_t>(16 / upw, TG);
+    // Few waves per unit: a workgroup of fewer waves is dispatched sooner (a
+    // timeline of the N = 1024 GEMV showed workgroup starts spread over 1.3 us
+    // at 10 waves each), so the most waves is not the fastest: M = 1, K = 5120,
+    // N = 1024 takes 3.35 us at 4 waves (three loads each) against 3.77 at 10,
+    // 3.39 at 3 and 3.8 at 2 (where each thread stages twice the x). At least
+    // as many as keep each wave at eight loads and the x stage at four chunks
+    // per thread.
+    const int64_t lo = std::max<int64_t>((TG + 7) / 8, (M * TG * TPL * 16 + kNarrowXChunks * 64 * upw - 1) /
+                                                            (kNarrowXChunks * 64 * upw));
+    const int64_t wpu = std::min<int64_t>(std::min<int64_t>(16 / upw, TG), std::max<int64_t>(4, lo));
     const int64_t lpw = (TG + wpu - 1) / wpu;
     if (lpw > 8) return false;
     const int64_t waves = upw * wpu;

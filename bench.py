@@ -361,8 +361,16 @@ def gpu_clocks():
     or None where rocm-smi is missing or prints nothing parseable."""
     import re
     import subprocess
+    import shutil
+    smi = shutil.which("rocm-smi") or "/opt/rocm/bin/rocm-smi"
+    if not os.path.exists(smi):
+        return None
     try:
-        txt = subprocess.run(["rocm-smi", "--showclkfrq"], capture_output=True, text=True, timeout=20).stdout
+        # the script run by this interpreter directly: its "#!/usr/bin/env"
+        # line would exec a second program from a process a profiler may have
+        # attached to the GPU already
+        txt = subprocess.run([sys.executable, os.path.realpath(smi), "--showclkfrq"], capture_output=True,
+                             text=True, timeout=20).stdout
     except Exception:
         return None
     out, cur = {}, None
@@ -953,11 +961,14 @@ def record_profile(dirs, command):
     grid, threads, _ = svq.launch_geometry(OPS[w["op"]], w["M"], w["N"], w["K"], group(w))
     kname = svq.kernel_name(OPS[w["op"]], w["M"], w["N"], w["K"], group(w))
     items = grid * threads
+    # the kernel's own instantiation: its last template argument is log2(G) (the
+    # same launch shape also runs the G = 32 / 64 instantiations)
+    inst = ", %d>" % (group(w).bit_length() - 1)
     durs, fetch, write, cfetch, cwrite = [], [], [], [], []
     copy_kib = (1 << 30) / 1024
     for _, disp, pmc in _rocpd_rows(dirs):
         for did, (name, n, dur) in disp.items():
-            mine = kname in name and n == items
+            mine = kname in name and n == items and inst in name
             if did in pmc:
                 c = pmc[did]
                 if mine:

@@ -24,7 +24,8 @@
 // 6.41 us for the same 26 MB in tiles, at N = K = 5120 in the M = 1 launch shape).
 // The three kernels mirror the W4A16 ones: a VALU dot2 kernel
 // with a row broadcast of x for M <= 8, a one-MFMA-tile kernel for M <= 16, and
-// the persistent stream-K MFMA kernel with LDS-staged x for larger M.
+// the split-K MFMA kernel with LDS-staged x for larger M (shared tiles'
+// partials summed by a second launch).
 #include "svq_dma.h"
 #include "svq_launch.h"
 #include "svq_streamk.h"

@@ -73,11 +73,13 @@ struct WidePlan {
 WidePlan plan_w4a16_wide(int64_t M, int64_t N, int64_t K, int num_cus);
 WidePlan plan_mxfp8_wide(int64_t M, int64_t N, int64_t K, int num_cus);
 
-// Schedule of the small-M kernels: one workgroup per (16-column block, K range
-// of S 128-row tiles); `splits` ranges per column block (1 unless the matrix has
-// too few column blocks to occupy the chip). The launcher picks the workgroup
-// size: the largest of 16, 8 or 4 waves for which the whole grid is resident at
-// once on `cus` compute units.
+// Schedule of the small-M kernels: each 16-column block's K range is cut into
+// `splits` ranges of S 128-row tiles (1 unless the matrix has too few column
+// blocks to occupy the chip). Each launcher maps (block, range) pairs to
+// workgroups and picks their size: the dot2 kernels one pair per workgroup
+// with the largest of 16, 8 or 4 waves for which the whole grid is resident on
+// `cus` compute units; the narrow kernel 4-column units over all of K; the
+// skinny kernels one or more blocks per workgroup (see their launchers).
 struct SmallPlan {
     int splits, S, cus;
     size_t workspace_bytes;  // arrival counters + fp32 partials (0 if splits == 1)

@@ -123,9 +123,10 @@ __global__ __launch_bounds__(64 * WAVES) void w4a16_dot2_kernel(
 // kernel above would leave three quarters of the CUs idle, and splitting K
 // across workgroups costs a cross-workgroup handoff). The work unit is 4
 // output columns over all of K, so N/4 units spread over all the CUs with no
-// split of K. Measured on the MI355X, M = 1, K = 5120: N = 1024 takes 4.4 us
-// against 5.0 us for the block kernel; with N >= 16 x CUs the block kernel is
-// as fast or faster, so it keeps those shapes.
+// split of K. Measured on the MI355X, M = 1, K = 5120: N = 1024 took 4.4 us
+// against 5.0 us for the block kernel when this kernel was introduced (3.35 us
+// now, with four waves per unit); with N >= 16 x CUs the block kernel is as
+// fast or faster, so it keeps those shapes.
 //  * A workgroup owns `upw` consecutive units; `wpu` waves share each unit's
 //    128-row tiles, four tiles per load: lane l reads the 16 bytes of tile
 //    4g + l/16 that hold rows 32*((l/4)%4).. of the unit's column l%4 (four

@@ -292,3 +292,17 @@ def test_noalloc_entry_point_validation_without_a_gpu(L):
     assert L.svq_w4a16_gemm_noalloc(FAKE, FAKE2, FAKE3, FAKE4, 0, 5120, 5120, 128, None) == 2
     assert L.svq_w4a16_gemm_noalloc(FAKE, FAKE2, FAKE3, FAKE4, 1, 5120, 5120, 16, None) == 3
     assert L.svq_w4a16_gemm_noalloc(FAKE, FAKE2, FAKE3, FAKE4, 256, 40960, 5120, 128, None) == 8
+
+
+def test_narrow_plan_waves_per_unit(L):
+    """The narrow-unit GEMV's plan (no device here: 256 CUs assumed): one 4-column
+    unit per workgroup at N = 1024, at most four waves per unit, more only where
+    eight four-tile loads per wave or four x chunks per thread would not cover K."""
+    g, t, l = ctypes.c_uint64(), ctypes.c_uint32(), ctypes.c_size_t()
+    geo = lambda M, N, K, G: (L.svq_launch_geometry(1, 1, M, N, K, G, ctypes.byref(g), ctypes.byref(t),
+                                                    ctypes.byref(l)), g.value, t.value)
+    assert geo(1, 1024, 5120, 128) == (0, 256, 256)      # 10 load groups: 4 waves of 3
+    assert geo(1, 1024, 1280, 128) == (0, 256, 192)      # 3 load groups: 3 waves
+    assert geo(1, 1024, 17408, 128) == (0, 256, 576)     # 34 groups: x needs 9 waves
+    assert geo(1, 4080, 5120, 64) == (0, 255, 1024)      # 4 units per workgroup x 4 waves
+    assert L.svq_w4a16_kernel_name(1, 1, 1024, 5120, 128) == b"w4a16_narrow_kernel"

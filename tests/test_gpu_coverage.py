@@ -1,11 +1,11 @@
 """GPU coverage of the launch paths through the C ABI: the automatic kernel choice
-over a sweep of M, the shortest K every kernel accepts, the cross-workgroup
-reduction's give-up path, and guard bytes around the workspace and the output.
+over a sweep of M, the shortest K every kernel accepts, output tiles shared by
+several workgroups of the wide kernels (their fp32 partials summed by a second
+launch), guard bytes around the workspace and the output, and the probes.
 
 Every result is compared with the CPU oracle (fp64 and fp32-sequential sums)
-under the parity gate max|err| <= 2e-2 * RMS(ref); repeated or fallback runs must
-also be bit-identical to the normal run, since all reductions run in a fixed
-order whichever workgroup performs them.
+under the parity gate max|err| <= 2e-2 * RMS(ref); repeated runs must also be
+bit-identical, since all reductions run in a fixed order.
 """
 import os
 import sys

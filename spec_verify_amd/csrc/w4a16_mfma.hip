@@ -28,6 +28,28 @@
 
 namespace svq {
 
+// Scale words of the NG groups of one K tile (G = 128 / NG): v is, in lane row
+// g, the word of group g (rows past NG repeat groups); on return o[q] holds in
+// every row the word of row q. Two permlane swaps for NG = 2, three for NG = 4.
+template <int NG>
+__device__ __forceinline__ void group_scale_words(uint32_t v, uint32_t (&o)[NG]) {
+    if constexpr (NG == 1) {
+        o[0] = v;
+    } else {
+        // rows (0, 1, 0, 1) and (2, 3, 2, 3)
+        const auto a = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+        // row 0 and row 1 in every row
+        const auto c = __builtin_amdgcn_permlane16_swap(a[0], a[0], false, false);
+        o[0] = c[0];
+        o[1] = c[1];
+        if constexpr (NG == 4) {
+            const auto e = __builtin_amdgcn_permlane16_swap(a[1], a[1], false, false);
+            o[2] = e[0];
+            o[3] = e[1];
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Skinny kernel: M <= 16, one 16-row MFMA tile (MFMA rows >= M repeat row M-1
 // and their results are dropped). A workgroup owns BPW consecutive 16-column
@@ -68,8 +90,10 @@ __global__ __launch_bounds__(64 * WAVES) void w4a16_skinny_kernel(
     const __amdgpu_buffer_rsrc_t wr = make_rsrc(wt + (size_t)nb * KT * 64, (uint32_t)KT * 1024);
     const __amdgpu_buffer_rsrc_t sr = make_rsrc(sc + nb * 16, (uint32_t)(((size_t)(K >> GSHIFT) * N - nb * 16) * 2));
     const uint32_t w_vo = lane * 16;
-    // the aligned dword holding this lane's fp16 scale; s_sh selects the half
-    const uint32_t s_vo = (r & 14) * 2;
+    // the aligned dword holding this lane's fp16 scale; s_sh selects the half.
+    // One load per tile brings the scales of all NG groups: lane row g loads
+    // group g mod NG, and group_scale_words hands every row all of them.
+    const uint32_t s_vo = (r & 14) * 2 + (uint32_t)(g & (NG - 1)) * (uint32_t)N * 2u;
     const int s_sh = (r & 1) * 16;
     // this workgroup's K range: tiles [kbeg, kbeg + kcnt) of the column block
     const int kbeg = sp * S;
@@ -78,12 +102,12 @@ __global__ __launch_bounds__(64 * WAVES) void w4a16_skinny_kernel(
     const uint4 bneg = make_uint4(kBf16Neg136Pair, kBf16Neg136Pair, kBf16Neg136Pair, kBf16Neg136Pair);
 
     uint4 wA[D], wB[D];
-    uint32_t sA[D][NG], sB[D][NG];
+    uint32_t sA[D], sB[D];
 #define SVQ_LOAD(W, SS, I0)                                                          \
     _Pragma("unroll") for (int d = 0; d < D; ++d) if ((I0) + d < ntile) {            \
         const int kt = kbeg + wsub + ((I0) + d) * wpb;                               \
         W[d] = bload16(wr, w_vo, kt * 1024);                                         \
-        _Pragma("unroll") for (int q = 0; q < NG; ++q) SS[d][q] = bload4(sr, s_vo, (kt * NG + q) * N * 2); \
+        SS[d] = bload4(sr, s_vo, kt * NG * N * 2);                                   \
     }
     // stage x[0..M)[128*kbeg, 128*(kbeg+kcnt)) in LDS by DMA (one 64-chunk
     // segment of a row per instruction); rows padded by 16 bytes so that the
@@ -105,7 +129,7 @@ __global__ __launch_bounds__(64 * WAVES) void w4a16_skinny_kernel(
     {
         const int na = ntile < D ? ntile : D;
         const int nb2 = ntile - D < 0 ? 0 : (ntile - D < D ? ntile - D : D);
-        wait_vmcnt_at_most<2 * D * (1 + NG)>((na + nb2) * (1 + NG));
+        wait_vmcnt_at_most<4 * D>((na + nb2) * 2);
     }
     // a bare barrier: __syncthreads() would also wait for the weight prefetch
     __builtin_amdgcn_s_barrier();
@@ -127,6 +151,8 @@ __global__ __launch_bounds__(64 * WAVES) void w4a16_skinny_kernel(
         _Pragma("unroll") for (int d = 0; d < D; ++d) {                              \
             if ((I0) + d < ntile) {                                                  \
                 const uint8_t *ap = abase + (wsub + ((I0) + d) * wpb) * 256;         \
+                uint32_t sw[NG];                                                     \
+                group_scale_words<NG>(SS[d], sw);                                    \
                 _Pragma("unroll") for (int q = 0; q < NG; ++q) {                     \
                     f32x4 P = {0.f, 0.f, 0.f, 0.f};                                  \
                     _Pragma("unroll") for (int jj = 0; jj < SPG; ++jj) {             \
@@ -135,7 +161,7 @@ __global__ __launch_bounds__(64 * WAVES) void w4a16_skinny_kernel(
                         P = mfma16x16x32(A, bneg, P);                                \
                         P = mfma16x16x32(A, word_to_bf16x8(wj[d][j]), P);            \
                     }                                                                \
-                    const float sf = fp16_bits_to_f32((uint16_t)(SS[d][q] >> s_sh));           \
+                    const float sf = fp16_bits_to_f32((uint16_t)(sw[q] >> s_sh));              \
                     _Pragma("unroll") for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(sf, P[i], acc[i]); \
                 }                                                                    \
             }                                                                        \

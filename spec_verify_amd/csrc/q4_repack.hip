@@ -20,28 +20,36 @@ __device__ __forceinline__ uint32_t gptq_to_slot_order(uint32_t v) {
     return r;
 }
 
-// Thread (row j of the GPTQ array, column n): n is fastest, so reads coalesce.
+// The 16 bytes lane l of tile (nb, kt) owns: the words of GPTQ rows
+// 4q .. 4q+3 of column n, q = 4*kt + l/16, n = 16*nb + l%16, word i in slot i.
+__device__ __forceinline__ uint4 repack_quad(const uint32_t *__restrict__ src, int64_t q, int64_t n,
+                                             int64_t ld) {
+    const uint32_t *p = src + 4 * q * ld + n;
+    return make_uint4(gptq_to_slot_order(p[0]), gptq_to_slot_order(p[ld]),
+                      gptq_to_slot_order(p[2 * ld]), gptq_to_slot_order(p[3 * ld]));
+}
+
+// Thread (quad q of GPTQ word rows, column n), n fastest: the four word reads
+// coalesce across the wave, and the wave writes 256-byte runs of whole lane
+// slots (four 4-byte stores per slot, each from another workgroup, doubled the
+// written bytes: 89 MB for 44.6 MB at K = 5120, N = 17408).
 __global__ __launch_bounds__(256) void q4_repack_kernel(const uint32_t *__restrict__ src,
-                                                       uint32_t *__restrict__ dst, int64_t N,
-                                                       int64_t K8, int64_t KT) {
+                                                       uint4 *__restrict__ dst, int64_t N,
+                                                       int64_t K32, int64_t KT) {
     const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (idx >= K8 * N) return;
-    const int64_t j = idx / N;         // GPTQ word row: rows 8j..8j+7
-    const int64_t n = idx - j * N;
-    const int64_t kt = j >> 4;         // 16 word rows per 128-row tile
-    const int64_t r = j & 15;          // = 4 * (row group) + word index
-    const int64_t nb = n >> 4;
-    const int64_t lane = (r >> 2) * 16 + (n & 15);
-    const int64_t w = ((nb * KT + kt) * 64 + lane) * 4 + (r & 3);
-    dst[w] = gptq_to_slot_order(src[idx]);
+    if (idx >= K32 * N) return;
+    const int64_t q = idx / N;         // GPTQ word rows 4q..4q+3 = K rows 32q..32q+31
+    const int64_t n = idx - q * N;
+    const int64_t lane = (q & 3) * 16 + (n & 15);
+    dst[((n >> 4) * KT + (q >> 2)) * 64 + lane] = repack_quad(src, q, n, N);
 }
 
 hipError_t launch_q4_repack(const int32_t *src, int32_t *dst, int64_t N, int64_t K,
                             hipStream_t stream) {
-    const int64_t total = (K / 8) * N;
+    const int64_t total = (K / 32) * N;
     const int64_t blocks = (total + 255) / 256;
     hipLaunchKernelGGL(q4_repack_kernel, dim3((uint32_t)blocks), dim3(256), 0, stream,
-                       (const uint32_t *)src, (uint32_t *)dst, N, K / 8, K / 128);
+                       (const uint32_t *)src, (uint4 *)dst, N, K / 32, K / 128);
     return hipGetLastError();
 }
 
@@ -52,9 +60,9 @@ hipError_t launch_q4_repack(const int32_t *src, int32_t *dst, int64_t N, int64_t
 // column-block-major and every width is a multiple of 16, part p's tiles are
 // its own repack placed at word col_off[p]*K/8; its scales are columns
 // col_off[p].. of the fused [K/G][N] array. One launch covers all parts: part p
-// owns workgroups [blk_off[p], blk_off[p+1]), one thread per GPTQ word (int4)
-// or per 16 bytes of int8 codes, the threads below (K/G)*N_p also moving one
-// scale each.
+// owns workgroups [blk_off[p], blk_off[p+1]), one thread per 16-byte lane slot
+// (four GPTQ words, int4) or per 16 bytes of int8 codes, the threads below
+// (K/G)*N_p also moving one scale each (K/G <= K/32 slots per column).
 struct FuseTable {
     const void *w[kMaxFuseParts];
     const uint16_t *s[kMaxFuseParts];
@@ -73,13 +81,12 @@ __global__ __launch_bounds__(256) void fuse_pack_kernel(FuseTable t, void *__res
     const int64_t n0 = t.col_off[p], Np = t.col_off[p + 1] - n0, Nt = t.col_off[t.parts];
     const int64_t idx = (b - t.blk_off[p]) * 256 + threadIdx.x;
     if (BITS == 4) {
-        const int64_t K8 = K / 8, KT = K / 128;
-        if (idx < K8 * Np) {
-            const int64_t j = idx / Np, n = idx - j * Np;
-            const int64_t nf = n0 + n, r = j & 15, kt = j >> 4;
-            const int64_t lane = (r >> 2) * 16 + (nf & 15);
-            const int64_t w = (((nf >> 4) * KT + kt) * 64 + lane) * 4 + (r & 3);
-            ((uint32_t *)dst_w)[w] = gptq_to_slot_order(((const uint32_t *)t.w[p])[idx]);
+        const int64_t K32 = K / 32, KT = K / 128;
+        if (idx < K32 * Np) {
+            const int64_t q = idx / Np, n = idx - q * Np, nf = n0 + n;
+            const int64_t lane = (q & 3) * 16 + (nf & 15);
+            ((uint4 *)dst_w)[((nf >> 4) * KT + (q >> 2)) * 64 + lane] =
+                repack_quad((const uint32_t *)t.w[p], q, n, Np);
         }
     } else {
         if (idx < Np * (K / 16))
@@ -100,7 +107,7 @@ hipError_t launch_fuse_pack(int bits, const void *const *w, const void *const *s
     for (int p = 0; p < parts; ++p) {
         t.w[p] = w[p];
         t.s[p] = (const uint16_t *)s[p];
-        const int64_t items = bits == 4 ? (K / 8) * widths[p] : widths[p] * (K / 16);
+        const int64_t items = bits == 4 ? (K / 32) * widths[p] : widths[p] * (K / 16);
         t.col_off[p + 1] = t.col_off[p] + widths[p];
         t.blk_off[p + 1] = t.blk_off[p] + (items + 255) / 256;
     }

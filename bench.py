@@ -296,18 +296,29 @@ def mfma_floor(torch, svq, w, geometry):
     per_wave = -(-per_wave // 8) * 8
     sink = torch.zeros(max(grid, 1), dtype=torch.float32, device="cuda:0")
     us = med(time_trials(torch, lambda i: svq.mfma_probe(grid, threads, per_wave, sink), MIN_LAUNCHES))
-    tfl = per_wave * waves * 16 * 16 * 32 * 2 / (us * 1e-6) / 1e12
-    return {"shape": [grid, threads], "mfma_per_wave": per_wave, "us": round(us, 3), "TFLOPs": round(tfl, 1)}
+    # random activation-like A and 128 + q B operands: the chip clocks lower under real data
+    us_r = med(time_trials(torch, lambda i: svq.mfma_probe(grid, threads, per_wave, sink, random_operands=True),
+                           MIN_LAUNCHES))
+    flop = per_wave * waves * 16 * 16 * 32 * 2
+    return {"shape": [grid, threads], "mfma_per_wave": per_wave, "us": round(us, 3),
+            "TFLOPs": round(flop / (us * 1e-6) / 1e12, 1), "us_random": round(us_r, 3),
+            "TFLOPs_random": round(flop / (us_r * 1e-6) / 1e12, 1)}
 
 
 def chip_mfma(torch, svq, cus):
     """The chip's sustained bf16 MFMA rate: the probe with two 8-wave workgroups per CU."""
     grid, threads, per_wave = 2 * cus, 512, 4096
     sink = torch.zeros(grid, dtype=torch.float32, device="cuda:0")
-    us = med(time_trials(torch, lambda i: svq.mfma_probe(grid, threads, per_wave, sink), 50))
-    tfl = grid * 8 * per_wave * 16 * 16 * 32 * 2 / (us * 1e-6) / 1e12
-    return {"shape": [grid, threads], "mfma_per_wave": per_wave, "us": round(us, 2), "TFLOPs": round(tfl, 1),
-            "mfma_frac": round(tfl / MFMA_BF16_PEAK_TFLOPS, 4)}
+    flop = grid * 8 * per_wave * 16 * 16 * 32 * 2
+    out = {"shape": [grid, threads], "mfma_per_wave": per_wave}
+    for key, rnd in (("", False), ("_random", True)):
+        us = med(time_trials(torch, lambda i: svq.mfma_probe(grid, threads, per_wave, sink, random_operands=rnd), 50))
+        tfl = flop / (us * 1e-6) / 1e12
+        # every CU busy: 4096 bf16 flop per clock per CU at the clock the chip held
+        out.update({"us" + key: round(us, 2), "TFLOPs" + key: round(tfl, 1),
+                    "mfma_frac" + key: round(tfl / MFMA_BF16_PEAK_TFLOPS, 4),
+                    "clock_MHz" + key: round(tfl * 1e12 / (cus * 4096) / 1e6)})
+    return out
 
 
 # ---- run record -----------------------------------------------------------------------------
@@ -495,6 +506,7 @@ def workload_table(torch, svq, oracle, names, cus, probe=True):
             if w["M"] > 16:
                 mf = mfma_floor(torch, svq, w, view.geometry)
                 mf["frac"] = round(mf["us"] / us, 4)
+                mf["frac_random"] = round(mf["us_random"] / us, 4)
                 row["mfma_probe"] = mf
         detail.append(row)
         pr = row.get("probe", {})
@@ -502,7 +514,8 @@ def workload_table(torch, svq, oracle, names, cus, probe=True):
         log(f"{n:17s} {row['kernel']:22s} {us:8.2f} {gbs:8.1f} {100 * gbs / HBM_PEAK_GBS:6.1f} "
             f"{pr.get('same_us', 0):7.2f} {100 * pr.get('frac_same', 0):7.1f} {pr.get('best_us', 0):7.2f} "
             f"{100 * pr.get('frac_best', 0):6.1f} {tfl:8.2f} {100 * tfl / MFMA_BF16_PEAK_TFLOPS:6.2f}"
-            + (f"   MFMA probe {mf['us']:.2f} µs ({100 * mf['frac']:.1f}%)" if mf else ""))
+            + (f"   MFMA probe {mf['us']:.2f} µs ({100 * mf['frac']:.1f}%), random operands "
+               f"{mf['us_random']:.2f} µs ({100 * mf['frac_random']:.1f}%)" if mf else ""))
         torch.cuda.empty_cache()
     return detail
 

@@ -390,10 +390,16 @@ int svq_stream_probe(const void *src, size_t bytes, uint32_t grid, uint32_t thre
  * register operands, with no memory traffic: the floor that MFMA issue sets
  * for a kernel doing that many MFMAs per wave in that launch shape (the
  * compute-bound batched-verify case of the autobench page "Qwen3.8-27B · vLLM ·
- * FP8 + MTP"). sink (grid floats, 4-byte aligned) may be written with
+ * FP8 + MTP"). operands: 0 = constant (one small value in every register: the
+ * issue floor at the clock the chip holds when the multipliers' inputs never
+ * change), 1 = random (per chain: A random bf16 like activations, B the bf16 of
+ * 128 + q for random nibbles q, the W4A16 weight operand; the matrix cores'
+ * power draw then lowers the shader clock as real data does); anything else
+ * is SVQ_ERR_DIM. sink (grid floats, 4-byte aligned) may be written with
  * data-dependent values; nothing else is.
  */
-int svq_mfma_probe(uint32_t grid, uint32_t threads, uint32_t per_wave, float *sink, void *stream);
+int svq_mfma_probe(uint32_t grid, uint32_t threads, uint32_t per_wave, int32_t operands, float *sink,
+                   void *stream);
 
 #ifdef __cplusplus
 }

@@ -121,7 +121,7 @@ def lib():
         L.svq_mxfp8_repack.restype = ctypes.c_int
         L.svq_mxfp8_repack.argtypes = [_p, _p, _i64, _i64, _p]
         L.svq_mfma_probe.restype = ctypes.c_int
-        L.svq_mfma_probe.argtypes = [ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32, _p, _p]
+        L.svq_mfma_probe.argtypes = [ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32, _i32, _p, _p]
         L.svq_w4a16_gemm_noalloc.restype = ctypes.c_int
         L.svq_w4a16_gemm_noalloc.argtypes = [_p, _p, _p, _p, _i64, _i64, _i64, _i32, _p]
         _lib = L
@@ -247,12 +247,15 @@ def stream_probe(src, nbytes, grid, threads, sink):
                                   _stream_ptr(src)), "svq_stream_probe")
 
 
-def mfma_probe(grid, threads, per_wave, sink):
+def mfma_probe(grid, threads, per_wave, sink, random_operands=False):
     """per_wave bf16 16x16x32 MFMAs per wave of (grid, threads), no memory
-    traffic; sink is a device tensor of at least grid floats."""
+    traffic; sink is a device tensor of at least grid floats. random_operands
+    selects random activation-like A and 128 + q B operands instead of one
+    constant value (the chip clocks lower under the switching of real data)."""
     if sink.numel() * sink.element_size() < 4 * grid:
         raise ValueError("sink too small")
-    _check(lib().svq_mfma_probe(grid, threads, per_wave, _dev_ptr(sink, "sink"), _stream_ptr(sink)),
+    _check(lib().svq_mfma_probe(grid, threads, per_wave, 1 if random_operands else 0, _dev_ptr(sink, "sink"),
+                                _stream_ptr(sink)),
            "svq_mfma_probe")
 
 

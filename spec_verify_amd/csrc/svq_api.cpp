@@ -504,13 +504,14 @@ int svq_stream_probe(const void *src, size_t bytes, uint32_t grid, uint32_t thre
                                                                                                    : SVQ_ERR_HIP;
 }
 
-int svq_mfma_probe(uint32_t grid, uint32_t threads, uint32_t per_wave, float *sink, void *stream) {
+int svq_mfma_probe(uint32_t grid, uint32_t threads, uint32_t per_wave, int32_t operands, float *sink,
+                   void *stream) {
     if (!sink) return SVQ_ERR_NULL;
     if (grid == 0 || grid > (1u << 24) || threads == 0 || threads > 1024 || threads % 64 || per_wave == 0 ||
-        per_wave % 8 || per_wave > (1u << 24))
+        per_wave % 8 || per_wave > (1u << 24) || (operands != 0 && operands != 1))
         return SVQ_ERR_DIM;
     if (!aligned(sink, 4)) return SVQ_ERR_ALIGN;
-    return launch_mfma_probe(grid, threads, per_wave, sink, (hipStream_t)stream) == hipSuccess ? SVQ_OK
+    return launch_mfma_probe(grid, threads, per_wave, operands, sink, (hipStream_t)stream) == hipSuccess ? SVQ_OK
                                                                                               : SVQ_ERR_HIP;
 }
 

@@ -42,7 +42,8 @@ hipError_t launch_stream_probe(const void *src, size_t bytes, uint32_t grid, uin
                                hipStream_t stream);
 // `per_wave` bf16 16x16x32 MFMAs (a multiple of 8) per wave of (grid, threads);
 // sink holds `grid` floats.
-hipError_t launch_mfma_probe(uint32_t grid, uint32_t threads, uint32_t per_wave, float *sink, hipStream_t stream);
+hipError_t launch_mfma_probe(uint32_t grid, uint32_t threads, uint32_t per_wave, int random, float *sink,
+                             hipStream_t stream);
 
 hipError_t launch_q4_repack(const int32_t *src, int32_t *dst, int64_t N, int64_t K,
                             hipStream_t stream);

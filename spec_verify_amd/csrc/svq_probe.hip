@@ -39,22 +39,67 @@ __global__ __launch_bounds__(1024) void stream_probe_kernel(const uint4 *__restr
 // accumulator chains on register operands, with no memory traffic. Its time is
 // the floor that MFMA issue alone sets for a kernel doing the same number of
 // MFMAs per wave in the same launch shape (batched verify: "FP8 decode is the
-// more compute-bound path", autobench "Qwen3.8-27B · vLLM · FP8 + MTP"). The
-// operands are small bf16 values, so the sums stay finite; their total decides
-// a store to sink[b] that never happens but keeps every MFMA live.
-__global__ __launch_bounds__(1024) void mfma_probe_kernel(uint32_t per_wave, float *__restrict__ sink) {
+// more compute-bound path", autobench "Qwen3.8-27B · vLLM · FP8 + MTP").
+//
+// Two operand sets. Constant: every A and B register holds one small value, so
+// the multipliers' inputs never change. Random: each chain has its own
+// operands, A random bf16 values (random sign and mantissa, magnitude in
+// [2^-2, 2^2)) like activations, B the bf16 of 128 + q for random nibbles q,
+// the W4A16 kernels' weight operand; consecutive MFMAs then switch every input
+// bit the data switches. The matrix cores' power draw depends on that
+// switching, and the chip lowers its shader clock under it, so the random set
+// gives the floor for real data. Either way the accumulator totals decide a
+// store to sink[b] that never happens but keeps every MFMA live.
+__device__ __forceinline__ uint32_t probe_mix(uint32_t x) {
+    x ^= x >> 16;
+    x *= 0x7feb352du;
+    x ^= x >> 15;
+    x *= 0x846ca68bu;
+    x ^= x >> 16;
+    return x;
+}
+
+__global__ __launch_bounds__(1024) void mfma_probe_kernel(uint32_t per_wave, int random, float *__restrict__ sink) {
     const uint32_t lane = threadIdx.x & 63;
-    // bf16 pairs of 2^-4 * (1 + lane/128) and 2^-4: exact, small
-    const uint32_t ha = 0x3D80u + (lane & 15u), hb = 0x3D80u;
-    uint4 a = make_uint4(ha | (ha << 16), ha | (ha << 16), ha | (ha << 16), ha | (ha << 16));
-    const uint4 b = make_uint4(hb | (hb << 16), hb | (hb << 16), hb | (hb << 16), hb | (hb << 16));
-    asm volatile("" : "+v"(a.x), "+v"(a.y), "+v"(a.z), "+v"(a.w));
+    uint4 a[8], b[8];
+    if (!random) {
+        // bf16 pairs of 2^-4 * (1 + lane/128) and 2^-4: exact, small
+        const uint32_t ha = 0x3D80u + (lane & 15u), hb = 0x3D80u;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            a[j] = make_uint4(ha | (ha << 16), ha | (ha << 16), ha | (ha << 16), ha | (ha << 16));
+            b[j] = make_uint4(hb | (hb << 16), hb | (hb << 16), hb | (hb << 16), hb | (hb << 16));
+        }
+    } else {
+        const uint32_t seed = (blockIdx.x * 1024u + threadIdx.x) * 64u;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            uint32_t wa[4], wb[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t h = probe_mix(seed + (uint32_t)(8 * j + 2 * e));
+                const uint32_t k = probe_mix(seed + (uint32_t)(8 * j + 2 * e + 1));
+                // sign and 7 mantissa bits from the hash, exponent 125..128
+                const uint32_t lo = (h & 0x807Fu) | ((0x7Du + ((h >> 8) & 3u)) << 7);
+                const uint32_t hi = ((h >> 16) & 0x807Fu) | ((0x7Du + ((h >> 24) & 3u)) << 7);
+                wa[e] = lo | (hi << 16);
+                wb[e] = (0x4300u | (k & 15u)) | ((0x4300u | ((k >> 16) & 15u)) << 16);
+            }
+            a[j] = make_uint4(wa[0], wa[1], wa[2], wa[3]);
+            b[j] = make_uint4(wb[0], wb[1], wb[2], wb[3]);
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        asm volatile("" : "+v"(a[j].x), "+v"(a[j].y), "+v"(a[j].z), "+v"(a[j].w));
+        asm volatile("" : "+v"(b[j].x), "+v"(b[j].y), "+v"(b[j].z), "+v"(b[j].w));
+    }
     f32x4 acc[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
     for (uint32_t i = 0; i < per_wave; i += 8) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[j] = mfma16x16x32(a, b, acc[j]);
+        for (int j = 0; j < 8; ++j) acc[j] = mfma16x16x32(a[j], b[j], acc[j]);
     }
     float t = 0.f;
 #pragma unroll
@@ -62,8 +107,9 @@ __global__ __launch_bounds__(1024) void mfma_probe_kernel(uint32_t per_wave, flo
     if (t == -1.0f) sink[blockIdx.x] = t;
 }
 
-hipError_t launch_mfma_probe(uint32_t grid, uint32_t threads, uint32_t per_wave, float *sink, hipStream_t stream) {
-    hipLaunchKernelGGL(mfma_probe_kernel, dim3(grid), dim3(threads), 0, stream, per_wave, sink);
+hipError_t launch_mfma_probe(uint32_t grid, uint32_t threads, uint32_t per_wave, int random, float *sink,
+                             hipStream_t stream) {
+    hipLaunchKernelGGL(mfma_probe_kernel, dim3(grid), dim3(threads), 0, stream, per_wave, random, sink);
     return hipGetLastError();
 }
 

@@ -275,14 +275,16 @@ def test_launch_geometry_and_stream_probe_validation(L):
     assert L.svq_stream_probe(FAKE, 1 << 20, 256, 2048, FAKE2, None) == 2
     assert L.svq_stream_probe(FAKE + 8, 1 << 20, 256, 256, FAKE2, None) == 6
     assert L.svq_stream_probe(FAKE, 1 << 20, 256, 256, FAKE + 64, None) == 7   # sink inside src
-    assert L.svq_mfma_probe(256, 512, 64, None, None) == 1
-    assert L.svq_mfma_probe(0, 512, 64, FAKE2, None) == 2
-    assert L.svq_mfma_probe(256, 96, 64, FAKE2, None) == 2               # threads % 64
-    assert L.svq_mfma_probe(256, 2048, 64, FAKE2, None) == 2
-    assert L.svq_mfma_probe(256, 512, 0, FAKE2, None) == 2
-    assert L.svq_mfma_probe(256, 512, 12, FAKE2, None) == 2              # not a multiple of 8
-    assert L.svq_mfma_probe(256, 512, 1 << 25, FAKE2, None) == 2
-    assert L.svq_mfma_probe(256, 512, 64, FAKE2 + 2, None) == 6
+    assert L.svq_mfma_probe(256, 512, 64, 0, None, None) == 1
+    assert L.svq_mfma_probe(0, 512, 64, 0, FAKE2, None) == 2
+    assert L.svq_mfma_probe(256, 96, 64, 0, FAKE2, None) == 2            # threads % 64
+    assert L.svq_mfma_probe(256, 2048, 64, 0, FAKE2, None) == 2
+    assert L.svq_mfma_probe(256, 512, 0, 0, FAKE2, None) == 2
+    assert L.svq_mfma_probe(256, 512, 12, 0, FAKE2, None) == 2           # not a multiple of 8
+    assert L.svq_mfma_probe(256, 512, 1 << 25, 0, FAKE2, None) == 2
+    assert L.svq_mfma_probe(256, 512, 64, 2, FAKE2, None) == 2           # operands: 0 or 1
+    assert L.svq_mfma_probe(256, 512, 64, -1, FAKE2, None) == 2
+    assert L.svq_mfma_probe(256, 512, 64, 1, FAKE2 + 2, None) == 6
 
 
 def test_noalloc_entry_point_validation_without_a_gpu(L):

@@ -332,11 +332,14 @@ def test_stream_probe_reads_every_unit(grid, threads):
 
 
 def test_mfma_probe_runs_and_leaves_the_sink():
-    """The matrix-core probe runs at several shapes; its sums are positive, so
-    the store it guards never happens and the sink keeps its contents."""
+    """The matrix-core probe runs at several shapes with both operand sets. The
+    constant set's sums are positive, and the random set's totals (a fixed
+    function of the shape) are not exactly -1, so the store they guard never
+    happens and the sink keeps its contents."""
     import spec_verify_amd as svq
-    for grid, threads, per_wave in ((1, 64, 8), (204, 512, 856), (256, 1024, 64)):
-        sink = torch.full((grid,), 7.0, dtype=torch.float32, device="cuda")
-        svq.mfma_probe(grid, threads, per_wave, sink)
-        torch.cuda.synchronize()
-        assert bool((sink == 7.0).all()), (grid, threads, per_wave)
+    for random_operands in (False, True):
+        for grid, threads, per_wave in ((1, 64, 8), (204, 512, 856), (256, 1024, 64)):
+            sink = torch.full((grid,), 7.0, dtype=torch.float32, device="cuda")
+            svq.mfma_probe(grid, threads, per_wave, sink, random_operands=random_operands)
+            torch.cuda.synchronize()
+            assert bool((sink == 7.0).all()), (grid, threads, per_wave, random_operands)

@@ -196,7 +196,10 @@ def _sample(M, N, n, seed):
 
 @pytest.mark.parametrize("name", ["tiny", "decode_n5120", "decode_n6144", "decode_n1024",
                                   "verify5_up", "verify5_down", "verify3_up", "verify3_down",
-                                  "batch128_up", "batch128_down"])
+                                  "batch128_up", "batch128_down",
+                                  # the compressed-tensors group sizes at decode, verify and batch shapes
+                                  "decode_n6144_g32", "decode_n6144_g64", "verify5_up_g32",
+                                  "verify5_up_g64", "batch128_up_g32", "batch128_up_g64"])
 def test_w4a16_workloads(name):
     w = synth.WORKLOADS[name]
     _say("w4a16 workload", name, w)
@@ -204,7 +207,7 @@ def test_w4a16_workloads(name):
     out, tiled = run_w4a16(inp)
     # every output against the full oracle (fp64 and fp32-sequential sums); at
     # M = 128 that is 2.2 M outputs per projection, a few seconds on the host
-    y64, y32 = oracle.w4a16(inp.x, inp.qweight, inp.scales)
+    y64, y32 = oracle.w4a16(inp.x, inp.qweight, inp.scales, inp.G)
     assert_gate(out, y64, y32, name)
     # the repacked weights of the full-size run are the oracle's, bit for bit
     np.testing.assert_array_equal(tiled.cpu().numpy(), oracle.q4_repack(inp.qweight))

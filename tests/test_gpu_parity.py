@@ -6,7 +6,7 @@ both the fp64-summed oracle and the fp32-sequential oracle. Integer-valued input
 have one exact answer: outputs must equal bf16_RNE(exact) bit for bit. Repack is
 bit-exact. Small shapes are compared element by element; the full-size
 workloads (in the launch configuration the benchmark times) over every output,
-except the vocabulary heads (N = 248320), which are checked on sampled outputs.
+including the vocabulary heads (N = 248320).
 """
 import os
 import sys
@@ -415,17 +415,16 @@ def test_vocab_head_workloads(name):
     w = synth.WORKLOADS[name]
     _say("vocab workload", name, w)
     inp = synth.gen_workload(name)
-    rows, cols = _sample(inp.M, inp.N, 1500, w["seed"])
+    # every one of the 248320 outputs against the full oracle (about 2.5 GFLOP per
+    # sum order: a few seconds on the host)
     if w["op"] == "w8a16":
         out = host_bits(svq.w8a16_gemm(dev(inp.x), dev(inp.w), dev(inp.scales), 128))
-        y64, y32 = oracle.w8a16_points(inp.x, inp.w, inp.scales, 128, rows, cols)
+        y64, y32 = oracle.w8a16(inp.x, inp.w, inp.scales, 128)
     else:
         out, _ = run_w4a16(inp)
-        y64, y32 = oracle.w4a16_points(inp.x, inp.qweight, inp.scales, 128, rows, cols)
+        y64, y32 = oracle.w4a16(inp.x, inp.qweight, inp.scales, 128)
     torch.cuda.synchronize()
-    ok, err, rms = oracle.gate(out[rows, cols], y64)
-    assert ok, f"{name}: err={err:.4g} rms={rms:.4g}"
-    assert oracle.gate(out[rows, cols], y32.astype(np.float64))[0]
+    assert_gate(out, y64, y32, name)
     assert np.all(np.isfinite(oracle.bf16_bits_to_f64(out)))
 
 

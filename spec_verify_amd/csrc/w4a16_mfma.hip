@@ -62,8 +62,22 @@ __device__ __forceinline__ void group_scale_words(uint32_t v, uint32_t (&o)[NG])
 // would not fit the chip's LDS (the launcher picks BPW). Memory-bound; the
 // MFMA pipe is mostly idle, so the -136 * sum(x) term is also computed on it,
 // by an MFMA against a constant -136 operand.
+//
+// G = 32 / 64 with few rows (PACK > 0): the 16 A-operand rows are split into
+// slots of RS rows, one slot per group, and a lane supplies x row r % RS of its
+// slot's group or zeros, so one MFMA chain leaves several groups' partial sums
+// in different output rows, and a single scale FMA per output element applies
+// the right group's scale (unpacked, every group needs its own chain and one
+// FMA per element). The groups' rows are summed across lane rows once, after
+// the loop. PACK 1 (G = 32: 4 slots of 4 rows, M <= 4; G = 64: 2 slots of 8
+// rows, M <= 8): the words stay as repacked, so in MFMA step j lane row g
+// supplies K-rows 32g + 8j.., of group g (G = 32) or g / 2 (G = 64): lane
+// (r, g) reads x when slot r / RS is that group; one chain per tile. PACK 2
+// (G = 32, M <= 8): transposed words (step j is group j), 2 slots of 8 rows:
+// steps 0 and 1 feed one chain with x in slot j, steps 2 and 3 a second chain
+// likewise. PACK 0: transposed words, one chain per group (any M).
 // ---------------------------------------------------------------------------
-template <int WAVES, int WPB, int D, int GSHIFT>
+template <int WAVES, int WPB, int D, int GSHIFT, int PACK>
 __global__ __launch_bounds__(64 * WAVES) void w4a16_skinny_kernel(
     const uint16_t *__restrict__ x, const uint4 *__restrict__ wt,
     const uint16_t *__restrict__ sc, uint16_t *__restrict__ out, uint32_t *__restrict__ cnt,
@@ -71,7 +85,10 @@ __global__ __launch_bounds__(64 * WAVES) void w4a16_skinny_kernel(
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     constexpr int NG = 128 >> GSHIFT;
     constexpr int SPG = 4 / NG;
-    constexpr bool kTrans = GSHIFT < 7;
+    static_assert(PACK == 0 || (GSHIFT == 5 && (PACK == 1 || PACK == 2)) || (GSHIFT == 6 && PACK == 1),
+                  "packed rows: G = 32 (one or two chains) or G = 64 (one chain)");
+    constexpr bool kTrans = GSHIFT < 7 && PACK != 1;
+    constexpr int RS = (GSHIFT == 5 && PACK == 1) ? 4 : 8;  // rows per slot when packed
     const int lane = threadIdx.x & 63;
     const int wave = wave_id();
     const int r = lane & 15, g = lane >> 4;
@@ -91,9 +108,13 @@ __global__ __launch_bounds__(64 * WAVES) void w4a16_skinny_kernel(
     const __amdgpu_buffer_rsrc_t sr = make_rsrc(sc + nb * 16, (uint32_t)(((size_t)(K >> GSHIFT) * N - nb * 16) * 2));
     const uint32_t w_vo = lane * 16;
     // the aligned dword holding this lane's fp16 scale; s_sh selects the half.
-    // One load per tile brings the scales of all NG groups: lane row g loads
-    // group g mod NG, and group_scale_words hands every row all of them.
-    const uint32_t s_vo = (r & 14) * 2 + (uint32_t)(g & (NG - 1)) * (uint32_t)N * 2u;
+    // Unpacked, one load per tile brings the scales of all NG groups: lane row g
+    // loads group g mod NG, and group_scale_words hands every row all of them.
+    // Packed, lane row g's output rows belong to one group per chain: g (PACK 1,
+    // G = 32), g / 2 (PACK 1, G = 64, and PACK 2's first chain; its second
+    // chain's group is 2 + g / 2, read by a second load)
+    const uint32_t s_grp = PACK == 0 ? (uint32_t)(g & (NG - 1)) : (RS == 4 ? (uint32_t)g : (uint32_t)(g >> 1));
+    const uint32_t s_vo = (r & 14) * 2 + s_grp * (uint32_t)N * 2u;
     const int s_sh = (r & 1) * 16;
     // this workgroup's K range: tiles [kbeg, kbeg + kcnt) of the column block
     const int kbeg = sp * S;
@@ -102,12 +123,13 @@ __global__ __launch_bounds__(64 * WAVES) void w4a16_skinny_kernel(
     const uint4 bneg = make_uint4(kBf16Neg136Pair, kBf16Neg136Pair, kBf16Neg136Pair, kBf16Neg136Pair);
 
     uint4 wA[D], wB[D];
-    uint32_t sA[D], sB[D];
-#define SVQ_LOAD(W, SS, I0)                                                          \
+    uint32_t sA[D], sB[D], sA2[D], sB2[D];
+#define SVQ_LOAD(W, SS, SS2, I0)                                                     \
     _Pragma("unroll") for (int d = 0; d < D; ++d) if ((I0) + d < ntile) {            \
         const int kt = kbeg + wsub + ((I0) + d) * wpb;                               \
         W[d] = bload16(wr, w_vo, kt * 1024);                                         \
         SS[d] = bload4(sr, s_vo, kt * NG * N * 2);                                   \
+        if constexpr (PACK == 2) SS2[d] = bload4(sr, s_vo + 4u * (uint32_t)N, kt * NG * N * 2); \
     }
     // stage x[0..M)[128*kbeg, 128*(kbeg+kcnt)) in LDS by DMA (one 64-chunk
     // segment of a row per instruction); rows padded by 16 bytes so that the
@@ -124,24 +146,39 @@ __global__ __launch_bounds__(64 * WAVES) void w4a16_skinny_kernel(
         }
     }
     // two stages of D tiles (weights and scales) in flight behind the x loads
-    if (ntile > 0) SVQ_LOAD(wA, sA, 0)
-    if (ntile > D) SVQ_LOAD(wB, sB, D)
+    if (ntile > 0) SVQ_LOAD(wA, sA, sA2, 0)
+    if (ntile > D) SVQ_LOAD(wB, sB, sB2, D)
+    // packed rows: 256 zero bytes after the x stage, read by the lanes whose
+    // slot does not hold the group of the step
+    const int zoff = M * xs_stride;
+    if constexpr (PACK > 0) {
+        if (threadIdx.x < 16) *(uint4 *)(smem + zoff + 16 * threadIdx.x) = make_uint4(0, 0, 0, 0);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    }
     {
+        constexpr int LPT = PACK == 2 ? 3 : 2;  // loads per prefetched tile
         const int na = ntile < D ? ntile : D;
         const int nb2 = ntile - D < 0 ? 0 : (ntile - D < D ? ntile - D : D);
-        wait_vmcnt_at_most<4 * D>((na + nb2) * 2);
+        wait_vmcnt_at_most<LPT * 2 * D>((na + nb2) * LPT);
     }
     // a bare barrier: __syncthreads() would also wait for the weight prefetch
     __builtin_amdgcn_s_barrier();
 
     // A operand of MFMA step j for tile i of the range: row min(r, M-1), 8 bf16
     // at K offset 32j + 8g (transposed words) or 32g + 8j
-    const int arow = r < M ? r : M - 1;
+    const int arow = PACK > 0 ? (r % RS < M ? r % RS : M - 1) : (r < M ? r : M - 1);
     const uint8_t *abase = smem + arow * xs_stride + (kTrans ? 16 * g : 64 * g);
     constexpr int kXStep = kTrans ? 64 : 16;
+    // packed rows: whether this lane reads x (rows past M of a slot read zeros):
+    // PACK 1 when its slot holds its lane row's group; PACK 2 in even steps
+    // for slot 0, in odd steps for slot 1
+    const int slot = r / RS;
+    const bool act0 = PACK == 0 || ((r % RS) < M && (PACK == 1 ? slot == (RS == 4 ? g : g >> 1) : slot == 0));
+    const bool act1 = PACK == 2 && (r % RS) < M && slot == 1;
+    const uint8_t *zrow = smem + zoff;
 
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#define SVQ_COMPUTE(W, SS, I0)                                                       \
+#define SVQ_COMPUTE(W, SS, SS2, I0)                                                  \
     {                                                                                \
         uint32_t wj[D][4];                                                           \
         _Pragma("unroll") for (int d = 0; d < D; ++d) {                              \
@@ -151,18 +188,42 @@ __global__ __launch_bounds__(64 * WAVES) void w4a16_skinny_kernel(
         _Pragma("unroll") for (int d = 0; d < D; ++d) {                              \
             if ((I0) + d < ntile) {                                                  \
                 const uint8_t *ap = abase + (wsub + ((I0) + d) * wpb) * 256;         \
-                uint32_t sw[NG];                                                     \
-                group_scale_words<NG>(SS[d], sw);                                    \
-                _Pragma("unroll") for (int q = 0; q < NG; ++q) {                     \
-                    f32x4 P = {0.f, 0.f, 0.f, 0.f};                                  \
-                    _Pragma("unroll") for (int jj = 0; jj < SPG; ++jj) {             \
-                        const int j = q * SPG + jj;                                  \
-                        const uint4 A = *(const uint4 *)(ap + j * kXStep);           \
-                        P = mfma16x16x32(A, bneg, P);                                \
-                        P = mfma16x16x32(A, word_to_bf16x8(wj[d][j]), P);            \
+                if constexpr (PACK == 0) {                                           \
+                    uint32_t sw[NG];                                                 \
+                    group_scale_words<NG>(SS[d], sw);                                \
+                    _Pragma("unroll") for (int q = 0; q < NG; ++q) {                 \
+                        f32x4 P = {0.f, 0.f, 0.f, 0.f};                              \
+                        _Pragma("unroll") for (int jj = 0; jj < SPG; ++jj) {         \
+                            const int j = q * SPG + jj;                              \
+                            const uint4 A = *(const uint4 *)(ap + j * kXStep);       \
+                            P = mfma16x16x32(A, bneg, P);                            \
+                            P = mfma16x16x32(A, word_to_bf16x8(wj[d][j]), P);        \
+                        }                                                            \
+                        const float sf = fp16_bits_to_f32((uint16_t)(sw[q] >> s_sh));          \
+                        _Pragma("unroll") for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(sf, P[i], acc[i]); \
                     }                                                                \
-                    const float sf = fp16_bits_to_f32((uint16_t)(sw[q] >> s_sh));              \
+                } else {                                                             \
+                    const uint8_t *a0 = act0 ? ap : zrow, *a1 = act1 ? ap : zrow;    \
+                    f32x4 P = {0.f, 0.f, 0.f, 0.f}, P2 = {0.f, 0.f, 0.f, 0.f};       \
+                    _Pragma("unroll") for (int j = 0; j < 4; ++j) {                  \
+                        const uint4 B = word_to_bf16x8(wj[d][j]);                    \
+                        if constexpr (PACK == 1) {                                   \
+                            const uint4 A = *(const uint4 *)(a0 + j * kXStep);       \
+                            P = mfma16x16x32(A, bneg, P);                            \
+                            P = mfma16x16x32(A, B, P);                               \
+                        } else {                                                     \
+                            const uint4 A = *(const uint4 *)(((j & 1) ? a1 : a0) + j * kXStep); \
+                            f32x4 &Q = j < 2 ? P : P2;                               \
+                            Q = mfma16x16x32(A, bneg, Q);                            \
+                            Q = mfma16x16x32(A, B, Q);                               \
+                        }                                                            \
+                    }                                                                \
+                    const float sf = fp16_bits_to_f32((uint16_t)(SS[d] >> s_sh));    \
                     _Pragma("unroll") for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(sf, P[i], acc[i]); \
+                    if constexpr (PACK == 2) {                                       \
+                        const float sf2 = fp16_bits_to_f32((uint16_t)(SS2[d] >> s_sh)); \
+                        _Pragma("unroll") for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(sf2, P2[i], acc[i]); \
+                    }                                                                \
                 }                                                                    \
             }                                                                        \
         }                                                                            \
@@ -170,16 +231,31 @@ __global__ __launch_bounds__(64 * WAVES) void w4a16_skinny_kernel(
 
     if (ntile > 0) {
         for (int i0 = 0;; i0 += 2 * D) {
-            SVQ_COMPUTE(wA, sA, i0)
+            SVQ_COMPUTE(wA, sA, sA2, i0)
             if (i0 + D >= ntile) break;
-            SVQ_LOAD(wA, sA, i0 + 2 * D)
-            SVQ_COMPUTE(wB, sB, i0 + D)
+            SVQ_LOAD(wA, sA, sA2, i0 + 2 * D)
+            SVQ_COMPUTE(wB, sB, sB2, i0 + D)
             if (i0 + 2 * D >= ntile) break;
-            SVQ_LOAD(wB, sB, i0 + 3 * D)
+            SVQ_LOAD(wB, sB, sB2, i0 + 3 * D)
         }
     }
 #undef SVQ_LOAD
 #undef SVQ_COMPUTE
+
+    if constexpr (PACK > 0) {
+        // each group's rows sit in another lane row: sum lane rows g and g ^ 2
+        // (and then g ^ 1 when the slots are 4 rows), which leaves output row
+        // 4g + i of the usual layout in lane row g for every valid row
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const auto a = __builtin_amdgcn_permlane32_swap(f32_bits(acc[i]), f32_bits(acc[i]), false, false);
+            acc[i] = bits_f32(a[0]) + bits_f32(a[1]);
+            if constexpr (RS == 4) {
+                const auto c = __builtin_amdgcn_permlane16_swap(f32_bits(acc[i]), f32_bits(acc[i]), false, false);
+                acc[i] = bits_f32(c[0]) + bits_f32(c[1]);
+            }
+        }
+    }
 
     // cross-wave sum of the valid rows through LDS (the x stage is dead now)
     __syncthreads();
@@ -583,14 +659,26 @@ struct SkinnyShape {
     int waves, wpb, groups;
 };
 
-template <int GS>
+// Packed rows for G = 32 / 64 (see the kernel): 1 = one chain, 2 = two chains,
+// 0 = transposed words (G = 128 and larger M).
+inline int skinny_pack(int GS, int M) {
+    if (GS == 5) return M <= 4 ? 1 : M <= 8 ? 2 : 0;
+    if (GS == 6) return M <= 8 ? 1 : 0;
+    return 0;
+}
+// the packed kernels keep 256 zero bytes after the x stage
+inline size_t skinny_lds(int M, int S, int waves, int pack) {
+    return skinny_lds_bytes(M, S, waves) + (pack ? 256 : 0);
+}
+
+template <int GS, int PACK>
 SkinnyShape skinny_shape(const SmallPlan &p, int M, int64_t N) {
-    static const int r16 = resident_blocks(w4a16_skinny_kernel<16, 4, kSkinnyDepth, GS>, 1024);
-    static const int r8 = resident_blocks(w4a16_skinny_kernel<8, 4, kSkinnyDepth, GS>, 512);
-    static const int r4 = resident_blocks(w4a16_skinny_kernel<4, 4, kSkinnyDepth, GS>, 256);
+    static const int r16 = resident_blocks(w4a16_skinny_kernel<16, 4, kSkinnyDepth, GS, PACK>, 1024);
+    static const int r8 = resident_blocks(w4a16_skinny_kernel<8, 4, kSkinnyDepth, GS, PACK>, 512);
+    static const int r4 = resident_blocks(w4a16_skinny_kernel<4, 4, kSkinnyDepth, GS, PACK>, 256);
     const int64_t blocks = N / 16;
     {
-        const int r = std::min(r16, (int)(kLdsPerCu / skinny_lds_bytes(M, p.S, 16)));
+        const int r = std::min(r16, (int)(kLdsPerCu / skinny_lds(M, p.S, 16, PACK)));
         const int64_t groups = std::min<int64_t>(blocks, (int64_t)p.cus / p.splits);
         const int64_t maxblk = groups > 0 ? (blocks + groups - 1) / groups : 0;
         if (r >= 1 && groups >= 1 && maxblk <= 8 && maxblk * M <= 64) {
@@ -602,7 +690,7 @@ SkinnyShape skinny_shape(const SmallPlan &p, int M, int64_t N) {
     int best_wpb = 0, best_bpw = 1;
     for (const int waves : {16, 8, 4}) {
         const int r_occ = waves == 16 ? r16 : waves == 8 ? r8 : r4;
-        const int r = std::min(r_occ, (int)(kLdsPerCu / skinny_lds_bytes(M, p.S, waves)));
+        const int r = std::min(r_occ, (int)(kLdsPerCu / skinny_lds(M, p.S, waves, PACK)));
         // bpw * 16 * M outputs are summed by one thread each: bpw * M <= 4 * waves
         for (int bpw = 1; bpw <= 4 && bpw * M <= 4 * waves; bpw *= 2) {
             if ((blocks + bpw - 1) / bpw * p.splits <= (int64_t)r * p.cus) {
@@ -620,22 +708,22 @@ SkinnyShape skinny_shape(const SmallPlan &p, int M, int64_t N) {
     return best;
 }
 
-template <int WAVES, int WPB, int GS>
+template <int WAVES, int WPB, int GS, int PACK>
 hipError_t skinny_launch_g(const SmallPlan &p, int groups, const void *x, const int32_t *wt, const void *sc,
                            void *out, int M, int64_t N, int64_t K, void *ws, hipStream_t stream) {
-    return launch_gemm(w4a16_skinny_kernel<WAVES, WPB, kSkinnyDepth, GS>,
+    return launch_gemm(w4a16_skinny_kernel<WAVES, WPB, kSkinnyDepth, GS, PACK>,
                        dim3((uint32_t)((int64_t)groups * p.splits)), dim3(64 * WAVES),
-                       skinny_lds_bytes(M, p.S, WAVES), stream,
+                       skinny_lds(M, p.S, WAVES, PACK), stream,
                        (const uint16_t *)x, (const uint4 *)wt, (const uint16_t *)sc, (uint16_t *)out,
                        ws_counters(ws), (float *)ws_partials(ws), M, (int)N, (int)K, p.splits, p.S, groups);
 }
 
-template <int GS>
+template <int GS, int PACK>
 hipError_t skinny_launch(const SmallPlan &p, const void *x, const int32_t *wt, const void *sc, void *out,
                          int M, int64_t N, int64_t K, void *ws, hipStream_t stream) {
-    const SkinnyShape sh = skinny_shape<GS>(p, M, N);
+    const SkinnyShape sh = skinny_shape<GS, PACK>(p, M, N);
     const int g = sh.groups;
-#define SVQ_SKINNY(W, P) return skinny_launch_g<W, P, GS>(p, g, x, wt, sc, out, M, N, K, ws, stream)
+#define SVQ_SKINNY(W, P) return skinny_launch_g<W, P, GS, PACK>(p, g, x, wt, sc, out, M, N, K, ws, stream)
     if (sh.waves == 16) {
         switch (sh.wpb) {
         case 16: SVQ_SKINNY(16, 16);
@@ -690,9 +778,16 @@ hipError_t launch_w4a16_skinny(const SmallPlan &plan, const void *x, const int32
                                const void *scales, void *out, int M, int64_t N, int64_t K, int G,
                                void *workspace, hipStream_t stream) {
     switch (G) {
-    case 32: return skinny_launch<5>(plan, x, wt, scales, out, M, N, K, workspace, stream);
-    case 64: return skinny_launch<6>(plan, x, wt, scales, out, M, N, K, workspace, stream);
-    case 128: return skinny_launch<7>(plan, x, wt, scales, out, M, N, K, workspace, stream);
+    case 32:
+        switch (skinny_pack(5, M)) {
+        case 1: return skinny_launch<5, 1>(plan, x, wt, scales, out, M, N, K, workspace, stream);
+        case 2: return skinny_launch<5, 2>(plan, x, wt, scales, out, M, N, K, workspace, stream);
+        default: return skinny_launch<5, 0>(plan, x, wt, scales, out, M, N, K, workspace, stream);
+        }
+    case 64:
+        return skinny_pack(6, M) ? skinny_launch<6, 1>(plan, x, wt, scales, out, M, N, K, workspace, stream)
+                                 : skinny_launch<6, 0>(plan, x, wt, scales, out, M, N, K, workspace, stream);
+    case 128: return skinny_launch<7, 0>(plan, x, wt, scales, out, M, N, K, workspace, stream);
     default: return hipErrorInvalidValue;
     }
 }

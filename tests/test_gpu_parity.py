@@ -108,6 +108,11 @@ def _ids(cases):
 W4_CASES = (
     [(1, m, K, N, G) for m in (1, 2, 3, 5, 8) for (K, N) in ((512, 48), (1280, 32)) for G in (32, 64, 128)]
     + [(2, m, K, N, G) for m in (1, 3, 5, 11, 16) for (K, N) in ((512, 48), (1280, 32)) for G in (32, 64, 128)]
+    # the skinny kernel's packed rows at G = 32 / 64: every row count at the slot
+    # boundaries (4 rows per slot up to M = 4, 8 rows up to M = 8, unpacked from 9),
+    # and K = 17408 split three ways over workgroups
+    + [(2, m, K, N, G) for m in (2, 4, 6, 7, 8, 9) for (K, N) in ((512, 48), (1280, 32)) for G in (32, 64)]
+    + [(2, m, 17408, 64, G) for m in (1, 4, 5, 8) for G in (32, 64)]
     + [(3, m, K, N, G) for m in (1, 17, 64, 65, 128, 130) for (K, N) in ((1024, 272), (2560, 128)) for G in (32, 128)]
     + [(3, 33, 640, 16, 64)]
     # dot2 with more column blocks than compute units (456, 336 and 576 blocks)

@@ -137,7 +137,7 @@ def test_auto_dispatch_mxfp8_m_sweep(M):
 SMALL_K_W4 = (
     [("dot2", 1, m, N, G) for m in (1, 3, 8) for N in (48,) for G in (32, 64, 128)]
     + [("narrow", 1, m, 1024, G) for m in (1, 2) for G in (32, 128)]
-    + [("skinny", 2, m, 48, G) for m in (5, 16) for G in (32, 64, 128)]
+    + [("skinny", 2, m, 48, G) for m in (2, 5, 8, 16) for G in (32, 64, 128)]
     + [("wide", 3, m, 272, G) for m in (17, 128) for G in (32, 64, 128)]
 )
 

@@ -157,8 +157,8 @@ def test_w4a16_narrow(kernel, M, K, N, G):
 EXTREME_SCALES = np.array([0x0000, 0x0001, 0x0400, 0x7BFF, 0xB800, 0x3C00, 0x8001, 0x03FF], dtype=np.uint16)
 
 
-@pytest.mark.parametrize("kernel,M,N", [(1, 1, 64), (1, 1, 1024), (1, 3, 64), (2, 5, 64), (3, 40, 64)],
-                         ids=["dot2-1", "narrow-1", "dot2-3", "skinny-5", "wide-40"])
+@pytest.mark.parametrize("kernel,M,N", [(1, 1, 64), (1, 1, 1024), (1, 3, 64), (2, 3, 64), (2, 5, 64), (3, 40, 64)],
+                         ids=["dot2-1", "narrow-1", "dot2-3", "skinny-3", "skinny-5", "wide-40"])
 @pytest.mark.parametrize("G", [32, 128])
 def test_w4a16_extreme_scales(kernel, M, N, G):
     _say("w4a16 extreme scales kernel", kernel, "M", M, "N", N, "G", G)
@@ -174,6 +174,8 @@ def test_w4a16_extreme_scales(kernel, M, N, G):
 W4_EXACT = [
     (1, 1, 1024, 32, 128), (1, 5, 1024, 32, 32), (1, 8, 640, 48, 64),
     (2, 1, 1024, 32, 128), (2, 7, 1024, 32, 32), (2, 16, 640, 48, 64),
+    # the skinny kernel's packed rows: 4-row slots (G = 32), 8-row slots (G = 64), two chains (G = 32)
+    (2, 3, 1024, 32, 32), (2, 5, 1024, 48, 64), (2, 8, 640, 32, 32),
     (3, 128, 1024, 272, 128), (3, 40, 1024, 144, 32), (3, 130, 640, 128, 64),
 ]
 
